@@ -1,0 +1,221 @@
+/*
+ * attn_ref.c -- plain fp64 CPU oracle for scaled dot-product attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark may load this library.  It shares no code,
+ * header, table or helper with the GPU path.
+ *
+ * What it computes (the plain definition of attention that FlashAttention-2
+ * reaches exactly up to rounding; "Attention Is All You Need", scaled
+ * dot-product attention, as named on the Colfax author page, "Introduction to
+ * Transformers" entry, and on the FlashAttention-2-on-Hopper abstract):
+ *
+ *   for every batch b, head h and query row i:
+ *     s_j   = scale * sum_c q[i][c] * k[j][c]           (fp64)
+ *     m     = max_j s_j
+ *     l     = sum_j exp(s_j - m)
+ *     O[c]  = sum_j exp(s_j - m) * v[j][c] / l
+ *     lse   = m + ln(l)           (natural-log logsumexp of the scaled logits)
+ *
+ * The problem restrictions follow the "Kernel Specification" section of the
+ * "Flash Attention 2 from scratch on Ampere" Part 1 page: forward only,
+ * non-causal (no mask), no dropout, equal query/key/value lengths, 16-bit
+ * (bf16 or fp16) inputs.  Inputs arrive as raw 16-bit patterns and are decoded
+ * exactly to fp64; nothing here rounds to 16 bits or to fp32.
+ *
+ * Layout: q, k, v are [B][H][N][d] contiguous; O is [rows][d] fp64 and lse is
+ * [rows] fp64, where rows are either all B*H*N rows in order or the caller's
+ * sorted list of flat row indices (b*H + h)*N + i.
+ */
+#define _GNU_SOURCE
+#include <math.h>
+#include <pthread.h>
+#include <sched.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ORACLE_BF16 = 0, ORACLE_FP16 = 1 };
+
+/* bf16 is the upper half of an IEEE binary32 pattern: exact in fp64. */
+static double decode_bf16(uint16_t bits) {
+  uint32_t u = (uint32_t)bits << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/* IEEE binary16: 1 sign, 5 exponent (bias 15), 10 mantissa bits. */
+static double decode_fp16(uint16_t bits) {
+  int sign = bits >> 15;
+  int expo = (bits >> 10) & 0x1f;
+  int man = bits & 0x3ff;
+  double mag;
+  if (expo == 0)
+    mag = ldexp((double)man, -24); /* subnormal: man * 2^-14 * 2^-10 */
+  else if (expo == 31)
+    mag = man ? NAN : INFINITY;
+  else
+    mag = ldexp((double)(1024 + man), expo - 25); /* (1 + man/1024) * 2^(e-15) */
+  return sign ? -mag : mag;
+}
+
+static double decode(uint16_t bits, int dtype) {
+  return dtype == ORACLE_BF16 ? decode_bf16(bits) : decode_fp16(bits);
+}
+
+int oracle_decode(const uint16_t* bits, int64_t n, int dtype, double* out) {
+  if (dtype != ORACLE_BF16 && dtype != ORACLE_FP16) return -1;
+  for (int64_t i = 0; i < n; ++i) out[i] = decode(bits[i], dtype);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  const uint16_t *q, *k, *v;
+  int dtype;
+  int64_t B, H, N, d;
+  double scale;
+  const int64_t* rows; /* sorted flat row ids, or NULL for all rows */
+  int64_t nrows;
+  double *o, *lse;
+  int64_t chunk;           /* rows per work item */
+  int64_t nitems;
+  int64_t next;            /* shared work counter (guarded by mu) */
+  int failed;              /* set by a worker that could not allocate */
+  pthread_mutex_t mu;
+} job_t;
+
+/* One query row against one decoded head: the definition, term by term. */
+static void one_row(const double* qrow, const double* K, const double* V,
+                    int64_t N, int64_t d, double scale, double* s,
+                    double* orow, double* lse_out) {
+  double m = -INFINITY;
+  for (int64_t j = 0; j < N; ++j) {
+    double dot = 0.0;
+    for (int64_t c = 0; c < d; ++c) dot += qrow[c] * K[j * d + c];
+    s[j] = scale * dot;
+    if (s[j] > m) m = s[j];
+  }
+  double l = 0.0;
+  for (int64_t j = 0; j < N; ++j) {
+    s[j] = exp(s[j] - m);
+    l += s[j];
+  }
+  for (int64_t c = 0; c < d; ++c) orow[c] = 0.0;
+  for (int64_t j = 0; j < N; ++j) {
+    const double w = s[j];
+    for (int64_t c = 0; c < d; ++c) orow[c] += w * V[j * d + c];
+  }
+  for (int64_t c = 0; c < d; ++c) orow[c] /= l;
+  *lse_out = m + log(l);
+}
+
+/* Work item = (head, block of that head's selected rows). */
+static void* worker(void* arg) {
+  job_t* J = (job_t*)arg;
+  const int64_t N = J->N, d = J->d;
+  double* K = (double*)malloc(sizeof(double) * (size_t)(N * d));
+  double* V = (double*)malloc(sizeof(double) * (size_t)(N * d));
+  double* q = (double*)malloc(sizeof(double) * (size_t)d);
+  double* s = (double*)malloc(sizeof(double) * (size_t)N);
+  int64_t loaded_head = -1;
+  if (!K || !V || !q || !s) {
+    pthread_mutex_lock(&J->mu);
+    J->failed = 1;
+    pthread_mutex_unlock(&J->mu);
+    goto done;
+  }
+  for (;;) {
+    pthread_mutex_lock(&J->mu);
+    int64_t item = J->next++;
+    pthread_mutex_unlock(&J->mu);
+    if (item >= J->nitems) break;
+    int64_t r0 = item * J->chunk;
+    int64_t r1 = r0 + J->chunk;
+    if (r1 > J->nrows) r1 = J->nrows;
+    for (int64_t r = r0; r < r1; ++r) {
+      int64_t flat = J->rows ? J->rows[r] : r;
+      int64_t head = flat / N;
+      if (head != loaded_head) {
+        const uint16_t* kh = J->k + head * N * d;
+        const uint16_t* vh = J->v + head * N * d;
+        for (int64_t t = 0; t < N * d; ++t) {
+          K[t] = decode(kh[t], J->dtype);
+          V[t] = decode(vh[t], J->dtype);
+        }
+        loaded_head = head;
+      }
+      const uint16_t* qr = J->q + flat * d;
+      for (int64_t c = 0; c < d; ++c) q[c] = decode(qr[c], J->dtype);
+      one_row(q, K, V, N, d, J->scale, s, J->o + r * d, J->lse + r);
+    }
+  }
+done:
+  free(K); free(V); free(q); free(s);
+  return NULL;
+}
+
+int oracle_host_threads(void) {
+  cpu_set_t set;
+  if (sched_getaffinity(0, sizeof set, &set) == 0) {
+    int n = CPU_COUNT(&set);
+    if (n > 0) return n;
+  }
+  return 1;
+}
+
+/*
+ * Attention rows.  rows == NULL computes all B*H*N rows; otherwise rows[] is a
+ * strictly increasing list of nrows flat row ids in [0, B*H*N).  nthreads <= 0
+ * uses every core in the affinity mask.  Returns 0, or -1 on a bad argument,
+ * -2 on allocation failure.
+ */
+int oracle_attn_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                     int dtype, int64_t B, int64_t H, int64_t N, int64_t d,
+                     double scale, const int64_t* rows, int64_t nrows,
+                     double* o, double* lse, int nthreads) {
+  if (dtype != ORACLE_BF16 && dtype != ORACLE_FP16) return -1;
+  if (B < 0 || H < 0 || N < 0 || d <= 0) return -1;
+  const int64_t total = B * H * N;
+  if (!rows) nrows = total;
+  if (nrows < 0 || nrows > total) return -1;
+  if (nrows == 0) return 0;
+  if (!q || !k || !v || !o || !lse) return -1;
+  if (rows) {
+    for (int64_t r = 0; r < nrows; ++r) {
+      if (rows[r] < 0 || rows[r] >= total) return -1;
+      if (r && rows[r] <= rows[r - 1]) return -1;
+    }
+  }
+  if (nthreads <= 0) nthreads = oracle_host_threads();
+
+  job_t J;
+  memset(&J, 0, sizeof J);
+  J.q = q; J.k = k; J.v = v; J.dtype = dtype;
+  J.B = B; J.H = H; J.N = N; J.d = d; J.scale = scale;
+  J.rows = rows; J.nrows = nrows; J.o = o; J.lse = lse;
+  /* rows of one head stay together inside an item so K/V decode once */
+  J.chunk = 64;
+  J.nitems = (nrows + J.chunk - 1) / J.chunk;
+  if (J.nitems < nthreads && nrows >= nthreads) {
+    J.chunk = (nrows + nthreads - 1) / nthreads;
+    J.nitems = (nrows + J.chunk - 1) / J.chunk;
+  }
+  if (nthreads > J.nitems) nthreads = (int)J.nitems;
+  pthread_mutex_init(&J.mu, NULL);
+
+  pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);
+  if (!th) return -2;
+  int started = 0;
+  for (int t = 0; t < nthreads; ++t) {
+    if (pthread_create(&th[t], NULL, worker, &J) != 0) break;
+    ++started;
+  }
+  if (started == 0) worker(&J);
+  for (int t = 0; t < started; ++t) pthread_join(th[t], NULL);
+  free(th);
+  pthread_mutex_destroy(&J.mu);
+  return J.failed ? -2 : 0;
+}

@@ -1,0 +1,348 @@
+"""Pins of the fp64 oracle: checks against what mathematics fixes, not itself.
+
+Each ``pin_*`` function takes an ``oracle.Oracle`` and raises AssertionError if
+that oracle disagrees with the definition of scaled dot-product attention
+(softmax(scale * Q K^T) V, natural-log logsumexp) through:
+  * exact fixtures hand-derived from the definition (tests/golden),
+  * closed forms (N = 1, N = 2, Q = 0, scale = 0, constant V, V = I),
+  * invariants (logit shift, permutations, head independence, linearity),
+  * brute force in pure Python (math.fsum) on tiny inputs,
+  * library routines (torch fp64 softmax / scaled_dot_product_attention),
+  * exact decoding of every 16-bit pattern, and extreme-logit stability.
+They are plain functions so the same pins also run against deliberately broken
+copies of the oracle (test_oracle_mutants.py), which they must reject.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+from flashattention_forward_tile_amd.workloads import bits, from_bits, make_inputs
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+DTYPES = ("bf16", "fp16")
+_TD = {"bf16": torch.bfloat16, "fp16": torch.float16}
+
+
+def _t16(x, dtype):
+    """Exact 16-bit tensor from float values (callers pass representable ones)."""
+    t = torch.as_tensor(np.asarray(x, dtype=np.float64)).to(_TD[dtype])
+    assert torch.equal(t.double(), torch.as_tensor(np.asarray(x, np.float64))), \
+        "fixture value not representable in %s" % dtype
+    return t
+
+
+def _f64(t):
+    return t.double().numpy()
+
+
+def _rand16(shape, dtype, seed, mult=1.0):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(shape, generator=g) * mult).to(_TD[dtype])
+
+
+def _run(orc, q, k, v, dtype, scale, **kw):
+    return orc.attention(bits(q), bits(k), bits(v), dtype, scale, **kw)
+
+
+# --------------------------------------------------------------------------
+# decoding
+
+def pin_decode_every_pattern(orc):
+    pats = np.arange(65536, dtype=np.uint16)
+    got = orc.decode(pats, "bf16")
+    ref = from_bits(pats, "bf16").double().numpy()
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok]), "bf16 decode"
+    got = orc.decode(pats, "fp16")
+    ref = pats.view(np.float16).astype(np.float64)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok]), "fp16 decode"
+
+
+# --------------------------------------------------------------------------
+# exact hand-derived fixtures
+
+def _parse_scale(s):
+    sign = -1.0 if s.startswith("-") else 1.0
+    body = s.lstrip("-")
+    assert body in ("ln2", "ln3")
+    return sign * math.log(2.0 if body == "ln2" else 3.0)
+
+
+def pin_worked_examples(orc):
+    with open(os.path.join(GOLDEN, "worked_examples.json")) as f:
+        cases = json.load(f)["cases"]
+    for case in cases:
+        scale = _parse_scale(case["scale"])
+        for dtype in DTYPES:
+            q = _t16(case["q"], dtype)[None, None]
+            k = _t16(case["k"], dtype)[None, None]
+            v = _t16(case["v"], dtype)[None, None]
+            o, lse = _run(orc, q, k, v, dtype, scale)
+            o_ref = np.array([[float(Fraction(x)) for x in row] for row in case["O"]])
+            lse_ref = np.array([math.log(Fraction(x)) for x in case["lse_ln"]])
+            assert np.allclose(o[0, 0], o_ref, rtol=0, atol=1e-13), case["name"]
+            assert np.allclose(lse[0, 0], lse_ref, rtol=0, atol=1e-13), case["name"]
+
+
+# --------------------------------------------------------------------------
+# brute force in pure Python
+
+def _brute_row(qi, K, V, scale):
+    """softmax by p_j = exp(s_j - lse), lse by max + log(fsum(exp))."""
+    s = [scale * math.fsum(a * b for a, b in zip(qi, kj)) for kj in K]
+    mx = max(s)
+    lse = mx + math.log(math.fsum(math.exp(x - mx) for x in s))
+    p = [math.exp(x - lse) for x in s]
+    o = [math.fsum(pj * vj[c] for pj, vj in zip(p, V)) for c in range(len(V[0]))]
+    return o, lse
+
+
+def pin_brute_force_tiny(orc):
+    rng = np.random.default_rng(7)
+    shapes = [(1, 1, 1, 1), (1, 2, 3, 2), (2, 1, 4, 3), (1, 1, 4, 4), (2, 2, 2, 5)]
+    scales = [1.0, 0.37, -0.8, 0.0, 2.5]
+    for dtype in DTYPES:
+        for shp, scale in zip(shapes, scales):
+            # entries on a grid of quarters in [-2, 2]: exact in both dtypes
+            q = rng.integers(-8, 9, size=shp) / 4.0
+            k = rng.integers(-8, 9, size=shp) / 4.0
+            v = rng.integers(-8, 9, size=shp) / 4.0
+            o, lse = _run(orc, _t16(q, dtype), _t16(k, dtype), _t16(v, dtype),
+                          dtype, scale)
+            B, H, N, d = shp
+            for b in range(B):
+                for h in range(H):
+                    for i in range(N):
+                        ob, lb = _brute_row(q[b, h, i].tolist(), k[b, h].tolist(),
+                                            v[b, h].tolist(), scale)
+                        assert np.allclose(o[b, h, i], ob, rtol=0, atol=1e-12), (shp, i)
+                        assert abs(lse[b, h, i] - lb) <= 1e-12 * max(1.0, abs(lb)), (shp, i)
+
+
+# --------------------------------------------------------------------------
+# library routines
+
+def pin_torch_fp64(orc):
+    import torch.nn.functional as F
+    for dtype, (B, H, N, d) in (("bf16", (1, 2, 256, 128)), ("fp16", (2, 1, 128, 64))):
+        q, k, v = make_inputs(B, H, N, d, dtype, "normal", seed=11)
+        scale = 1.0 / math.sqrt(d)
+        o, lse = _run(orc, q, k, v, dtype, scale)
+        qd, kd, vd = q.double(), k.double(), v.double()
+        logits = scale * (qd @ kd.transpose(-1, -2))
+        o_ref = torch.softmax(logits, dim=-1) @ vd
+        o_sdpa = F.scaled_dot_product_attention(qd, kd, vd, scale=scale)
+        lse_ref = torch.logsumexp(logits, dim=-1)
+        assert np.allclose(o, o_ref.numpy(), rtol=0, atol=1e-10)
+        assert np.allclose(o, o_sdpa.numpy(), rtol=0, atol=1e-10)
+        assert np.allclose(lse, lse_ref.numpy(), rtol=1e-12, atol=0)
+
+
+# --------------------------------------------------------------------------
+# closed forms
+
+def pin_identity_values_are_probabilities(orc):
+    """V = I (N <= d): O_i is the probability row; rows sum to 1, P = exp(s - lse)."""
+    for dtype in DTYPES:
+        N = d = 64
+        q = _rand16((1, 1, N, d), dtype, 21)
+        k = _rand16((1, 1, N, d), dtype, 22)
+        v = torch.eye(N, d).to(_TD[dtype])[None, None]
+        scale = 0.3
+        o, lse = _run(orc, q, k, v, dtype, scale)
+        p = o[0, 0]
+        assert np.all(p >= 0)
+        assert np.allclose(p.sum(axis=1), 1.0, rtol=0, atol=1e-12)
+        s = scale * (_f64(q[0, 0]) @ _f64(k[0, 0]).T)
+        assert np.allclose(p, np.exp(s - lse[0, 0][:, None]), rtol=1e-12, atol=1e-300)
+
+
+def pin_constant_values(orc):
+    """Every row of V equal to c: O_i = c for every query."""
+    for dtype in DTYPES:
+        B, H, N, d = 1, 2, 96, 32
+        q = _rand16((B, H, N, d), dtype, 31, 2.0)
+        k = _rand16((B, H, N, d), dtype, 32)
+        c = _rand16((1, 1, 1, d), dtype, 33)
+        v = c.expand(B, H, N, d).contiguous()
+        o, _ = _run(orc, q, k, v, dtype, 0.5)
+        assert np.allclose(o, np.broadcast_to(_f64(c), o.shape), rtol=1e-13, atol=1e-15)
+
+
+def pin_uniform_attention(orc):
+    """Q = 0 or scale = 0: O_i = column mean of V and lse_i = ln N."""
+    for dtype in DTYPES:
+        B, H, N, d = 1, 2, 256, 16
+        k = _rand16((B, H, N, d), dtype, 41)
+        v = _rand16((B, H, N, d), dtype, 42)
+        mean = _f64(v).mean(axis=2, keepdims=True)
+        for q, scale in ((torch.zeros(B, H, N, d, dtype=_TD[dtype]), 0.7),
+                         (_rand16((B, H, N, d), dtype, 43), 0.0)):
+            o, lse = _run(orc, q, k, v, dtype, scale)
+            assert np.allclose(o, np.broadcast_to(mean, o.shape), rtol=0, atol=1e-14)
+            # ln 256 = 8 ln 2 = 5.545177444479562
+            assert np.allclose(lse, 5.545177444479562, rtol=0, atol=1e-14)
+
+
+def pin_single_key(orc):
+    """N = 1: O = v_0 exactly; lse = the one logit."""
+    for dtype in DTYPES:
+        q = _rand16((2, 3, 1, 8), dtype, 51)
+        k = _rand16((2, 3, 1, 8), dtype, 52)
+        v = _rand16((2, 3, 1, 8), dtype, 53)
+        o, lse = _run(orc, q, k, v, dtype, 0.9)
+        assert np.array_equal(o, _f64(v))
+        s = 0.9 * np.einsum("bhnc,bhnc->bhn", _f64(q), _f64(k))
+        assert np.allclose(lse, s, rtol=1e-14, atol=1e-15)
+
+
+def pin_two_keys(orc):
+    """N = 2: O_i = sigma(s_i0 - s_i1) v_0 + sigma(s_i1 - s_i0) v_1."""
+    for dtype in DTYPES:
+        q = _rand16((1, 2, 2, 8), dtype, 61, 2.0)
+        k = _rand16((1, 2, 2, 8), dtype, 62)
+        v = _rand16((1, 2, 2, 8), dtype, 63)
+        scale = 0.75
+        o, lse = _run(orc, q, k, v, dtype, scale)
+        qd, kd, vd = _f64(q), _f64(k), _f64(v)
+        for h in range(2):
+            for i in range(2):
+                s0 = scale * math.fsum(qd[0, h, i] * kd[0, h, 0])
+                s1 = scale * math.fsum(qd[0, h, i] * kd[0, h, 1])
+                w0 = 1.0 / (1.0 + math.exp(s1 - s0))
+                w1 = 1.0 / (1.0 + math.exp(s0 - s1))
+                ref = w0 * vd[0, h, 0] + w1 * vd[0, h, 1]
+                assert np.allclose(o[0, h, i], ref, rtol=0, atol=1e-14)
+                big = max(s0, s1)
+                lref = big + math.log1p(math.exp(min(s0, s1) - big))
+                assert abs(lse[0, h, i] - lref) <= 1e-14 * max(1.0, abs(lref))
+
+
+# --------------------------------------------------------------------------
+# invariants
+
+def pin_logit_shift(orc):
+    """K -> K + 1 u^T adds scale*<q_i, u> to row i's logits: O unchanged,
+    lse shifted by exactly that amount.  K and u sit on a 1/16 grid with
+    |K + u| < 16, so K + u is exact in bf16 and fp16."""
+    rng = np.random.default_rng(71)
+    for dtype in DTYPES:
+        B, H, N, d = 1, 2, 128, 32
+        q = _rand16((B, H, N, d), dtype, 72)
+        kk = np.clip(np.round(rng.standard_normal((B, H, N, d)) * 16) / 16, -7.5, 7.5)
+        u = np.clip(np.round(rng.standard_normal((1, 1, 1, d)) * 32) / 16, -7.5, 7.5)
+        k0 = _t16(kk, dtype)
+        k1 = _t16(kk + u, dtype)
+        v = _rand16((B, H, N, d), dtype, 73)
+        scale = 0.4
+        o0, l0 = _run(orc, q, k0, v, dtype, scale)
+        o1, l1 = _run(orc, q, k1, v, dtype, scale)
+        assert np.allclose(o0, o1, rtol=0, atol=1e-12)
+        shift = scale * (_f64(q) @ u[0, 0, 0])
+        assert np.allclose(l1 - l0, shift, rtol=0, atol=1e-11)
+
+
+def pin_permutations(orc):
+    """Permuting K and V rows together leaves O alone; permuting Q rows permutes O."""
+    for dtype in DTYPES:
+        B, H, N, d = 1, 1, 64, 16
+        q = _rand16((B, H, N, d), dtype, 81)
+        k = _rand16((B, H, N, d), dtype, 82)
+        v = _rand16((B, H, N, d), dtype, 83)
+        perm = torch.randperm(N, generator=torch.Generator().manual_seed(84))
+        o, lse = _run(orc, q, k, v, dtype, 0.6)
+        o_kv, lse_kv = _run(orc, q, k[:, :, perm], v[:, :, perm], dtype, 0.6)
+        assert np.allclose(o, o_kv, rtol=0, atol=1e-13)
+        assert np.allclose(lse, lse_kv, rtol=1e-14, atol=0)
+        o_q, lse_q = _run(orc, q[:, :, perm], k, v, dtype, 0.6)
+        assert np.array_equal(o_q, o[:, :, perm.numpy()])
+        assert np.array_equal(lse_q, lse[:, :, perm.numpy()])
+
+
+def pin_value_linearity(orc):
+    """O is linear in V: V -> 2V and V -> -V scale O exactly (bit for bit)."""
+    for dtype in DTYPES:
+        q = _rand16((1, 2, 48, 24), dtype, 91)
+        k = _rand16((1, 2, 48, 24), dtype, 92)
+        v = _rand16((1, 2, 48, 24), dtype, 93)
+        o, lse = _run(orc, q, k, v, dtype, 0.3)
+        o2, lse2 = _run(orc, q, k, v * 2, dtype, 0.3)
+        on, _ = _run(orc, q, k, -v, dtype, 0.3)
+        assert np.array_equal(o2, 2 * o)
+        assert np.array_equal(on, -o)
+        assert np.array_equal(lse2, lse)
+
+
+def pin_head_independence(orc):
+    """Each (b, h) is attention on its own slice: a batched call equals the
+    per-head calls bit for bit, and rows= equals the full result."""
+    for dtype in DTYPES:
+        B, H, N, d = 2, 3, 40, 8
+        q = _rand16((B, H, N, d), dtype, 101)
+        k = _rand16((B, H, N, d), dtype, 102)
+        v = _rand16((B, H, N, d), dtype, 103)
+        o, lse = _run(orc, q, k, v, dtype, 0.5)
+        for b in range(B):
+            for h in range(H):
+                sl = (slice(b, b + 1), slice(h, h + 1))
+                oh, lh = _run(orc, q[sl], k[sl], v[sl], dtype, 0.5)
+                assert np.array_equal(oh[0, 0], o[b, h])
+                assert np.array_equal(lh[0, 0], lse[b, h])
+        rows = np.array([5, 0, B * H * N - 1, 77, 123])
+        orow, lrow = _run(orc, q, k, v, dtype, 0.5, rows=rows)
+        assert np.array_equal(orow, o.reshape(-1, d)[rows])
+        assert np.array_equal(lrow, lse.reshape(-1)[rows])
+
+
+def pin_extreme_logits(orc):
+    """Logits of magnitude ~1e3 (exp overflows/underflows in fp64 without the
+    max subtraction): a key ahead by a gap >> 40 takes all the weight, and lse
+    equals that key's logit."""
+    for dtype in DTYPES:
+        N, d = 8, 4
+        q = _t16(np.full((1, 1, N, d), 4.0), dtype)
+        kk = np.zeros((1, 1, N, d))
+        kk[0, 0, :, 0] = [-3.0, 1.0, 2.0, -1.0, 0.0, 3.0, 0.5, -2.0]  # key 5 wins
+        k = _t16(kk, dtype)
+        v = _rand16((1, 1, N, d), dtype, 111)
+        for scale in (100.0, 250.0):  # logits scale*4*k0 reach 3000 and -3000
+            o, lse = _run(orc, q, k, v, dtype, scale)
+            assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+            assert np.allclose(o[0, 0], np.broadcast_to(_f64(v)[0, 0, 5], (N, d)),
+                               rtol=0, atol=1e-12)
+            assert np.allclose(lse[0, 0], scale * 4 * 3.0, rtol=1e-15, atol=0)
+        # every logit very negative: still a proper softmax
+        kk[0, 0, :, 0] = -np.array([3.0, 2.0, 2.5, 3.0, 2.0, 3.0, 2.25, 3.0])
+        k = _t16(kk, dtype)
+        o, lse = _run(orc, q, k, v, dtype, 100.0)
+        assert np.all(np.isfinite(o))
+        w = np.zeros(N)
+        w[[1, 4]] = 0.5  # the two keys at logit -800 share the weight
+        assert np.allclose(o[0, 0], np.broadcast_to(w @ _f64(v)[0, 0], (N, d)),
+                           rtol=0, atol=1e-12)
+        assert np.allclose(lse[0, 0], -800.0 + math.log(2.0), rtol=1e-15, atol=0)
+
+
+ALL_PINS = [
+    pin_decode_every_pattern,
+    pin_worked_examples,
+    pin_brute_force_tiny,
+    pin_torch_fp64,
+    pin_identity_values_are_probabilities,
+    pin_constant_values,
+    pin_uniform_attention,
+    pin_single_key,
+    pin_two_keys,
+    pin_logit_shift,
+    pin_permutations,
+    pin_value_linearity,
+    pin_head_independence,
+    pin_extreme_logits,
+]

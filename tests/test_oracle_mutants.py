@@ -1,0 +1,48 @@
+"""Plant plausible mistakes in a copy of the oracle (on the CPU) and check that
+the pins reject every one of them, so a passing pin suite means something."""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+from oracle import build as oracle_build
+from oracle_pins import ALL_PINS
+
+# (name, text in attn_ref.c, replacement)
+MUTANTS = [
+    ("dropped_scale", "s[j] = scale * dot;", "s[j] = dot;"),
+    ("transposed_k", "dot += qrow[c] * K[j * d + c];", "dot += qrow[c] * K[c * N + j];"),
+    ("transposed_v", "orow[c] += w * V[j * d + c];", "orow[c] += w * V[c * N + j];"),
+    ("no_normalisation", "for (int64_t c = 0; c < d; ++c) orow[c] /= l;", ""),
+    ("lse_without_max", "*lse_out = m + log(l);", "*lse_out = log(l);"),
+    ("exp_sign_flipped", "s[j] = exp(s[j] - m);", "s[j] = exp(m - s[j]);"),
+    ("max_starts_at_zero", "double m = -INFINITY;", "double m = 0.0;"),
+    ("min_instead_of_max", "if (s[j] > m) m = s[j];", "if (s[j] < m) m = s[j];"),
+    ("bf16_shift", "(uint32_t)bits << 16;", "(uint32_t)bits << 15;"),
+    ("fp16_bias", "expo - 25);", "expo - 24);"),
+    ("fp16_subnormal", "ldexp((double)man, -24);", "ldexp((double)man, -25);"),
+    ("q_row_ignores_head", "J->q + flat * d;", "J->q + (flat % N) * d;"),
+    ("k_ignores_head", "J->k + head * N * d;", "J->k;"),
+    ("v_ignores_head", "J->v + head * N * d;", "J->v;"),
+    ("head_reload_skipped", "if (head != loaded_head) {", "if (loaded_head < 0) {"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_reject_mutant(tmp_path, name, old, new):
+    src = open(oracle_build.SRC).read()
+    assert src.count(old) == 1, "mutation site not unique: %r" % old
+    mutated = tmp_path / "attn_mut.c"
+    mutated.write_text(src.replace(old, new))
+    lib = tmp_path / ("liboracle_%s.so" % name)
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
+                    "-w", "-o", str(lib), str(mutated), "-lm"], check=True)
+    orc = oracle.Oracle(str(lib))
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin(orc)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, "no pin rejects mutant %s" % name
