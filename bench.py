@@ -1,0 +1,169 @@
+"""Benchmark of the FlashAttention-2 forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload headline]
+
+A step is one fa2_fwd launch over the whole workload (every (b, h) and query
+row of one batch), inputs resident in HBM.  W untimed steps, then exactly K
+steps timed with HIP events on the launch stream, bracketed by device
+synchronisation.  Prints ONE JSON line: forward attention TFLOP/s counting
+4*B*H*N^2*d FLOPs, the roofline of the kernel against the dense bf16/fp16 MFMA
+peak, and the fp64 CPU oracle's rate on a bounded sample of the same workload
+on this host's cores.
+
+Other modes: --workload NAME for any of the parity workloads (one line each),
+--no-cpu-baseline to skip the oracle timing, --calibrate-copy to run only a
+plain device copy of known size (for scaling HBM byte counters).
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fwd attention TFLOP/s, bf16 d=128 N=4096 non-causal; % of MFMA peak"
+# MI355X dense (no sparsity) MFMA peak for bf16/fp16: 256 CUs x 2.4 GHz x
+# 4096 FLOP/CU/clk = 2516.6 TFLOP/s, the published 2.5 PFLOP/s figure.
+MFMA_PEAK_TFLOPS = 2516.6
+HBM_PEAK_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "flashattention_forward_tile_amd", "csrc", "fa2_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa2_fwd_headline_traffic.json")
+CPU_SAMPLE_SECONDS = 12.0
+
+
+def kernel_digest() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    counts, if they were taken on this workload with this kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_sha256") != kernel_digest() or t.get("workload") != workload:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, q, k, v):
+    """The fp64 oracle as it stands, on whole heads of the same inputs, until
+    about CPU_SAMPLE_SECONDS of wall time have passed (at least one head)."""
+    import numpy as np
+
+    import oracle
+    from flashattention_forward_tile_amd.workloads import bits
+
+    qb, kb, vb = bits(q), bits(k), bits(v)
+    threads = oracle.host_threads()
+    heads = 0
+    t0 = time.perf_counter()
+    while heads < w.B * w.H:
+        b, h = divmod(heads, w.H)
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        oracle.attention(np.ascontiguousarray(qb[sl]), np.ascontiguousarray(kb[sl]),
+                         np.ascontiguousarray(vb[sl]), w.dtype, w.scale, nthreads=threads)
+        heads += 1
+        if time.perf_counter() - t0 >= CPU_SAMPLE_SECONDS:
+            break
+    dt = time.perf_counter() - t0
+    flops = 4.0 * heads * w.N * w.N * w.d
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "%d of %d heads (all %d query rows each) of the %s workload, "
+                      "fp64, %.1f s wall" % (heads, w.B * w.H, w.N, w.name, dt)}
+
+
+def calibrate_copy(nbytes=1 << 30, reps=5):
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes_read": nbytes, "bytes_written": nbytes,
+                      "reps": reps}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="headline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU only (the per-GPU share of "
+              "independent (batch, head) work); --gpus %d is not supported" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+
+    from flashattention_forward_tile_amd import fa2
+    from flashattention_forward_tile_amd.workloads import WORKLOADS, workload_inputs
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    q, k, v = workload_inputs(w, seed=0)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    o = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+
+    for _ in range(args.warmup):
+        fa2.fwd(qd, kd, vd, scale=w.scale, out=o, lse=lse)
+    torch.cuda.synchronize(dev)
+    if not (torch.isfinite(o[0, 0].float()).all() and torch.isfinite(lse).all()):
+        raise RuntimeError("non-finite output")
+
+    stream = torch.cuda.current_stream(dev)  # fa2.fwd launches on this stream
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        fa2.fwd(qd, kd, vd, scale=w.scale, out=o, lse=lse)
+    stop.record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - wall0
+    ms = start.elapsed_time(stop) / args.steps
+
+    tflops = w.flops / (ms * 1e-3) / 1e12
+    traffic = measured_traffic(w.name)
+    roofline = {"bound": "mfma", "achieved": round(tflops, 3), "peak": MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tflops / MFMA_PEAK_TFLOPS, 4),
+                "traffic": traffic}
+    out = {
+        "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": dict(w.describe(), kernel="fa2_fwd_kernel", launches_per_step=1,
+                       algo_hbm_bytes=w.algo_bytes,
+                       algo_hbm_gbs=round(w.algo_bytes / (ms * 1e-3) / 1e9, 1),
+                       wall_ms_per_step=round(wall * 1e3 / args.steps, 5)),
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, q, k, v)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,130 @@
+"""Thin Python binding of the C ABI in include/fa2.h (argument marshalling only).
+
+Every step of the computation runs in the HIP kernels of libfa2.so; this module
+checks tensor metadata, allocates outputs with torch, passes raw device
+pointers and the current HIP stream, and turns status codes into exceptions.
+There is no fallback: if libfa2.so is missing, every call raises.
+"""
+import ctypes
+import math
+import os
+
+import torch
+
+from . import _build
+
+OK = 0
+ERR_NULL = -1
+ERR_SHAPE = -2
+ERR_HEADDIM = -3
+ERR_DTYPE = -4
+ERR_ALIGN = -5
+ERR_SCALE = -6
+ERR_ALIAS = -7
+ERR_HIP = -8
+
+BF16 = 0
+FP16 = 1
+_DTYPE = {torch.bfloat16: BF16, torch.float16: FP16}
+
+# Entry points declared in include/fa2.h, with their ctypes signatures.
+_SIGNATURES = {
+    "fa2_fwd": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                               ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                               ctypes.c_float, ctypes.c_int, ctypes.c_void_p]),
+    "fa2_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+    "fa2_tile_config": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int,
+                                       ctypes.POINTER(ctypes.c_int),
+                                       ctypes.POINTER(ctypes.c_int),
+                                       ctypes.POINTER(ctypes.c_int)]),
+}
+
+_lib = None
+
+
+class FA2Error(RuntimeError):
+    def __init__(self, code):
+        self.code = code
+        super().__init__("fa2_fwd failed (%d): %s" % (code, strerror(code)))
+
+
+def library_path() -> str:
+    return _build.LIB
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libfa2.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            raise RuntimeError(
+                "libfa2.so is not built (%s); run __graft_entry__.build()" % _build.LIB)
+        handle = ctypes.CDLL(_build.LIB)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return lib().fa2_strerror(int(code)).decode()
+
+
+def tile_config(d: int, dtype=torch.bfloat16):
+    """(block_q, block_k, waves) that fa2_fwd uses for this head dim / dtype."""
+    code_dtype = _DTYPE.get(dtype, -1) if isinstance(dtype, torch.dtype) else int(dtype)
+    bq, bk, nw = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    code = lib().fa2_tile_config(int(d), code_dtype, ctypes.byref(bq),
+                                 ctypes.byref(bk), ctypes.byref(nw))
+    if code != OK:
+        raise FA2Error(code)
+    return bq.value, bk.value, nw.value
+
+
+def fwd_raw(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, N, d, scale, dtype,
+            stream=0) -> int:
+    """Direct C-ABI call with integer pointers; returns the status code."""
+    return lib().fa2_fwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, N, d,
+                         float(scale), int(dtype), stream)
+
+
+def fwd(q, k, v, scale=None, out=None, lse=None):
+    """Attention forward: returns (o, lse) for q, k, v of shape [B, H, N, d].
+
+    q, k, v: contiguous bf16 or fp16 CUDA(HIP) tensors of one shape and dtype.
+    scale: logit multiplier, default 1/sqrt(d).
+    out, lse: optional preallocated outputs ([B, H, N, d] of q's dtype and
+    [B, H, N] float32, contiguous, on q's device).
+    The kernel is enqueued on torch's current stream of q's device.
+    """
+    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must share one [B, H, N, d] shape")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DTYPE:
+        raise ValueError("q, k, v must all be bfloat16 or all float16")
+    if not (q.is_cuda and k.device == q.device and v.device == q.device):
+        raise ValueError("q, k, v must be on one GPU")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or out.device != q.device \
+            or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    elif lse.shape != (B, H, N) or lse.dtype != torch.float32 \
+            or lse.device != q.device or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        code = fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                       lse.data_ptr(), B, H, N, d, scale, _DTYPE[q.dtype], stream)
+    if code != OK:
+        raise FA2Error(code)
+    return out, lse

@@ -1,0 +1,106 @@
+/*
+ * fa2.h -- C ABI of the MI355X (gfx950) FlashAttention-2 forward pass.
+ *
+ * The operation is the forward pass of FlashAttention-2: non-causal scaled
+ * dot-product attention computed tile by tile with an online softmax, so the
+ * N x N score matrix never reaches HBM ("A Case Study in CUDA Kernel Fusion:
+ * Implementing FlashAttention-2 on NVIDIA Hopper Architecture using the CUTLASS
+ * Library", abstract; "Flash Attention 2 from scratch on Ampere", Part 1,
+ * sections "Why Flash Attention?" and "Kernel Specification").  For every
+ * batch b, head h and query row i:
+ *
+ *     s_ij  = scale * sum_c q[b,h,i,c] * k[b,h,j,c]
+ *     o[b,h,i,:] = sum_j softmax_j(s_i.) * v[b,h,j,:]
+ *     lse[b,h,i] = ln sum_j exp(s_ij)
+ *
+ * Scope follows the Kernel Specification section of the Ampere Part 1 page:
+ * forward only, non-causal, no dropout, no KV cache, equal query and key
+ * lengths, 16-bit (bf16 or fp16) inputs and outputs, softmax in fp32.  The head
+ * dimension may be 64, 128 (the page's) or 256.  Unlike the page, N need not
+ * be a multiple of the block size: the last key tile is masked.
+ *
+ * All entry points are plain C.  Pointers are device pointers unless stated.
+ */
+#ifndef FA2_H
+#define FA2_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k, v and o. */
+enum fa2_dtype {
+  FA2_BF16 = 0, /* bfloat16 (8-bit exponent, 7-bit mantissa) */
+  FA2_FP16 = 1  /* IEEE binary16 */
+};
+
+/* Return codes.  Every negative code except FA2_ERR_HIP is detected on the
+ * host before any HIP call is made, and nothing is written. */
+enum fa2_status {
+  FA2_OK = 0,
+  FA2_ERR_NULL = -1,    /* a required pointer is NULL */
+  FA2_ERR_SHAPE = -2,   /* B, H or N negative, or sizes overflow the grid or
+                           64-bit element offsets */
+  FA2_ERR_HEADDIM = -3, /* d is not 64, 128 or 256 */
+  FA2_ERR_DTYPE = -4,   /* dtype is not an fa2_dtype */
+  FA2_ERR_ALIGN = -5,   /* q, k, v or o not 16-byte aligned, lse not 4-byte */
+  FA2_ERR_SCALE = -6,   /* scale is NaN or infinite */
+  FA2_ERR_ALIAS = -7,   /* o or lse overlaps q, k, v, or each other */
+  FA2_ERR_HIP = -8      /* the kernel launch failed (HIP error) */
+};
+
+/*
+ * fa2_fwd -- attention forward for B*H independent heads.
+ *
+ *   q, k, v  in : [B][H][N][d] contiguous, element type `dtype`; element
+ *                 (b,h,n,c) at ((b*H + h)*N + n)*d + c.  16-byte aligned.
+ *   o        out: same shape, layout and type as q.  16-byte aligned.
+ *   lse      out: [B][H][N] contiguous fp32, lse(b,h,n) at (b*H + h)*N + n:
+ *                 the natural-log logsumexp of row n's scaled logits.
+ *   B, H, N  : batch, heads, sequence length (queries = keys = N), each >= 0.
+ *              If B*H*N == 0 the call returns FA2_OK and touches nothing
+ *              (pointers may then be NULL).
+ *   d        : head dimension, 64, 128 or 256.
+ *   scale    : multiplies the logits; any finite value (1/sqrt(d) is usual;
+ *              0 gives uniform attention, negative values are allowed).
+ *   dtype    : an fa2_dtype.
+ *   stream   : a hipStream_t, or NULL for the default stream.
+ *
+ * Ownership: the caller owns every buffer; the library allocates nothing and
+ * keeps no state between calls, so concurrent calls on any streams are safe as
+ * long as their outputs do not overlap.  o and lse must not overlap q, k, v or
+ * each other.
+ *
+ * Asynchrony: the work is enqueued on `stream` and the call returns at once;
+ * synchronise the stream before reading o or lse.
+ *
+ * Numerics: logits are accumulated in fp32 from the exact 16-bit inputs; the
+ * softmax runs in fp32 with exp2; probabilities are rounded to `dtype` for the
+ * second product, accumulated in fp32; o is rounded to `dtype` (nearest even).
+ * Non-finite inputs propagate and are not diagnosed.
+ *
+ * Returns FA2_OK, or a negative fa2_status.
+ */
+int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+            int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+            int dtype, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* fa2_strerror(int status);
+
+/*
+ * fa2_tile_config -- the tile shape fa2_fwd uses for head dimension d and
+ * dtype: *block_q query rows per workgroup, *block_k key rows per K/V tile,
+ * *waves wavefronts (of 64 lanes) per workgroup.  Host-only, no HIP call.
+ * Returns FA2_OK, FA2_ERR_HEADDIM, FA2_ERR_DTYPE or FA2_ERR_NULL.
+ */
+int fa2_tile_config(int64_t d, int dtype, int* block_q, int* block_k,
+                    int* waves);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA2_H */

@@ -1,0 +1,99 @@
+"""The C-ABI library without a GPU: it loads, exports what include/fa2.h
+declares, and rejects bad arguments on the host before any HIP call.
+
+Every fa2_fwd call here fails validation by construction (the pointers are
+never dereferenced), so these tests are also safe on a GPU machine."""
+import os
+import re
+
+import pytest
+
+from flashattention_forward_tile_amd import _build, fa2
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa2.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa2_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_build.LIB):
+        _build.build()
+    return fa2.lib()
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == ["fa2_fwd", "fa2_strerror", "fa2_tile_config"]
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_strerror_covers_every_status(lib):
+    texts = set()
+    for code in range(0, -9, -1):
+        s = fa2.strerror(code)
+        assert s and s != "unknown status", code
+        texts.add(s)
+    assert len(texts) == 9
+    assert fa2.strerror(17) == "unknown status"
+
+
+def test_tile_config(lib):
+    for d in (64, 128, 256):
+        bq, bk, nw = fa2.tile_config(d, fa2.BF16)
+        assert bq == 32 * nw and bk % 32 == 0 and nw >= 1
+    with pytest.raises(fa2.FA2Error) as e:
+        fa2.tile_config(96)
+    assert e.value.code == fa2.ERR_HEADDIM
+    with pytest.raises(fa2.FA2Error) as e:
+        fa2.tile_config(128, 7)
+    assert e.value.code == fa2.ERR_DTYPE
+
+
+A = 0x100000      # fake, 16-byte aligned, never dereferenced
+GOOD = dict(B=2, H=3, N=100, d=128, scale=0.1, dtype=fa2.BF16)
+
+
+def call(q=A, k=A + 0x1000000, v=A + 0x2000000, o=A + 0x3000000,
+         lse=A + 0x4000000, **kw):
+    p = dict(GOOD)
+    p.update(kw)
+    return fa2.fwd_raw(q, k, v, o, lse, p["B"], p["H"], p["N"], p["d"],
+                       p["scale"], p["dtype"], 0)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), fa2.ERR_NULL), (dict(k=0), fa2.ERR_NULL), (dict(v=0), fa2.ERR_NULL),
+    (dict(o=0), fa2.ERR_NULL), (dict(lse=0), fa2.ERR_NULL),
+    (dict(B=-1), fa2.ERR_SHAPE), (dict(H=-2), fa2.ERR_SHAPE), (dict(N=-5), fa2.ERR_SHAPE),
+    (dict(N=1 << 31), fa2.ERR_SHAPE), (dict(B=1 << 40, H=1 << 30), fa2.ERR_SHAPE),
+    (dict(d=96), fa2.ERR_HEADDIM), (dict(d=0), fa2.ERR_HEADDIM), (dict(d=512), fa2.ERR_HEADDIM),
+    (dict(dtype=2), fa2.ERR_DTYPE), (dict(dtype=-1), fa2.ERR_DTYPE),
+    (dict(scale=float("nan")), fa2.ERR_SCALE), (dict(scale=float("inf")), fa2.ERR_SCALE),
+    (dict(q=A + 2), fa2.ERR_ALIGN), (dict(o=A + 0x3000008), fa2.ERR_ALIGN),
+    (dict(lse=A + 0x4000002), fa2.ERR_ALIGN),
+    (dict(o=A), fa2.ERR_ALIAS), (dict(o=A + 0x1000000 + 4096), fa2.ERR_ALIAS),
+    (dict(lse=A + 0x2000000 + 64), fa2.ERR_ALIAS), (dict(lse=A + 0x3000000), fa2.ERR_ALIAS),
+])
+def test_host_validation(lib, kw, code):
+    assert call(**kw) == code
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(N=0)])
+def test_empty_problem_is_a_no_op(lib, kw):
+    assert call(q=0, k=0, v=0, o=0, lse=0, **kw) == fa2.OK
+
+
+def test_no_silent_fallback(monkeypatch):
+    monkeypatch.setattr(_build, "LIB", "/nonexistent/libfa2.so")
+    monkeypatch.setattr(fa2, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        fa2.lib()

@@ -1,0 +1,271 @@
+"""GPU parity of the HIP path against the fp64 oracle (needs an MI355X).
+
+Every case prints its name, shape and seed before touching the GPU, so a
+failing run names its case.  Inputs come from the seeded generators in
+flashattention_forward_tile_amd.workloads; expected values come only from the
+oracle or from closed forms computed here in fp64.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from flashattention_forward_tile_amd import fa2
+from flashattention_forward_tile_amd.workloads import (WORKLOADS, bits, make_inputs,
+                                                       torch_dtype, workload_inputs)
+from parity import assert_parity, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+_TD = {"bf16": torch.bfloat16, "fp16": torch.float16}
+
+
+def announce(*what):
+    print("CASE", *what, flush=True)
+
+
+def run_gpu(q, k, v, scale):
+    o, lse = fa2.fwd(q.to(DEV), k.to(DEV), v.to(DEV), scale=scale)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+def f64(t):
+    return t.double().numpy()
+
+
+def check_full(q, k, v, dtype, scale, tag, **kw):
+    o, lse = run_gpu(q, k, v, scale)
+    o_ref, lse_ref = oracle.attention(bits(q), bits(k), bits(v), dtype, scale)
+    return assert_parity(f64(o), f64(lse), o_ref, lse_ref, tag, **kw)
+
+
+def check_sampled(q, k, v, dtype, scale, tag, per_head=6, seed=0):
+    B, H, N, d = q.shape
+    bq, _, _ = fa2.tile_config(d, _TD[dtype])
+    o, lse = run_gpu(q, k, v, scale)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all(), tag
+    rows = sample_rows(B, H, N, bq, per_head, seed)
+    o_ref, lse_ref = oracle.attention(bits(q), bits(k), bits(v), dtype, scale, rows=rows)
+    return assert_parity(f64(o).reshape(-1, d)[rows], f64(lse).reshape(-1)[rows],
+                         o_ref, lse_ref, tag)
+
+
+# ---------------------------------------------------------------- workloads
+
+def test_tiny_full():
+    w = WORKLOADS["tiny"]
+    announce(w)
+    q, k, v = workload_inputs(w, seed=0)
+    check_full(q, k, v, w.dtype, w.scale, w.name)
+
+
+def test_stress_full():
+    w = WORKLOADS["stress"]
+    announce(w)
+    q, k, v = workload_inputs(w, seed=0)
+    check_full(q, k, v, w.dtype, w.scale, w.name)
+
+
+def test_headline_sampled():
+    w = WORKLOADS["headline"]
+    announce(w)
+    q, k, v = workload_inputs(w, seed=0)
+    check_sampled(q, k, v, w.dtype, w.scale, w.name)
+
+
+@pytest.mark.parametrize("name", [n for n in WORKLOADS if n.startswith("sweep_")])
+def test_sweep_sampled(name):
+    w = WORKLOADS[name]
+    announce(w)
+    q, k, v = workload_inputs(w, seed=0)
+    check_sampled(q, k, v, w.dtype, w.scale, w.name, per_head=4)
+
+
+@pytest.mark.parametrize("name", ["d64", "d256"])
+def test_headdim_sampled(name):
+    w = WORKLOADS[name]
+    announce(w)
+    q, k, v = workload_inputs(w, seed=0)
+    check_sampled(q, k, v, w.dtype, w.scale, w.name)
+
+
+# ---------------------------------------------------------------- edge cases
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("N", [1, 2, 3, 31, 33, 64, 65, 127, 129, 200, 257, 1000])
+def test_ragged_lengths(N, dtype, d):
+    announce("ragged", N, dtype, d)
+    q, k, v = make_inputs(1, 2, N, d, dtype, "normal", seed=N)
+    check_full(q, k, v, dtype, 1.0 / math.sqrt(d), "ragged N=%d %s d=%d" % (N, dtype, d))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("scale", [0.0, -0.09, 0.5, 1e-3, -1.0])
+def test_scales(scale, dtype):
+    announce("scale", scale, dtype)
+    q, k, v = make_inputs(2, 2, 300, 128, dtype, "normal", seed=5)
+    # lse can sit near 0 for a negative scale; bound it absolutely there too
+    check_full(q, k, v, dtype, scale, "scale=%g %s" % (scale, dtype), lse_abs=1e-3)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_stress_distribution_all_head_dims(d):
+    announce("stress", d)
+    q, k, v = make_inputs(1, 4, 512, d, "bf16", "stress", seed=d)
+    check_full(q, k, v, "bf16", 1.0 / math.sqrt(d), "stress d=%d" % d)
+
+
+def test_empty_inputs():
+    announce("empty")
+    for shape in ((0, 2, 64, 128), (1, 0, 64, 128), (1, 2, 0, 128)):
+        q = torch.empty(shape, dtype=torch.bfloat16, device=DEV)
+        o, lse = fa2.fwd(q, q.clone(), q.clone())
+        assert o.shape == shape and lse.shape == shape[:3]
+
+
+# ---------------------------------------------------------------- closed forms
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_constant_values(dtype):
+    """All rows of V equal c: O = c.  The weights are rounded to 16 bits for
+    the second product while l sums them unrounded, so O may differ from c by
+    the weights' rounding, well under one 16-bit ulp of c on average."""
+    announce("constant V", dtype)
+    B, H, N, d = 2, 2, 777, 128
+    q, k, _ = make_inputs(B, H, N, d, dtype, "normal", seed=3)
+    c = torch.randn(1, 1, 1, d, generator=torch.Generator().manual_seed(4)).to(_TD[dtype])
+    v = c.expand(B, H, N, d).contiguous()
+    o, _ = run_gpu(q, k, v, 1.0 / math.sqrt(d))
+    rel = np.abs(f64(o) - f64(v)) / np.abs(f64(v))
+    ulp = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -11
+    assert rel.max() <= 2 * ulp and (o == v).double().mean() >= 0.9
+
+
+@pytest.mark.parametrize("N", [256, 4096])
+def test_uniform_attention(N):
+    """Q = 0: O is the column mean of V and lse = ln N."""
+    announce("Q=0", N)
+    d = 128
+    _, k, v = make_inputs(1, 2, N, d, "bf16", "normal", seed=6)
+    q = torch.zeros_like(k)
+    o, lse = run_gpu(q, k, v, 1.0 / math.sqrt(d))
+    mean = f64(v).mean(axis=2, keepdims=True)
+    assert np.abs(f64(o) - mean).max() <= 2e-2 * 0.1
+    assert np.allclose(f64(lse), math.log(N), rtol=1e-6, atol=0)
+
+
+def test_rank_one_logits_closed_form():
+    """Q and K nonzero only in coordinate 0: s_ij = scale * a_i * b_j, so the
+    softmax is computable directly in fp64 without the oracle."""
+    announce("rank-one logits")
+    B, H, N, d = 1, 2, 512, 64
+    g = torch.Generator().manual_seed(8)
+    a = torch.randn(B, H, N, generator=g).to(torch.bfloat16)
+    b = torch.randn(B, H, N, generator=g).to(torch.bfloat16)
+    q = torch.zeros(B, H, N, d, dtype=torch.bfloat16)
+    k = torch.zeros(B, H, N, d, dtype=torch.bfloat16)
+    q[..., 0] = a
+    k[..., 0] = b
+    v = torch.randn(B, H, N, d, generator=g).to(torch.bfloat16)
+    scale = 3.0
+    o, lse = run_gpu(q, k, v, scale)
+    s = scale * f64(a)[..., :, None] * f64(b)[..., None, :]
+    mx = s.max(axis=-1, keepdims=True)
+    w = np.exp(s - mx)
+    o_ref = (w @ f64(v)) / w.sum(axis=-1, keepdims=True)
+    lse_ref = mx[..., 0] + np.log(w.sum(axis=-1))
+    assert_parity(f64(o), f64(lse), o_ref, lse_ref, "rank-one", lse_abs=1e-3)
+
+
+# ---------------------------------------------------------------- invariants
+
+def test_logit_shift_invariance():
+    """K -> K + 1 u^T (exact in bf16) leaves O alone and shifts lse by
+    scale * <q_i, u>, on the GPU itself."""
+    announce("shift")
+    B, H, N, d = 1, 2, 1024, 128
+    rng = np.random.default_rng(9)
+    q, _, v = make_inputs(B, H, N, d, "bf16", "normal", seed=9)
+    kk = np.clip(np.round(rng.standard_normal((B, H, N, d)) * 16) / 16, -7.5, 7.5)
+    u = np.clip(np.round(rng.standard_normal(d) * 16) / 16, -7.5, 7.5)
+    k0 = torch.from_numpy(kk).to(torch.bfloat16)
+    k1 = torch.from_numpy(kk + u).to(torch.bfloat16)
+    assert torch.equal(k1.double(), torch.from_numpy(kk + u))
+    scale = 1.0 / math.sqrt(d)
+    o0, l0 = run_gpu(q, k0, v, scale)
+    o1, l1 = run_gpu(q, k1, v, scale)
+    diff = np.abs(f64(o0) - f64(o1))
+    assert diff.max() <= 2e-2 and diff.mean() <= 2e-3
+    shift = scale * (f64(q) @ u)
+    assert np.allclose(f64(l1) - f64(l0), shift, rtol=0, atol=2e-3 * np.abs(f64(l1)).max())
+
+
+def test_key_permutation_invariance():
+    announce("permutation")
+    B, H, N, d = 1, 2, 640, 128
+    q, k, v = make_inputs(B, H, N, d, "bf16", "normal", seed=10)
+    perm = torch.randperm(N, generator=torch.Generator().manual_seed(11))
+    o0, l0 = run_gpu(q, k, v, 0.1)
+    o1, l1 = run_gpu(q, k[:, :, perm].contiguous(), v[:, :, perm].contiguous(), 0.1)
+    diff = np.abs(f64(o0) - f64(o1))
+    assert diff.max() <= 2e-2 and diff.mean() <= 2e-3
+    assert np.allclose(f64(l0), f64(l1), rtol=1e-4)
+    oq, lq = run_gpu(q[:, :, perm].contiguous(), k, v, 0.1)
+    assert torch.equal(oq, o0[:, :, perm]) and torch.equal(lq, l0[:, :, perm])
+
+
+# ---------------------------------------------------------------- hygiene
+
+def test_deterministic_and_fully_written():
+    """Two runs into NaN-prefilled outputs give bit-identical, finite results."""
+    w = WORKLOADS["headline"]
+    announce("determinism", w)
+    q, k, v = (t.to(DEV) for t in workload_inputs(w, seed=1))
+    outs = []
+    for _ in range(2):
+        o = torch.full_like(q, float("nan"))
+        lse = torch.full((w.B, w.H, w.N), float("nan"), device=DEV)
+        fa2.fwd(q, k, v, scale=w.scale, out=o, lse=lse)
+        torch.cuda.synchronize()
+        assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+        outs.append((o, lse))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+def test_non_default_stream():
+    announce("stream")
+    q, k, v = make_inputs(2, 4, 512, 128, "fp16", "normal", seed=12)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    ref_o, ref_l = fa2.fwd(qd, kd, vd)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        o, lse = fa2.fwd(qd, kd, vd)
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref_o) and torch.equal(lse, ref_l)
+
+
+def test_device_argument_errors():
+    announce("errors")
+    q = torch.randn(1, 2, 64, 128, device=DEV).to(torch.bfloat16)
+    k, v = q.clone(), q.clone()
+    o = torch.empty_like(q)
+    lse = torch.empty(1, 2, 64, device=DEV)
+    p = lambda t: t.data_ptr()
+    # misaligned by one element
+    assert fa2.fwd_raw(p(q) + 2, p(k), p(v), p(o), p(lse), 1, 2, 63, 128, 0.1, fa2.BF16) == fa2.ERR_ALIGN
+    # output on top of an input
+    assert fa2.fwd_raw(p(q), p(k), p(v), p(q), p(lse), 1, 2, 64, 128, 0.1, fa2.BF16) == fa2.ERR_ALIAS
+    assert fa2.fwd_raw(p(q), p(k), p(v), p(o), p(lse), 1, 2, 64, 96, 0.1, fa2.BF16) == fa2.ERR_HEADDIM
+    with pytest.raises(ValueError):
+        fa2.fwd(q, k.to(torch.float16), v)
+    with pytest.raises(ValueError):
+        fa2.fwd(q.transpose(2, 3), k.transpose(2, 3), v.transpose(2, 3))
+    with pytest.raises(ValueError):
+        fa2.fwd(q.cpu(), k.cpu(), v.cpu())
