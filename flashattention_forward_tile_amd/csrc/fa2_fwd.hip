@@ -69,23 +69,73 @@ __device__ __forceinline__ f32x16 mfma32x32x16(typename Vec<FP16>::x8 a,
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// XOR swizzle of 16-byte chunks within an LDS row of CPR chunks, chosen so the
-// 16 lanes of a ds_read_b128 phase that read one logical chunk from 16
-// consecutive rows hit 16 distinct bank groups.
+// LDS tiles are row-major with 16-byte chunks XOR-swizzled per row.  The
+// K tile is read with ds_read_b128 by 16 lanes at 16 consecutive rows and one
+// logical chunk; the V tile is read with ds_read_b64_tr_b16 by 16 lanes at 4
+// consecutive rows and 4 consecutive chunks.  Each swizzle spreads its pattern
+// over distinct bank groups; CPR is the row length in chunks.
 template <int CPR>
-__device__ __forceinline__ int swizzle(int row, int chunk) {
-  static_assert(CPR == 4 || CPR == 8 || CPR == 16 || CPR == 32,
-                "row of 64, 128, 256 or 512 B");
+__device__ __forceinline__ int k_swizzle(int row, int chunk) {
+  static_assert(CPR == 8 || CPR == 16 || CPR == 32, "row of 128, 256 or 512 B");
   if constexpr (CPR >= 16)
-    return chunk ^ (row & 15);  // rows start on the same bank: spread by row
-  else if constexpr (CPR == 8)
-    return chunk ^ ((row ^ (row >> 3)) & 7);  // 128 B rows: two rows per sweep
+    return chunk ^ (row & 15);
+  else  // 128 B rows: two rows share one sweep of the banks
+    return chunk ^ ((row >> 1) & 7);
+}
+template <int CPR>
+__device__ __forceinline__ int v_swizzle(int row, int chunk) {
+  static_assert(CPR == 8 || CPR == 16 || CPR == 32, "row of 128, 256 or 512 B");
+  if constexpr (CPR >= 16)
+    return chunk ^ ((row & 3) << 2);
   else
-    return chunk ^ ((row >> 2) & 3);  // 64 B rows: four rows per sweep
+    return chunk ^ (((row >> 1) & 1) << 2);
 }
 
-// Tile shape per head dimension: D, key rows per tile, waves per workgroup,
-// waves per SIMD the register budget is sized for.
+// v_waitcnt with only vmcnt(0): every buffer load of this wave, including
+// the ones that write LDS directly, has landed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+typedef __attribute__((address_space(3))) char lds_char;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Buffer descriptor words 2 and 3: num_records = `bytes`, then a raw untyped
+// 32-bit buffer format; loads past `bytes` return zeros.
+constexpr int kBufferWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base,
+                                                          uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes,
+                                           kBufferWord3);
+}
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// The same descriptor as four wave-uniform words, for the inline-asm loads.
+__device__ __forceinline__ i32x4 make_rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));  // stride 0
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = kBufferWord3;
+  return r;
+}
+
+// 16 bytes per lane from buffer offset `voff` straight into LDS: lane l writes
+// LDS bytes [m0 + 16 l, m0 + 16 l + 16).  Written as inline asm so the compiler
+// does not guard every later LDS read with a wait on these loads (it cannot
+// tell the double buffers apart); the caller waits with wait_vmem() before
+// the barrier that publishes the tile.
+__device__ __forceinline__ void load_lds16(i32x4 rsrc, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "{m0}"(lds_addr)
+               : "memory");
+}
+
+// Tile shape per head dimension: key rows per tile, waves per workgroup, and
+// the waves per SIMD the register budget is sized for.
 template <int D> struct Cfg;
 template <> struct Cfg<64> { static constexpr int BC = 64, NW = 4, OCC = 2; };
 template <> struct Cfg<128> { static constexpr int BC = 64, NW = 4, OCC = 2; };
@@ -101,23 +151,20 @@ fa2_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                float c) {
   constexpr int BC = Cfg<D>::BC;
   constexpr int NW = Cfg<D>::NW;
-  constexpr int NT = NW * 64;
-  constexpr int BR = NW * 32;        // query rows per workgroup
-  constexpr int CPR = D / 8;         // 16-byte chunks per K row
-  constexpr int CPRV = BC / 8;       // 16-byte chunks per V^T row
-  constexpr int KCH = BC * CPR / NT; // K chunks staged per thread
-  constexpr int VUNITS = (BC / 4) * CPR;       // 4 keys x 8 dims per unit
-  constexpr int VU = (VUNITS + NT - 1) / NT;   // units per thread
-  constexpr int KBYTES = BC * D * 2;
-  static_assert(BC * CPR % NT == 0, "K staging must divide evenly");
+  constexpr int BR = NW * 32;         // query rows per workgroup
+  constexpr int CPR = D / 8;          // 16-byte chunks per K/V row
+  constexpr int TBYTES = BC * D * 2;  // one K or V tile
+  constexpr int LOADS = TBYTES / (NW * 64 * 16);  // 1 KiB wave loads per thread
+  static_assert(TBYTES % (NW * 64 * 16) == 0, "tile must split into wave loads");
   static_assert(BC % 32 == 0 && D % 32 == 0, "MFMA 32x32 blocking");
   using X8 = typename Vec<FP16>::x8;
   using X4 = typename Vec<FP16>::x4;
+  using X2 = typename Vec<FP16>::x2;
   using E = typename Vec<FP16>::e;
 
-  __shared__ __attribute__((aligned(16))) char smem[4 * KBYTES];
-  char* const k_lds = smem;                 // [2][BC][D] row-major, swizzled
-  char* const v_lds = smem + 2 * KBYTES;    // [2][D][BC] transposed, swizzled
+  // [2][BC][D] K tiles then [2][BC][D] V tiles, row-major, swizzled
+  __shared__ __attribute__((aligned(16))) char smem[4 * TBYTES];
+  lds_char* const lds = (lds_char*)smem;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -132,18 +179,59 @@ fa2_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const int bh = id / q_tiles;
   const int qt = id - bh * q_tiles;
   const int64_t head = (int64_t)bh * N * D;
-  const uint16_t* __restrict__ qh = q + head;
-  const uint16_t* __restrict__ kh = k + head;
-  const uint16_t* __restrict__ vh = v + head;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const __amdgpu_buffer_rsrc_t q_rs = make_rsrc(q + head, head_bytes);
+  const i32x4 k_rs = make_rsrc_words(k + head, head_bytes);
+  const i32x4 v_rs = make_rsrc_words(v + head, head_bytes);
+  const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+
+  // Global -> LDS without registers: each wave load moves 64 x 16 B into 1 KiB
+  // of LDS (lane l to byte 16*l).  The swizzle is applied on the global side:
+  // lane l fetches the logical chunk that belongs at its LDS position.  Rows
+  // past N read as zeros (buffer range check); their keys are masked later.
+  uint32_t src_off[LOADS];  // byte offset of this lane's chunk within a tile
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int lin = (i * NW + wave) * 64 + lane;  // physical chunk in the tile
+    const int row = lin / CPR, pc = lin % CPR;
+    src_off[i] = (uint32_t)(row * D * 2 + k_swizzle<CPR>(row, pc) * 16);
+  }
+  uint32_t src_off_v[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int lin = (i * NW + wave) * 64 + lane;
+    const int row = lin / CPR, pc = lin % CPR;
+    src_off_v[i] = (uint32_t)(row * D * 2 + v_swizzle<CPR>(row, pc) * 16);
+  }
+  auto issue_tile = [&](int j) {
+    const int buf = j & 1;
+    const uint32_t base = (uint32_t)j * TBYTES;  // tile j starts at key j*BC
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const uint32_t dst = lds_base + buf * TBYTES + (i * NW + wave) * 1024;
+      load_lds16(k_rs, base + src_off[i], dst);
+      load_lds16(v_rs, base + src_off_v[i], dst + 2 * TBYTES);
+    }
+  };
 
   // Q_i fragments: the B operand of S^T = K_j Q_i^T, held for the whole loop.
   const int qrow = qt * BR + wave * 32 + l32;
-  const int qrow_c = qrow < N ? qrow : N - 1;
   X8 qf[D / 16];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks)
     qf[ks] = __builtin_bit_cast(
-        X8, *(const u32x4*)(qh + (int64_t)qrow_c * D + ks * 16 + half * 8));
+        X8, __builtin_amdgcn_raw_buffer_load_b128(
+                q_rs, (uint32_t)(qrow * D * 2 + ks * 32 + half * 16), 0, 0));
+
+  const int n_tiles = (N + BC - 1) / BC;
+  issue_tile(0);
+  // Retire the Q loads and tile 0 before the loop: vmcnt is a counter, so a
+  // load still in flight at the loop head would make every iteration wait on
+  // its own prefetch.
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) asm volatile("" ::"v"(qf[ks]));
+  wait_vmem();
+  __syncthreads();
 
   f32x16 acc[D / 32];
 #pragma unroll
@@ -153,87 +241,19 @@ fa2_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   float m_ref = -INFINITY;  // reference max of this query, log2 units
   float l_part = 0.0f;      // this lane's share of the row sum
 
-  u32x4 kst[KCH];
-  u32x4 vst[VU][4];
-
-  auto load_tile = [&](int key0) {
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int ch = tid + NT * i;
-      const int row = ch / CPR, cc = ch % CPR;
-      int kr = key0 + row;
-      kr = kr < N ? kr : N - 1;
-      kst[i] = *(const u32x4*)(kh + (int64_t)kr * D + cc * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < VU; ++i) {
-      const int u = tid + NT * i;
-      if (VUNITS % NT == 0 || u < VUNITS) {
-        const int g4 = u / CPR, dc = u % CPR;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          int vr = key0 + 4 * g4 + r;
-          vr = vr < N ? vr : N - 1;
-          vst[i][r] = *(const u32x4*)(vh + (int64_t)vr * D + dc * 8);
-        }
-      }
-    }
-  };
-
-  auto store_tile = [&](int buf) {
-    char* kb = k_lds + buf * KBYTES;
-    char* vb = v_lds + buf * KBYTES;
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int ch = tid + NT * i;
-      const int row = ch / CPR, cc = ch % CPR;
-      *(u32x4*)(kb + row * (D * 2) + swizzle<CPR>(row, cc) * 16) = kst[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VU; ++i) {
-      const int u = tid + NT * i;
-      if (VUNITS % NT == 0 || u < VUNITS) {
-        const int g4 = u / CPR, dc = u % CPR;
-        // Key group g4 = 4 consecutive keys.  Within each 16-key step the
-        // second and third groups trade places, matching the key order of the
-        // S^T accumulator (lane half h, slot s -> key (s/4)*8 + h*4 + s%4).
-        const int gi = g4 & 3;
-        const int pg = ((gi & 1) << 1) | (gi >> 1);
-        const int chunk = (g4 >> 2) * 2 + (pg >> 1);
-        const int hoff = (pg & 1) * 8;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int w = e >> 1;
-          uint32_t lo, hi;
-          if (e & 1) {
-            lo = (vst[i][0][w] >> 16) | (vst[i][1][w] & 0xffff0000u);
-            hi = (vst[i][2][w] >> 16) | (vst[i][3][w] & 0xffff0000u);
-          } else {
-            lo = (vst[i][0][w] & 0xffffu) | (vst[i][1][w] << 16);
-            hi = (vst[i][2][w] & 0xffffu) | (vst[i][3][w] << 16);
-          }
-          const int d = dc * 8 + e;
-          u32x2 pk;
-          pk[0] = lo;
-          pk[1] = hi;
-          *(u32x2*)(vb + d * (BC * 2) + swizzle<CPRV>(d, chunk) * 16 + hoff) = pk;
-        }
-      }
-    }
-  };
-
-  const int n_tiles = (N + BC - 1) / BC;
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
+  // lane roles for the transposed V reads (16-lane groups)
+  const int g = lane >> 4;       // group 0..3; half = g >> 1
+  const int gi = lane & 15;
+  const int tr_row = half * 4 + (gi >> 2);               // + step*16 + sg*8
+  const int tr_col = 16 * (g & 1) + 4 * (gi & 3);        // + db*32 (elements)
 
   for (int j = 0; j < n_tiles; ++j) {
     const int buf = j & 1;
     const bool more = j + 1 < n_tiles;
-    if (more) load_tile((j + 1) * BC);
+    if (more) issue_tile(j + 1);
 
-    const char* kb = k_lds + buf * KBYTES;
-    const char* vb = v_lds + buf * KBYTES;
+    const lds_char* kb = lds + buf * TBYTES;
+    const lds_char* vb = lds + 2 * TBYTES + buf * TBYTES;
 
     // ---- S^T = K_j Q_i^T : [BC keys] x [32 queries] per wave
     f32x16 s[BC / 32];
@@ -245,8 +265,8 @@ fa2_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
         const X8 a = __builtin_bit_cast(
-            X8, *(const u32x4*)(kb + row * (D * 2) +
-                                swizzle<CPR>(row, ks * 2 + half) * 16));
+            X8, *(const __attribute__((address_space(3))) u32x4*)(
+                    kb + row * (D * 2) + k_swizzle<CPR>(row, ks * 2 + half) * 16));
         s[kb32] = mfma32x32x16<FP16>(a, qf[ks], s[kb32]);
       }
     }
@@ -287,6 +307,17 @@ fa2_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       m_ref = m_new;
     }
 
+#pragma unroll
+    for (int kb32 = 0; kb32 < BC / 32; ++kb32)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[kb32][i] = __builtin_fmaf(s[kb32][i], c, -m_ref);
+    if (tail) {  // masked keys hold +-inf, which c = 0 would turn into NaN
+#pragma unroll
+      for (int kb32 = 0; kb32 < BC / 32; ++kb32)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (key_of(kb32, i) >= N) s[kb32][i] = -INFINITY;
+    }
     // p in fp32; the row sum takes the unrounded p, the second product takes
     // p rounded to the input type.
     float rs = 0.0f;
@@ -294,14 +325,12 @@ fa2_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     for (int kb32 = 0; kb32 < BC / 32; ++kb32)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb32][i], c, -m_ref));
-        if (tail && key_of(kb32, i) >= N) p = 0.0f;
+        const float p = __builtin_amdgcn_exp2f(s[kb32][i]);
         s[kb32][i] = p;
         rs += p;
       }
     l_part += rs;
 
-    using X2 = typename Vec<FP16>::x2;
     X8 pf[BC / 16];
 #pragma unroll
     for (int st = 0; st < BC / 16; ++st) {
@@ -315,20 +344,28 @@ fa2_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       pf[st] = __builtin_bit_cast(X8, w);
     }
 
-    // ---- O^T += V_j^T P^T : [D] x [32 queries] per wave
+    // ---- O^T += V_j^T P^T : [D] x [32 queries] per wave.  The A operand
+    // (V^T, 8 keys per lane in the S^T accumulator's key order) comes from the
+    // row-major V tile through two transposing LDS reads of 4 keys each.
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
-      const int d = db * 32 + l32;
 #pragma unroll
       for (int st = 0; st < BC / 16; ++st) {
+        s16x4 part[2];
+#pragma unroll
+        for (int sg = 0; sg < 2; ++sg) {
+          const int row = st * 16 + sg * 8 + tr_row;
+          const int col = db * 32 + tr_col;  // element; chunk = col / 8
+          const int off = row * (D * 2) + v_swizzle<CPR>(row, col >> 3) * 16 + (col & 7) * 2;
+          part[sg] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + off));
+        }
         const X8 a = __builtin_bit_cast(
-            X8, *(const u32x4*)(vb + d * (BC * 2) +
-                                swizzle<CPRV>(d, st * 2 + half) * 16));
+            X8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
         acc[db] = mfma32x32x16<FP16>(a, pf[st], acc[db]);
       }
     }
 
-    if (more) store_tile(buf ^ 1);
+    if (more) wait_vmem();  // tile j+1 has landed in LDS (this wave's share)
     __syncthreads();
   }
 
@@ -340,11 +377,11 @@ fa2_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+      for (int g4 = 0; g4 < 4; ++g4) {
         X4 ov;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ov[e] = (E)(acc[db][g * 4 + e] * inv);
-        *(u32x2*)(orow + db * 32 + g * 8 + half * 4) = __builtin_bit_cast(u32x2, ov);
+        for (int e = 0; e < 4; ++e) ov[e] = (E)(acc[db][g4 * 4 + e] * inv);
+        *(u32x2*)(orow + db * 32 + g4 * 8 + half * 4) = __builtin_bit_cast(u32x2, ov);
       }
     if (half == 0)
       lse[(int64_t)bh * N + qrow] = (m_ref + __log2f(l_tot)) * kLn2;
