@@ -83,12 +83,14 @@ def cpu_baseline(w, q, k, v):
 
 
 def calibrate_copy(nbytes=1 << 30, reps=5):
+    """A copy-shaped elementwise kernel (dst = -src, fp32) that reads and
+    writes exactly nbytes each, to scale the HBM byte counters."""
     import torch
     src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
     for _ in range(reps):
-        dst.copy_(src)
+        torch.neg(src, out=dst)
     torch.cuda.synchronize()
     print(json.dumps({"calibrate_copy_bytes_read": nbytes, "bytes_written": nbytes,
                       "reps": reps}), flush=True)

@@ -141,7 +141,11 @@ template <> struct Cfg<64> { static constexpr int BC = 64, NW = 4, OCC = 2; };
 template <> struct Cfg<128> { static constexpr int BC = 64, NW = 4, OCC = 2; };
 template <> struct Cfg<256> { static constexpr int BC = 32, NW = 4, OCC = 1; };
 
-template <int D, bool FP16, bool NEG>
+// Sign of the folded scale c = scale * log2(e): the running extreme of the raw
+// logits is a max for c > 0 and a min for c < 0; c == 0 is uniform attention.
+enum ScaleMode { kPositive = 0, kNegative = 1, kZero = 2 };
+
+template <int D, bool FP16, int MODE>
 __global__ void __attribute__((amdgpu_flat_work_group_size(Cfg<D>::NW * 64,
                                                            Cfg<D>::NW * 64),
                                amdgpu_waves_per_eu(Cfg<D>::OCC, Cfg<D>::OCC)))
@@ -153,8 +157,11 @@ fa2_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   constexpr int NW = Cfg<D>::NW;
   constexpr int BR = NW * 32;         // query rows per workgroup
   constexpr int CPR = D / 8;          // 16-byte chunks per K/V row
-  constexpr int TBYTES = BC * D * 2;  // one K or V tile
+  constexpr int RB = D * 2;           // bytes per K/V row
+  constexpr int TBYTES = BC * RB;     // one K or V tile
   constexpr int LOADS = TBYTES / (NW * 64 * 16);  // 1 KiB wave loads per thread
+  constexpr int KS = D / 16;          // k-steps of the first product
+  constexpr int ST = BC / 16;         // k-steps of the second product
   static_assert(TBYTES % (NW * 64 * 16) == 0, "tile must split into wave loads");
   static_assert(BC % 32 == 0 && D % 32 == 0, "MFMA 32x32 blocking");
   using X8 = typename Vec<FP16>::x8;
@@ -162,7 +169,8 @@ fa2_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   using X2 = typename Vec<FP16>::x2;
   using E = typename Vec<FP16>::e;
 
-  // [2][BC][D] K tiles then [2][BC][D] V tiles, row-major, swizzled
+  // LDS: K tiles [2][BC][D] at 0, V tiles [2][BC][D] at 2*TBYTES; row-major,
+  // swizzled.  Tile j of K and of V lives in buffer j & 1.
   __shared__ __attribute__((aligned(16))) char smem[4 * TBYTES];
   lds_char* const lds = (lds_char*)smem;
 
@@ -189,49 +197,91 @@ fa2_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   // of LDS (lane l to byte 16*l).  The swizzle is applied on the global side:
   // lane l fetches the logical chunk that belongs at its LDS position.  Rows
   // past N read as zeros (buffer range check); their keys are masked later.
-  uint32_t src_off[LOADS];  // byte offset of this lane's chunk within a tile
+  uint32_t k_src[LOADS], v_src[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
     const int lin = (i * NW + wave) * 64 + lane;  // physical chunk in the tile
     const int row = lin / CPR, pc = lin % CPR;
-    src_off[i] = (uint32_t)(row * D * 2 + k_swizzle<CPR>(row, pc) * 16);
+    k_src[i] = (uint32_t)(row * RB + k_swizzle<CPR>(row, pc) * 16);
+    v_src[i] = (uint32_t)(row * RB + v_swizzle<CPR>(row, pc) * 16);
   }
-  uint32_t src_off_v[LOADS];
+  auto issue_k = [&](int j) {
+    const uint32_t dst = lds_base + (j & 1) * TBYTES + wave * 1024;
 #pragma unroll
-  for (int i = 0; i < LOADS; ++i) {
-    const int lin = (i * NW + wave) * 64 + lane;
-    const int row = lin / CPR, pc = lin % CPR;
-    src_off_v[i] = (uint32_t)(row * D * 2 + v_swizzle<CPR>(row, pc) * 16);
-  }
-  auto issue_tile = [&](int j) {
-    const int buf = j & 1;
-    const uint32_t base = (uint32_t)j * TBYTES;  // tile j starts at key j*BC
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const uint32_t dst = lds_base + buf * TBYTES + (i * NW + wave) * 1024;
-      load_lds16(k_rs, base + src_off[i], dst);
-      load_lds16(v_rs, base + src_off_v[i], dst + 2 * TBYTES);
-    }
+    for (int i = 0; i < LOADS; ++i)
+      load_lds16(k_rs, (uint32_t)j * TBYTES + k_src[i], dst + i * NW * 1024);
   };
+  auto issue_v = [&](int j) {
+    const uint32_t dst = lds_base + 2 * TBYTES + (j & 1) * TBYTES + wave * 1024;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i)
+      load_lds16(v_rs, (uint32_t)j * TBYTES + v_src[i], dst + i * NW * 1024);
+  };
+
+  // Per-lane LDS byte offsets of the MFMA operands within a tile.  The
+  // swizzle term depends only on the lane (row bits below the 32- or 16-row
+  // block), so every other index becomes an instruction immediate.
+  //   K (A operand of S^T): row kb32*32 + l32, logical chunk ks*2 + half.
+  //   V^T (A operand of O^T), via ds_read_b64_tr_b16: the 16-lane group g
+  //   reads rows st*16 + sg*8 + half*4 + (lane%16)/4 and 4 elements at column
+  //   db*32 + 16*(g&1) + 4*(lane%4); lane l then holds V[key][db*32 + l32]
+  //   for keys st*16 + sg*8 + half*4 + 0..3.
+  uint32_t k_off[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    k_off[ks] = (uint32_t)(l32 * RB + k_swizzle<CPR>(l32, ks * 2 + half) * 16);
+  const int tr_row = half * 4 + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  uint32_t v_off[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    const int col = db * 32 + tr_col;
+    v_off[db] = (uint32_t)(2 * TBYTES + tr_row * RB +
+                           v_swizzle<CPR>(tr_row, col >> 3) * 16 + (col & 7) * 2);
+  }
 
   // Q_i fragments: the B operand of S^T = K_j Q_i^T, held for the whole loop.
   const int qrow = qt * BR + wave * 32 + l32;
-  X8 qf[D / 16];
+  X8 qf[KS];
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks)
+  for (int ks = 0; ks < KS; ++ks)
     qf[ks] = __builtin_bit_cast(
         X8, __builtin_amdgcn_raw_buffer_load_b128(
-                q_rs, (uint32_t)(qrow * D * 2 + ks * 32 + half * 16), 0, 0));
+                q_rs, (uint32_t)(qrow * RB + ks * 32 + half * 16), 0, 0));
+
+  // S^T_j = K_j Q_i^T : [BC keys] x [32 queries] per wave
+  auto gemm1 = [&](int j, f32x16* sd) {
+    const lds_char* kb = lds + (j & 1) * TBYTES;
+#pragma unroll
+    for (int kb32 = 0; kb32 < BC / 32; ++kb32)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sd[kb32][i] = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int kb32 = 0; kb32 < BC / 32; ++kb32) {
+        const X8 a = __builtin_bit_cast(
+            X8, *(const __attribute__((address_space(3))) u32x4*)(
+                    kb + kb32 * 32 * RB + k_off[ks]));
+        sd[kb32] = mfma32x32x16<FP16>(a, qf[ks], sd[kb32]);
+      }
+  };
 
   const int n_tiles = (N + BC - 1) / BC;
-  issue_tile(0);
-  // Retire the Q loads and tile 0 before the loop: vmcnt is a counter, so a
-  // load still in flight at the loop head would make every iteration wait on
-  // its own prefetch.
+  // Prologue: K_0, V_0 and K_1 in flight, S_0 computed.  Q and tile 0 retire
+  // before the loop: vmcnt is a counter, so a load still in flight at the
+  // loop head would make every iteration wait on its own prefetch.
+  issue_k(0);
+  issue_v(0);
+  if (n_tiles > 1) issue_k(1);
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) asm volatile("" ::"v"(qf[ks]));
+  for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]));
   wait_vmem();
   __syncthreads();
+
+  f32x16 s[BC / 32];
+  gemm1(0, s);
+  __syncthreads();  // every wave is done with K_0 before K_2 may overwrite it
 
   f32x16 acc[D / 32];
 #pragma unroll
@@ -241,37 +291,16 @@ fa2_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   float m_ref = -INFINITY;  // reference max of this query, log2 units
   float l_part = 0.0f;      // this lane's share of the row sum
 
-  // lane roles for the transposed V reads (16-lane groups)
-  const int g = lane >> 4;       // group 0..3; half = g >> 1
-  const int gi = lane & 15;
-  const int tr_row = half * 4 + (gi >> 2);               // + step*16 + sg*8
-  const int tr_col = 16 * (g & 1) + 4 * (gi & 3);        // + db*32 (elements)
-
+  // Iteration j: softmax of S_j overlapped with S_{j+1} = K_{j+1} Q^T on the
+  // matrix cores, then O += P_j V_j.  K runs one tile ahead of V, so the
+  // loads issued here are K_{j+2} and V_{j+1}; each buffer is refilled only
+  // after the barrier that ends the iteration which last read it.
   for (int j = 0; j < n_tiles; ++j) {
-    const int buf = j & 1;
-    const bool more = j + 1 < n_tiles;
-    if (more) issue_tile(j + 1);
+    const bool next = j + 1 < n_tiles;
+    if (j + 2 < n_tiles) issue_k(j + 2);
+    if (next) issue_v(j + 1);
 
-    const lds_char* kb = lds + buf * TBYTES;
-    const lds_char* vb = lds + 2 * TBYTES + buf * TBYTES;
-
-    // ---- S^T = K_j Q_i^T : [BC keys] x [32 queries] per wave
-    f32x16 s[BC / 32];
-#pragma unroll
-    for (int kb32 = 0; kb32 < BC / 32; ++kb32) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[kb32][i] = 0.0f;
-      const int row = kb32 * 32 + l32;
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const X8 a = __builtin_bit_cast(
-            X8, *(const __attribute__((address_space(3))) u32x4*)(
-                    kb + row * (D * 2) + k_swizzle<CPR>(row, ks * 2 + half) * 16));
-        s[kb32] = mfma32x32x16<FP16>(a, qf[ks], s[kb32]);
-      }
-    }
-
-    // ---- online softmax (fp32, log2 units, scale folded into c)
+    // ---- online softmax of S_j (fp32, log2 units, scale folded into c)
     const int key0 = j * BC;
     const bool tail = key0 + BC > N;  // wave-uniform
     auto key_of = [&](int kb32, int i) {
@@ -282,14 +311,14 @@ fa2_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       for (int kb32 = 0; kb32 < BC / 32; ++kb32)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          if (key_of(kb32, i) >= N) s[kb32][i] = NEG ? INFINITY : -INFINITY;
+          if (key_of(kb32, i) >= N) s[kb32][i] = MODE == kNegative ? INFINITY : -INFINITY;
     }
     float ext = s[0][0];
 #pragma unroll
     for (int kb32 = 0; kb32 < BC / 32; ++kb32)
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        ext = NEG ? fminf(ext, s[kb32][i]) : fmaxf(ext, s[kb32][i]);
+        ext = MODE == kNegative ? fminf(ext, s[kb32][i]) : fmaxf(ext, s[kb32][i]);
     const float t_max = __builtin_isfinite(ext) ? ext * c : -INFINITY;
 
     if (__builtin_amdgcn_ballot_w64(t_max > m_ref + kRescaleSlack) != 0) {
@@ -307,65 +336,77 @@ fa2_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       m_ref = m_new;
     }
 
-#pragma unroll
-    for (int kb32 = 0; kb32 < BC / 32; ++kb32)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[kb32][i] = __builtin_fmaf(s[kb32][i], c, -m_ref);
-    if (tail) {  // masked keys hold +-inf, which c = 0 would turn into NaN
+    // x = t - m_ref.  A masked key holds -inf (c > 0) or +inf (c < 0), so
+    // its x is -inf and its p is 0.  With c == 0 every logit is 0.
+    if constexpr (MODE == kZero) {
 #pragma unroll
       for (int kb32 = 0; kb32 < BC / 32; ++kb32)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          if (key_of(kb32, i) >= N) s[kb32][i] = -INFINITY;
+          s[kb32][i] = tail && key_of(kb32, i) >= N ? -INFINITY : -m_ref;
+    } else {
+#pragma unroll
+      for (int kb32 = 0; kb32 < BC / 32; ++kb32)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[kb32][i] = __builtin_fmaf(s[kb32][i], c, -m_ref);
     }
-    // p in fp32; the row sum takes the unrounded p, the second product takes
-    // p rounded to the input type.
-    float rs = 0.0f;
-#pragma unroll
-    for (int kb32 = 0; kb32 < BC / 32; ++kb32)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(s[kb32][i]);
-        s[kb32][i] = p;
-        rs += p;
-      }
-    l_part += rs;
 
-    X8 pf[BC / 16];
+    // p in fp32; the row sum takes the unrounded p, the second product takes
+    // p rounded to the input type.  The next tile's first product is issued
+    // in the same block so the matrix cores run while the VALU does this.
+    X8 pf[ST];
+    f32x16 sn[BC / 32];
+    auto softmax_p = [&]() {
+      float rs = 0.0f;
 #pragma unroll
-    for (int st = 0; st < BC / 16; ++st) {
-      u32x4 w;
+      for (int st = 0; st < ST; ++st) {
+        u32x4 w;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const X2 pair = {(E)s[st >> 1][(st & 1) * 8 + 2 * e],
-                         (E)s[st >> 1][(st & 1) * 8 + 2 * e + 1]};
-        w[e] = __builtin_bit_cast(uint32_t, pair);
+        for (int e = 0; e < 4; ++e) {
+          const int i0 = (st & 1) * 8 + 2 * e;
+          const float p0 = __builtin_amdgcn_exp2f(s[st >> 1][i0]);
+          const float p1 = __builtin_amdgcn_exp2f(s[st >> 1][i0 + 1]);
+          rs += p0;
+          rs += p1;
+          const X2 pair = {(E)p0, (E)p1};
+          w[e] = __builtin_bit_cast(uint32_t, pair);
+        }
+        pf[st] = __builtin_bit_cast(X8, w);
       }
-      pf[st] = __builtin_bit_cast(X8, w);
+      l_part += rs;
+    };
+    // The last iteration also runs this product on whatever the idle K
+    // buffer holds and drops the result; that keeps one straight-line block
+    // for the scheduler to interleave.
+    gemm1(j + 1, sn);
+    softmax_p();
+#pragma unroll
+    for (int t = 0; t < KS * (BC / 32); ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // 6 VALU
     }
 
     // ---- O^T += V_j^T P^T : [D] x [32 queries] per wave.  The A operand
     // (V^T, 8 keys per lane in the S^T accumulator's key order) comes from the
     // row-major V tile through two transposing LDS reads of 4 keys each.
+    const lds_char* vb = lds + (j & 1) * TBYTES;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
+    for (int st = 0; st < ST; ++st)
 #pragma unroll
-      for (int st = 0; st < BC / 16; ++st) {
-        s16x4 part[2];
-#pragma unroll
-        for (int sg = 0; sg < 2; ++sg) {
-          const int row = st * 16 + sg * 8 + tr_row;
-          const int col = db * 32 + tr_col;  // element; chunk = col / 8
-          const int off = row * (D * 2) + v_swizzle<CPR>(row, col >> 3) * 16 + (col & 7) * 2;
-          part[sg] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + off));
-        }
+      for (int db = 0; db < D / 32; ++db) {
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(vb + v_off[db] + (st * 16) * RB));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(vb + v_off[db] + (st * 16 + 8) * RB));
         const X8 a = __builtin_bit_cast(
-            X8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+            X8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         acc[db] = mfma32x32x16<FP16>(a, pf[st], acc[db]);
       }
-    }
 
-    if (more) wait_vmem();  // tile j+1 has landed in LDS (this wave's share)
+#pragma unroll
+    for (int kb32 = 0; kb32 < BC / 32; ++kb32) s[kb32] = sn[kb32];
+    if (next) wait_vmem();  // this wave's share of K_{j+2} and V_{j+1} landed
     __syncthreads();
   }
 
@@ -391,10 +432,18 @@ fa2_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 typedef void (*kernel_fn)(const uint16_t*, const uint16_t*, const uint16_t*,
                           uint16_t*, float*, int, int, int, float);
 
+template <int D, bool FP16>
+kernel_fn pick_mode(int mode) {
+  switch (mode) {
+    case kNegative: return fa2_fwd_kernel<D, FP16, kNegative>;
+    case kZero: return fa2_fwd_kernel<D, FP16, kZero>;
+    default: return fa2_fwd_kernel<D, FP16, kPositive>;
+  }
+}
+
 template <int D>
-kernel_fn pick(bool fp16, bool neg) {
-  if (fp16) return neg ? fa2_fwd_kernel<D, true, true> : fa2_fwd_kernel<D, true, false>;
-  return neg ? fa2_fwd_kernel<D, false, true> : fa2_fwd_kernel<D, false, false>;
+kernel_fn pick(bool fp16, int mode) {
+  return fp16 ? pick_mode<D, true>(mode) : pick_mode<D, false>(mode);
 }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -465,10 +514,10 @@ int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
   // logits in log2 units: t = s * scale * log2(e)
   const float c = (float)((double)scale * 1.4426950408889634074);
   const bool fp16 = dtype == FA2_FP16;
-  const bool neg = c < 0.0f;
-  fa2::kernel_fn fn = d == 64 ? fa2::pick<64>(fp16, neg)
-                    : d == 128 ? fa2::pick<128>(fp16, neg)
-                               : fa2::pick<256>(fp16, neg);
+  const int mode = c > 0.0f ? fa2::kPositive : c < 0.0f ? fa2::kNegative : fa2::kZero;
+  fa2::kernel_fn fn = d == 64 ? fa2::pick<64>(fp16, mode)
+                    : d == 128 ? fa2::pick<128>(fp16, mode)
+                               : fa2::pick<256>(fp16, mode);
   const uint16_t* qp = (const uint16_t*)q;
   const uint16_t* kp = (const uint16_t*)k;
   const uint16_t* vp = (const uint16_t*)v;
