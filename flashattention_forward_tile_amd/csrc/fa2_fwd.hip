@@ -33,6 +33,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fa2.h"
 
 namespace fa2 {
@@ -47,8 +49,6 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-// p = exp2(t - m_ref) may reach 2^kRescaleSlack before O is rescaled.
-constexpr float kRescaleSlack = 8.0f;
 constexpr float kLn2 = 0.69314718055994530942f;
 
 template <bool FP16> struct Vec;
@@ -134,12 +134,17 @@ __device__ __forceinline__ void load_lds16(i32x4 rsrc, uint32_t voff, uint32_t l
                : "memory");
 }
 
-// Tile shape per head dimension: key rows per tile, waves per workgroup, and
-// the waves per SIMD the register budget is sized for.
+// Tile shape per head dimension: key rows per tile (BC), waves per workgroup
+// (NW) and the waves per SIMD the register budget is sized for (OCC).
 template <int D> struct Cfg;
 template <> struct Cfg<64> { static constexpr int BC = 64, NW = 4, OCC = 2; };
 template <> struct Cfg<128> { static constexpr int BC = 64, NW = 4, OCC = 2; };
 template <> struct Cfg<256> { static constexpr int BC = 32, NW = 4, OCC = 1; };
+
+// p = exp2(t - m_ref) is summed over each lane's keys of a tile; while that
+// sum stays at or below kSumLimit no p exceeds it, and the reference max is
+// left alone.  Otherwise the row's reference moves to its true running max.
+constexpr float kSumLimit = 256.0f;
 
 // Sign of the folded scale c = scale * log2(e): the running extreme of the raw
 // logits is a max for c > 0 and a min for c < 0; c == 0 is uniform attention.
@@ -162,6 +167,8 @@ fa2_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   constexpr int LOADS = TBYTES / (NW * 64 * 16);  // 1 KiB wave loads per thread
   constexpr int KS = D / 16;          // k-steps of the first product
   constexpr int ST = BC / 16;         // k-steps of the second product
+  constexpr int KB = BC / 32;         // 32-key blocks per tile
+  constexpr int DB = D / 32;          // 32-dim blocks of the output
   static_assert(TBYTES % (NW * 64 * 16) == 0, "tile must split into wave loads");
   static_assert(BC % 32 == 0 && D % 32 == 0, "MFMA 32x32 blocking");
   using X8 = typename Vec<FP16>::x8;
@@ -221,7 +228,7 @@ fa2_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   // Per-lane LDS byte offsets of the MFMA operands within a tile.  The
   // swizzle term depends only on the lane (row bits below the 32- or 16-row
   // block), so every other index becomes an instruction immediate.
-  //   K (A operand of S^T): row kb32*32 + l32, logical chunk ks*2 + half.
+  //   K (A operand of S^T): row kb*32 + l32, logical chunk ks*2 + half.
   //   V^T (A operand of O^T), via ds_read_b64_tr_b16: the 16-lane group g
   //   reads rows st*16 + sg*8 + half*4 + (lane%16)/4 and 4 elements at column
   //   db*32 + 16*(g&1) + 4*(lane%4); lane l then holds V[key][db*32 + l32]
@@ -232,9 +239,9 @@ fa2_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     k_off[ks] = (uint32_t)(l32 * RB + k_swizzle<CPR>(l32, ks * 2 + half) * 16);
   const int tr_row = half * 4 + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  uint32_t v_off[D / 32];
+  uint32_t v_off[DB];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) {
+  for (int db = 0; db < DB; ++db) {
     const int col = db * 32 + tr_col;
     v_off[db] = (uint32_t)(2 * TBYTES + tr_row * RB +
                            v_swizzle<CPR>(tr_row, col >> 3) * 16 + (col & 7) * 2);
@@ -249,152 +256,44 @@ fa2_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         X8, __builtin_amdgcn_raw_buffer_load_b128(
                 q_rs, (uint32_t)(qrow * RB + ks * 32 + half * 16), 0, 0));
 
-  // S^T_j = K_j Q_i^T : [BC keys] x [32 queries] per wave
-  auto gemm1 = [&](int j, f32x16* sd) {
-    const lds_char* kb = lds + (j & 1) * TBYTES;
+  f32x16 acc[DB];
 #pragma unroll
-    for (int kb32 = 0; kb32 < BC / 32; ++kb32)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sd[kb32][i] = 0.0f;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int kb32 = 0; kb32 < BC / 32; ++kb32) {
-        const X8 a = __builtin_bit_cast(
-            X8, *(const __attribute__((address_space(3))) u32x4*)(
-                    kb + kb32 * 32 * RB + k_off[ks]));
-        sd[kb32] = mfma32x32x16<FP16>(a, qf[ks], sd[kb32]);
-      }
-  };
-
-  const int n_tiles = (N + BC - 1) / BC;
-  // Prologue: K_0, V_0 and K_1 in flight, S_0 computed.  Q and tile 0 retire
-  // before the loop: vmcnt is a counter, so a load still in flight at the
-  // loop head would make every iteration wait on its own prefetch.
-  issue_k(0);
-  issue_v(0);
-  if (n_tiles > 1) issue_k(1);
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]));
-  wait_vmem();
-  __syncthreads();
-
-  f32x16 s[BC / 32];
-  gemm1(0, s);
-  __syncthreads();  // every wave is done with K_0 before K_2 may overwrite it
-
-  f32x16 acc[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[db][i] = 0.0f;
   float m_ref = -INFINITY;  // reference max of this query, log2 units
   float l_part = 0.0f;      // this lane's share of the row sum
 
-  // Iteration j: softmax of S_j overlapped with S_{j+1} = K_{j+1} Q^T on the
-  // matrix cores, then O += P_j V_j.  K runs one tile ahead of V, so the
-  // loads issued here are K_{j+2} and V_{j+1}; each buffer is refilled only
-  // after the barrier that ends the iteration which last read it.
-  for (int j = 0; j < n_tiles; ++j) {
-    const bool next = j + 1 < n_tiles;
-    if (j + 2 < n_tiles) issue_k(j + 2);
-    if (next) issue_v(j + 1);
-
-    // ---- online softmax of S_j (fp32, log2 units, scale folded into c)
-    const int key0 = j * BC;
-    const bool tail = key0 + BC > N;  // wave-uniform
-    auto key_of = [&](int kb32, int i) {
-      return key0 + kb32 * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-    };
-    if (tail) {
+  // S^T_j = K_j Q_i^T : [BC keys] x [32 queries] per wave.  With a zero
+  // scale every logit is 0 whatever Q and K hold, so S stays 0 and c is taken
+  // as 1 (x = s - m_ref keeps masked keys at -inf).
+  auto gemm1 = [&](int j, f32x16 (&sd)[KB]) {
+    const lds_char* kb = lds + (j & 1) * TBYTES;
 #pragma unroll
-      for (int kb32 = 0; kb32 < BC / 32; ++kb32)
+    for (int kk = 0; kk < KB; ++kk)
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (key_of(kb32, i) >= N) s[kb32][i] = MODE == kNegative ? INFINITY : -INFINITY;
-    }
-    float ext = s[0][0];
+      for (int i = 0; i < 16; ++i) sd[kk][i] = 0.0f;
+    if constexpr (MODE == kZero) return;
 #pragma unroll
-    for (int kb32 = 0; kb32 < BC / 32; ++kb32)
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        ext = MODE == kNegative ? fminf(ext, s[kb32][i]) : fmaxf(ext, s[kb32][i]);
-    const float t_max = __builtin_isfinite(ext) ? ext * c : -INFINITY;
-
-    if (__builtin_amdgcn_ballot_w64(t_max > m_ref + kRescaleSlack) != 0) {
-      // Only rows whose own max outgrew the slack move their reference, so a
-      // row's arithmetic never depends on the other rows sharing its wave.
-      const float t_row = fmaxf(t_max, __shfl_xor(t_max, 32));
-      const float m_new = t_row > m_ref + kRescaleSlack ? t_row : m_ref;
-      const float alpha =
-          m_new == m_ref ? 1.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
-      l_part *= alpha;
-      m_ref = m_new;
-    }
-
-    // x = t - m_ref.  A masked key holds -inf (c > 0) or +inf (c < 0), so
-    // its x is -inf and its p is 0.  With c == 0 every logit is 0.
-    if constexpr (MODE == kZero) {
-#pragma unroll
-      for (int kb32 = 0; kb32 < BC / 32; ++kb32)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          s[kb32][i] = tail && key_of(kb32, i) >= N ? -INFINITY : -m_ref;
-    } else {
-#pragma unroll
-      for (int kb32 = 0; kb32 < BC / 32; ++kb32)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[kb32][i] = __builtin_fmaf(s[kb32][i], c, -m_ref);
-    }
-
-    // p in fp32; the row sum takes the unrounded p, the second product takes
-    // p rounded to the input type.  The next tile's first product is issued
-    // in the same block so the matrix cores run while the VALU does this.
-    X8 pf[ST];
-    f32x16 sn[BC / 32];
-    auto softmax_p = [&]() {
-      float rs = 0.0f;
-#pragma unroll
-      for (int st = 0; st < ST; ++st) {
-        u32x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i0 = (st & 1) * 8 + 2 * e;
-          const float p0 = __builtin_amdgcn_exp2f(s[st >> 1][i0]);
-          const float p1 = __builtin_amdgcn_exp2f(s[st >> 1][i0 + 1]);
-          rs += p0;
-          rs += p1;
-          const X2 pair = {(E)p0, (E)p1};
-          w[e] = __builtin_bit_cast(uint32_t, pair);
-        }
-        pf[st] = __builtin_bit_cast(X8, w);
+      for (int kk = 0; kk < KB; ++kk) {
+        const X8 a = __builtin_bit_cast(
+            X8, *(const __attribute__((address_space(3))) u32x4*)(
+                    kb + kk * 32 * RB + k_off[ks]));
+        sd[kk] = mfma32x32x16<FP16>(a, qf[ks], sd[kk]);
       }
-      l_part += rs;
-    };
-    // The last iteration also runs this product on whatever the idle K
-    // buffer holds and drops the result; that keeps one straight-line block
-    // for the scheduler to interleave.
-    gemm1(j + 1, sn);
-    softmax_p();
-#pragma unroll
-    for (int t = 0; t < KS * (BC / 32); ++t) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // 6 VALU
-    }
+  };
 
-    // ---- O^T += V_j^T P^T : [D] x [32 queries] per wave.  The A operand
-    // (V^T, 8 keys per lane in the S^T accumulator's key order) comes from the
-    // row-major V tile through two transposing LDS reads of 4 keys each.
+  // O^T += V_j^T P_j^T : [D] x [32 queries] per wave.  The A operand (V^T,
+  // 8 keys per lane in the S^T accumulator's key order) comes from the
+  // row-major V tile through two transposing LDS reads of 4 keys each.
+  auto gemm2 = [&](int j, const X8 (&pf)[ST]) {
     const lds_char* vb = lds + (j & 1) * TBYTES;
 #pragma unroll
     for (int st = 0; st < ST; ++st)
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
+      for (int db = 0; db < DB; ++db) {
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (lds_s16x4*)(vb + v_off[db] + (st * 16) * RB));
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -403,11 +302,130 @@ fa2_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
             X8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         acc[db] = mfma32x32x16<FP16>(a, pf[st], acc[db]);
       }
+  };
 
+  // p = exp2(s*c - m_ref): rounded pairs into pf, the unrounded sum returned.
+  // A masked key holds -inf (c > 0) or +inf (c < 0), so its p is 0.
+  auto probs = [&](const f32x16 (&sc)[KB], X8 (&pf)[ST]) -> float {
+    float rs = 0.0f;
 #pragma unroll
-    for (int kb32 = 0; kb32 < BC / 32; ++kb32) s[kb32] = sn[kb32];
-    if (next) wait_vmem();  // this wave's share of K_{j+2} and V_{j+1} landed
+    for (int st = 0; st < ST; ++st) {
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i0 = (st & 1) * 8 + 2 * e;
+        const float x0 = __builtin_fmaf(sc[st >> 1][i0], c, -m_ref);
+        const float x1 = __builtin_fmaf(sc[st >> 1][i0 + 1], c, -m_ref);
+        const float p0 = __builtin_amdgcn_exp2f(x0);
+        const float p1 = __builtin_amdgcn_exp2f(x1);
+        rs += p0;
+        rs += p1;
+        const X2 pair = {(E)p0, (E)p1};
+        w[e] = __builtin_bit_cast(uint32_t, pair);
+      }
+      pf[st] = __builtin_bit_cast(X8, w);
+    }
+    return rs;
+  };
+
+  const int n_tiles = (N + BC - 1) / BC;
+
+  // One iteration j, as a single straight-line block for the scheduler:
+  // S_{j+1} = K_{j+1} Q^T and O += P_{j-1} V_{j-1} on the matrix cores while
+  // the VALU turns S_j into P_j.  K runs two tiles ahead of the V the block
+  // consumes; the loads issued here are K_{j+2} and V_j.  Every buffer is
+  // refilled only after the barrier ending the iteration that last read it.
+  // The last iteration's S_{j+1} product reads whatever the idle K buffer
+  // holds and is dropped.
+  auto step = [&](auto first, int j, f32x16 (&s_cur)[KB], f32x16 (&s_nxt)[KB],
+                  const X8 (&p_prev)[ST], X8 (&p_cur)[ST]) {
+    if (j + 2 < n_tiles) issue_k(j + 2);
+    issue_v(j);
+
+    const int key0 = j * BC;
+    const bool tail = key0 + BC > N;  // wave-uniform
+    if (tail) {
+#pragma unroll
+      for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (key0 + kk * 32 + (i >> 2) * 8 + half * 4 + (i & 3) >= N)
+            s_cur[kk][i] = MODE == kNegative ? INFINITY : -INFINITY;
+    }
+
+    gemm1(j + 1, s_nxt);
+    if constexpr (!decltype(first)::value) gemm2(j - 1, p_prev);
+    float rs = probs(s_cur, p_cur);
+    constexpr int MF = (MODE == kZero ? 0 : KS * KB) + (decltype(first)::value ? 0 : ST * DB);
+#pragma unroll
+    for (int t = 0; t < MF; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+    }
+
+    // While the unrounded sum of a lane's p stays at or below kSumLimit no p
+    // exceeds it and the reference max stands.  Otherwise (always on the
+    // first tile, where the sum is inf or NaN) rows whose sum outgrew the
+    // limit move their reference to their running max, rescale O and l, and
+    // get their p recomputed; other rows keep their reference, so a row's
+    // arithmetic never depends on its wave-mates.
+    if (__builtin_amdgcn_ballot_w64(!(rs <= kSumLimit)) != 0) {
+      float ext = s_cur[0][0];
+#pragma unroll
+      for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          ext = MODE == kNegative ? fminf(ext, s_cur[kk][i]) : fmaxf(ext, s_cur[kk][i]);
+      const float t_max = __builtin_isfinite(ext) ? ext * c : -INFINITY;
+      const float t_row = fmaxf(t_max, __shfl_xor(t_max, 32));
+      const float mine = !(rs <= kSumLimit) ? 1.0f : 0.0f;
+      const bool move = fmaxf(mine, __shfl_xor(mine, 32)) > 0.0f;
+      const float m_new = move ? fmaxf(m_ref, t_row) : m_ref;
+      const float alpha = m_new == m_ref ? 1.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+      l_part *= alpha;
+      m_ref = m_new;
+      rs = probs(s_cur, p_cur);
+    }
+    l_part += rs;
+
+    wait_vmem();  // this wave's share of K_{j+2} and V_j has landed
     __syncthreads();
+  };
+
+  // Prologue: Q, K_0 and K_1 resident, S_0 computed.  Q and the tiles retire
+  // before the loop: vmcnt is a counter, so a load still in flight at the
+  // loop head would make every iteration wait on its own prefetch.
+  issue_k(0);
+  if (n_tiles > 1) issue_k(1);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]));
+  wait_vmem();
+  __syncthreads();
+
+  f32x16 sA[KB], sB[KB];
+  X8 pA[ST], pB[ST];
+  gemm1(0, sA);
+  __syncthreads();  // every wave is done with K_0 before K_2 may overwrite it
+
+  // Iterations run in pairs so the S and P register sets swap roles without
+  // copies: even j computes (S_j in sA, S_{j+1} into sB, P_j into pA).
+  step(std::true_type{}, 0, sA, sB, pB, pA);
+  int j = 1;
+  for (; j + 1 < n_tiles; j += 2) {
+    step(std::false_type{}, j, sB, sA, pA, pB);
+    step(std::false_type{}, j + 1, sA, sB, pB, pA);
+  }
+  if (j < n_tiles) {
+    step(std::false_type{}, j, sB, sA, pA, pB);
+    gemm2(j, pB);
+  } else {
+    gemm2(j - 1, pA);
   }
 
   // ---- epilogue: O = acc / l, lse = (m_ref + log2 l) * ln 2
@@ -416,7 +434,7 @@ fa2_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   if (qrow < N) {
     uint16_t* orow = o + head + (int64_t)qrow * D;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         X4 ov;
@@ -515,6 +533,7 @@ int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
   const float c = (float)((double)scale * 1.4426950408889634074);
   const bool fp16 = dtype == FA2_FP16;
   const int mode = c > 0.0f ? fa2::kPositive : c < 0.0f ? fa2::kNegative : fa2::kZero;
+  const float c_arg = mode == fa2::kZero ? 1.0f : c;  // zero mode: logits are 0, t = s
   fa2::kernel_fn fn = d == 64 ? fa2::pick<64>(fp16, mode)
                     : d == 128 ? fa2::pick<128>(fp16, mode)
                                : fa2::pick<256>(fp16, mode);
@@ -523,7 +542,7 @@ int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
   const uint16_t* vp = (const uint16_t*)v;
   uint16_t* op = (uint16_t*)o;
   int n32 = (int)N, qt32 = (int)q_tiles, g32 = (int)groups;
-  void* args[] = {&qp, &kp, &vp, &op, &lse, &n32, &qt32, &g32, (void*)&c};
+  void* args[] = {&qp, &kp, &vp, &op, &lse, &n32, &qt32, &g32, (void*)&c_arg};
   hipError_t err = hipLaunchKernel((const void*)fn, dim3((unsigned)groups),
                                    dim3((unsigned)(nw * 64)), args, 0,
                                    (hipStream_t)stream);
