@@ -135,11 +135,13 @@ __device__ __forceinline__ void load_lds16(i32x4 rsrc, uint32_t voff, uint32_t l
 }
 
 // Tile shape per head dimension: key rows per tile (BC), waves per workgroup
-// (NW) and the waves per SIMD the register budget is sized for (OCC).
+// (NW), 32-query blocks per wave (QB) and the waves per SIMD the register
+// budget is sized for (OCC).  Each K or V operand read from LDS feeds QB
+// matrix instructions, so LDS bytes per FLOP fall as 1/QB.
 template <int D> struct Cfg;
-template <> struct Cfg<64> { static constexpr int BC = 64, NW = 4, OCC = 2; };
-template <> struct Cfg<128> { static constexpr int BC = 64, NW = 4, OCC = 2; };
-template <> struct Cfg<256> { static constexpr int BC = 32, NW = 4, OCC = 1; };
+template <> struct Cfg<64> { static constexpr int BC = 64, NW = 4, QB = 1, OCC = 2; };
+template <> struct Cfg<128> { static constexpr int BC = 32, NW = 8, QB = 1, OCC = 2; };
+template <> struct Cfg<256> { static constexpr int BC = 32, NW = 4, QB = 1, OCC = 1; };
 
 // p = exp2(t - m_ref) is summed over each lane's keys of a tile; while that
 // sum stays at or below kSumLimit no p exceeds it, and the reference max is
@@ -160,7 +162,8 @@ fa2_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                float c) {
   constexpr int BC = Cfg<D>::BC;
   constexpr int NW = Cfg<D>::NW;
-  constexpr int BR = NW * 32;         // query rows per workgroup
+  constexpr int QB = Cfg<D>::QB;
+  constexpr int BR = NW * 32 * QB;    // query rows per workgroup
   constexpr int CPR = D / 8;          // 16-byte chunks per K/V row
   constexpr int RB = D * 2;           // bytes per K/V row
   constexpr int TBYTES = BC * RB;     // one K or V tile
@@ -247,32 +250,41 @@ fa2_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                            v_swizzle<CPR>(tr_row, col >> 3) * 16 + (col & 7) * 2);
   }
 
-  // Q_i fragments: the B operand of S^T = K_j Q_i^T, held for the whole loop.
-  const int qrow = qt * BR + wave * 32 + l32;
-  X8 qf[KS];
+  // Q_i fragments: the B operands of S^T = K_j Q_i^T, held for the whole
+  // loop.  Query block b of this wave is rows q0 + 32*b + l32.
+  const int q0 = qt * BR + wave * 32 * QB;
+  X8 qf[QB][KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
-    qf[ks] = __builtin_bit_cast(
-        X8, __builtin_amdgcn_raw_buffer_load_b128(
-                q_rs, (uint32_t)(qrow * RB + ks * 32 + half * 16), 0, 0));
+  for (int b = 0; b < QB; ++b)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[b][ks] = __builtin_bit_cast(
+          X8, __builtin_amdgcn_raw_buffer_load_b128(
+                  q_rs, (uint32_t)((q0 + 32 * b + l32) * RB + ks * 32 + half * 16), 0, 0));
 
-  f32x16 acc[DB];
+  f32x16 acc[QB][DB];
+  float m_ref[QB], l_part[QB];  // reference max (log2 units), lane's row sum
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+  for (int b = 0; b < QB; ++b) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[db][i] = 0.0f;
-  float m_ref = -INFINITY;  // reference max of this query, log2 units
-  float l_part = 0.0f;      // this lane's share of the row sum
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[b][db][i] = 0.0f;
+    m_ref[b] = -INFINITY;
+    l_part[b] = 0.0f;
+  }
 
   // S^T_j = K_j Q_i^T : [BC keys] x [32 queries] per wave.  With a zero
   // scale every logit is 0 whatever Q and K hold, so S stays 0 and c is taken
   // as 1 (x = s - m_ref keeps masked keys at -inf).
-  auto gemm1 = [&](int j, f32x16 (&sd)[KB]) {
+  auto gemm1 = [&](int j, f32x16 (&sd)[QB][KB]) {
     const lds_char* kb = lds + (j & 1) * TBYTES;
 #pragma unroll
-    for (int kk = 0; kk < KB; ++kk)
+    for (int b = 0; b < QB; ++b)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sd[kk][i] = 0.0f;
+      for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sd[b][kk][i] = 0.0f;
     if constexpr (MODE == kZero) return;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
@@ -281,14 +293,15 @@ fa2_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         const X8 a = __builtin_bit_cast(
             X8, *(const __attribute__((address_space(3))) u32x4*)(
                     kb + kk * 32 * RB + k_off[ks]));
-        sd[kk] = mfma32x32x16<FP16>(a, qf[ks], sd[kk]);
+#pragma unroll
+        for (int b = 0; b < QB; ++b) sd[b][kk] = mfma32x32x16<FP16>(a, qf[b][ks], sd[b][kk]);
       }
   };
 
   // O^T += V_j^T P_j^T : [D] x [32 queries] per wave.  The A operand (V^T,
   // 8 keys per lane in the S^T accumulator's key order) comes from the
   // row-major V tile through two transposing LDS reads of 4 keys each.
-  auto gemm2 = [&](int j, const X8 (&pf)[ST]) {
+  auto gemm2 = [&](int j, const X8 (&pf)[QB][ST]) {
     const lds_char* vb = lds + (j & 1) * TBYTES;
 #pragma unroll
     for (int st = 0; st < ST; ++st)
@@ -300,13 +313,14 @@ fa2_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
             (lds_s16x4*)(vb + v_off[db] + (st * 16 + 8) * RB));
         const X8 a = __builtin_bit_cast(
             X8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        acc[db] = mfma32x32x16<FP16>(a, pf[st], acc[db]);
+#pragma unroll
+        for (int b = 0; b < QB; ++b) acc[b][db] = mfma32x32x16<FP16>(a, pf[b][st], acc[b][db]);
       }
   };
 
   // p = exp2(s*c - m_ref): rounded pairs into pf, the unrounded sum returned.
   // A masked key holds -inf (c > 0) or +inf (c < 0), so its p is 0.
-  auto probs = [&](const f32x16 (&sc)[KB], X8 (&pf)[ST]) -> float {
+  auto probs = [&](const f32x16 (&sc)[KB], X8 (&pf)[ST], float m) -> float {
     float rs = 0.0f;
 #pragma unroll
     for (int st = 0; st < ST; ++st) {
@@ -314,8 +328,8 @@ fa2_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i0 = (st & 1) * 8 + 2 * e;
-        const float x0 = __builtin_fmaf(sc[st >> 1][i0], c, -m_ref);
-        const float x1 = __builtin_fmaf(sc[st >> 1][i0 + 1], c, -m_ref);
+        const float x0 = __builtin_fmaf(sc[st >> 1][i0], c, -m);
+        const float x1 = __builtin_fmaf(sc[st >> 1][i0 + 1], c, -m);
         const float p0 = __builtin_amdgcn_exp2f(x0);
         const float p1 = __builtin_amdgcn_exp2f(x1);
         rs += p0;
@@ -337,8 +351,8 @@ fa2_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   // refilled only after the barrier ending the iteration that last read it.
   // The last iteration's S_{j+1} product reads whatever the idle K buffer
   // holds and is dropped.
-  auto step = [&](auto first, int j, f32x16 (&s_cur)[KB], f32x16 (&s_nxt)[KB],
-                  const X8 (&p_prev)[ST], X8 (&p_cur)[ST]) {
+  auto step = [&](auto first, int j, f32x16 (&s_cur)[QB][KB], f32x16 (&s_nxt)[QB][KB],
+                  const X8 (&p_prev)[QB][ST], X8 (&p_cur)[QB][ST]) {
     if (j + 2 < n_tiles) issue_k(j + 2);
     issue_v(j);
 
@@ -346,22 +360,30 @@ fa2_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const bool tail = key0 + BC > N;  // wave-uniform
     if (tail) {
 #pragma unroll
-      for (int kk = 0; kk < KB; ++kk)
+      for (int b = 0; b < QB; ++b)
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (key0 + kk * 32 + (i >> 2) * 8 + half * 4 + (i & 3) >= N)
-            s_cur[kk][i] = MODE == kNegative ? INFINITY : -INFINITY;
+        for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (key0 + kk * 32 + (i >> 2) * 8 + half * 4 + (i & 3) >= N)
+              s_cur[b][kk][i] = MODE == kNegative ? INFINITY : -INFINITY;
     }
 
     gemm1(j + 1, s_nxt);
     if constexpr (!decltype(first)::value) gemm2(j - 1, p_prev);
-    float rs = probs(s_cur, p_cur);
-    constexpr int MF = (MODE == kZero ? 0 : KS * KB) + (decltype(first)::value ? 0 : ST * DB);
+    float rs[QB];
+    bool over = false;
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+      rs[b] = probs(s_cur[b], p_cur[b], m_ref[b]);
+      over |= !(rs[b] <= kSumLimit);  // also true for inf / NaN
+    }
+    constexpr int MF = QB * ((MODE == kZero ? 0 : KS * KB) + (decltype(first)::value ? 0 : ST * DB));
 #pragma unroll
     for (int t = 0; t < MF; ++t) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
     }
 
@@ -371,28 +393,33 @@ fa2_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     // limit move their reference to their running max, rescale O and l, and
     // get their p recomputed; other rows keep their reference, so a row's
     // arithmetic never depends on its wave-mates.
-    if (__builtin_amdgcn_ballot_w64(!(rs <= kSumLimit)) != 0) {
-      float ext = s_cur[0][0];
+    if (__builtin_amdgcn_ballot_w64(over) != 0) {
 #pragma unroll
-      for (int kk = 0; kk < KB; ++kk)
+      for (int b = 0; b < QB; ++b) {
+        float ext = s_cur[b][0][0];
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          ext = MODE == kNegative ? fminf(ext, s_cur[kk][i]) : fmaxf(ext, s_cur[kk][i]);
-      const float t_max = __builtin_isfinite(ext) ? ext * c : -INFINITY;
-      const float t_row = fmaxf(t_max, __shfl_xor(t_max, 32));
-      const float mine = !(rs <= kSumLimit) ? 1.0f : 0.0f;
-      const bool move = fmaxf(mine, __shfl_xor(mine, 32)) > 0.0f;
-      const float m_new = move ? fmaxf(m_ref, t_row) : m_ref;
-      const float alpha = m_new == m_ref ? 1.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
+        for (int kk = 0; kk < KB; ++kk)
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+          for (int i = 0; i < 16; ++i)
+            ext = MODE == kNegative ? fminf(ext, s_cur[b][kk][i]) : fmaxf(ext, s_cur[b][kk][i]);
+        const float t_max = __builtin_isfinite(ext) ? ext * c : -INFINITY;
+        const float t_row = fmaxf(t_max, __shfl_xor(t_max, 32));
+        const float mine = !(rs[b] <= kSumLimit) ? 1.0f : 0.0f;
+        const bool move = fmaxf(mine, __shfl_xor(mine, 32)) > 0.0f;
+        const float m_new = move ? fmaxf(m_ref[b], t_row) : m_ref[b];
+        const float alpha =
+            m_new == m_ref[b] ? 1.0f : __builtin_amdgcn_exp2f(m_ref[b] - m_new);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
-      l_part *= alpha;
-      m_ref = m_new;
-      rs = probs(s_cur, p_cur);
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[b][db][i] *= alpha;
+        l_part[b] *= alpha;
+        m_ref[b] = m_new;
+        rs[b] = probs(s_cur[b], p_cur[b], m_ref[b]);
+      }
     }
-    l_part += rs;
+#pragma unroll
+    for (int b = 0; b < QB; ++b) l_part[b] += rs[b];
 
     wait_vmem();  // this wave's share of K_{j+2} and V_j has landed
     __syncthreads();
@@ -404,12 +431,14 @@ fa2_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   issue_k(0);
   if (n_tiles > 1) issue_k(1);
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]));
+  for (int b = 0; b < QB; ++b)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[b][ks]));
   wait_vmem();
   __syncthreads();
 
-  f32x16 sA[KB], sB[KB];
-  X8 pA[ST], pB[ST];
+  f32x16 sA[QB][KB], sB[QB][KB];
+  X8 pA[QB][ST], pB[QB][ST];
   gemm1(0, sA);
   __syncthreads();  // every wave is done with K_0 before K_2 may overwrite it
 
@@ -429,21 +458,25 @@ fa2_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   }
 
   // ---- epilogue: O = acc / l, lse = (m_ref + log2 l) * ln 2
-  const float l_tot = l_part + __shfl_xor(l_part, 32);
-  const float inv = 1.0f / l_tot;
-  if (qrow < N) {
-    uint16_t* orow = o + head + (int64_t)qrow * D;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+  for (int b = 0; b < QB; ++b) {
+    const int qrow = q0 + 32 * b + l32;
+    const float l_tot = l_part[b] + __shfl_xor(l_part[b], 32);
+    const float inv = 1.0f / l_tot;
+    if (qrow < N) {
+      uint16_t* orow = o + head + (int64_t)qrow * D;
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        X4 ov;
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ov[e] = (E)(acc[db][g4 * 4 + e] * inv);
-        *(u32x2*)(orow + db * 32 + g4 * 8 + half * 4) = __builtin_bit_cast(u32x2, ov);
-      }
-    if (half == 0)
-      lse[(int64_t)bh * N + qrow] = (m_ref + __log2f(l_tot)) * kLn2;
+        for (int g4 = 0; g4 < 4; ++g4) {
+          X4 ov;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ov[e] = (E)(acc[b][db][g4 * 4 + e] * inv);
+          *(u32x2*)(orow + db * 32 + g4 * 8 + half * 4) = __builtin_bit_cast(u32x2, ov);
+        }
+      if (half == 0)
+        lse[(int64_t)bh * N + qrow] = (m_ref[b] + __log2f(l_tot)) * kLn2;
+    }
   }
 }
 
@@ -492,9 +525,9 @@ int fa2_tile_config(int64_t d, int dtype, int* block_q, int* block_k, int* waves
   if (!block_q || !block_k || !waves) return FA2_ERR_NULL;
   if (dtype != FA2_BF16 && dtype != FA2_FP16) return FA2_ERR_DTYPE;
   switch (d) {
-    case 64: *block_q = fa2::Cfg<64>::NW * 32; *block_k = fa2::Cfg<64>::BC; *waves = fa2::Cfg<64>::NW; break;
-    case 128: *block_q = fa2::Cfg<128>::NW * 32; *block_k = fa2::Cfg<128>::BC; *waves = fa2::Cfg<128>::NW; break;
-    case 256: *block_q = fa2::Cfg<256>::NW * 32; *block_k = fa2::Cfg<256>::BC; *waves = fa2::Cfg<256>::NW; break;
+    case 64: *block_q = fa2::Cfg<64>::NW * 32 * fa2::Cfg<64>::QB; *block_k = fa2::Cfg<64>::BC; *waves = fa2::Cfg<64>::NW; break;
+    case 128: *block_q = fa2::Cfg<128>::NW * 32 * fa2::Cfg<128>::QB; *block_k = fa2::Cfg<128>::BC; *waves = fa2::Cfg<128>::NW; break;
+    case 256: *block_q = fa2::Cfg<256>::NW * 32 * fa2::Cfg<256>::QB; *block_k = fa2::Cfg<256>::BC; *waves = fa2::Cfg<256>::NW; break;
     default: return FA2_ERR_HEADDIM;
   }
   return FA2_OK;
