@@ -12,7 +12,9 @@ on this host's cores.
 
 Other modes: --workload NAME for any of the parity workloads (one line each),
 --no-cpu-baseline to skip the oracle timing, --calibrate-copy to run only a
-plain device copy of known size (for scaling HBM byte counters).
+plain device copy of known size (for scaling HBM byte counters), and
+--traffic-from to turn rocprofv3 FETCH_SIZE / WRITE_SIZE runs into the traffic
+record under profiles/ that the roofline's "traffic" field reads.
 """
 import argparse
 import hashlib
@@ -52,6 +54,41 @@ def measured_traffic(workload):
     if t.get("kernel_sha256") != kernel_digest() or t.get("workload") != workload:
         return None
     return t.get("hbm_bytes_per_launch")
+
+
+def _mean_counter(csv_path, counter, kernel_substr):
+    import csv
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(csv_path))
+            if r["Counter_Name"] == counter and kernel_substr in r["Kernel_Name"]]
+    if not vals:
+        raise ValueError("no %s rows for %s in %s" % (counter, kernel_substr, csv_path))
+    return sum(vals) / len(vals)
+
+
+def write_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, workload,
+                  copy_bytes=1 << 30):
+    """HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs (KiB per
+    dispatch), each scaled by what the same counter reads for the copy kernel
+    of --calibrate-copy, which moves exactly copy_bytes each way."""
+    fetch_kib = _mean_counter(fetch_csv, "FETCH_SIZE", "fa2_fwd")
+    write_kib = _mean_counter(write_csv, "WRITE_SIZE", "fa2_fwd")
+    copy_fetch_kib = _mean_counter(copy_fetch_csv, "FETCH_SIZE", "elementwise")
+    copy_write_kib = _mean_counter(copy_write_csv, "WRITE_SIZE", "elementwise")
+    f_scale = copy_bytes / (copy_fetch_kib * 1024.0)
+    w_scale = copy_bytes / (copy_write_kib * 1024.0)
+    rd = fetch_kib * 1024.0 * f_scale
+    wr = write_kib * 1024.0 * w_scale
+    out = {"workload": workload, "kernel_sha256": kernel_digest(),
+           "fetch_kib_per_launch": fetch_kib, "write_kib_per_launch": write_kib,
+           "copy_fetch_kib": copy_fetch_kib, "copy_write_kib": copy_write_kib,
+           "copy_bytes_each_way": copy_bytes, "fetch_scale": round(f_scale, 4),
+           "write_scale": round(w_scale, 4), "hbm_read_bytes_per_launch": round(rd),
+           "hbm_write_bytes_per_launch": round(wr), "hbm_bytes_per_launch": round(rd + wr)}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
 
 
 def cpu_baseline(w, q, k, v):
@@ -104,7 +141,14 @@ def main():
     ap.add_argument("--workload", default="headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV",
+                                                         "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="write the HBM traffic record from rocprofv3 counter CSVs")
     args = ap.parse_args()
+
+    if args.traffic_from:
+        write_traffic(*args.traffic_from, workload=args.workload)
+        return
 
     if args.gpus != 1:
         print("bench.py: this build measures one GPU only (the per-GPU share of "
