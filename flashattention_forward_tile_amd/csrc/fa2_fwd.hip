@@ -135,13 +135,14 @@ __device__ __forceinline__ void load_lds16(i32x4 rsrc, uint32_t voff, uint32_t l
 }
 
 // Tile shape per head dimension: key rows per tile (BC), waves per workgroup
-// (NW), 32-query blocks per wave (QB) and the waves per SIMD the register
-// budget is sized for (OCC).  Each K or V operand read from LDS feeds QB
+// (NW), 32-query blocks per wave (QB), the waves per SIMD the register
+// budget is sized for (OCC), and whether the iteration block carries explicit
+// MFMA / LDS / VALU interleave hints (SGB).  Each K or V operand read from LDS feeds QB
 // matrix instructions, so LDS bytes per FLOP fall as 1/QB.
 template <int D> struct Cfg;
-template <> struct Cfg<64> { static constexpr int BC = 64, NW = 4, QB = 1, OCC = 2; };
-template <> struct Cfg<128> { static constexpr int BC = 32, NW = 8, QB = 1, OCC = 2; };
-template <> struct Cfg<256> { static constexpr int BC = 32, NW = 4, QB = 1, OCC = 1; };
+template <> struct Cfg<64> { static constexpr int BC = 64, NW = 4, QB = 1, OCC = 2, SGB = 1; };
+template <> struct Cfg<128> { static constexpr int BC = 32, NW = 8, QB = 1, OCC = 2, SGB = 1; };
+template <> struct Cfg<256> { static constexpr int BC = 32, NW = 4, QB = 1, OCC = 1, SGB = 0; };
 
 // p = exp2(t - m_ref) is summed over each lane's keys of a tile; while that
 // sum stays at or below kSumLimit no p exceeds it, and the reference max is
@@ -236,15 +237,20 @@ fa2_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   //   reads rows st*16 + sg*8 + half*4 + (lane%16)/4 and 4 elements at column
   //   db*32 + 16*(g&1) + 4*(lane%4); lane l then holds V[key][db*32 + l32]
   //   for keys st*16 + sg*8 + half*4 + 0..3.
-  uint32_t k_off[KS];
+  // The swizzles touch only the low 4 bits of a chunk index, so offsets
+  // repeat every 16 chunks (256 B) along a row: keep at most 8 K offsets and
+  // 4 V offsets and reach the rest with an immediate.
+  constexpr int KOFF = KS < 8 ? KS : 8;
+  constexpr int VOFF = DB < 4 ? DB : 4;
+  uint32_t k_off[KOFF];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
+  for (int ks = 0; ks < KOFF; ++ks)
     k_off[ks] = (uint32_t)(l32 * RB + k_swizzle<CPR>(l32, ks * 2 + half) * 16);
   const int tr_row = half * 4 + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  uint32_t v_off[DB];
+  uint32_t v_off[VOFF];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) {
+  for (int db = 0; db < VOFF; ++db) {
     const int col = db * 32 + tr_col;
     v_off[db] = (uint32_t)(2 * TBYTES + tr_row * RB +
                            v_swizzle<CPR>(tr_row, col >> 3) * 16 + (col & 7) * 2);
@@ -292,7 +298,7 @@ fa2_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       for (int kk = 0; kk < KB; ++kk) {
         const X8 a = __builtin_bit_cast(
             X8, *(const __attribute__((address_space(3))) u32x4*)(
-                    kb + kk * 32 * RB + k_off[ks]));
+                    kb + kk * 32 * RB + k_off[ks % KOFF] + (ks / KOFF) * 256));
 #pragma unroll
         for (int b = 0; b < QB; ++b) sd[b][kk] = mfma32x32x16<FP16>(a, qf[b][ks], sd[b][kk]);
       }
@@ -307,10 +313,11 @@ fa2_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     for (int st = 0; st < ST; ++st)
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
+        const uint32_t vo = v_off[db % VOFF] + (db / VOFF) * 256;
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4*)(vb + v_off[db] + (st * 16) * RB));
+            (lds_s16x4*)(vb + vo + (st * 16) * RB));
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4*)(vb + v_off[db] + (st * 16 + 8) * RB));
+            (lds_s16x4*)(vb + vo + (st * 16 + 8) * RB));
         const X8 a = __builtin_bit_cast(
             X8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
@@ -380,7 +387,7 @@ fa2_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     }
     constexpr int MF = QB * ((MODE == kZero ? 0 : KS * KB) + (decltype(first)::value ? 0 : ST * DB));
 #pragma unroll
-    for (int t = 0; t < MF; ++t) {
+    for (int t = 0; t < (Cfg<D>::SGB ? MF : 0); ++t) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
       __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
