@@ -10,22 +10,29 @@
  * dot-product attention, as named on the Colfax author page, "Introduction to
  * Transformers" entry, and on the FlashAttention-2-on-Hopper abstract):
  *
- *   for every batch b, head h and query row i:
+ *   for every batch b, query head h and query row i, over the keys j that
+ *   row may see (all Nk keys; with the causal option, j <= i + Nk - Nq):
  *     s_j   = scale * sum_c q[i][c] * k[j][c]           (fp64)
  *     m     = max_j s_j
  *     l     = sum_j exp(s_j - m)
  *     O[c]  = sum_j exp(s_j - m) * v[j][c] / l
  *     lse   = m + ln(l)           (natural-log logsumexp of the scaled logits)
+ *   A row that may see no key gets O = 0 and lse = -inf.
  *
- * The problem restrictions follow the "Kernel Specification" section of the
+ * The base problem follows the "Kernel Specification" section of the
  * "Flash Attention 2 from scratch on Ampere" Part 1 page: forward only,
- * non-causal (no mask), no dropout, equal query/key/value lengths, 16-bit
- * (bf16 or fp16) inputs.  Inputs arrive as raw 16-bit patterns and are decoded
- * exactly to fp64; nothing here rounds to 16 bits or to fp32.
+ * non-causal, no dropout, equal query/key/value lengths, 16-bit (bf16 or
+ * fp16) inputs.  The options widen it along the rows that page excludes:
+ * causal masking (aligned so the last query row sees every key), unequal
+ * query and key lengths, and grouped key/value heads (query head h reads
+ * key/value head h / (Hq / Hkv), as in the MQA/GQA setting of the Colfax
+ * FlashAttention-3 inference post).  Inputs arrive as raw 16-bit patterns and
+ * are decoded exactly to fp64; nothing here rounds to 16 bits or to fp32.
  *
- * Layout: q, k, v are [B][H][N][d] contiguous; O is [rows][d] fp64 and lse is
- * [rows] fp64, where rows are either all B*H*N rows in order or the caller's
- * sorted list of flat row indices (b*H + h)*N + i.
+ * Layout: q is [B][Hq][Nq][d], k and v are [B][Hkv][Nk][d], all contiguous;
+ * O is [rows][d] fp64 and lse is [rows] fp64, where rows are either all
+ * B*Hq*Nq rows in order or the caller's sorted list of flat row ids
+ * (b*Hq + h)*Nq + i.
  */
 #define _GNU_SOURCE
 #include <math.h>
@@ -75,7 +82,8 @@ int oracle_decode(const uint16_t* bits, int64_t n, int dtype, double* out) {
 typedef struct {
   const uint16_t *q, *k, *v;
   int dtype;
-  int64_t B, H, N, d;
+  int64_t B, Hq, Hkv, Nq, Nk, d;
+  int causal;
   double scale;
   const int64_t* rows; /* sorted flat row ids, or NULL for all rows */
   int64_t nrows;
@@ -87,10 +95,16 @@ typedef struct {
   pthread_mutex_t mu;
 } job_t;
 
-/* One query row against one decoded head: the definition, term by term. */
+/* One query row against the first N keys of one decoded head: the
+ * definition, term by term.  N == 0 (no visible key) gives O = 0, lse = -inf. */
 static void one_row(const double* qrow, const double* K, const double* V,
                     int64_t N, int64_t d, double scale, double* s,
                     double* orow, double* lse_out) {
+  if (N <= 0) {
+    for (int64_t c = 0; c < d; ++c) orow[c] = 0.0;
+    *lse_out = -INFINITY;
+    return;
+  }
   double m = -INFINITY;
   for (int64_t j = 0; j < N; ++j) {
     double dot = 0.0;
@@ -115,11 +129,12 @@ static void one_row(const double* qrow, const double* K, const double* V,
 /* Work item = (head, block of that head's selected rows). */
 static void* worker(void* arg) {
   job_t* J = (job_t*)arg;
-  const int64_t N = J->N, d = J->d;
-  double* K = (double*)malloc(sizeof(double) * (size_t)(N * d));
-  double* V = (double*)malloc(sizeof(double) * (size_t)(N * d));
+  const int64_t Nq = J->Nq, Nk = J->Nk, d = J->d;
+  const int64_t group = J->Hq / J->Hkv;  /* query heads per key/value head */
+  double* K = (double*)malloc(sizeof(double) * (size_t)(Nk * d + 1));
+  double* V = (double*)malloc(sizeof(double) * (size_t)(Nk * d + 1));
   double* q = (double*)malloc(sizeof(double) * (size_t)d);
-  double* s = (double*)malloc(sizeof(double) * (size_t)N);
+  double* s = (double*)malloc(sizeof(double) * (size_t)(Nk + 1));
   int64_t loaded_head = -1;
   if (!K || !V || !q || !s) {
     pthread_mutex_lock(&J->mu);
@@ -137,19 +152,24 @@ static void* worker(void* arg) {
     if (r1 > J->nrows) r1 = J->nrows;
     for (int64_t r = r0; r < r1; ++r) {
       int64_t flat = J->rows ? J->rows[r] : r;
-      int64_t head = flat / N;
-      if (head != loaded_head) {
-        const uint16_t* kh = J->k + head * N * d;
-        const uint16_t* vh = J->v + head * N * d;
-        for (int64_t t = 0; t < N * d; ++t) {
+      int64_t head = flat / Nq, i = flat % Nq;  /* head = b*Hq + h */
+      int64_t kv_head = (head / J->Hq) * J->Hkv + (head % J->Hq) / group;
+      if (kv_head != loaded_head) {
+        const uint16_t* kh = J->k + kv_head * Nk * d;
+        const uint16_t* vh = J->v + kv_head * Nk * d;
+        for (int64_t t = 0; t < Nk * d; ++t) {
           K[t] = decode(kh[t], J->dtype);
           V[t] = decode(vh[t], J->dtype);
         }
-        loaded_head = head;
+        loaded_head = kv_head;
       }
+      /* keys 0 .. visible-1; causal rows are aligned so that the last query
+       * row sees all Nk keys */
+      int64_t visible = Nk;
+      if (J->causal && i + 1 + Nk - Nq < visible) visible = i + 1 + Nk - Nq;
       const uint16_t* qr = J->q + flat * d;
       for (int64_t c = 0; c < d; ++c) q[c] = decode(qr[c], J->dtype);
-      one_row(q, K, V, N, d, J->scale, s, J->o + r * d, J->lse + r);
+      one_row(q, K, V, visible, d, J->scale, s, J->o + r * d, J->lse + r);
     }
   }
 done:
@@ -167,22 +187,25 @@ int oracle_host_threads(void) {
 }
 
 /*
- * Attention rows.  rows == NULL computes all B*H*N rows; otherwise rows[] is a
- * strictly increasing list of nrows flat row ids in [0, B*H*N).  nthreads <= 0
- * uses every core in the affinity mask.  Returns 0, or -1 on a bad argument,
- * -2 on allocation failure.
+ * Attention rows, general form.  q [B][Hq][Nq][d], k and v [B][Hkv][Nk][d],
+ * Hq a multiple of Hkv >= 1, causal 0 or 1.  rows == NULL computes all
+ * B*Hq*Nq rows; otherwise rows[] is a strictly increasing list of nrows flat
+ * row ids in [0, B*Hq*Nq).  nthreads <= 0 uses every core in the affinity
+ * mask.  Returns 0, or -1 on a bad argument, -2 on allocation failure.
  */
-int oracle_attn_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                     int dtype, int64_t B, int64_t H, int64_t N, int64_t d,
-                     double scale, const int64_t* rows, int64_t nrows,
-                     double* o, double* lse, int nthreads) {
+int oracle_attn_general(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                        int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq,
+                        int64_t Nk, int64_t d, double scale, int causal,
+                        const int64_t* rows, int64_t nrows, double* o, double* lse,
+                        int nthreads) {
   if (dtype != ORACLE_BF16 && dtype != ORACLE_FP16) return -1;
-  if (B < 0 || H < 0 || N < 0 || d <= 0) return -1;
-  const int64_t total = B * H * N;
+  if (B < 0 || Hq < 0 || Hkv <= 0 || Nq < 0 || Nk < 0 || d <= 0) return -1;
+  if (Hq % Hkv != 0 || (causal != 0 && causal != 1)) return -1;
+  const int64_t total = B * Hq * Nq;
   if (!rows) nrows = total;
   if (nrows < 0 || nrows > total) return -1;
   if (nrows == 0) return 0;
-  if (!q || !k || !v || !o || !lse) return -1;
+  if (!q || !o || !lse || (Nk > 0 && (!k || !v))) return -1;
   if (rows) {
     for (int64_t r = 0; r < nrows; ++r) {
       if (rows[r] < 0 || rows[r] >= total) return -1;
@@ -194,7 +217,8 @@ int oracle_attn_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   job_t J;
   memset(&J, 0, sizeof J);
   J.q = q; J.k = k; J.v = v; J.dtype = dtype;
-  J.B = B; J.H = H; J.N = N; J.d = d; J.scale = scale;
+  J.B = B; J.Hq = Hq; J.Hkv = Hkv; J.Nq = Nq; J.Nk = Nk; J.d = d;
+  J.causal = causal; J.scale = scale;
   J.rows = rows; J.nrows = nrows; J.o = o; J.lse = lse;
   /* rows of one head stay together inside an item so K/V decode once */
   J.chunk = 64;
@@ -218,4 +242,14 @@ int oracle_attn_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   free(th);
   pthread_mutex_destroy(&J.mu);
   return J.failed ? -2 : 0;
+}
+
+/* The base problem: equal heads and lengths, no mask. */
+int oracle_attn_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                     int dtype, int64_t B, int64_t H, int64_t N, int64_t d,
+                     double scale, const int64_t* rows, int64_t nrows,
+                     double* o, double* lse, int nthreads) {
+  if (H <= 0) return (B >= 0 && H == 0 && N >= 0 && d > 0) ? 0 : -1;
+  return oracle_attn_general(q, k, v, dtype, B, H, H, N, N, d, scale, 0, rows,
+                             nrows, o, lse, nthreads);
 }

@@ -9,6 +9,10 @@ that oracle disagrees with the definition of scaled dot-product attention
   * brute force in pure Python (math.fsum) on tiny inputs,
   * library routines (torch fp64 softmax / scaled_dot_product_attention),
   * exact decoding of every 16-bit pattern, and extreme-logit stability.
+Causal masking, unequal query/key lengths and grouped key/value heads are
+pinned the same ways: truncation to the visible prefix, torch fp64 SDPA with an
+explicit bottom-right mask or enable_gqa, repeated key/value heads, brute
+force, and the closed forms of the first row and of rows that see no key.
 They are plain functions so the same pins also run against deliberately broken
 copies of the oracle (test_oracle_mutants.py), which they must reject.
 """
@@ -46,6 +50,11 @@ def _rand16(shape, dtype, seed, mult=1.0):
 
 def _run(orc, q, k, v, dtype, scale, **kw):
     return orc.attention(bits(q), bits(k), bits(v), dtype, scale, **kw)
+
+
+def _visible(i, Nq, Nk):
+    """Keys a causal row i sees: 0 .. i + Nk - Nq (bottom-right aligned)."""
+    return max(0, min(Nk, i + 1 + Nk - Nq))
 
 
 # --------------------------------------------------------------------------
@@ -330,6 +339,124 @@ def pin_extreme_logits(orc):
         assert np.allclose(lse[0, 0], -800.0 + math.log(2.0), rtol=1e-15, atol=0)
 
 
+# --------------------------------------------------------------------------
+# causal masking, unequal lengths, grouped heads
+
+def pin_causal_is_prefix_attention(orc):
+    """Causal row i equals plain attention of q_i over the keys it sees, bit
+    for bit; rows that see no key get O = 0 and lse = -inf."""
+    for dtype in DTYPES:
+        for Nq, Nk in ((40, 40), (24, 40), (40, 24), (1, 9)):
+            q = _rand16((1, 2, Nq, 8), dtype, 121)
+            k = _rand16((1, 2, Nk, 8), dtype, 122)
+            v = _rand16((1, 2, Nk, 8), dtype, 123)
+            o, lse = _run(orc, q, k, v, dtype, 0.7, causal=True)
+            for h in range(2):
+                for i in range(Nq):
+                    n = _visible(i, Nq, Nk)
+                    if n == 0:
+                        assert np.all(o[0, h, i] == 0.0) and lse[0, h, i] == -np.inf
+                        continue
+                    sl = (slice(0, 1), slice(h, h + 1))
+                    op, lp = _run(orc, q[sl][:, :, i:i + 1], k[sl][:, :, :n].contiguous(),
+                                  v[sl][:, :, :n].contiguous(), dtype, 0.7)
+                    # a single query row against n keys: same arithmetic
+                    assert np.array_equal(op[0, 0, 0], o[0, h, i]), (Nq, Nk, i)
+                    assert np.array_equal(lp[0, 0, 0], lse[0, h, i]), (Nq, Nk, i)
+
+
+def pin_causal_first_row(orc):
+    """Nq == Nk, causal: row 0 sees key 0 only, so O_0 = v_0 exactly and lse_0 is
+    its logit."""
+    for dtype in DTYPES:
+        q = _rand16((2, 2, 16, 8), dtype, 131)
+        k = _rand16((2, 2, 16, 8), dtype, 132)
+        v = _rand16((2, 2, 16, 8), dtype, 133)
+        o, lse = _run(orc, q, k, v, dtype, 0.5, causal=True)
+        assert np.array_equal(o[:, :, 0], _f64(v)[:, :, 0])
+        s00 = 0.5 * np.einsum("bhc,bhc->bh", _f64(q)[:, :, 0], _f64(k)[:, :, 0])
+        assert np.allclose(lse[:, :, 0], s00, rtol=1e-14, atol=1e-15)
+
+
+def pin_causal_and_lengths_torch(orc):
+    """torch fp64 SDPA with an explicit bottom-right boolean mask (causal) or
+    none, for Nq != Nk."""
+    import torch.nn.functional as F
+    for dtype in DTYPES:
+        for Nq, Nk, causal in ((48, 80, True), (80, 48, True), (48, 80, False),
+                               (64, 64, True)):
+            q = _rand16((1, 2, Nq, 16), dtype, 141)
+            k = _rand16((1, 2, Nk, 16), dtype, 142)
+            v = _rand16((1, 2, Nk, 16), dtype, 143)
+            o, lse = _run(orc, q, k, v, dtype, 0.25, causal=causal)
+            qd, kd, vd = q.double(), k.double(), v.double()
+            if causal:
+                i = torch.arange(Nq)[:, None]
+                j = torch.arange(Nk)[None, :]
+                mask = j <= i + (Nk - Nq)
+            else:
+                mask = torch.ones(Nq, Nk, dtype=torch.bool)
+            rows = mask.any(dim=1).numpy()
+            ref = F.scaled_dot_product_attention(qd, kd, vd, attn_mask=mask, scale=0.25)
+            logits = (0.25 * qd @ kd.transpose(-1, -2)).masked_fill(~mask, float("-inf"))
+            lref = torch.logsumexp(logits, dim=-1)
+            assert np.allclose(o[:, :, rows], ref.numpy()[:, :, rows], rtol=0, atol=1e-10)
+            assert np.allclose(lse[:, :, rows], lref.numpy()[:, :, rows], rtol=1e-12, atol=0)
+            assert np.all(o[:, :, ~rows] == 0.0) and np.all(lse[:, :, ~rows] == -np.inf)
+
+
+def pin_causal_brute_force(orc):
+    rng = np.random.default_rng(151)
+    for dtype in DTYPES:
+        for (Nq, Nk) in ((3, 3), (2, 4), (4, 2), (1, 3)):
+            q = rng.integers(-8, 9, size=(1, 1, Nq, 3)) / 4.0
+            k = rng.integers(-8, 9, size=(1, 1, Nk, 3)) / 4.0
+            v = rng.integers(-8, 9, size=(1, 1, Nk, 3)) / 4.0
+            o, lse = _run(orc, _t16(q, dtype), _t16(k, dtype), _t16(v, dtype), dtype, 0.9,
+                          causal=True)
+            for i in range(Nq):
+                n = _visible(i, Nq, Nk)
+                if n == 0:
+                    assert lse[0, 0, i] == -np.inf
+                    continue
+                ob, lb = _brute_row(q[0, 0, i].tolist(), k[0, 0, :n].tolist(),
+                                    v[0, 0, :n].tolist(), 0.9)
+                assert np.allclose(o[0, 0, i], ob, rtol=0, atol=1e-12)
+                assert abs(lse[0, 0, i] - lb) <= 1e-12 * max(1.0, abs(lb))
+
+
+def pin_grouped_heads_are_repeated_heads(orc):
+    """Hkv < Hq: identical, bit for bit, to repeating each key/value head for
+    its Hq/Hkv query heads; and equal to torch SDPA with enable_gqa."""
+    import torch.nn.functional as F
+    for dtype in DTYPES:
+        for Hq, Hkv in ((4, 2), (6, 1), (4, 4)):
+            q = _rand16((2, Hq, 20, 8), dtype, 161)
+            k = _rand16((2, Hkv, 28, 8), dtype, 162)
+            v = _rand16((2, Hkv, 28, 8), dtype, 163)
+            for causal in (False, True):
+                o, lse = _run(orc, q, k, v, dtype, 0.6, causal=causal)
+                rep = Hq // Hkv
+                kr = k.repeat_interleave(rep, dim=1).contiguous()
+                vr = v.repeat_interleave(rep, dim=1).contiguous()
+                o2, l2 = _run(orc, q, kr, vr, dtype, 0.6, causal=causal)
+                assert np.array_equal(o, o2) and np.array_equal(lse, l2)
+            ref = F.scaled_dot_product_attention(q.double(), k.double(), v.double(),
+                                                 scale=0.6, enable_gqa=True)
+            o, _ = _run(orc, q, k, v, dtype, 0.6)
+            assert np.allclose(o, ref.numpy(), rtol=0, atol=1e-10)
+
+
+def pin_single_key_any_length(orc):
+    """Nk = 1: every row (non-causal) is v_0 exactly, whatever Nq."""
+    for dtype in DTYPES:
+        q = _rand16((1, 3, 7, 8), dtype, 171)
+        k = _rand16((1, 3, 1, 8), dtype, 172)
+        v = _rand16((1, 3, 1, 8), dtype, 173)
+        o, _ = _run(orc, q, k, v, dtype, 1.3)
+        assert np.array_equal(o, np.broadcast_to(_f64(v), o.shape))
+
+
 ALL_PINS = [
     pin_decode_every_pattern,
     pin_worked_examples,
@@ -345,4 +472,10 @@ ALL_PINS = [
     pin_value_linearity,
     pin_head_independence,
     pin_extreme_logits,
+    pin_causal_is_prefix_attention,
+    pin_causal_first_row,
+    pin_causal_and_lengths_torch,
+    pin_causal_brute_force,
+    pin_grouped_heads_are_repeated_heads,
+    pin_single_key_any_length,
 ]

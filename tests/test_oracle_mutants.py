@@ -22,10 +22,15 @@ MUTANTS = [
     ("bf16_shift", "(uint32_t)bits << 16;", "(uint32_t)bits << 15;"),
     ("fp16_bias", "expo - 25);", "expo - 24);"),
     ("fp16_subnormal", "ldexp((double)man, -24);", "ldexp((double)man, -25);"),
-    ("q_row_ignores_head", "J->q + flat * d;", "J->q + (flat % N) * d;"),
-    ("k_ignores_head", "J->k + head * N * d;", "J->k;"),
-    ("v_ignores_head", "J->v + head * N * d;", "J->v;"),
-    ("head_reload_skipped", "if (head != loaded_head) {", "if (loaded_head < 0) {"),
+    ("q_row_ignores_head", "J->q + flat * d;", "J->q + (flat % Nq) * d;"),
+    ("k_ignores_head", "J->k + kv_head * Nk * d;", "J->k;"),
+    ("v_ignores_head", "J->v + kv_head * Nk * d;", "J->v;"),
+    ("head_reload_skipped", "if (kv_head != loaded_head) {", "if (loaded_head < 0) {"),
+    ("gqa_heads_interleaved", "(head % J->Hq) / group;", "(head % J->Hq) % J->Hkv;"),
+    ("causal_off_by_one", "visible = i + 1 + Nk - Nq;", "visible = i + Nk - Nq;"),
+    ("causal_top_left", "if (J->causal && i + 1 + Nk - Nq < visible) visible = i + 1 + Nk - Nq;",
+     "if (J->causal && i + 1 < visible) visible = i + 1;"),
+    ("empty_row_lse_zero", "*lse_out = -INFINITY;", "*lse_out = 0.0;"),
 ]
 
 
