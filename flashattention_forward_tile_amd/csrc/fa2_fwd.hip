@@ -153,14 +153,30 @@ constexpr float kSumLimit = 256.0f;
 // logits is a max for c > 0 and a min for c < 0; c == 0 is uniform attention.
 enum ScaleMode { kPositive = 0, kNegative = 1, kZero = 2 };
 
-template <int D, bool FP16, int MODE>
+// Kernel arguments.  q, o: [B][hq][nq][D]; k, v: [B][hq/group][nk][D];
+// lse: [B][hq][nq].  Query head h reads key/value head h / group.  With the
+// causal option row i sees keys j <= i + causal_off (causal_off = nk - nq).
+struct Problem {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  int nq, nk;        // query and key rows per head
+  int hq, group;     // query heads per batch entry, query heads per K/V head
+  int q_tiles;       // query tiles per head
+  int n_groups;      // workgroups in the grid
+  int causal_off;
+  float c;           // scale * log2(e) (1 when the scale is 0)
+};
+
+template <int D, bool FP16, int MODE, bool CAUSAL>
 __global__ void __attribute__((amdgpu_flat_work_group_size(Cfg<D>::NW * 64,
                                                            Cfg<D>::NW * 64),
                                amdgpu_waves_per_eu(Cfg<D>::OCC, Cfg<D>::OCC)))
-fa2_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-               const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
-               float* __restrict__ lse, int N, int q_tiles, int n_groups,
-               float c) {
+fa2_fwd_kernel(const Problem P) {
+  const int N = P.nk;  // keys per head
+  const float c = P.c;
   constexpr int BC = Cfg<D>::BC;
   constexpr int NW = Cfg<D>::NW;
   constexpr int QB = Cfg<D>::QB;
@@ -193,15 +209,19 @@ fa2_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 
   // All query tiles of one head go to one XCD (dispatch is round-robin over
   // the 8 XCDs): the k-th workgroup on XCD x takes logical tile x*G/8 + k.
+  // Query heads sharing a K/V head are adjacent, so they share it too.  With
+  // the causal mask the later (longer) query tiles of a head start first.
   int id = blockIdx.x;
-  if ((n_groups & 7) == 0) id = (id & 7) * (n_groups >> 3) + (id >> 3);
-  const int bh = id / q_tiles;
-  const int qt = id - bh * q_tiles;
-  const int64_t head = (int64_t)bh * N * D;
-  const uint32_t head_bytes = (uint32_t)N * D * 2;
-  const __amdgpu_buffer_rsrc_t q_rs = make_rsrc(q + head, head_bytes);
-  const i32x4 k_rs = make_rsrc_words(k + head, head_bytes);
-  const i32x4 v_rs = make_rsrc_words(v + head, head_bytes);
+  if ((P.n_groups & 7) == 0) id = (id & 7) * (P.n_groups >> 3) + (id >> 3);
+  const int bh = id / P.q_tiles;  // b * hq + h
+  int qt = id - bh * P.q_tiles;
+  if constexpr (CAUSAL) qt = P.q_tiles - 1 - qt;
+  const int kvh = (bh / P.hq) * (P.hq / P.group) + (bh % P.hq) / P.group;
+  const int64_t q_head = (int64_t)bh * P.nq * D;
+  const int64_t kv_head = (int64_t)kvh * N * D;
+  const __amdgpu_buffer_rsrc_t q_rs = make_rsrc(P.q + q_head, (uint32_t)P.nq * D * 2);
+  const i32x4 k_rs = make_rsrc_words(P.k + kv_head, (uint32_t)N * D * 2);
+  const i32x4 v_rs = make_rsrc_words(P.v + kv_head, (uint32_t)N * D * 2);
   const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
 
   // Global -> LDS without registers: each wave load moves 64 x 16 B into 1 KiB
@@ -259,6 +279,15 @@ fa2_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   // Q_i fragments: the B operands of S^T = K_j Q_i^T, held for the whole
   // loop.  Query block b of this wave is rows q0 + 32*b + l32.
   const int q0 = qt * BR + wave * 32 * QB;
+
+  // Key tiles this workgroup needs: all of them, or with the causal mask those
+  // up to the last key its last row sees.  A workgroup whose rows see no key
+  // writes O = 0 and lse = -inf.
+  int n_tiles = (N + BC - 1) / BC;
+  if constexpr (CAUSAL) {
+    const int last_key = qt * BR + BR - 1 + P.causal_off;  // may be < 0
+    n_tiles = last_key < 0 ? 0 : min(n_tiles, last_key / BC + 1);
+  }
   X8 qf[QB][KS];
 #pragma unroll
   for (int b = 0; b < QB; ++b)
@@ -328,6 +357,9 @@ fa2_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   // p = exp2(s*c - m_ref): rounded pairs into pf, the unrounded sum returned.
   // A masked key holds -inf (c > 0) or +inf (c < 0), so its p is 0.
   auto probs = [&](const f32x16 (&sc)[KB], X8 (&pf)[ST], float m) -> float {
+    // A causal row that has seen no key yet has m = -inf and only masked
+    // logits; reference 0 gives them p = 0 rather than NaN.
+    if constexpr (CAUSAL) m = m == -INFINITY ? 0.0f : m;
     float rs = 0.0f;
 #pragma unroll
     for (int st = 0; st < ST; ++st) {
@@ -349,8 +381,6 @@ fa2_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     return rs;
   };
 
-  const int n_tiles = (N + BC - 1) / BC;
-
   // One iteration j, as a single straight-line block for the scheduler:
   // S_{j+1} = K_{j+1} Q^T and O += P_{j-1} V_{j-1} on the matrix cores while
   // the VALU turns S_j into P_j.  K runs two tiles ahead of the V the block
@@ -363,17 +393,23 @@ fa2_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     if (j + 2 < n_tiles) issue_k(j + 2);
     issue_v(j);
 
+    // Mask keys past N and, with the causal option, keys past a row's
+    // diagonal (key > row + causal_off).  Decided per wave: its rows are
+    // q0 .. q0 + 32*QB - 1.
     const int key0 = j * BC;
-    const bool tail = key0 + BC > N;  // wave-uniform
-    if (tail) {
+    bool masked = key0 + BC > N;
+    if constexpr (CAUSAL) masked |= key0 + BC - 1 > q0 + P.causal_off;
+    if (masked) {
 #pragma unroll
-      for (int b = 0; b < QB; ++b)
+      for (int b = 0; b < QB; ++b) {
+        const int lim = CAUSAL ? min(N - 1, q0 + 32 * b + l32 + P.causal_off) : N - 1;
 #pragma unroll
         for (int kk = 0; kk < KB; ++kk)
 #pragma unroll
           for (int i = 0; i < 16; ++i)
-            if (key0 + kk * 32 + (i >> 2) * 8 + half * 4 + (i & 3) >= N)
+            if (key0 + kk * 32 + (i >> 2) * 8 + half * 4 + (i & 3) > lim)
               s_cur[b][kk][i] = MODE == kNegative ? INFINITY : -INFINITY;
+      }
     }
 
     gemm1(j + 1, s_nxt);
@@ -384,6 +420,9 @@ fa2_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     for (int b = 0; b < QB; ++b) {
       rs[b] = probs(s_cur[b], p_cur[b], m_ref[b]);
       over |= !(rs[b] <= kSumLimit);  // also true for inf / NaN
+      // Causal rows that see no key keep m_ref = -inf; they take the rare
+      // path, which leaves their p at 0.
+      if constexpr (CAUSAL) over |= m_ref[b] == -INFINITY;
     }
     constexpr int MF = QB * ((MODE == kZero ? 0 : KS * KB) + (decltype(first)::value ? 0 : ST * DB));
 #pragma unroll
@@ -412,7 +451,8 @@ fa2_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         const float t_max = __builtin_isfinite(ext) ? ext * c : -INFINITY;
         const float t_row = fmaxf(t_max, __shfl_xor(t_max, 32));
         const float mine = !(rs[b] <= kSumLimit) ? 1.0f : 0.0f;
-        const bool move = fmaxf(mine, __shfl_xor(mine, 32)) > 0.0f;
+        // a row still at -inf takes its first reference from any visible key
+        const bool move = fmaxf(mine, __shfl_xor(mine, 32)) > 0.0f || m_ref[b] == -INFINITY;
         const float m_new = move ? fmaxf(m_ref[b], t_row) : m_ref[b];
         const float alpha =
             m_new == m_ref[b] ? 1.0f : __builtin_amdgcn_exp2f(m_ref[b] - m_new);
@@ -432,46 +472,49 @@ fa2_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     __syncthreads();
   };
 
-  // Prologue: Q, K_0 and K_1 resident, S_0 computed.  Q and the tiles retire
-  // before the loop: vmcnt is a counter, so a load still in flight at the
-  // loop head would make every iteration wait on its own prefetch.
-  issue_k(0);
-  if (n_tiles > 1) issue_k(1);
+  if (n_tiles > 0) {
+    // Prologue: Q, K_0 and K_1 resident, S_0 computed.  Q and the tiles retire
+    // before the loop: vmcnt is a counter, so a load still in flight at the
+    // loop head would make every iteration wait on its own prefetch.
+    issue_k(0);
+    if (n_tiles > 1) issue_k(1);
 #pragma unroll
-  for (int b = 0; b < QB; ++b)
+    for (int b = 0; b < QB; ++b)
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[b][ks]));
-  wait_vmem();
-  __syncthreads();
+      for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[b][ks]));
+    wait_vmem();
+    __syncthreads();
 
-  f32x16 sA[QB][KB], sB[QB][KB];
-  X8 pA[QB][ST], pB[QB][ST];
-  gemm1(0, sA);
-  __syncthreads();  // every wave is done with K_0 before K_2 may overwrite it
+    f32x16 sA[QB][KB], sB[QB][KB];
+    X8 pA[QB][ST], pB[QB][ST];
+    gemm1(0, sA);
+    __syncthreads();  // every wave is done with K_0 before K_2 may overwrite it
 
-  // Iterations run in pairs so the S and P register sets swap roles without
-  // copies: even j computes (S_j in sA, S_{j+1} into sB, P_j into pA).
-  step(std::true_type{}, 0, sA, sB, pB, pA);
-  int j = 1;
-  for (; j + 1 < n_tiles; j += 2) {
-    step(std::false_type{}, j, sB, sA, pA, pB);
-    step(std::false_type{}, j + 1, sA, sB, pB, pA);
+    // Iterations run in pairs so the S and P register sets swap roles without
+    // copies: even j computes (S_j in sA, S_{j+1} into sB, P_j into pA).
+    step(std::true_type{}, 0, sA, sB, pB, pA);
+    int j = 1;
+    for (; j + 1 < n_tiles; j += 2) {
+      step(std::false_type{}, j, sB, sA, pA, pB);
+      step(std::false_type{}, j + 1, sA, sB, pB, pA);
+    }
+    if (j < n_tiles) {
+      step(std::false_type{}, j, sB, sA, pA, pB);
+      gemm2(j, pB);
+    } else {
+      gemm2(j - 1, pA);
+    }
   }
-  if (j < n_tiles) {
-    step(std::false_type{}, j, sB, sA, pA, pB);
-    gemm2(j, pB);
-  } else {
-    gemm2(j - 1, pA);
-  }
 
-  // ---- epilogue: O = acc / l, lse = (m_ref + log2 l) * ln 2
+  // ---- epilogue: O = acc / l, lse = (m_ref + log2 l) * ln 2; a row that saw
+  // no key (l = 0) gets O = 0 and lse = -inf
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
     const int qrow = q0 + 32 * b + l32;
     const float l_tot = l_part[b] + __shfl_xor(l_part[b], 32);
-    const float inv = 1.0f / l_tot;
-    if (qrow < N) {
-      uint16_t* orow = o + head + (int64_t)qrow * D;
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    if (qrow < P.nq) {
+      uint16_t* orow = P.o + q_head + (int64_t)qrow * D;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -482,29 +525,31 @@ fa2_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
           *(u32x2*)(orow + db * 32 + g4 * 8 + half * 4) = __builtin_bit_cast(u32x2, ov);
         }
       if (half == 0)
-        lse[(int64_t)bh * N + qrow] = (m_ref[b] + __log2f(l_tot)) * kLn2;
+        P.lse[(int64_t)bh * P.nq + qrow] =
+            l_tot > 0.0f ? (m_ref[b] + __log2f(l_tot)) * kLn2 : -INFINITY;
     }
   }
 }
 
-typedef void (*kernel_fn)(const uint16_t*, const uint16_t*, const uint16_t*,
-                          uint16_t*, float*, int, int, int, float);
+typedef void (*kernel_fn)(const Problem);
 
-template <int D, bool FP16>
+template <int D, bool FP16, bool CAUSAL>
 kernel_fn pick_mode(int mode) {
   switch (mode) {
-    case kNegative: return fa2_fwd_kernel<D, FP16, kNegative>;
-    case kZero: return fa2_fwd_kernel<D, FP16, kZero>;
-    default: return fa2_fwd_kernel<D, FP16, kPositive>;
+    case kNegative: return fa2_fwd_kernel<D, FP16, kNegative, CAUSAL>;
+    case kZero: return fa2_fwd_kernel<D, FP16, kZero, CAUSAL>;
+    default: return fa2_fwd_kernel<D, FP16, kPositive, CAUSAL>;
   }
 }
 
 template <int D>
-kernel_fn pick(bool fp16, int mode) {
-  return fp16 ? pick_mode<D, true>(mode) : pick_mode<D, false>(mode);
+kernel_fn pick(bool fp16, int mode, bool causal) {
+  if (fp16) return causal ? pick_mode<D, true, true>(mode) : pick_mode<D, true, false>(mode);
+  return causal ? pick_mode<D, false, true>(mode) : pick_mode<D, false, false>(mode);
 }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (na == 0 || nb == 0) return false;
   const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
   return x < y + nb && y < x + na;
 }
@@ -517,13 +562,14 @@ const char* fa2_strerror(int status) {
   switch (status) {
     case FA2_OK: return "success";
     case FA2_ERR_NULL: return "a required pointer is NULL";
-    case FA2_ERR_SHAPE: return "B, H or N negative, or sizes too large";
+    case FA2_ERR_SHAPE: return "a size is negative, heads do not group, or sizes are too large";
     case FA2_ERR_HEADDIM: return "head dimension must be 64, 128 or 256";
     case FA2_ERR_DTYPE: return "dtype must be FA2_BF16 or FA2_FP16";
     case FA2_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
     case FA2_ERR_SCALE: return "scale must be finite";
     case FA2_ERR_ALIAS: return "o or lse overlaps an input or each other";
     case FA2_ERR_HIP: return "kernel launch failed";
+    case FA2_ERR_OPTION: return "causal must be 0 or 1";
     default: return "unknown status";
   }
 }
@@ -540,53 +586,72 @@ int fa2_tile_config(int64_t d, int dtype, int* block_q, int* block_k, int* waves
   return FA2_OK;
 }
 
-int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-            int64_t B, int64_t H, int64_t N, int64_t d, float scale, int dtype,
-            void* stream) {
+int fa2_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse,
+                int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
+                float scale, int causal, int dtype, void* stream) {
   if (dtype != FA2_BF16 && dtype != FA2_FP16) return FA2_ERR_DTYPE;
   if (d != 64 && d != 128 && d != 256) return FA2_ERR_HEADDIM;
-  if (B < 0 || H < 0 || N < 0) return FA2_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return FA2_ERR_OPTION;
+  if (B < 0 || Hq < 0 || Hkv < 0 || Nq < 0 || Nk < 0) return FA2_ERR_SHAPE;
   if (!__builtin_isfinite(scale)) return FA2_ERR_SCALE;
-  if (B == 0 || H == 0 || N == 0) return FA2_OK;
-  // N*d elements of one head are addressed with 32-bit row offsets; the
-  // workgroup count must fit a 1-D grid.
-  if (N > (int64_t)1 << 30 || N * d > ((int64_t)1 << 31) - 1) return FA2_ERR_SHAPE;
+  if (B == 0 || Hq == 0 || Nq == 0) return FA2_OK;  // no output rows
+  if (Hkv == 0 || Hq % Hkv != 0) return FA2_ERR_SHAPE;
+  // One head's rows are addressed with 32-bit offsets (plus slack for the
+  // prefetch of tiles past the end); the workgroup count fits a 1-D grid.
+  const int64_t lim = ((int64_t)1 << 31) - ((int64_t)1 << 20);
+  if (Nq > (int64_t)1 << 30 || Nk > (int64_t)1 << 30 || Nq * d > lim || Nk * d > lim)
+    return FA2_ERR_SHAPE;
   int bq = 0, bk = 0, nw = 0;
   fa2_tile_config(d, dtype, &bq, &bk, &nw);
-  const int64_t q_tiles = (N + bq - 1) / bq;
-  if (B > ((int64_t)1 << 31) / H) return FA2_ERR_SHAPE;
-  const int64_t bh = B * H;
+  const int64_t q_tiles = (Nq + bq - 1) / bq;
+  if (B > (((int64_t)1 << 31) - 1) / Hq) return FA2_ERR_SHAPE;
+  const int64_t bh = B * Hq;
   if (bh > (((int64_t)1 << 31) - 1) / q_tiles) return FA2_ERR_SHAPE;
   const int64_t groups = bh * q_tiles;
-  if (!q || !k || !v || !o || !lse) return FA2_ERR_NULL;
+  if (!q || !o || !lse || (Nk > 0 && (!k || !v))) return FA2_ERR_NULL;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return FA2_ERR_ALIGN;
   if ((uintptr_t)lse & 3) return FA2_ERR_ALIGN;
-  const size_t tbytes = (size_t)(bh * N * d) * 2;
-  const size_t lbytes = (size_t)(bh * N) * 4;
-  if (fa2::overlaps(o, tbytes, q, tbytes) || fa2::overlaps(o, tbytes, k, tbytes) ||
-      fa2::overlaps(o, tbytes, v, tbytes) || fa2::overlaps(lse, lbytes, q, tbytes) ||
-      fa2::overlaps(lse, lbytes, k, tbytes) || fa2::overlaps(lse, lbytes, v, tbytes) ||
-      fa2::overlaps(lse, lbytes, o, tbytes))
+  const size_t qbytes = (size_t)(bh * Nq * d) * 2;
+  const size_t kbytes = (size_t)(B * Hkv * Nk * d) * 2;
+  const size_t lbytes = (size_t)(bh * Nq) * 4;
+  if (fa2::overlaps(o, qbytes, q, qbytes) || fa2::overlaps(o, qbytes, k, kbytes) ||
+      fa2::overlaps(o, qbytes, v, kbytes) || fa2::overlaps(lse, lbytes, q, qbytes) ||
+      fa2::overlaps(lse, lbytes, k, kbytes) || fa2::overlaps(lse, lbytes, v, kbytes) ||
+      fa2::overlaps(lse, lbytes, o, qbytes))
     return FA2_ERR_ALIAS;
 
   // logits in log2 units: t = s * scale * log2(e)
   const float c = (float)((double)scale * 1.4426950408889634074);
   const bool fp16 = dtype == FA2_FP16;
   const int mode = c > 0.0f ? fa2::kPositive : c < 0.0f ? fa2::kNegative : fa2::kZero;
-  const float c_arg = mode == fa2::kZero ? 1.0f : c;  // zero mode: logits are 0, t = s
-  fa2::kernel_fn fn = d == 64 ? fa2::pick<64>(fp16, mode)
-                    : d == 128 ? fa2::pick<128>(fp16, mode)
-                               : fa2::pick<256>(fp16, mode);
-  const uint16_t* qp = (const uint16_t*)q;
-  const uint16_t* kp = (const uint16_t*)k;
-  const uint16_t* vp = (const uint16_t*)v;
-  uint16_t* op = (uint16_t*)o;
-  int n32 = (int)N, qt32 = (int)q_tiles, g32 = (int)groups;
-  void* args[] = {&qp, &kp, &vp, &op, &lse, &n32, &qt32, &g32, (void*)&c_arg};
+  fa2::Problem P;
+  P.q = (const uint16_t*)q;
+  P.k = (const uint16_t*)k;
+  P.v = (const uint16_t*)v;
+  P.o = (uint16_t*)o;
+  P.lse = lse;
+  P.nq = (int)Nq;
+  P.nk = (int)Nk;
+  P.hq = (int)Hq;
+  P.group = (int)(Hq / Hkv);
+  P.q_tiles = (int)q_tiles;
+  P.n_groups = (int)groups;
+  P.causal_off = (int)(Nk - Nq);
+  P.c = mode == fa2::kZero ? 1.0f : c;  // zero mode: logits are 0, t = s
+  fa2::kernel_fn fn = d == 64 ? fa2::pick<64>(fp16, mode, causal)
+                    : d == 128 ? fa2::pick<128>(fp16, mode, causal)
+                               : fa2::pick<256>(fp16, mode, causal);
+  void* args[] = {&P};
   hipError_t err = hipLaunchKernel((const void*)fn, dim3((unsigned)groups),
                                    dim3((unsigned)(nw * 64)), args, 0,
                                    (hipStream_t)stream);
   return err == hipSuccess ? FA2_OK : FA2_ERR_HIP;
+}
+
+int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+            int64_t B, int64_t H, int64_t N, int64_t d, float scale, int dtype,
+            void* stream) {
+  return fa2_fwd_ext(q, k, v, o, lse, B, H, H, N, N, d, scale, 0, dtype, stream);
 }
 
 }  // extern "C"

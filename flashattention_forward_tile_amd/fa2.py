@@ -22,6 +22,7 @@ ERR_ALIGN = -5
 ERR_SCALE = -6
 ERR_ALIAS = -7
 ERR_HIP = -8
+ERR_OPTION = -9
 
 BF16 = 0
 FP16 = 1
@@ -33,6 +34,11 @@ _SIGNATURES = {
                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                ctypes.c_float, ctypes.c_int, ctypes.c_void_p]),
+    "fa2_fwd_ext": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                   ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                   ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
+                                   ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
     "fa2_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "fa2_tile_config": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int,
                                        ctypes.POINTER(ctypes.c_int),
@@ -91,24 +97,36 @@ def fwd_raw(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, N, d, scale, dtype,
                          float(scale), int(dtype), stream)
 
 
-def fwd(q, k, v, scale=None, out=None, lse=None):
-    """Attention forward: returns (o, lse) for q, k, v of shape [B, H, N, d].
+def fwd_ext_raw(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, Hq, Hkv, Nq, Nk, d, scale,
+                causal, dtype, stream=0) -> int:
+    """Direct call of fa2_fwd_ext with integer pointers; returns the status."""
+    return lib().fa2_fwd_ext(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, Hq, Hkv, Nq, Nk,
+                             d, float(scale), int(causal), int(dtype), stream)
 
-    q, k, v: contiguous bf16 or fp16 CUDA(HIP) tensors of one shape and dtype.
-    scale: logit multiplier, default 1/sqrt(d).
-    out, lse: optional preallocated outputs ([B, H, N, d] of q's dtype and
-    [B, H, N] float32, contiguous, on q's device).
+
+def fwd(q, k, v, scale=None, causal=False, out=None, lse=None):
+    """Attention forward: returns (o, lse).
+
+    q: [B, Hq, Nq, d]; k, v: [B, Hkv, Nk, d] with Hq a multiple of Hkv; all
+    contiguous bf16 or fp16 CUDA(HIP) tensors of one dtype on one device.
+    scale: logit multiplier, default 1/sqrt(d).  causal: row i sees keys
+    j <= i + Nk - Nq.  out, lse: optional preallocated outputs ([B, Hq, Nq, d]
+    of q's dtype and [B, Hq, Nq] float32, contiguous, on q's device).
+    Equal shapes and causal=False call fa2_fwd; anything else fa2_fwd_ext.
     The kernel is enqueued on torch's current stream of q's device.
     """
-    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
-        raise ValueError("q, k, v must share one [B, H, N, d] shape")
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape:
+        raise ValueError("q must be [B, Hq, Nq, d] and k, v one [B, Hkv, Nk, d] shape")
+    B, Hq, Nq, d = q.shape
+    _, Hkv, Nk, dk = k.shape
+    if k.shape[0] != B or dk != d:
+        raise ValueError("k, v must share q's batch and head dimension")
     if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DTYPE:
         raise ValueError("q, k, v must all be bfloat16 or all float16")
     if not (q.is_cuda and k.device == q.device and v.device == q.device):
         raise ValueError("q, k, v must be on one GPU")
     if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
         raise ValueError("q, k, v must be contiguous")
-    B, H, N, d = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
@@ -117,14 +135,19 @@ def fwd(q, k, v, scale=None, out=None, lse=None):
             or not out.is_contiguous():
         raise ValueError("out must be a contiguous tensor like q")
     if lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    elif lse.shape != (B, H, N) or lse.dtype != torch.float32 \
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    elif lse.shape != (B, Hq, Nq) or lse.dtype != torch.float32 \
             or lse.device != q.device or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+        raise ValueError("lse must be a contiguous float32 [B, Hq, Nq] tensor")
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        code = fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                       lse.data_ptr(), B, H, N, d, scale, _DTYPE[q.dtype], stream)
+        if q.shape == k.shape and not causal:
+            code = fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                           lse.data_ptr(), B, Hq, Nq, d, scale, _DTYPE[q.dtype], stream)
+        else:
+            code = fwd_ext_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                               lse.data_ptr(), B, Hq, Hkv, Nq, Nk, d, scale,
+                               1 if causal else 0, _DTYPE[q.dtype], stream)
     if code != OK:
         raise FA2Error(code)
     return out, lse

@@ -17,7 +17,8 @@
  * forward only, non-causal, no dropout, no KV cache, equal query and key
  * lengths, 16-bit (bf16 or fp16) inputs and outputs, softmax in fp32.  The head
  * dimension may be 64, 128 (the page's) or 256.  Unlike the page, N need not
- * be a multiple of the block size: the last key tile is masked.
+ * be a multiple of the block size: the last key tile is masked.  fa2_fwd_ext
+ * adds causal masking, Nq != Nk and grouped key/value heads.
  *
  * All entry points are plain C.  Pointers are device pointers unless stated.
  */
@@ -41,14 +42,15 @@ enum fa2_dtype {
 enum fa2_status {
   FA2_OK = 0,
   FA2_ERR_NULL = -1,    /* a required pointer is NULL */
-  FA2_ERR_SHAPE = -2,   /* B, H or N negative, or sizes overflow the grid or
-                           64-bit element offsets */
+  FA2_ERR_SHAPE = -2,   /* a size is negative, Hq is not a multiple of Hkv,
+                           or sizes overflow the grid or per-head offsets */
   FA2_ERR_HEADDIM = -3, /* d is not 64, 128 or 256 */
   FA2_ERR_DTYPE = -4,   /* dtype is not an fa2_dtype */
   FA2_ERR_ALIGN = -5,   /* q, k, v or o not 16-byte aligned, lse not 4-byte */
   FA2_ERR_SCALE = -6,   /* scale is NaN or infinite */
   FA2_ERR_ALIAS = -7,   /* o or lse overlaps q, k, v, or each other */
-  FA2_ERR_HIP = -8      /* the kernel launch failed (HIP error) */
+  FA2_ERR_HIP = -8,     /* the kernel launch failed (HIP error) */
+  FA2_ERR_OPTION = -9   /* causal is not 0 or 1 */
 };
 
 /*
@@ -86,6 +88,32 @@ enum fa2_status {
 int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
             int64_t B, int64_t H, int64_t N, int64_t d, float scale,
             int dtype, void* stream);
+
+/*
+ * fa2_fwd_ext -- the same operation widened along the rows the "Kernel
+ * Specification" section of the Ampere Part 1 page leaves out: causal
+ * masking, unequal query and key lengths (cross-attention, a key/value
+ * cache), and grouped key/value heads (MQA/GQA, the setting of the Colfax
+ * "FlashAttention-3 for Inference" post).
+ *
+ *   q, o     : [B][Hq][Nq][d] contiguous, element type `dtype`.
+ *   k, v     : [B][Hkv][Nk][d] contiguous; query head h reads key/value head
+ *              h / (Hq / Hkv).  Hq must be a multiple of Hkv >= 1.
+ *   lse      : [B][Hq][Nq] fp32.
+ *   causal   : 0 = every row sees all Nk keys; 1 = row i sees keys
+ *              j <= i + Nk - Nq (the last row sees every key; with Nq == Nk
+ *              this is the usual lower-triangular mask).
+ *   A row that sees no key (causal with Nq > Nk, or Nk == 0) gets O = 0 and
+ *   lse = -inf.  k and v may be NULL when Nk == 0.
+ *
+ * Other arguments, alignment, ownership, asynchrony, numerics and return
+ * codes are those of fa2_fwd; fa2_fwd(q, k, v, o, lse, B, H, N, d, ...) is
+ * fa2_fwd_ext(q, k, v, o, lse, B, H, H, N, N, d, scale, 0, dtype, stream).
+ * B*Hq*Nq == 0 returns FA2_OK and touches nothing.
+ */
+int fa2_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse,
+                int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
+                int64_t d, float scale, int causal, int dtype, void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* fa2_strerror(int status);

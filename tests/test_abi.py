@@ -28,7 +28,8 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["fa2_fwd", "fa2_strerror", "fa2_tile_config"]
+    assert declared_functions() == ["fa2_fwd", "fa2_fwd_ext", "fa2_strerror",
+                                    "fa2_tile_config"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -38,11 +39,11 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_strerror_covers_every_status(lib):
     texts = set()
-    for code in range(0, -9, -1):
+    for code in range(0, -10, -1):
         s = fa2.strerror(code)
         assert s and s != "unknown status", code
         texts.add(s)
-    assert len(texts) == 9
+    assert len(texts) == 10
     assert fa2.strerror(17) == "unknown status"
 
 
@@ -97,3 +98,31 @@ def test_no_silent_fallback(monkeypatch):
     monkeypatch.setattr(fa2, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         fa2.lib()
+
+
+EXT = dict(B=2, Hq=4, Hkv=2, Nq=100, Nk=70, d=128, scale=0.1, causal=1, dtype=fa2.BF16)
+
+
+def call_ext(q=A, k=A + 0x1000000, v=A + 0x2000000, o=A + 0x3000000,
+             lse=A + 0x4000000, **kw):
+    p = dict(EXT)
+    p.update(kw)
+    return fa2.fwd_ext_raw(q, k, v, o, lse, p["B"], p["Hq"], p["Hkv"], p["Nq"], p["Nk"],
+                           p["d"], p["scale"], p["causal"], p["dtype"], 0)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(causal=2), fa2.ERR_OPTION), (dict(causal=-1), fa2.ERR_OPTION),
+    (dict(Hkv=3), fa2.ERR_SHAPE), (dict(Hkv=0), fa2.ERR_SHAPE), (dict(Hkv=-1), fa2.ERR_SHAPE),
+    (dict(Nk=-1), fa2.ERR_SHAPE), (dict(Nq=-1), fa2.ERR_SHAPE),
+    (dict(Nk=1 << 31), fa2.ERR_SHAPE), (dict(q=0), fa2.ERR_NULL), (dict(k=0), fa2.ERR_NULL),
+    (dict(d=32), fa2.ERR_HEADDIM), (dict(k=A + 0x1000004), fa2.ERR_ALIGN),
+    (dict(o=A + 0x2000000 + 512), fa2.ERR_ALIAS), (dict(scale=float("nan")), fa2.ERR_SCALE),
+])
+def test_ext_host_validation(lib, kw, code):
+    assert call_ext(**kw) == code
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(Hq=0, Hkv=0), dict(Nq=0)])
+def test_ext_empty_output_is_a_no_op(lib, kw):
+    assert call_ext(q=0, k=0, v=0, o=0, lse=0, **kw) == fa2.OK

@@ -1,0 +1,129 @@
+"""GPU parity of fa2_fwd_ext (causal masking, Nq != Nk, grouped K/V heads)
+against the fp64 oracle (needs an MI355X)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from flashattention_forward_tile_amd import fa2
+from flashattention_forward_tile_amd.workloads import bits
+from parity import assert_parity, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+_TD = {"bf16": torch.bfloat16, "fp16": torch.float16}
+
+
+def announce(*what):
+    print("CASE", *what, flush=True)
+
+
+def rand(shape, dtype, seed, mult=1.0):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(shape, generator=g) * mult).to(_TD[dtype])
+
+
+def inputs(B, Hq, Hkv, Nq, Nk, d, dtype, seed):
+    return (rand((B, Hq, Nq, d), dtype, seed), rand((B, Hkv, Nk, d), dtype, seed + 1),
+            rand((B, Hkv, Nk, d), dtype, seed + 2))
+
+
+def run_gpu(q, k, v, scale, causal):
+    o, lse = fa2.fwd(q.to(DEV), k.to(DEV), v.to(DEV), scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+def f64(t):
+    return t.double().numpy()
+
+
+def check(q, k, v, dtype, scale, causal, tag, rows=None):
+    o, lse = run_gpu(q, k, v, scale, causal)
+    o_ref, lse_ref = oracle.attention(bits(q), bits(k), bits(v), dtype, scale, rows=rows,
+                                      causal=causal)
+    d = q.shape[-1]
+    og = f64(o) if rows is None else f64(o).reshape(-1, d)[rows]
+    lg = f64(lse) if rows is None else f64(lse).reshape(-1)[rows]
+    seen = np.isfinite(lse_ref)
+    # rows that see no key: exactly O = 0 and lse = -inf
+    assert np.all(og[~seen] == 0.0) and np.all(lg[~seen] == -np.inf), tag
+    assert_parity(og[seen], lg[seen], o_ref[seen], lse_ref[seen], tag, lse_abs=1e-3)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("N", [1, 7, 64, 255, 256, 1000])
+def test_causal_square(N, dtype, d):
+    announce("causal", N, dtype, d)
+    q, k, v = inputs(1, 2, 2, N, N, d, dtype, seed=N + d)
+    check(q, k, v, dtype, 1.0 / math.sqrt(d), True, "causal N=%d %s d=%d" % (N, dtype, d))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Nq,Nk", [(100, 300), (300, 100), (1, 1000), (257, 513), (600, 31)])
+def test_unequal_lengths(Nq, Nk, causal):
+    announce("lengths", Nq, Nk, causal)
+    q, k, v = inputs(2, 2, 2, Nq, Nk, 128, "bf16", seed=Nq * 7 + Nk)
+    check(q, k, v, "bf16", 1.0 / math.sqrt(128), causal,
+          "Nq=%d Nk=%d causal=%d" % (Nq, Nk, causal))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (8, 1), (6, 3)])
+def test_grouped_heads(Hq, Hkv, causal):
+    announce("gqa", Hq, Hkv, causal)
+    q, k, v = inputs(2, Hq, Hkv, 200, 330, 128, "fp16", seed=Hq * 10 + Hkv)
+    check(q, k, v, "fp16", 1.0 / math.sqrt(128), causal,
+          "Hq=%d Hkv=%d causal=%d" % (Hq, Hkv, causal))
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.2, 1.5])
+def test_causal_scales(scale):
+    announce("causal scale", scale)
+    q, k, v = inputs(1, 2, 2, 300, 300, 64, "bf16", seed=77)
+    check(q, k, v, "bf16", scale, True, "causal scale=%g" % scale)
+
+
+def test_causal_headline_sampled():
+    """B=4, H=16, N=4096, d=128 bf16 causal, sampled rows."""
+    announce("causal headline")
+    q, k, v = inputs(4, 16, 16, 4096, 4096, 128, "bf16", seed=5)
+    bq, _, _ = fa2.tile_config(128)
+    check(q, k, v, "bf16", 1.0 / math.sqrt(128), True, "causal headline",
+          rows=sample_rows(4, 16, 4096, bq, per_head=4, seed=3))
+
+
+def test_no_keys():
+    """Nk = 0: every row sees no key (O = 0, lse = -inf), with or without mask."""
+    announce("Nk=0")
+    q = rand((1, 2, 50, 128), "bf16", 1).to(DEV)
+    k = torch.empty((1, 2, 0, 128), dtype=torch.bfloat16, device=DEV)
+    for causal in (False, True):
+        o, lse = fa2.fwd(q, k, k.clone(), causal=causal)
+        torch.cuda.synchronize()
+        assert torch.all(o == 0) and torch.all(lse == -float("inf"))
+
+
+def test_causal_last_row_equals_full_attention():
+    """The last causal row sees every key: bit for bit the non-causal row."""
+    announce("causal last row")
+    q, k, v = inputs(1, 4, 4, 777, 777, 128, "bf16", seed=9)
+    oc, lc = run_gpu(q, k, v, 0.09, True)
+    of, lf = run_gpu(q, k, v, 0.09, False)
+    assert torch.equal(oc[:, :, -1], of[:, :, -1]) and torch.equal(lc[:, :, -1], lf[:, :, -1])
+
+
+def test_grouped_heads_equal_repeated_heads():
+    """Hkv < Hq gives bit for bit what repeating each K/V head gives."""
+    announce("gqa repeat")
+    q, k, v = inputs(2, 8, 2, 300, 300, 128, "bf16", seed=11)
+    for causal in (False, True):
+        og, lg = run_gpu(q, k, v, 0.1, causal)
+        kr = k.repeat_interleave(4, dim=1).contiguous()
+        vr = v.repeat_interleave(4, dim=1).contiguous()
+        orr, lr = run_gpu(q, kr, vr, 0.1, causal)
+        assert torch.equal(og, orr) and torch.equal(lg, lr)
