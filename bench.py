@@ -2,8 +2,10 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload headline]
 
-A step is one fa2_fwd launch over the whole workload (every (b, h) and query
-row of one batch), inputs resident in HBM.  W untimed steps, then exactly K
+A step is one fa2_fwd (or fa2_fwd_ext, for the causal / grouped-head / unequal
+length workloads) launch over the whole workload (every (b, h) and query row
+of one batch), inputs resident in HBM.  FLOPs count the two products over the
+(query, key) pairs that enter the softmax: 4*B*H*N^2*d without a mask.  W untimed steps, then exactly K
 steps timed with HIP events on the launch stream, bracketed by device
 synchronisation.  Prints ONE JSON line: forward attention TFLOP/s counting
 4*B*H*N^2*d FLOPs, the roofline of the kernel against the dense bf16/fp16 MFMA
@@ -101,18 +103,21 @@ def cpu_baseline(w, q, k, v):
 
     qb, kb, vb = bits(q), bits(k), bits(v)
     threads = oracle.host_threads()
+    group = w.H // w.kv_heads
     heads = 0
     t0 = time.perf_counter()
     while heads < w.B * w.H:
         b, h = divmod(heads, w.H)
-        sl = (slice(b, b + 1), slice(h, h + 1))
-        oracle.attention(np.ascontiguousarray(qb[sl]), np.ascontiguousarray(kb[sl]),
-                         np.ascontiguousarray(vb[sl]), w.dtype, w.scale, nthreads=threads)
+        qs = (slice(b, b + 1), slice(h, h + 1))
+        ks = (slice(b, b + 1), slice(h // group, h // group + 1))
+        oracle.attention(np.ascontiguousarray(qb[qs]), np.ascontiguousarray(kb[ks]),
+                         np.ascontiguousarray(vb[ks]), w.dtype, w.scale, nthreads=threads,
+                         causal=w.causal)
         heads += 1
         if time.perf_counter() - t0 >= CPU_SAMPLE_SECONDS:
             break
     dt = time.perf_counter() - t0
-    flops = 4.0 * heads * w.N * w.N * w.d
+    flops = 4.0 * heads * w.visible_pairs * w.d
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
             "sample": "%d of %d heads (all %d query rows each) of the %s workload, "
@@ -173,9 +178,9 @@ def main():
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
 
     for _ in range(args.warmup):
-        fa2.fwd(qd, kd, vd, scale=w.scale, out=o, lse=lse)
+        fa2.fwd(qd, kd, vd, scale=w.scale, causal=w.causal, out=o, lse=lse)
     torch.cuda.synchronize(dev)
-    if not (torch.isfinite(o[0, 0].float()).all() and torch.isfinite(lse).all()):
+    if not (torch.isfinite(o[0, 0].float()).all() and torch.isfinite(lse[:, :, -1]).all()):
         raise RuntimeError("non-finite output")
 
     stream = torch.cuda.current_stream(dev)  # fa2.fwd launches on this stream
@@ -184,7 +189,7 @@ def main():
     wall0 = time.perf_counter()
     start.record(stream)
     for _ in range(args.steps):
-        fa2.fwd(qd, kd, vd, scale=w.scale, out=o, lse=lse)
+        fa2.fwd(qd, kd, vd, scale=w.scale, causal=w.causal, out=o, lse=lse)
     stop.record(stream)
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - wall0

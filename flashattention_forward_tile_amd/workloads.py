@@ -29,6 +29,7 @@ _TORCH_DTYPES = {"bf16": torch.bfloat16, "fp16": torch.float16}
 
 @dataclass(frozen=True)
 class Workload:
+    """H query heads of N rows; Hkv key/value heads of Nk rows (default H, N)."""
     name: str
     B: int
     H: int
@@ -36,26 +37,58 @@ class Workload:
     d: int
     dtype: str = "bf16"
     dist: str = "normal"
+    Hkv: int = 0
+    Nk: int = 0
+    causal: bool = False
+
+    @property
+    def kv_heads(self) -> int:
+        return self.Hkv or self.H
+
+    @property
+    def keys(self) -> int:
+        return self.Nk or self.N
 
     @property
     def scale(self) -> float:
         return 1.0 / math.sqrt(self.d)
 
     @property
+    def visible_pairs(self) -> int:
+        """(query row, key) pairs that enter the softmax, per (b, h)."""
+        nq, nk = self.N, self.keys
+        if not self.causal:
+            return nq * nk
+        # row i sees min(nk, max(0, i + 1 + nk - nq)) keys
+        total = 0
+        first = max(0, nq - nk)           # rows before this see nothing
+        full = max(first, nq)             # rows never exceed nk keys here
+        for i in range(first, full):
+            total += min(nk, i + 1 + nk - nq)
+        return total
+
+    @property
     def flops(self) -> int:
-        """Two N x N x d contractions per (b, h): 4 * B * H * N^2 * d."""
-        return 4 * self.B * self.H * self.N * self.N * self.d
+        """Two contractions over the visible pairs: 4 * B * H * pairs * d
+        (4 * B * H * N^2 * d without a mask)."""
+        return 4 * self.B * self.H * self.visible_pairs * self.d
 
     @property
     def algo_bytes(self) -> int:
         """Q, K, V read once and O written once (16-bit), LSE written (fp32)."""
-        elems = self.B * self.H * self.N * self.d
-        return 4 * elems * 2 + self.B * self.H * self.N * 4
+        q = self.B * self.H * self.N * self.d
+        kv = self.B * self.kv_heads * self.keys * self.d
+        return 2 * (2 * q + 2 * kv) + self.B * self.H * self.N * 4
 
     def describe(self) -> dict:
-        return {"workload": self.name, "B": self.B, "H": self.H, "N": self.N,
-                "d": self.d, "dtype": self.dtype, "inputs": self.dist,
-                "causal": False, "scale": "1/sqrt(d)"}
+        out = {"workload": self.name, "B": self.B, "H": self.H, "N": self.N,
+               "d": self.d, "dtype": self.dtype, "inputs": self.dist,
+               "causal": self.causal, "scale": "1/sqrt(d)"}
+        if self.kv_heads != self.H:
+            out["Hkv"] = self.kv_heads
+        if self.keys != self.N:
+            out["Nk"] = self.keys
+        return out
 
 
 def _sweep():
@@ -73,6 +106,10 @@ WORKLOADS = {
     **_sweep(),
     "d64": Workload("d64", 4, 16, 4096, 64, "bf16"),
     "d256": Workload("d256", 4, 8, 4096, 256, "bf16"),
+    # the rows the Kernel Specification section leaves out
+    "causal": Workload("causal", 4, 16, 4096, 128, "bf16", causal=True),
+    "gqa": Workload("gqa", 4, 16, 4096, 128, "bf16", Hkv=2),
+    "kv_cache": Workload("kv_cache", 4, 16, 1024, 128, "bf16", Hkv=4, Nk=8192, causal=True),
 }
 
 
@@ -80,17 +117,19 @@ def torch_dtype(dtype: str) -> torch.dtype:
     return _TORCH_DTYPES[dtype]
 
 
-def make_inputs(B, H, N, d, dtype="bf16", dist="normal", seed=0):
-    """Seeded CPU tensors (q, k, v) of shape [B, H, N, d] in the 16-bit dtype."""
+def make_inputs(B, H, N, d, dtype="bf16", dist="normal", seed=0, Hkv=None, Nk=None):
+    """Seeded CPU tensors q [B, H, N, d] and k, v [B, Hkv, Nk, d] (default Hkv =
+    H, Nk = N) in the 16-bit dtype."""
     g = torch.Generator().manual_seed(seed)
     shape = (B, H, N, d)
+    kv_shape = (B, Hkv or H, Nk if Nk is not None else N, d)
     q = torch.randn(shape, generator=g, dtype=torch.float32)
-    k = torch.randn(shape, generator=g, dtype=torch.float32)
+    k = torch.randn(kv_shape, generator=g, dtype=torch.float32)
     if dist == "normal":
-        v = torch.randn(shape, generator=g, dtype=torch.float32)
+        v = torch.randn(kv_shape, generator=g, dtype=torch.float32)
     elif dist == "stress":
         q.mul_(4.0)
-        v = torch.rand(shape, generator=g, dtype=torch.float32).mul_(2.0).sub_(1.0)
+        v = torch.rand(kv_shape, generator=g, dtype=torch.float32).mul_(2.0).sub_(1.0)
     else:
         raise ValueError("unknown input distribution %r" % dist)
     t = _TORCH_DTYPES[dtype]
@@ -98,7 +137,7 @@ def make_inputs(B, H, N, d, dtype="bf16", dist="normal", seed=0):
 
 
 def workload_inputs(w: Workload, seed=0):
-    return make_inputs(w.B, w.H, w.N, w.d, w.dtype, w.dist, seed)
+    return make_inputs(w.B, w.H, w.N, w.d, w.dtype, w.dist, seed, w.kv_heads, w.keys)
 
 
 def bits(t: torch.Tensor) -> np.ndarray:

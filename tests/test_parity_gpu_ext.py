@@ -127,3 +127,15 @@ def test_grouped_heads_equal_repeated_heads():
         vr = v.repeat_interleave(4, dim=1).contiguous()
         orr, lr = run_gpu(q, kr, vr, 0.1, causal)
         assert torch.equal(og, orr) and torch.equal(lg, lr)
+
+
+@pytest.mark.parametrize("name", ["gqa", "kv_cache"])
+def test_widened_workloads_sampled(name):
+    """The grouped-head and KV-cache workloads bench.py times, sampled rows."""
+    from flashattention_forward_tile_amd.workloads import WORKLOADS, workload_inputs
+    w = WORKLOADS[name]
+    announce(w)
+    q, k, v = workload_inputs(w, seed=0)
+    bq, _, _ = fa2.tile_config(w.d)
+    check(q, k, v, w.dtype, w.scale, w.causal, w.name,
+          rows=sample_rows(w.B, w.H, w.N, bq, per_head=4, seed=4))
