@@ -210,12 +210,28 @@ fa2_fwd_kernel(const Problem P) {
   // All query tiles of one head go to one XCD (dispatch is round-robin over
   // the 8 XCDs): the k-th workgroup on XCD x takes logical tile x*G/8 + k.
   // Query heads sharing a K/V head are adjacent, so they share it too.  With
-  // the causal mask the later (longer) query tiles of a head start first.
-  int id = blockIdx.x;
-  if ((P.n_groups & 7) == 0) id = (id & 7) * (P.n_groups >> 3) + (id >> 3);
-  const int bh = id / P.q_tiles;  // b * hq + h
-  int qt = id - bh * P.q_tiles;
-  if constexpr (CAUSAL) qt = P.q_tiles - 1 - qt;
+  // the causal mask the later (longer) query tiles start first.
+  int bh, qt;  // bh = b * hq + h
+  const int id = blockIdx.x;
+  const int per_xcd = P.n_groups >> 3;
+  if ((P.n_groups & 7) == 0) {
+    const int x = id & 7, kx = id >> 3;  // k-th workgroup dispatched on XCD x
+    if (CAUSAL && per_xcd % P.q_tiles == 0) {
+      // this XCD's heads, longest query tiles of all of them first
+      const int heads = per_xcd / P.q_tiles;
+      bh = x * heads + kx % heads;
+      qt = P.q_tiles - 1 - kx / heads;
+    } else {
+      const int logical = x * per_xcd + kx;
+      bh = logical / P.q_tiles;
+      qt = logical - bh * P.q_tiles;
+      if constexpr (CAUSAL) qt = P.q_tiles - 1 - qt;
+    }
+  } else {
+    bh = id / P.q_tiles;
+    qt = id - bh * P.q_tiles;
+    if constexpr (CAUSAL) qt = P.q_tiles - 1 - qt;
+  }
   const int kvh = (bh / P.hq) * (P.hq / P.group) + (bh % P.hq) / P.group;
   const int64_t q_head = (int64_t)bh * P.nq * D;
   const int64_t kv_head = (int64_t)kvh * N * D;
