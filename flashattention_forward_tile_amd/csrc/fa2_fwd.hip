@@ -252,14 +252,20 @@ fa2_fwd_kernel(const Problem P) {
     k_src[i] = (uint32_t)(row * RB + k_swizzle<CPR>(row, pc) * 16);
     v_src[i] = (uint32_t)(row * RB + v_swizzle<CPR>(row, pc) * 16);
   }
-  auto issue_k = [&](int j) {
-    const uint32_t dst = lds_base + (j & 1) * TBYTES + wave * 1024;
+  // `buf` (an integral constant) is j & 1, known at compile time in the
+  // unrolled loop, so LDS buffer offsets fold into instruction immediates.
+  // d = 256 keeps the offset in a register: with immediates its schedule
+  // hoists more loads and spills.
+  constexpr bool kImmBuf = D != 256;
+  auto buffer = [](int j, auto buf) { return kImmBuf ? decltype(buf)::value : (j & 1); };
+  auto issue_k = [&](int j, auto buf) {
+    const uint32_t dst = lds_base + buffer(j, buf) * TBYTES + wave * 1024;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i)
       load_lds16(k_rs, (uint32_t)j * TBYTES + k_src[i], dst + i * NW * 1024);
   };
-  auto issue_v = [&](int j) {
-    const uint32_t dst = lds_base + 2 * TBYTES + (j & 1) * TBYTES + wave * 1024;
+  auto issue_v = [&](int j, auto buf) {
+    const uint32_t dst = lds_base + 2 * TBYTES + buffer(j, buf) * TBYTES + wave * 1024;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i)
       load_lds16(v_rs, (uint32_t)j * TBYTES + v_src[i], dst + i * NW * 1024);
@@ -328,8 +334,8 @@ fa2_fwd_kernel(const Problem P) {
   // S^T_j = K_j Q_i^T : [BC keys] x [32 queries] per wave.  With a zero
   // scale every logit is 0 whatever Q and K hold, so S stays 0 and c is taken
   // as 1 (x = s - m_ref keeps masked keys at -inf).
-  auto gemm1 = [&](int j, f32x16 (&sd)[QB][KB]) {
-    const lds_char* kb = lds + (j & 1) * TBYTES;
+  auto gemm1 = [&](int j, auto buf, f32x16 (&sd)[QB][KB]) {
+    const lds_char* kb = lds + buffer(j, buf) * TBYTES;
 #pragma unroll
     for (int b = 0; b < QB; ++b)
 #pragma unroll
@@ -352,8 +358,8 @@ fa2_fwd_kernel(const Problem P) {
   // O^T += V_j^T P_j^T : [D] x [32 queries] per wave.  The A operand (V^T,
   // 8 keys per lane in the S^T accumulator's key order) comes from the
   // row-major V tile through two transposing LDS reads of 4 keys each.
-  auto gemm2 = [&](int j, const X8 (&pf)[QB][ST]) {
-    const lds_char* vb = lds + (j & 1) * TBYTES;
+  auto gemm2 = [&](int j, auto buf, const X8 (&pf)[QB][ST]) {
+    const lds_char* vb = lds + buffer(j, buf) * TBYTES;
 #pragma unroll
     for (int st = 0; st < ST; ++st)
 #pragma unroll
@@ -404,10 +410,13 @@ fa2_fwd_kernel(const Problem P) {
   // refilled only after the barrier ending the iteration that last read it.
   // The last iteration's S_{j+1} product reads whatever the idle K buffer
   // holds and is dropped.
-  auto step = [&](auto first, int j, f32x16 (&s_cur)[QB][KB], f32x16 (&s_nxt)[QB][KB],
+  using Even = std::integral_constant<int, 0>;
+  using Odd = std::integral_constant<int, 1>;
+  auto step = [&](auto first, auto par, int j, f32x16 (&s_cur)[QB][KB], f32x16 (&s_nxt)[QB][KB],
                   const X8 (&p_prev)[QB][ST], X8 (&p_cur)[QB][ST]) {
-    if (j + 2 < n_tiles) issue_k(j + 2);
-    issue_v(j);
+    using Other = std::integral_constant<int, 1 - decltype(par)::value>;
+    if (j + 2 < n_tiles) issue_k(j + 2, par);
+    issue_v(j, par);
 
     // Mask keys past N and, with the causal option, keys past a row's
     // diagonal (key > row + causal_off).  Decided per wave: its rows are
@@ -428,8 +437,8 @@ fa2_fwd_kernel(const Problem P) {
       }
     }
 
-    gemm1(j + 1, s_nxt);
-    if constexpr (!decltype(first)::value) gemm2(j - 1, p_prev);
+    gemm1(j + 1, Other{}, s_nxt);
+    if constexpr (!decltype(first)::value) gemm2(j - 1, Other{}, p_prev);
     float rs[QB];
     bool over = false;
 #pragma unroll
@@ -492,8 +501,8 @@ fa2_fwd_kernel(const Problem P) {
     // Prologue: Q, K_0 and K_1 resident, S_0 computed.  Q and the tiles retire
     // before the loop: vmcnt is a counter, so a load still in flight at the
     // loop head would make every iteration wait on its own prefetch.
-    issue_k(0);
-    if (n_tiles > 1) issue_k(1);
+    issue_k(0, Even{});
+    if (n_tiles > 1) issue_k(1, Odd{});
 #pragma unroll
     for (int b = 0; b < QB; ++b)
 #pragma unroll
@@ -503,22 +512,22 @@ fa2_fwd_kernel(const Problem P) {
 
     f32x16 sA[QB][KB], sB[QB][KB];
     X8 pA[QB][ST], pB[QB][ST];
-    gemm1(0, sA);
+    gemm1(0, Even{}, sA);
     __syncthreads();  // every wave is done with K_0 before K_2 may overwrite it
 
     // Iterations run in pairs so the S and P register sets swap roles without
     // copies: even j computes (S_j in sA, S_{j+1} into sB, P_j into pA).
-    step(std::true_type{}, 0, sA, sB, pB, pA);
+    step(std::true_type{}, Even{}, 0, sA, sB, pB, pA);
     int j = 1;
     for (; j + 1 < n_tiles; j += 2) {
-      step(std::false_type{}, j, sB, sA, pA, pB);
-      step(std::false_type{}, j + 1, sA, sB, pB, pA);
+      step(std::false_type{}, Odd{}, j, sB, sA, pA, pB);
+      step(std::false_type{}, Even{}, j + 1, sA, sB, pB, pA);
     }
     if (j < n_tiles) {
-      step(std::false_type{}, j, sB, sA, pA, pB);
-      gemm2(j, pB);
+      step(std::false_type{}, Odd{}, j, sB, sA, pA, pB);
+      gemm2(j, Odd{}, pB);
     } else {
-      gemm2(j - 1, pA);
+      gemm2(j - 1, Even{}, pA);
     }
   }
 
