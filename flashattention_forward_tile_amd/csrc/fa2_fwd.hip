@@ -91,9 +91,16 @@ __device__ __forceinline__ int v_swizzle(int row, int chunk) {
     return chunk ^ (((row >> 1) & 1) << 2);
 }
 
-// v_waitcnt with only vmcnt(0): every buffer load of this wave, including
+// s_waitcnt with only vmcnt(0): every buffer load of this wave, including
 // the ones that write LDS directly, has landed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt vmcnt(N): all but this wave's N most recent buffer loads have
+// landed (loads complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmem_but() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
 
 typedef __attribute__((address_space(3))) char lds_char;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -136,13 +143,25 @@ __device__ __forceinline__ void load_lds16(i32x4 rsrc, uint32_t voff, uint32_t l
 
 // Tile shape per head dimension: key rows per tile (BC), waves per workgroup
 // (NW), 32-query blocks per wave (QB), the waves per SIMD the register
-// budget is sized for (OCC), and whether the iteration block carries explicit
-// MFMA / LDS / VALU interleave hints (SGB).  Each K or V operand read from LDS feeds QB
+// budget is sized for (OCC), whether the iteration block carries explicit
+// MFMA / LDS / VALU interleave hints (SGB), the LDS slots per K and V ring
+// (RING), and how many K and V operands of each product are read from LDS one
+// iteration early (PK, PV).  Each K or V operand read from LDS feeds QB
 // matrix instructions, so LDS bytes per FLOP fall as 1/QB.
+//
+// K and V tiles cycle through rings of RING LDS slots: tile t sits in slot
+// t % RING and K_t is loaded during iteration t - RING.  With RING = 4, V_t
+// is loaded during iteration t - 2 and each iteration waits only for the
+// loads of the one before it, so every load has two iterations to land and
+// the operands an iteration reads were published one barrier early (which
+// is what lets PK, PV > 0).  With RING = 2 (double buffering), V_t is loaded
+// during iteration t and each iteration waits for its own loads.
 template <int D> struct Cfg;
-template <> struct Cfg<64> { static constexpr int BC = 64, NW = 4, QB = 1, OCC = 2, SGB = 1; };
-template <> struct Cfg<128> { static constexpr int BC = 32, NW = 8, QB = 1, OCC = 2, SGB = 1; };
-template <> struct Cfg<256> { static constexpr int BC = 32, NW = 4, QB = 1, OCC = 1, SGB = 0; };
+template <> struct Cfg<64> { static constexpr int BC = 64, NW = 4, QB = 1, OCC = 2, SGB = 1, RING = 4, PK = 4, PV = 2; };
+template <> struct Cfg<128> { static constexpr int BC = 32, NW = 8, QB = 1, OCC = 2, SGB = 0, RING = 4, PK = 4, PV = 2; };
+template <> struct Cfg<256> { static constexpr int BC = 32, NW = 4, QB = 1, OCC = 1, SGB = 0, RING = 2, PK = 0, PV = 0; };
+// Ring slots and loop phases as compile-time constants.
+template <int X> using Ic = std::integral_constant<int, X>;
 
 // p = exp2(t - m_ref) is summed over each lane's keys of a tile; while that
 // sum stays at or below kSumLimit no p exceeds it, and the reference max is
@@ -196,9 +215,16 @@ fa2_fwd_kernel(const Problem P) {
   using X2 = typename Vec<FP16>::x2;
   using E = typename Vec<FP16>::e;
 
-  // LDS: K tiles [2][BC][D] at 0, V tiles [2][BC][D] at 2*TBYTES; row-major,
-  // swizzled.  Tile j of K and of V lives in buffer j & 1.
-  __shared__ __attribute__((aligned(16))) char smem[4 * TBYTES];
+  constexpr int PK = Cfg<D>::PK;      // K operands read one iteration early
+  constexpr int PV = Cfg<D>::PV;      // V operands read one iteration early
+  constexpr int KO = KS * KB;         // K operands (A of the first product) per tile
+  constexpr int VO = ST * DB;         // V operands (A of the second product) per tile
+  constexpr int RING = Cfg<D>::RING;
+  static_assert(RING == 2 || RING == 4, "ring of 2 or 4 slots");
+  static_assert(PK <= KO && PV <= VO && (RING == 4 || PK + PV == 0), "prefetch depth");
+  // LDS: the K ring [RING][BC][D] at 0, the V ring at RING*TBYTES; tiles
+  // row-major, swizzled.
+  __shared__ __attribute__((aligned(16))) char smem[2 * RING * TBYTES];
   lds_char* const lds = (lds_char*)smem;
 
   const int tid = threadIdx.x;
@@ -252,23 +278,25 @@ fa2_fwd_kernel(const Problem P) {
     k_src[i] = (uint32_t)(row * RB + k_swizzle<CPR>(row, pc) * 16);
     v_src[i] = (uint32_t)(row * RB + v_swizzle<CPR>(row, pc) * 16);
   }
-  // `buf` (an integral constant) is j & 1, known at compile time in the
-  // unrolled loop, so LDS buffer offsets fold into instruction immediates.
-  // d = 256 keeps the offset in a register: with immediates its schedule
-  // hoists more loads and spills.
+  // `s` (an integral constant) is t modulo 4, known at compile time in the
+  // loop (unrolled by 4), so the ring slot t % RING and its LDS offsets fold
+  // into instruction immediates.  d = 256 keeps the slot in a register: with
+  // immediates its schedule hoists more loads and spills.
   constexpr bool kImmBuf = D != 256;
-  auto buffer = [](int j, auto buf) { return kImmBuf ? decltype(buf)::value : (j & 1); };
-  auto issue_k = [&](int j, auto buf) {
-    const uint32_t dst = lds_base + buffer(j, buf) * TBYTES + wave * 1024;
+  auto slot = [](int t, auto s) { return kImmBuf ? decltype(s)::value % RING : (t & (RING - 1)); };
+  // Tiles past the last one read as zeros (buffer range check) and are never
+  // used; loading them keeps the per-iteration load count fixed.
+  auto issue_k = [&](int t, auto s) {
+    const uint32_t dst = lds_base + slot(t, s) * TBYTES + wave * 1024;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i)
-      load_lds16(k_rs, (uint32_t)j * TBYTES + k_src[i], dst + i * NW * 1024);
+      load_lds16(k_rs, (uint32_t)t * TBYTES + k_src[i], dst + i * NW * 1024);
   };
-  auto issue_v = [&](int j, auto buf) {
-    const uint32_t dst = lds_base + 2 * TBYTES + buffer(j, buf) * TBYTES + wave * 1024;
+  auto issue_v = [&](int t, auto s) {
+    const uint32_t dst = lds_base + (RING + slot(t, s)) * TBYTES + wave * 1024;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i)
-      load_lds16(v_rs, (uint32_t)j * TBYTES + v_src[i], dst + i * NW * 1024);
+      load_lds16(v_rs, (uint32_t)t * TBYTES + v_src[i], dst + i * NW * 1024);
   };
 
   // Per-lane LDS byte offsets of the MFMA operands within a tile.  The
@@ -294,8 +322,7 @@ fa2_fwd_kernel(const Problem P) {
 #pragma unroll
   for (int db = 0; db < VOFF; ++db) {
     const int col = db * 32 + tr_col;
-    v_off[db] = (uint32_t)(2 * TBYTES + tr_row * RB +
-                           v_swizzle<CPR>(tr_row, col >> 3) * 16 + (col & 7) * 2);
+    v_off[db] = (uint32_t)(tr_row * RB + v_swizzle<CPR>(tr_row, col >> 3) * 16 + (col & 7) * 2);
   }
 
   // Q_i fragments: the B operands of S^T = K_j Q_i^T, held for the whole
@@ -331,11 +358,37 @@ fa2_fwd_kernel(const Problem P) {
     l_part[b] = 0.0f;
   }
 
-  // S^T_j = K_j Q_i^T : [BC keys] x [32 queries] per wave.  With a zero
-  // scale every logit is 0 whatever Q and K hold, so S stays 0 and c is taken
-  // as 1 (x = s - m_ref keeps masked keys at -inf).
-  auto gemm1 = [&](int j, auto buf, f32x16 (&sd)[QB][KB]) {
-    const lds_char* kb = lds + buffer(j, buf) * TBYTES;
+  // First operands of the next products, read one iteration early.
+  X8 kpre[PK > 0 ? PK : 1], vpre[PV > 0 ? PV : 1];
+
+  // Operand o of the first product, o = ks*KB + kk: rows kk*32 .. +31 of
+  // K_t (k-step ks), as the A operand of S^T = K_t Q_i^T.
+  auto k_operand = [&](int t, auto s, int o) -> X8 {
+    const int ks = o / KB, kk = o % KB;
+    const lds_char* kb = lds + slot(t, s) * TBYTES;
+    return __builtin_bit_cast(
+        X8, *(const __attribute__((address_space(3))) u32x4*)(
+                kb + kk * 32 * RB + k_off[ks % KOFF] + (ks / KOFF) * 256));
+  };
+  // Operand o of the second product, o = st*DB + db: V_t^T for output rows
+  // db*32 .. +31 and keys st*16 .. +15 in the S^T accumulator's key order,
+  // from the row-major V tile through two transposing LDS reads of 4 keys.
+  auto v_operand = [&](int t, auto s, int o) -> X8 {
+    const int st = o / DB, db = o % DB;
+    const lds_char* vb = lds + (RING + slot(t, s)) * TBYTES;
+    const uint32_t vo = v_off[db % VOFF] + (db / VOFF) * 256;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)(vb + vo + (st * 16) * RB));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)(vb + vo + (st * 16 + 8) * RB));
+    return __builtin_bit_cast(X8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  // S^T_t = K_t Q_i^T : [BC keys] x [32 queries] per wave.  The first PK
+  // operands come from `pre` (read during the previous iteration), the rest
+  // from LDS.  With a zero scale every logit is 0 whatever Q and K hold, so S
+  // stays 0 and c is taken as 1 (x = s - m_ref keeps masked keys at -inf).
+  auto gemm1 = [&](int t, auto s, const X8 (&pre)[PK > 0 ? PK : 1], f32x16 (&sd)[QB][KB]) {
 #pragma unroll
     for (int b = 0; b < QB; ++b)
 #pragma unroll
@@ -344,40 +397,36 @@ fa2_fwd_kernel(const Problem P) {
         for (int i = 0; i < 16; ++i) sd[b][kk][i] = 0.0f;
     if constexpr (MODE == kZero) return;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+    for (int o = 0; o < KO; ++o) {
+      const X8 a = o < PK ? pre[o < PK ? o : 0] : k_operand(t, s, o);
 #pragma unroll
-      for (int kk = 0; kk < KB; ++kk) {
-        const X8 a = __builtin_bit_cast(
-            X8, *(const __attribute__((address_space(3))) u32x4*)(
-                    kb + kk * 32 * RB + k_off[ks % KOFF] + (ks / KOFF) * 256));
-#pragma unroll
-        for (int b = 0; b < QB; ++b) sd[b][kk] = mfma32x32x16<FP16>(a, qf[b][ks], sd[b][kk]);
-      }
+      for (int b = 0; b < QB; ++b)
+        sd[b][o % KB] = mfma32x32x16<FP16>(a, qf[b][o / KB], sd[b][o % KB]);
+    }
   };
 
-  // O^T += V_j^T P_j^T : [D] x [32 queries] per wave.  The A operand (V^T,
-  // 8 keys per lane in the S^T accumulator's key order) comes from the
-  // row-major V tile through two transposing LDS reads of 4 keys each.
-  auto gemm2 = [&](int j, auto buf, const X8 (&pf)[QB][ST]) {
-    const lds_char* vb = lds + buffer(j, buf) * TBYTES;
+  // O^T += V_t^T P_t^T : [D] x [32 queries] per wave; the first PV operands
+  // come from `pre`.
+  auto gemm2 = [&](int t, auto s, const X8 (&pre)[PV > 0 ? PV : 1], const X8 (&pf)[QB][ST]) {
 #pragma unroll
-    for (int st = 0; st < ST; ++st)
+    for (int o = 0; o < VO; ++o) {
+      const X8 a = o < PV ? pre[o < PV ? o : 0] : v_operand(t, s, o);
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const uint32_t vo = v_off[db % VOFF] + (db / VOFF) * 256;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4*)(vb + vo + (st * 16) * RB));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4*)(vb + vo + (st * 16 + 8) * RB));
-        const X8 a = __builtin_bit_cast(
-            X8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-        for (int b = 0; b < QB; ++b) acc[b][db] = mfma32x32x16<FP16>(a, pf[b][st], acc[b][db]);
-      }
+      for (int b = 0; b < QB; ++b) acc[b][o % DB] = mfma32x32x16<FP16>(a, pf[b][o / DB], acc[b][o % DB]);
+    }
   };
 
-  // p = exp2(s*c - m_ref): rounded pairs into pf, the unrounded sum returned.
-  // A masked key holds -inf (c > 0) or +inf (c < 0), so its p is 0.
+  // The first PK / PV operands of the next iteration's products.
+  auto prefetch_k = [&](int t, auto s, X8 (&pre)[PK > 0 ? PK : 1]) {
+    if constexpr (MODE == kZero) return;
+#pragma unroll
+    for (int o = 0; o < PK; ++o) pre[o] = k_operand(t, s, o);
+  };
+  auto prefetch_v = [&](int t, auto s, X8 (&pre)[PV > 0 ? PV : 1]) {
+#pragma unroll
+    for (int o = 0; o < PV; ++o) pre[o] = v_operand(t, s, o);
+  };
+
   auto probs = [&](const f32x16 (&sc)[KB], X8 (&pf)[ST], float m) -> float {
     // A causal row that has seen no key yet has m = -inf and only masked
     // logits; reference 0 gives them p = 0 rather than NaN.
@@ -405,18 +454,24 @@ fa2_fwd_kernel(const Problem P) {
 
   // One iteration j, as a single straight-line block for the scheduler:
   // S_{j+1} = K_{j+1} Q^T and O += P_{j-1} V_{j-1} on the matrix cores while
-  // the VALU turns S_j into P_j.  K runs two tiles ahead of the V the block
-  // consumes; the loads issued here are K_{j+2} and V_j.  Every buffer is
-  // refilled only after the barrier ending the iteration that last read it.
-  // The last iteration's S_{j+1} product reads whatever the idle K buffer
-  // holds and is dropped.
-  using Even = std::integral_constant<int, 0>;
-  using Odd = std::integral_constant<int, 1>;
-  auto step = [&](auto first, auto par, int j, f32x16 (&s_cur)[QB][KB], f32x16 (&s_nxt)[QB][KB],
+  // the VALU turns S_j into P_j.  The loads issued here are K_{j+RING} and
+  // V_{j+RING-2}; each goes to the ring slot whose previous tile (K_j,
+  // V_{j-2}) was last read before the barrier that ended iteration j-1.
+  // With RING = 4 the iteration then reads the first operands of iteration
+  // j+1 (K_{j+2}, V_j: loaded during iteration j-2 and published by the last
+  // barrier) and waits only for the loads issued during iteration j-1.  The
+  // last iteration's S_{j+1} product reads a tile past the end and is
+  // dropped.  `ph` is j % 4.
+  auto step = [&](auto first, auto ph, int j, f32x16 (&s_cur)[QB][KB], f32x16 (&s_nxt)[QB][KB],
                   const X8 (&p_prev)[QB][ST], X8 (&p_cur)[QB][ST]) {
-    using Other = std::integral_constant<int, 1 - decltype(par)::value>;
-    if (j + 2 < n_tiles) issue_k(j + 2, par);
-    issue_v(j, par);
+    constexpr int p = decltype(ph)::value;
+    using S0 = Ic<p>;
+    using S1 = Ic<(p + 1) % 4>;
+    using S2 = Ic<(p + 2) % 4>;
+    using S3 = Ic<(p + 3) % 4>;
+    // (RING = 2 skips loads past the end: at d = 256 that keeps it from spilling)
+    if (RING == 4 || j + RING < n_tiles) issue_k(j + RING, S0{});
+    issue_v(j + RING - 2, Ic<(p + RING - 2) % 4>{});
 
     // Mask keys past N and, with the causal option, keys past a row's
     // diagonal (key > row + causal_off).  Decided per wave: its rows are
@@ -437,8 +492,8 @@ fa2_fwd_kernel(const Problem P) {
       }
     }
 
-    gemm1(j + 1, Other{}, s_nxt);
-    if constexpr (!decltype(first)::value) gemm2(j - 1, Other{}, p_prev);
+    gemm1(j + 1, S1{}, kpre, s_nxt);
+    if constexpr (!decltype(first)::value) gemm2(j - 1, S3{}, vpre, p_prev);
     float rs[QB];
     bool over = false;
 #pragma unroll
@@ -449,7 +504,7 @@ fa2_fwd_kernel(const Problem P) {
       // path, which leaves their p at 0.
       if constexpr (CAUSAL) over |= m_ref[b] == -INFINITY;
     }
-    constexpr int MF = QB * ((MODE == kZero ? 0 : KS * KB) + (decltype(first)::value ? 0 : ST * DB));
+    constexpr int MF = QB * ((MODE == kZero ? 0 : KO) + (decltype(first)::value ? 0 : VO));
 #pragma unroll
     for (int t = 0; t < (Cfg<D>::SGB ? MF : 0); ++t) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
@@ -457,6 +512,11 @@ fa2_fwd_kernel(const Problem P) {
       __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
     }
+
+    // First operands of the next iteration: K_{j+2} and V_j, both published
+    // by the barrier that ended the previous iteration.
+    prefetch_k(j + 2, S2{}, kpre);
+    prefetch_v(j, S0{}, vpre);
 
     // While the unrounded sum of a lane's p stays at or below kSumLimit no p
     // exceeds it and the reference max stands.  Otherwise (always on the
@@ -493,16 +553,25 @@ fa2_fwd_kernel(const Problem P) {
 #pragma unroll
     for (int b = 0; b < QB; ++b) l_part[b] += rs[b];
 
-    wait_vmem();  // this wave's share of K_{j+2} and V_j has landed
+    // RING = 4: the loads issued during iteration j-1 have landed; RING = 2:
+    // this iteration's own.
+    wait_vmem_but<RING == 4 ? 2 * LOADS : 0>();
     __syncthreads();
   };
 
   if (n_tiles > 0) {
-    // Prologue: Q, K_0 and K_1 resident, S_0 computed.  Q and the tiles retire
+    // Prologue: Q, K_0 .. K_{RING-1} and V_0 .. V_{RING-3} resident, S_0
+    // computed, the first operands of K_1 in registers.  Everything retires
     // before the loop: vmcnt is a counter, so a load still in flight at the
-    // loop head would make every iteration wait on its own prefetch.
-    issue_k(0, Even{});
-    if (n_tiles > 1) issue_k(1, Odd{});
+    // loop head would make every iteration wait on it.
+    issue_k(0, Ic<0>{});
+    issue_k(1, Ic<1>{});
+    if constexpr (RING == 4) {
+      issue_k(2, Ic<2>{});
+      issue_k(3, Ic<3>{});
+      issue_v(0, Ic<0>{});
+      issue_v(1, Ic<1>{});
+    }
 #pragma unroll
     for (int b = 0; b < QB; ++b)
 #pragma unroll
@@ -512,22 +581,50 @@ fa2_fwd_kernel(const Problem P) {
 
     f32x16 sA[QB][KB], sB[QB][KB];
     X8 pA[QB][ST], pB[QB][ST];
-    gemm1(0, Even{}, sA);
-    __syncthreads();  // every wave is done with K_0 before K_2 may overwrite it
+    prefetch_k(0, Ic<0>{}, kpre);
+    gemm1(0, Ic<0>{}, kpre, sA);
+    prefetch_k(1, Ic<1>{}, kpre);
+    __syncthreads();  // every wave is done with K_0 before K_RING may overwrite it
 
-    // Iterations run in pairs so the S and P register sets swap roles without
-    // copies: even j computes (S_j in sA, S_{j+1} into sB, P_j into pA).
-    step(std::true_type{}, Even{}, 0, sA, sB, pB, pA);
+    // Iterations run in groups of 4 so ring slots and the S / P register
+    // sets (even j: S_j in sA, S_{j+1} into sB, P_j into pA) are compile-time.
+    step(std::true_type{}, Ic<0>{}, 0, sA, sB, pB, pA);
     int j = 1;
-    for (; j + 1 < n_tiles; j += 2) {
-      step(std::false_type{}, Odd{}, j, sB, sA, pA, pB);
-      step(std::false_type{}, Even{}, j + 1, sA, sB, pB, pA);
-    }
-    if (j < n_tiles) {
-      step(std::false_type{}, Odd{}, j, sB, sA, pA, pB);
-      gemm2(j, Odd{}, pB);
+    if constexpr (RING == 2) {  // pairs suffice; a longer body spills at d = 256
+      for (; j + 1 < n_tiles; j += 2) {
+        step(std::false_type{}, Ic<1>{}, j, sB, sA, pA, pB);
+        step(std::false_type{}, Ic<2>{}, j + 1, sA, sB, pB, pA);
+      }
+      if (j < n_tiles) {
+        step(std::false_type{}, Ic<1>{}, j, sB, sA, pA, pB);
+        gemm2(j, Ic<1>{}, vpre, pB);
+      } else {
+        gemm2(j - 1, Ic<0>{}, vpre, pA);
+      }
     } else {
-      gemm2(j - 1, Even{}, pA);
+      for (; j + 3 < n_tiles; j += 4) {
+        step(std::false_type{}, Ic<1>{}, j, sB, sA, pA, pB);
+        step(std::false_type{}, Ic<2>{}, j + 1, sA, sB, pB, pA);
+        step(std::false_type{}, Ic<3>{}, j + 2, sB, sA, pA, pB);
+        step(std::false_type{}, Ic<0>{}, j + 3, sA, sB, pB, pA);
+      }
+      // Up to three iterations left (j % 4 == 1), then O += P_{n-1} V_{n-1}.
+      if (j < n_tiles) {
+        step(std::false_type{}, Ic<1>{}, j, sB, sA, pA, pB);
+        if (j + 1 < n_tiles) {
+          step(std::false_type{}, Ic<2>{}, j + 1, sA, sB, pB, pA);
+          if (j + 2 < n_tiles) {
+            step(std::false_type{}, Ic<3>{}, j + 2, sB, sA, pA, pB);
+            gemm2(j + 2, Ic<3>{}, vpre, pB);
+          } else {
+            gemm2(j + 1, Ic<2>{}, vpre, pA);
+          }
+        } else {
+          gemm2(j, Ic<1>{}, vpre, pB);
+        }
+      } else {
+        gemm2(j - 1, Ic<0>{}, vpre, pA);
+      }
     }
   }
 
