@@ -172,18 +172,22 @@ constexpr float kSumLimit = 256.0f;
 // logits is a max for c > 0 and a min for c < 0; c == 0 is uniform attention.
 enum ScaleMode { kPositive = 0, kNegative = 1, kZero = 2 };
 
-// Kernel arguments.  q, o: [B][hq][nq][D]; k, v: [B][hq/group][nk][D];
-// lse: [B][hq][nq].  Query head h reads key/value head h / group.  With the
-// causal option row i sees keys j <= i + causal_off (causal_off = nk - nq).
+// Kernel arguments.  q, o: [B][hq][nq][D]; k, v: [B][hkv][nk][D]; lse:
+// [B][hq][nq].  Query head h reads key/value head h / (hq / hkv).  The query
+// heads of one K/V head are adjacent, so their rows form one block of
+// rows = (hq / hkv) * nq rows in q, o and lse; workgroups tile that block
+// (query-head packing), and packed row r is row r % nq of its head.  With
+// the causal option row i of a head sees keys j <= i + causal_off
+// (causal_off = nk - nq).
 struct Problem {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
   uint16_t* o;
   float* lse;
-  int nq, nk;        // query and key rows per head
-  int hq, group;     // query heads per batch entry, query heads per K/V head
-  int q_tiles;       // query tiles per head
+  int nq, nk;        // query rows per query head, key rows per K/V head
+  int rows;          // query rows per K/V head (its query heads back to back)
+  int q_tiles;       // query tiles per K/V head
   int n_groups;      // workgroups in the grid
   int causal_off;
   float c;           // scale * log2(e) (1 when the scale is 0)
@@ -233,11 +237,11 @@ fa2_fwd_kernel(const Problem P) {
   const int half = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // All query tiles of one head go to one XCD (dispatch is round-robin over
-  // the 8 XCDs): the k-th workgroup on XCD x takes logical tile x*G/8 + k.
-  // Query heads sharing a K/V head are adjacent, so they share it too.  With
-  // the causal mask the later (longer) query tiles start first.
-  int bh, qt;  // bh = b * hq + h
+  // All query tiles of one K/V head go to one XCD (dispatch is round-robin
+  // over the 8 XCDs): the k-th workgroup on XCD x takes logical tile
+  // x*G/8 + k.  With the causal mask the later (longer) query tiles start
+  // first.
+  int bh, qt;  // bh = b * hkv + (K/V head)
   const int id = blockIdx.x;
   const int per_xcd = P.n_groups >> 3;
   if ((P.n_groups & 7) == 0) {
@@ -258,10 +262,9 @@ fa2_fwd_kernel(const Problem P) {
     qt = id - bh * P.q_tiles;
     if constexpr (CAUSAL) qt = P.q_tiles - 1 - qt;
   }
-  const int kvh = (bh / P.hq) * (P.hq / P.group) + (bh % P.hq) / P.group;
-  const int64_t q_head = (int64_t)bh * P.nq * D;
-  const int64_t kv_head = (int64_t)kvh * N * D;
-  const __amdgpu_buffer_rsrc_t q_rs = make_rsrc(P.q + q_head, (uint32_t)P.nq * D * 2);
+  const int64_t q_head = (int64_t)bh * P.rows * D;  // the group's first query row
+  const int64_t kv_head = (int64_t)bh * N * D;
+  const __amdgpu_buffer_rsrc_t q_rs = make_rsrc(P.q + q_head, (uint32_t)P.rows * D * 2);
   const i32x4 k_rs = make_rsrc_words(P.k + kv_head, (uint32_t)N * D * 2);
   const i32x4 v_rs = make_rsrc_words(P.v + kv_head, (uint32_t)N * D * 2);
   const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
@@ -326,15 +329,29 @@ fa2_fwd_kernel(const Problem P) {
   }
 
   // Q_i fragments: the B operands of S^T = K_j Q_i^T, held for the whole
-  // loop.  Query block b of this wave is rows q0 + 32*b + l32.
+  // loop.  Query block b of this wave is packed rows q0 + 32*b + l32.
   const int q0 = qt * BR + wave * 32 * QB;
 
+  // Causal limits: a lane's last visible key (its row within its head plus
+  // causal_off), and the smallest such row among the wave's rows (packed rows
+  // wrap to 0 at a head boundary).
+  int row_lim[QB];
+  int wave_row_min = 0;
+  if constexpr (CAUSAL) {
+#pragma unroll
+    for (int b = 0; b < QB; ++b) row_lim[b] = (q0 + 32 * b + l32) % P.nq + P.causal_off;
+    const int r0 = q0 % P.nq;
+    wave_row_min = r0 + 32 * QB - 1 < P.nq ? r0 : 0;
+  }
+
   // Key tiles this workgroup needs: all of them, or with the causal mask those
-  // up to the last key its last row sees.  A workgroup whose rows see no key
-  // writes O = 0 and lse = -inf.
+  // up to the last key its rows see.  A workgroup whose rows see no key writes
+  // O = 0 and lse = -inf.
   int n_tiles = (N + BC - 1) / BC;
   if constexpr (CAUSAL) {
-    const int last_key = qt * BR + BR - 1 + P.causal_off;  // may be < 0
+    const int first = qt * BR, last = min(P.rows, first + BR) - 1;
+    const int row_max = first / P.nq != last / P.nq ? P.nq - 1 : last % P.nq;
+    const int last_key = row_max + P.causal_off;  // may be < 0
     n_tiles = last_key < 0 ? 0 : min(n_tiles, last_key / BC + 1);
   }
   X8 qf[QB][KS];
@@ -474,15 +491,15 @@ fa2_fwd_kernel(const Problem P) {
     issue_v(j + RING - 2, Ic<(p + RING - 2) % 4>{});
 
     // Mask keys past N and, with the causal option, keys past a row's
-    // diagonal (key > row + causal_off).  Decided per wave: its rows are
-    // q0 .. q0 + 32*QB - 1.
+    // diagonal (key > row + causal_off).  Decided per wave, from its
+    // smallest row within a head.
     const int key0 = j * BC;
     bool masked = key0 + BC > N;
-    if constexpr (CAUSAL) masked |= key0 + BC - 1 > q0 + P.causal_off;
+    if constexpr (CAUSAL) masked |= key0 + BC - 1 > wave_row_min + P.causal_off;
     if (masked) {
 #pragma unroll
       for (int b = 0; b < QB; ++b) {
-        const int lim = CAUSAL ? min(N - 1, q0 + 32 * b + l32 + P.causal_off) : N - 1;
+        const int lim = CAUSAL ? min(N - 1, row_lim[b]) : N - 1;
 #pragma unroll
         for (int kk = 0; kk < KB; ++kk)
 #pragma unroll
@@ -635,7 +652,7 @@ fa2_fwd_kernel(const Problem P) {
     const int qrow = q0 + 32 * b + l32;
     const float l_tot = l_part[b] + __shfl_xor(l_part[b], 32);
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    if (qrow < P.nq) {
+    if (qrow < P.rows) {
       uint16_t* orow = P.o + q_head + (int64_t)qrow * D;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -647,7 +664,7 @@ fa2_fwd_kernel(const Problem P) {
           *(u32x2*)(orow + db * 32 + g4 * 8 + half * 4) = __builtin_bit_cast(u32x2, ov);
         }
       if (half == 0)
-        P.lse[(int64_t)bh * P.nq + qrow] =
+        P.lse[(int64_t)bh * P.rows + qrow] =
             l_tot > 0.0f ? (m_ref[b] + __log2f(l_tot)) * kLn2 : -INFINITY;
     }
   }
@@ -718,18 +735,21 @@ int fa2_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse
   if (!__builtin_isfinite(scale)) return FA2_ERR_SCALE;
   if (B == 0 || Hq == 0 || Nq == 0) return FA2_OK;  // no output rows
   if (Hkv == 0 || Hq % Hkv != 0) return FA2_ERR_SHAPE;
-  // One head's rows are addressed with 32-bit offsets (plus slack for the
-  // prefetch of tiles past the end); the workgroup count fits a 1-D grid.
+  // The query rows of one K/V head's group (group * Nq) and the key rows of
+  // one K/V head are addressed with 32-bit offsets (plus slack for the loads
+  // of tiles past the end); the workgroup count fits a 1-D grid.
   const int64_t lim = ((int64_t)1 << 31) - ((int64_t)1 << 20);
-  if (Nq > (int64_t)1 << 30 || Nk > (int64_t)1 << 30 || Nq * d > lim || Nk * d > lim)
-    return FA2_ERR_SHAPE;
+  if (Nq > (int64_t)1 << 30 || Nk > (int64_t)1 << 30 || Nk * d > lim) return FA2_ERR_SHAPE;
+  const int64_t group = Hq / Hkv;
+  if (group > lim / (Nq * d)) return FA2_ERR_SHAPE;
+  const int64_t rows = group * Nq;  // query rows per K/V head
   int bq = 0, bk = 0, nw = 0;
   fa2_tile_config(d, dtype, &bq, &bk, &nw);
-  const int64_t q_tiles = (Nq + bq - 1) / bq;
+  const int64_t q_tiles = (rows + bq - 1) / bq;
   if (B > (((int64_t)1 << 31) - 1) / Hq) return FA2_ERR_SHAPE;
   const int64_t bh = B * Hq;
-  if (bh > (((int64_t)1 << 31) - 1) / q_tiles) return FA2_ERR_SHAPE;
-  const int64_t groups = bh * q_tiles;
+  if (B * Hkv > (((int64_t)1 << 31) - 1) / q_tiles) return FA2_ERR_SHAPE;
+  const int64_t groups = B * Hkv * q_tiles;
   if (!q || !o || !lse || (Nk > 0 && (!k || !v))) return FA2_ERR_NULL;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return FA2_ERR_ALIGN;
   if ((uintptr_t)lse & 3) return FA2_ERR_ALIGN;
@@ -754,8 +774,7 @@ int fa2_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse
   P.lse = lse;
   P.nq = (int)Nq;
   P.nk = (int)Nk;
-  P.hq = (int)Hq;
-  P.group = (int)(Hq / Hkv);
+  P.rows = (int)rows;
   P.q_tiles = (int)q_tiles;
   P.n_groups = (int)groups;
   P.causal_off = (int)(Nk - Nq);

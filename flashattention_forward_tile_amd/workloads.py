@@ -110,6 +110,9 @@ WORKLOADS = {
     "causal": Workload("causal", 4, 16, 4096, 128, "bf16", causal=True),
     "gqa": Workload("gqa", 4, 16, 4096, 128, "bf16", Hkv=2),
     "kv_cache": Workload("kv_cache", 4, 16, 1024, 128, "bf16", Hkv=4, Nk=8192, causal=True),
+    # a 64-row prefill chunk against a 4096-key cache, 4 query heads per K/V
+    # head: the rows of a K/V head's query heads share workgroups
+    "gqa_chunk": Workload("gqa_chunk", 16, 32, 64, 128, "bf16", Hkv=8, Nk=4096, causal=True),
 }
 
 

@@ -43,7 +43,9 @@ enum fa2_status {
   FA2_OK = 0,
   FA2_ERR_NULL = -1,    /* a required pointer is NULL */
   FA2_ERR_SHAPE = -2,   /* a size is negative, Hq is not a multiple of Hkv,
-                           or sizes overflow the grid or per-head offsets */
+                           the grid overflows, or the query rows of one K/V
+                           head ((Hq/Hkv)*Nq*d) or its key rows (Nk*d) exceed
+                           2^31 - 2^20 elements */
   FA2_ERR_HEADDIM = -3, /* d is not 64, 128 or 256 */
   FA2_ERR_DTYPE = -4,   /* dtype is not an fa2_dtype */
   FA2_ERR_ALIGN = -5,   /* q, k, v or o not 16-byte aligned, lse not 4-byte */
@@ -94,7 +96,9 @@ int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * Specification" section of the Ampere Part 1 page leaves out: causal
  * masking, unequal query and key lengths (cross-attention, a key/value
  * cache), and grouped key/value heads (MQA/GQA, the setting of the Colfax
- * "FlashAttention-3 for Inference" post).
+ * "FlashAttention-3 for Inference" post).  The query heads that share a key/value
+ * head are processed together: their rows are tiled as one block, so short
+ * query blocks (a prefill chunk, a few decode rows) still fill the tiles.
  *
  *   q, o     : [B][Hq][Nq][d] contiguous, element type `dtype`.
  *   k, v     : [B][Hkv][Nk][d] contiguous; query head h reads key/value head

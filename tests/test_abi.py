@@ -116,6 +116,8 @@ def call_ext(q=A, k=A + 0x1000000, v=A + 0x2000000, o=A + 0x3000000,
     (dict(Hkv=3), fa2.ERR_SHAPE), (dict(Hkv=0), fa2.ERR_SHAPE), (dict(Hkv=-1), fa2.ERR_SHAPE),
     (dict(Nk=-1), fa2.ERR_SHAPE), (dict(Nq=-1), fa2.ERR_SHAPE),
     (dict(Nk=1 << 31), fa2.ERR_SHAPE), (dict(q=0), fa2.ERR_NULL), (dict(k=0), fa2.ERR_NULL),
+    # each query head fits 32-bit offsets, but a K/V head's 64 query heads do not
+    (dict(Hq=64, Hkv=1, Nq=1 << 18, d=128), fa2.ERR_SHAPE),
     (dict(d=32), fa2.ERR_HEADDIM), (dict(k=A + 0x1000004), fa2.ERR_ALIGN),
     (dict(o=A + 0x2000000 + 512), fa2.ERR_ALIAS), (dict(scale=float("nan")), fa2.ERR_SCALE),
 ])

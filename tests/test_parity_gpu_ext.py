@@ -129,7 +129,34 @@ def test_grouped_heads_equal_repeated_heads():
         assert torch.equal(og, orr) and torch.equal(lg, lr)
 
 
-@pytest.mark.parametrize("name", ["gqa", "kv_cache"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Hq,Hkv,Nq,Nk", [(32, 4, 1, 1000), (32, 4, 5, 300), (16, 2, 64, 4100),
+                                          (8, 8, 3, 513), (12, 3, 100, 90), (32, 1, 17, 2048)])
+def test_packed_query_heads(Hq, Hkv, Nq, Nk, causal):
+    """Short query blocks: the rows of a K/V head's query heads are tiled
+    together, so one workgroup mixes heads (and, causal, rows at different
+    diagonal offsets; Nq > Nk leaves rows that see no key)."""
+    announce("packed", Hq, Hkv, Nq, Nk, causal)
+    q, k, v = inputs(2, Hq, Hkv, Nq, Nk, 128, "bf16", seed=Hq + Nq + Nk)
+    check(q, k, v, "bf16", 1.0 / math.sqrt(128), causal,
+          "packed Hq=%d Hkv=%d Nq=%d Nk=%d causal=%d" % (Hq, Hkv, Nq, Nk, causal))
+
+
+@pytest.mark.parametrize("Nq,Nk", [(37, 700), (300, 200), (1, 64)])
+def test_packed_heads_equal_repeated_heads(Nq, Nk):
+    """Packed rows get bit for bit the result they get in their own head's
+    tiles (repeated K/V heads, one query head per K/V head)."""
+    announce("packed repeat", Nq, Nk)
+    q, k, v = inputs(2, 16, 2, Nq, Nk, 64, "fp16", seed=Nq + 3 * Nk)
+    for causal in (False, True):
+        og, lg = run_gpu(q, k, v, 0.2, causal)
+        kr = k.repeat_interleave(8, dim=1).contiguous()
+        vr = v.repeat_interleave(8, dim=1).contiguous()
+        orr, lr = run_gpu(q, kr, vr, 0.2, causal)
+        assert torch.equal(og, orr) and torch.equal(lg, lr), causal
+
+
+@pytest.mark.parametrize("name", ["gqa", "kv_cache", "gqa_chunk"])
 def test_widened_workloads_sampled(name):
     """The grouped-head and KV-cache workloads bench.py times, sampled rows."""
     from flashattention_forward_tile_amd.workloads import WORKLOADS, workload_inputs
