@@ -139,6 +139,26 @@ def make_inputs(B, H, N, d, dtype="bf16", dist="normal", seed=0, Hkv=None, Nk=No
     return q.to(t), k.to(t), v.to(t)
 
 
+def make_inputs_kv_int8(B, Hq, Hkv, Nq, Nk, d, dtype="bf16", seed=0):
+    """Seeded CPU inputs for attention over an INT8 key/value cache: q
+    [B, Hq, Nq, d] in the 16-bit dtype (standard normal), kq and vq
+    [B, Hkv, Nk, d] int8 codes (a standard normal times 127/4.5, rounded and
+    clipped to [-127, 127], the shape of a per-channel symmetric cache of
+    normal data), and ks, vs [B, Hkv, d] float32 per-channel scales
+    (4.5/127 times a factor drawn uniformly from [0.5, 1.5))."""
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn((B, Hq, Nq, d), generator=g, dtype=torch.float32)
+    codes = []
+    for _ in range(2):
+        c = torch.randn((B, Hkv, Nk, d), generator=g, dtype=torch.float32) * (127.0 / 4.5)
+        codes.append(c.round().clamp(-127, 127).to(torch.int8))
+    scales = []
+    for _ in range(2):
+        u = torch.rand((B, Hkv, d), generator=g, dtype=torch.float32)
+        scales.append(((u + 0.5) * (4.5 / 127.0)).to(torch.float32))
+    return q.to(_TORCH_DTYPES[dtype]), codes[0], scales[0], codes[1], scales[1]
+
+
 def workload_inputs(w: Workload, seed=0):
     return make_inputs(w.B, w.H, w.N, w.d, w.dtype, w.dist, seed, w.kv_heads, w.keys)
 

@@ -17,6 +17,11 @@ causal masking (row i sees keys j <= i + Nk - Nq), unequal query/key lengths,
 and grouped key/value heads.  Inputs
 are passed as raw 16-bit patterns (numpy ``uint16``) with a dtype tag, so the
 oracle sees bit for bit what the GPU sees.
+
+``attention_kv_int8`` computes the same over an INT8 key/value cache (int8
+codes with fp32 per-channel scales; the query rows quantized to int8 after the
+key scales are folded in, every quantization step in binary32 as spelled out in
+``attn_ref.c``), and ``quantize_q`` exposes that query quantization alone.
 """
 import ctypes
 import os
@@ -58,6 +63,17 @@ class Oracle:
             ctypes.c_int64, ctypes.c_int64, ctypes.c_double, ctypes.c_int,
             i64p, ctypes.c_int64, f64p, f64p, ctypes.c_int]
         lib.oracle_attn_general.restype = ctypes.c_int
+        i8p = ctypes.POINTER(ctypes.c_int8)
+        f32p = ctypes.POINTER(ctypes.c_float)
+        lib.oracle_attn_kv_int8.argtypes = [
+            u16p, ctypes.c_int, i8p, f32p, i8p, f32p,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_double, ctypes.c_int,
+            i64p, ctypes.c_int64, f64p, f64p, ctypes.c_int]
+        lib.oracle_attn_kv_int8.restype = ctypes.c_int
+        lib.oracle_quantize_q.argtypes = [u16p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                          f32p, i8p, f32p]
+        lib.oracle_quantize_q.restype = ctypes.c_int
         lib.oracle_decode.argtypes = [u16p, ctypes.c_int64, ctypes.c_int, f64p]
         lib.oracle_decode.restype = ctypes.c_int
         lib.oracle_host_threads.argtypes = []
@@ -101,10 +117,80 @@ class Oracle:
         B, Hq, Nq, d = q.shape
         if k.shape[0] != B or k.shape[3] != d or k.shape[1] < 1 or Hq % k.shape[1]:
             raise ValueError("k/v batch and head dim must match q, Hq a multiple of Hkv")
+        Hkv, Nk = k.shape[1], k.shape[2]
+
+        def run(rp, nr, o, lse):
+            return self.lib.oracle_attn_general(
+                _ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16),
+                _ptr(v, ctypes.c_uint16), _DTYPES[dtype], B, Hq, Hkv, Nq, Nk, d,
+                float(scale), 1 if causal else 0, rp, nr, _ptr(o, ctypes.c_double),
+                _ptr(lse, ctypes.c_double), int(nthreads))
+        return self._rows_call(q.shape, rows, run, "oracle_attn_general")
+
+    def attention_kv_int8(self, q_bits, kq, ks, vq, vs, dtype, scale, rows=None,
+                          nthreads=0, causal=False):
+        """fp64 attention over an INT8 key/value cache.
+
+        q_bits: uint16 [B, Hq, Nq, d] (16-bit patterns of `dtype`); kq, vq:
+        int8 [B, Hkv, Nk, d] codes; ks, vs: float32 [B, Hkv, d] per-channel
+        scales (k = ks * kq, v = vs * vq).  Each query row is quantized to int8
+        after the key scales are folded in (see the module docstring); the
+        other arguments and the result are those of `attention`.
+        """
+        q = np.ascontiguousarray(q_bits, dtype=np.uint16)
+        kq = np.ascontiguousarray(kq, dtype=np.int8)
+        vq = np.ascontiguousarray(vq, dtype=np.int8)
+        ks = np.ascontiguousarray(ks, dtype=np.float32)
+        vs = np.ascontiguousarray(vs, dtype=np.float32)
+        if q.ndim != 4 or kq.ndim != 4 or kq.shape != vq.shape:
+            raise ValueError("q must be [B, Hq, Nq, d], kq and vq one [B, Hkv, Nk, d] shape")
+        B, Hq, Nq, d = q.shape
+        Hkv, Nk = kq.shape[1], kq.shape[2]
+        if kq.shape[0] != B or kq.shape[3] != d or Hkv < 1 or Hq % Hkv:
+            raise ValueError("kq/vq batch and head dim must match q, Hq a multiple of Hkv")
+        if ks.shape != (B, Hkv, d) or vs.shape != (B, Hkv, d):
+            raise ValueError("ks and vs must be [B, Hkv, d]")
+
+        def run(rp, nr, o, lse):
+            return self.lib.oracle_attn_kv_int8(
+                _ptr(q, ctypes.c_uint16), _DTYPES[dtype], _ptr(kq, ctypes.c_int8),
+                _ptr(ks, ctypes.c_float), _ptr(vq, ctypes.c_int8), _ptr(vs, ctypes.c_float),
+                B, Hq, Hkv, Nq, Nk, d, float(scale), 1 if causal else 0, rp, nr,
+                _ptr(o, ctypes.c_double), _ptr(lse, ctypes.c_double), int(nthreads))
+        return self._rows_call(q.shape, rows, run, "oracle_attn_kv_int8")
+
+    def quantize_q(self, q_bits, ks, dtype):
+        """INT8 codes and row scales of query rows: q_bits uint16 [..., d]
+        (16-bit patterns), ks float32 [d] key scales.  Returns (codes int8
+        [..., d], sq float32 [...])."""
+        q = np.ascontiguousarray(q_bits, dtype=np.uint16)
+        ks = np.ascontiguousarray(ks, dtype=np.float32).ravel()
+        d = q.shape[-1]
+        if ks.size != d:
+            raise ValueError("ks must hold d scales")
+        n = q.size // d
+        codes = np.empty(q.shape, dtype=np.int8)
+        sq = np.empty(q.shape[:-1], dtype=np.float32)
+        rc = self.lib.oracle_quantize_q(_ptr(q, ctypes.c_uint16), _DTYPES[dtype], n, d,
+                                        _ptr(ks, ctypes.c_float), _ptr(codes, ctypes.c_int8),
+                                        _ptr(sq, ctypes.c_float))
+        if rc != 0:
+            raise ValueError("oracle_quantize_q failed (%d)" % rc)
+        return codes, sq
+
+    @staticmethod
+    def _rows_call(qshape, rows, run, name):
+        """Run `run(rows_ptr, nrows, o, lse)` over every row (O shaped [B, Hq,
+        Nq, d]) or over the given distinct flat row ids (O shaped [len, d], in
+        the caller's order)."""
+        B, Hq, Nq, d = qshape
         if rows is None:
             o = np.empty((B, Hq, Nq, d), dtype=np.float64)
             lse = np.empty((B, Hq, Nq), dtype=np.float64)
-            self._run(q, k, v, dtype, scale, causal, None, o, lse, nthreads)
+            if B and Hq and Nq:
+                rc = run(None, 0, o, lse)
+                if rc != 0:
+                    raise RuntimeError("%s failed (%d)" % (name, rc))
             return o, lse
         rows = np.asarray(rows, dtype=np.int64).ravel()
         order = np.argsort(rows, kind="stable")
@@ -113,27 +199,15 @@ class Oracle:
             raise ValueError("rows must not repeat")
         o_s = np.empty((srt.size, d), dtype=np.float64)
         lse_s = np.empty((srt.size,), dtype=np.float64)
-        self._run(q, k, v, dtype, scale, causal, srt, o_s, lse_s, nthreads)
+        if srt.size and B and Hq and Nq:
+            rc = run(_ptr(srt, ctypes.c_int64), srt.size, o_s, lse_s)
+            if rc != 0:
+                raise RuntimeError("%s failed (%d)" % (name, rc))
         o = np.empty_like(o_s)
         lse = np.empty_like(lse_s)
         o[order] = o_s
         lse[order] = lse_s
         return o, lse
-
-    def _run(self, q, k, v, dtype, scale, causal, rows, o, lse, nthreads):
-        B, Hq, Nq, d = q.shape
-        Hkv, Nk = k.shape[1], k.shape[2]
-        rp = None if rows is None else _ptr(rows, ctypes.c_int64)
-        nr = 0 if rows is None else rows.size
-        if Hq == 0 or B == 0 or Nq == 0:
-            return
-        rc = self.lib.oracle_attn_general(
-            _ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16),
-            _ptr(v, ctypes.c_uint16), _DTYPES[dtype], B, Hq, Hkv, Nq, Nk, d,
-            float(scale), 1 if causal else 0, rp, nr, _ptr(o, ctypes.c_double),
-            _ptr(lse, ctypes.c_double), int(nthreads))
-        if rc != 0:
-            raise RuntimeError("oracle_attn_general failed (%d)" % rc)
 
 
 _default = None
@@ -160,3 +234,15 @@ def attention(q_bits, k_bits, v_bits, dtype, scale, rows=None, nthreads=0,
     """See Oracle.attention."""
     return default().attention(q_bits, k_bits, v_bits, dtype, scale, rows,
                                nthreads, causal)
+
+
+def attention_kv_int8(q_bits, kq, ks, vq, vs, dtype, scale, rows=None, nthreads=0,
+                      causal=False):
+    """See Oracle.attention_kv_int8."""
+    return default().attention_kv_int8(q_bits, kq, ks, vq, vs, dtype, scale, rows,
+                                       nthreads, causal)
+
+
+def quantize_q(q_bits, ks, dtype):
+    """See Oracle.quantize_q."""
+    return default().quantize_q(q_bits, ks, dtype)

@@ -33,6 +33,23 @@
  * O is [rows][d] fp64 and lse is [rows] fp64, where rows are either all
  * B*Hq*Nq rows in order or the caller's sorted list of flat row ids
  * (b*Hq + h)*Nq + i.
+ *
+ * INT8 key/value cache.  The Colfax author page lists the post
+ * "FlashAttention-3 for Inference: INT8 Quantization and Query Head Packing
+ * for MQA/GQA" by title only, with a teaser about in-kernel pre-processing of
+ * tensors; the scheme below is this oracle's reading of that title, not a
+ * quotation.  Keys and values arrive as int8 codes with fp32 per-channel
+ * scales of their key/value head:
+ *     k[j][c] = ks[c] * kq[j][c],   v[j][c] = vs[c] * vq[j][c].
+ * Each query row is quantized to int8 after the key scales are folded into
+ * it, every step in IEEE binary32 (the function quantize_q_row below):
+ *     u[c]  = f32(q[c] * ks[c]),   amax = max_c |u[c]|,
+ *     qq[c] = amax > 0 ? clamp(rint(f32(u[c] * f32(127 / amax))), -127, 127) : 0
+ *             (rint rounds half to even),
+ *     sq    = f32(amax / 127).
+ * The logits are s_j = scale * sq * sum_c qq[c] * kq[j][c] (an exact integer
+ * dot product), and the softmax, O and lse follow the definition above with
+ * the dequantized v.
  */
 #define _GNU_SOURCE
 #include <math.h>
@@ -77,10 +94,60 @@ int oracle_decode(const uint16_t* bits, int64_t n, int dtype, double* out) {
   return 0;
 }
 
+/* The INT8 scheme's query quantization for one row (see the header): every
+ * operation in binary32, rounding half to even.  q holds the decoded 16-bit
+ * values (exact in binary32), ks the key scales of the row's key/value head;
+ * writes the codes to qq and returns sq. */
+static float quantize_q_row(const double* q, const float* ks, int64_t d, double* qq) {
+  float amax = 0.0f;
+  for (int64_t c = 0; c < d; ++c) {
+    const float u = (float)q[c] * ks[c];
+    if (fabsf(u) > amax) amax = fabsf(u);
+  }
+  if (!(amax > 0.0f)) {
+    for (int64_t c = 0; c < d; ++c) qq[c] = 0.0;
+    return 0.0f;
+  }
+  const float inv = 127.0f / amax;
+  for (int64_t c = 0; c < d; ++c) {
+    const float u = (float)q[c] * ks[c];
+    float code = rintf(u * inv);
+    if (code > 127.0f) code = 127.0f;
+    if (code < -127.0f) code = -127.0f;
+    qq[c] = (double)code;
+  }
+  return amax / 127.0f;
+}
+
+/* Quantized codes and row scales of n query rows (16-bit patterns, d each),
+ * all against the same key scales ks[d].  Returns 0, or -1 on a bad
+ * argument. */
+int oracle_quantize_q(const uint16_t* q, int dtype, int64_t n, int64_t d, const float* ks,
+                      int8_t* qq, float* sq) {
+  if ((dtype != ORACLE_BF16 && dtype != ORACLE_FP16) || n < 0 || d <= 0) return -1;
+  double* row = (double*)malloc(sizeof(double) * (size_t)d);
+  double* codes = (double*)malloc(sizeof(double) * (size_t)d);
+  if (!row || !codes) {
+    free(row);
+    free(codes);
+    return -1;
+  }
+  for (int64_t i = 0; i < n; ++i) {
+    for (int64_t c = 0; c < d; ++c) row[c] = decode(q[i * d + c], dtype);
+    sq[i] = quantize_q_row(row, ks, d, codes);
+    for (int64_t c = 0; c < d; ++c) qq[i * d + c] = (int8_t)codes[c];
+  }
+  free(row);
+  free(codes);
+  return 0;
+}
+
 /* ------------------------------------------------------------------------ */
 
 typedef struct {
   const uint16_t *q, *k, *v;
+  const int8_t *kq, *vq;   /* INT8 cache codes (k, v unused then) */
+  const float *ks, *vs;    /* their per-channel scales, [B][Hkv][d] */
   int dtype;
   int64_t B, Hq, Hkv, Nq, Nk, d;
   int causal;
@@ -155,11 +222,23 @@ static void* worker(void* arg) {
       int64_t head = flat / Nq, i = flat % Nq;  /* head = b*Hq + h */
       int64_t kv_head = (head / J->Hq) * J->Hkv + (head % J->Hq) / group;
       if (kv_head != loaded_head) {
-        const uint16_t* kh = J->k + kv_head * Nk * d;
-        const uint16_t* vh = J->v + kv_head * Nk * d;
-        for (int64_t t = 0; t < Nk * d; ++t) {
-          K[t] = decode(kh[t], J->dtype);
-          V[t] = decode(vh[t], J->dtype);
+        if (J->kq) {
+          /* K holds the integer codes (the scales are folded into the
+           * query); V the dequantized values, each an exact fp64 product */
+          const int8_t* kh = J->kq + kv_head * Nk * d;
+          const int8_t* vh = J->vq + kv_head * Nk * d;
+          const float* vs = J->vs + kv_head * d;
+          for (int64_t t = 0; t < Nk * d; ++t) {
+            K[t] = (double)kh[t];
+            V[t] = (double)vs[t % d] * (double)vh[t];
+          }
+        } else {
+          const uint16_t* kh = J->k + kv_head * Nk * d;
+          const uint16_t* vh = J->v + kv_head * Nk * d;
+          for (int64_t t = 0; t < Nk * d; ++t) {
+            K[t] = decode(kh[t], J->dtype);
+            V[t] = decode(vh[t], J->dtype);
+          }
         }
         loaded_head = kv_head;
       }
@@ -169,7 +248,12 @@ static void* worker(void* arg) {
       if (J->causal && i + 1 + Nk - Nq < visible) visible = i + 1 + Nk - Nq;
       const uint16_t* qr = J->q + flat * d;
       for (int64_t c = 0; c < d; ++c) q[c] = decode(qr[c], J->dtype);
-      one_row(q, K, V, visible, d, J->scale, s, J->o + r * d, J->lse + r);
+      double row_scale = J->scale;
+      if (J->kq) {  /* quantized query: codes in q, logits times sq */
+        const float sq = quantize_q_row(q, J->ks + kv_head * d, d, q);
+        row_scale = J->scale * (double)sq;
+      }
+      one_row(q, K, V, visible, d, row_scale, s, J->o + r * d, J->lse + r);
     }
   }
 done:
@@ -193,11 +277,11 @@ int oracle_host_threads(void) {
  * row ids in [0, B*Hq*Nq).  nthreads <= 0 uses every core in the affinity
  * mask.  Returns 0, or -1 on a bad argument, -2 on allocation failure.
  */
-int oracle_attn_general(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                        int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq,
-                        int64_t Nk, int64_t d, double scale, int causal,
-                        const int64_t* rows, int64_t nrows, double* o, double* lse,
-                        int nthreads) {
+static int run_job(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                   const int8_t* kq, const float* ks, const int8_t* vq, const float* vs,
+                   int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
+                   int64_t d, double scale, int causal, const int64_t* rows, int64_t nrows,
+                   double* o, double* lse, int nthreads) {
   if (dtype != ORACLE_BF16 && dtype != ORACLE_FP16) return -1;
   if (B < 0 || Hq < 0 || Hkv <= 0 || Nq < 0 || Nk < 0 || d <= 0) return -1;
   if (Hq % Hkv != 0 || (causal != 0 && causal != 1)) return -1;
@@ -205,7 +289,8 @@ int oracle_attn_general(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   if (!rows) nrows = total;
   if (nrows < 0 || nrows > total) return -1;
   if (nrows == 0) return 0;
-  if (!q || !o || !lse || (Nk > 0 && (!k || !v))) return -1;
+  if (!q || !o || !lse) return -1;
+  if (kq ? (!ks || (Nk > 0 && (!vq || !vs))) : (Nk > 0 && (!k || !v))) return -1;
   if (rows) {
     for (int64_t r = 0; r < nrows; ++r) {
       if (rows[r] < 0 || rows[r] >= total) return -1;
@@ -217,6 +302,7 @@ int oracle_attn_general(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   job_t J;
   memset(&J, 0, sizeof J);
   J.q = q; J.k = k; J.v = v; J.dtype = dtype;
+  J.kq = kq; J.ks = ks; J.vq = vq; J.vs = vs;
   J.B = B; J.Hq = Hq; J.Hkv = Hkv; J.Nq = Nq; J.Nk = Nk; J.d = d;
   J.causal = causal; J.scale = scale;
   J.rows = rows; J.nrows = nrows; J.o = o; J.lse = lse;
@@ -242,6 +328,31 @@ int oracle_attn_general(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   free(th);
   pthread_mutex_destroy(&J.mu);
   return J.failed ? -2 : 0;
+}
+
+int oracle_attn_general(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                        int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq,
+                        int64_t Nk, int64_t d, double scale, int causal,
+                        const int64_t* rows, int64_t nrows, double* o, double* lse,
+                        int nthreads) {
+  return run_job(q, k, v, NULL, NULL, NULL, NULL, dtype, B, Hq, Hkv, Nq, Nk, d, scale,
+                 causal, rows, nrows, o, lse, nthreads);
+}
+
+/*
+ * Attention over an INT8 key/value cache (the scheme in the header): q
+ * [B][Hq][Nq][d] 16-bit patterns; kq, vq [B][Hkv][Nk][d] int8 codes; ks, vs
+ * [B][Hkv][d] fp32 per-channel scales.  Rows, threads and the return codes
+ * are those of oracle_attn_general.
+ */
+int oracle_attn_kv_int8(const uint16_t* q, int dtype, const int8_t* kq, const float* ks,
+                        const int8_t* vq, const float* vs, int64_t B, int64_t Hq,
+                        int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, double scale,
+                        int causal, const int64_t* rows, int64_t nrows, double* o,
+                        double* lse, int nthreads) {
+  if (!kq) return -1;
+  return run_job(q, NULL, NULL, kq, ks, vq, vs, dtype, B, Hq, Hkv, Nq, Nk, d, scale, causal,
+                 rows, nrows, o, lse, nthreads);
 }
 
 /* The base problem: equal heads and lengths, no mask. */

@@ -457,6 +457,127 @@ def pin_single_key_any_length(orc):
         assert np.array_equal(o, np.broadcast_to(_f64(v), o.shape))
 
 
+# --------------------------------------------------------------------------
+# INT8 key/value cache: the reading spelled out in oracle/attn_ref.c (int8
+# codes with per-channel scales; query rows quantized in binary32 after the
+# key scales are folded in).
+
+
+def pin_int8_query_codes_golden(orc):
+    """Hand-derived codes and row scales (tests/golden/int8_query_codes.json):
+    ties to even, key scales folded into the row, a zero row, a negative
+    extreme, and a row where binary32 rounding gives a different code than
+    exact rationals would."""
+    with open(os.path.join(GOLDEN, "int8_query_codes.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        q = _t16(c["q"], c["dtype"])
+        codes, sq = orc.quantize_q(bits(q)[None, :], np.asarray(c["ks"], np.float32), c["dtype"])
+        assert codes[0].tolist() == c["codes"], (c["name"], codes[0].tolist())
+        assert int(sq.view(np.uint32)[0]) == int(c["sq_bits"], 16), (c["name"], hex(sq.view(np.uint32)[0]))
+
+
+def _int8_cache(B, Hkv, Nk, d, seed, pow2_scales=False):
+    """Random int8 codes [B, Hkv, Nk, d] and float32 scales [B, Hkv, d]."""
+    rng = np.random.default_rng(seed)
+    kq = rng.integers(-127, 128, size=(B, Hkv, Nk, d)).astype(np.int8)
+    vq = rng.integers(-127, 128, size=(B, Hkv, Nk, d)).astype(np.int8)
+    if pow2_scales:
+        ks = np.exp2(-rng.integers(2, 7, size=(B, Hkv, d))).astype(np.float32)
+        vs = np.exp2(-rng.integers(2, 7, size=(B, Hkv, d))).astype(np.float32)
+    else:
+        ks = rng.uniform(0.01, 0.05, size=(B, Hkv, d)).astype(np.float32)
+        vs = rng.uniform(0.01, 0.05, size=(B, Hkv, d)).astype(np.float32)
+    return kq, ks, vq, vs
+
+
+def pin_int8_reduces_to_dequantized_attention(orc):
+    """A query row whose key-scaled values u = q*ks are integers with max |u| =
+    127 quantizes to itself (codes u, sq = 1), so its logits are exactly those
+    of plain attention on q and the dequantized k = ks*kq; with v = vs*vq the
+    whole result must equal the (separately pinned) 16-bit oracle on q,
+    ks*kq, vs*vq.  Power-of-two scales keep every value exact in 16 bits."""
+    rng = np.random.default_rng(7)
+    for dtype in DTYPES:
+        for causal in (False, True):
+            B, Hq, Hkv, Nq, Nk, d = 2, 4, 2, 5, 7, 16
+            kq, ks, vq, vs = _int8_cache(B, Hkv, Nk, d, seed=11, pow2_scales=True)
+            u = rng.integers(-126, 127, size=(B, Hq, Nq, d)).astype(np.float64)
+            u[..., 3] = np.where(rng.random((B, Hq, Nq)) < 0.5, 127.0, -127.0)
+            group = Hq // Hkv
+            ks_q = np.repeat(ks, group, axis=1)[:, :, None, :].astype(np.float64)
+            q = _t16(u / ks_q, dtype)
+            kd = _t16(ks[:, :, None, :].astype(np.float64) * kq, dtype)
+            vd = _t16(vs[:, :, None, :].astype(np.float64) * vq, dtype)
+            o8, l8 = orc.attention_kv_int8(bits(q), kq, ks, vq, vs, dtype, 0.125, causal=causal)
+            o, lse = _run(orc, q, kd, vd, dtype, 0.125, causal=causal)
+            np.testing.assert_allclose(o8, o, rtol=1e-13, atol=1e-13)
+            np.testing.assert_allclose(l8, lse, rtol=1e-13, atol=0)
+
+
+def pin_int8_zero_query_is_uniform(orc):
+    """A zero query row has codes 0 and sq = 0, so every logit is 0: O is the
+    mean of the dequantized values the row sees and lse = ln(keys seen)."""
+    B, Hq, Hkv, Nq, Nk, d = 1, 2, 1, 3, 6, 8
+    kq, ks, vq, vs = _int8_cache(B, Hkv, Nk, d, seed=5)
+    q = _t16(np.zeros((B, Hq, Nq, d)), "bf16")
+    for causal in (False, True):
+        o, lse = orc.attention_kv_int8(bits(q), kq, ks, vq, vs, "bf16", 0.3, causal=causal)
+        vdq = vs[:, :, None, :].astype(np.float64) * vq
+        for i in range(Nq):
+            n = _visible(i, Nq, Nk) if causal else Nk
+            want = vdq[0, 0, :n].mean(axis=0)
+            np.testing.assert_allclose(o[0, :, i], np.broadcast_to(want, (Hq, d)), rtol=1e-12, atol=1e-15)
+            np.testing.assert_allclose(lse[0, :, i], math.log(n), rtol=1e-14)
+
+
+def _int8_brute_row(q16, ksh, kqh, vsh, vqh, n, scale):
+    """The scheme term by term: numpy binary32 for the query quantization,
+    Python integers for the code dot products, math.exp / math.fsum after."""
+    u = (q16.astype(np.float32) * ksh).astype(np.float32)
+    amax = np.float32(np.max(np.abs(u)))
+    if amax > 0:
+        inv = np.float32(np.float32(127.0) / amax)
+        codes = np.clip(np.rint((u * inv).astype(np.float32)), -127, 127).astype(np.int64)
+        sq = float(np.float32(amax / np.float32(127.0)))
+    else:
+        codes = np.zeros(u.shape, np.int64)
+        sq = 0.0
+    d = u.size
+    if n == 0:
+        return [0.0] * d, -math.inf
+    s = [scale * sq * float(sum(int(codes[c]) * int(kqh[j, c]) for c in range(d))) for j in range(n)]
+    m = max(s)
+    w = [math.exp(x - m) for x in s]
+    l = math.fsum(w)
+    o = [math.fsum(w[j] * float(vsh[c]) * float(vqh[j, c]) for j in range(n)) / l for c in range(d)]
+    return o, m + math.log(l)
+
+
+def pin_int8_brute_force(orc):
+    """Tiny random problems (grouped heads, both masks, Nq != Nk) against the
+    term-by-term evaluation above."""
+    for dtype, causal, (B, Hq, Hkv, Nq, Nk, d) in (
+            ("bf16", False, (1, 4, 2, 3, 5, 8)), ("fp16", True, (2, 2, 1, 4, 3, 16)),
+            ("bf16", True, (1, 3, 3, 2, 6, 4))):
+        kq, ks, vq, vs = _int8_cache(B, Hkv, Nk, d, seed=Nk + d)
+        q = _rand16((B, Hq, Nq, d), dtype, seed=d)
+        o, lse = orc.attention_kv_int8(bits(q), kq, ks, vq, vs, dtype, 0.7, causal=causal)
+        qn = _f64(q)
+        group = Hq // Hkv
+        for b in range(B):
+            for h in range(Hq):
+                g = h // group
+                for i in range(Nq):
+                    n = _visible(i, Nq, Nk) if causal else Nk
+                    ob, lb = _int8_brute_row(qn[b, h, i], ks[b, g], kq[b, g], vs[b, g], vq[b, g], n, 0.7)
+                    np.testing.assert_allclose(o[b, h, i], ob, rtol=1e-12, atol=1e-14)
+                    if n:
+                        assert abs(lse[b, h, i] - lb) <= 1e-12 * max(1.0, abs(lb))
+                    else:
+                        assert lse[b, h, i] == -math.inf
+
+
 ALL_PINS = [
     pin_decode_every_pattern,
     pin_worked_examples,
@@ -478,4 +599,8 @@ ALL_PINS = [
     pin_causal_brute_force,
     pin_grouped_heads_are_repeated_heads,
     pin_single_key_any_length,
+    pin_int8_query_codes_golden,
+    pin_int8_reduces_to_dequantized_attention,
+    pin_int8_zero_query_is_uniform,
+    pin_int8_brute_force,
 ]

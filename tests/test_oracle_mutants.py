@@ -31,6 +31,22 @@ MUTANTS = [
     ("causal_top_left", "if (J->causal && i + 1 + Nk - Nq < visible) visible = i + 1 + Nk - Nq;",
      "if (J->causal && i + 1 < visible) visible = i + 1;"),
     ("empty_row_lse_zero", "*lse_out = -INFINITY;", "*lse_out = 0.0;"),
+    # INT8 key/value cache
+    ("int8_truncates", "float code = rintf(u * inv);", "float code = truncf(u * inv);"),
+    ("int8_ties_away", "float code = rintf(u * inv);", "float code = roundf(u * inv);"),
+    ("int8_exact_rationals", "float code = rintf(u * inv);",
+     "float code = (float)rint((double)u * 127.0 / (double)amax);"),
+    ("int8_amax_signed", "if (fabsf(u) > amax) amax = fabsf(u);", "if (u > amax) amax = u;"),
+    ("int8_sq_over_128", "return amax / 127.0f;", "return amax / 128.0f;"),
+    ("int8_key_scale_not_folded", "const float u = (float)q[c] * ks[c];\n    if",
+     "const float u = (float)q[c];\n    if"),
+    ("int8_value_scale_dropped", "V[t] = (double)vs[t % d] * (double)vh[t];",
+     "V[t] = (double)vh[t];"),
+    ("int8_value_scale_by_key", "V[t] = (double)vs[t % d] * (double)vh[t];",
+     "V[t] = (double)vs[(t / d) % d] * (double)vh[t];"),
+    ("int8_row_scale_dropped", "row_scale = J->scale * (double)sq;", "row_scale = J->scale;"),
+    ("int8_wrong_head_scales", "quantize_q_row(q, J->ks + kv_head * d, d, q);",
+     "quantize_q_row(q, J->ks, d, q);"),
 ]
 
 
