@@ -101,18 +101,25 @@ def cpu_baseline(w, q, k, v):
     import oracle
     from flashattention_forward_tile_amd.workloads import bits
 
-    qb, kb, vb = bits(q), bits(k), bits(v)
     threads = oracle.host_threads()
     group = w.H // w.kv_heads
     heads = 0
+    c = np.ascontiguousarray
+    if w.kv_int8:
+        qb, kq, ksc, vq, vsc = bits(q), k[0].numpy(), k[1].numpy(), v[0].numpy(), v[1].numpy()
+    else:
+        qb, kb, vb = bits(q), bits(k), bits(v)
     t0 = time.perf_counter()
     while heads < w.B * w.H:
         b, h = divmod(heads, w.H)
         qs = (slice(b, b + 1), slice(h, h + 1))
         ks = (slice(b, b + 1), slice(h // group, h // group + 1))
-        oracle.attention(np.ascontiguousarray(qb[qs]), np.ascontiguousarray(kb[ks]),
-                         np.ascontiguousarray(vb[ks]), w.dtype, w.scale, nthreads=threads,
-                         causal=w.causal)
+        if w.kv_int8:
+            oracle.attention_kv_int8(c(qb[qs]), c(kq[ks]), c(ksc[ks]), c(vq[ks]), c(vsc[ks]),
+                                     w.dtype, w.scale, nthreads=threads, causal=w.causal)
+        else:
+            oracle.attention(c(qb[qs]), c(kb[ks]), c(vb[ks]), w.dtype, w.scale,
+                             nthreads=threads, causal=w.causal)
         heads += 1
         if time.perf_counter() - t0 >= CPU_SAMPLE_SECONDS:
             break
@@ -172,13 +179,21 @@ def main():
 
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
-    q, k, v = workload_inputs(w, seed=0)
-    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
-    o = torch.empty_like(qd)
+    inputs = workload_inputs(w, seed=0)
+    dev_in = [t.to(dev) for t in inputs]
+    o = torch.empty_like(dev_in[0])
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    if w.kv_int8:
+        def launch():
+            fa2.fwd_kv_int8(*dev_in, scale=w.scale, causal=w.causal, out=o, lse=lse)
+        q, k, v = inputs[0], (inputs[1], inputs[2]), (inputs[3], inputs[4])
+    else:
+        def launch():
+            fa2.fwd(*dev_in, scale=w.scale, causal=w.causal, out=o, lse=lse)
+        q, k, v = inputs
 
     for _ in range(args.warmup):
-        fa2.fwd(qd, kd, vd, scale=w.scale, causal=w.causal, out=o, lse=lse)
+        launch()
     torch.cuda.synchronize(dev)
     if not (torch.isfinite(o[0, 0].float()).all() and torch.isfinite(lse[:, :, -1]).all()):
         raise RuntimeError("non-finite output")
@@ -189,7 +204,7 @@ def main():
     wall0 = time.perf_counter()
     start.record(stream)
     for _ in range(args.steps):
-        fa2.fwd(qd, kd, vd, scale=w.scale, causal=w.causal, out=o, lse=lse)
+        launch()
     stop.record(stream)
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - wall0

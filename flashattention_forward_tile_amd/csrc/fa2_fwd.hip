@@ -30,6 +30,7 @@
 //    and share that XCD's L2 copy of the head's K and V.
 
 #include <hip/hip_runtime.h>
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 
@@ -42,6 +43,7 @@ namespace fa2 {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -140,6 +142,13 @@ __device__ __forceinline__ void load_lds16(i32x4 rsrc, uint32_t voff, uint32_t l
                : "v"(voff), "s"(rsrc), "{m0}"(lds_addr)
                : "memory");
 }
+// The same with 4 bytes per lane: lane l writes LDS bytes [m0 + 4 l, m0 + 4 l + 4).
+__device__ __forceinline__ void load_lds4(i32x4 rsrc, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("buffer_load_dword %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "{m0}"(lds_addr)
+               : "memory");
+}
 
 // Tile shape per head dimension: key rows per tile (BC), waves per workgroup
 // (NW), 32-query blocks per wave (QB), the waves per SIMD the register
@@ -160,6 +169,11 @@ template <int D> struct Cfg;
 template <> struct Cfg<64> { static constexpr int BC = 64, NW = 4, QB = 1, OCC = 2, SGB = 1, RING = 4, PK = 4, PV = 2; };
 template <> struct Cfg<128> { static constexpr int BC = 32, NW = 8, QB = 1, OCC = 2, SGB = 0, RING = 4, PK = 4, PV = 2; };
 template <> struct Cfg<256> { static constexpr int BC = 32, NW = 4, QB = 1, OCC = 1, SGB = 0, RING = 2, PK = 0, PV = 0; };
+
+// Tile shape of the INT8 key/value cache kernels (d = 128 only).
+template <int D> struct Cfg8;
+template <> struct Cfg8<128> { static constexpr int BC = 32, NW = 8, QB = 1, OCC = 2, SGB = 0, RING = 4, PK = 2, PV = 2; };
+template <int D, bool Q8> using KCfg = std::conditional_t<Q8, Cfg8<D>, Cfg<D>>;
 // Ring slots and loop phases as compile-time constants.
 template <int X> using Ic = std::integral_constant<int, X>;
 
@@ -181,10 +195,12 @@ enum ScaleMode { kPositive = 0, kNegative = 1, kZero = 2 };
 // (causal_off = nk - nq).
 struct Problem {
   const uint16_t* q;
-  const uint16_t* k;
-  const uint16_t* v;
+  const char* k;     // 16-bit elements, or int8 codes for the INT8 cache
+  const char* v;
   uint16_t* o;
   float* lse;
+  const float* ks;   // INT8 cache only: per-channel scales [B][hkv][D]
+  const float* vs;
   int nq, nk;        // query rows per query head, key rows per K/V head
   int rows;          // query rows per K/V head (its query heads back to back)
   int q_tiles;       // query tiles per K/V head
@@ -193,42 +209,64 @@ struct Problem {
   float c;           // scale * log2(e) (1 when the scale is 0)
 };
 
-template <int D, bool FP16, int MODE, bool CAUSAL>
-__global__ void __attribute__((amdgpu_flat_work_group_size(Cfg<D>::NW * 64,
-                                                           Cfg<D>::NW * 64),
-                               amdgpu_waves_per_eu(Cfg<D>::OCC, Cfg<D>::OCC)))
+// Q8 selects the INT8 key/value cache: K and V arrive as int8 codes with
+// per-channel scales; the first product runs on int8 matrix instructions
+// against the in-kernel quantized query, and V is widened to fp16 in LDS for
+// the second product (see the header of fa2.h for the scheme).
+template <int D, bool FP16, int MODE, bool CAUSAL, bool Q8>
+__global__ void __attribute__((amdgpu_flat_work_group_size(KCfg<D, Q8>::NW * 64,
+                                                           KCfg<D, Q8>::NW * 64),
+                               amdgpu_waves_per_eu(KCfg<D, Q8>::OCC, KCfg<D, Q8>::OCC)))
 fa2_fwd_kernel(const Problem P) {
+  using C = KCfg<D, Q8>;
   const int N = P.nk;  // keys per head
   const float c = P.c;
-  constexpr int BC = Cfg<D>::BC;
-  constexpr int NW = Cfg<D>::NW;
-  constexpr int QB = Cfg<D>::QB;
+  constexpr int BC = C::BC;
+  constexpr int NW = C::NW;
+  constexpr int QB = C::QB;
   constexpr int BR = NW * 32 * QB;    // query rows per workgroup
-  constexpr int CPR = D / 8;          // 16-byte chunks per K/V row
-  constexpr int RB = D * 2;           // bytes per K/V row
-  constexpr int TBYTES = BC * RB;     // one K or V tile
-  constexpr int LOADS = TBYTES / (NW * 64 * 16);  // 1 KiB wave loads per thread
-  constexpr int KS = D / 16;          // k-steps of the first product
+  constexpr int CPR = D / 8;          // 16-byte chunks per (16-bit) V row
+  constexpr int RB = D * 2;           // bytes per (16-bit) V row in LDS
+  constexpr int TBYTES = BC * RB;     // one V tile in LDS
+  constexpr int RBK = Q8 ? D : RB;    // bytes per K row in LDS (int8 or 16-bit)
+  constexpr int CPRK = RBK / 16;      // 16-byte chunks per K row
+  constexpr int TBK = BC * RBK;       // one K tile in LDS (and one int8 V tile)
+  constexpr int LW = Q8 ? 4 : 16;     // bytes per lane of one HBM -> LDS load
+  constexpr int LOADS = TBK / (NW * 64 * LW);  // K loads per thread per tile (V: the same)
+  constexpr int KS = Q8 ? D / 32 : D / 16;     // k-steps of the first product
   constexpr int ST = BC / 16;         // k-steps of the second product
   constexpr int KB = BC / 32;         // 32-key blocks per tile
   constexpr int DB = D / 32;          // 32-dim blocks of the output
-  static_assert(TBYTES % (NW * 64 * 16) == 0, "tile must split into wave loads");
+  static_assert(TBK % (NW * 64 * LW) == 0, "tile must split into wave loads");
   static_assert(BC % 32 == 0 && D % 32 == 0, "MFMA 32x32 blocking");
-  using X8 = typename Vec<FP16>::x8;
+  // Q and O are bf16 or fp16; P and V meet on fp16 matrix instructions in the
+  // INT8 kernels (V is widened exactly), on the input type otherwise.
+  constexpr bool F16B = FP16 || Q8;
+  using X8 = typename Vec<F16B>::x8;  // operands of the second product
   using X4 = typename Vec<FP16>::x4;
-  using X2 = typename Vec<FP16>::x2;
-  using E = typename Vec<FP16>::e;
+  using X2 = typename Vec<F16B>::x2;
+  using E = typename Vec<FP16>::e;    // element type of Q and O
+  using EP = typename Vec<F16B>::e;   // element type of P
+  using KOp = std::conditional_t<Q8, i32x4, X8>;        // A operand of the first product
+  using SAcc = std::conditional_t<Q8, i32x16, f32x16>;  // its accumulator
 
-  constexpr int PK = Cfg<D>::PK;      // K operands read one iteration early
-  constexpr int PV = Cfg<D>::PV;      // V operands read one iteration early
+  constexpr int PK = C::PK;           // K operands read one iteration early
+  constexpr int PV = C::PV;           // V operands read one iteration early
   constexpr int KO = KS * KB;         // K operands (A of the first product) per tile
   constexpr int VO = ST * DB;         // V operands (A of the second product) per tile
-  constexpr int RING = Cfg<D>::RING;
+  constexpr int RING = C::RING;
   static_assert(RING == 2 || RING == 4, "ring of 2 or 4 slots");
   static_assert(PK <= KO && PV <= VO && (RING == 4 || PK + PV == 0), "prefetch depth");
-  // LDS: the K ring [RING][BC][D] at 0, the V ring at RING*TBYTES; tiles
-  // row-major, swizzled.
-  __shared__ __attribute__((aligned(16))) char smem[2 * RING * TBYTES];
+  static_assert(!Q8 || RING == 4, "INT8 staging assumes four slots");
+  // V_t is loaded during iteration t - VAHEAD: as int8 into a staging ring
+  // three iterations ahead (Q8; widened to fp16 during iteration t - 1), else
+  // straight into the V ring.
+  constexpr int VAHEAD = Q8 ? 3 : RING - 2;
+  // LDS: the K ring [RING][BC][D] at 0, the (16-bit) V ring at VBASE, and with
+  // Q8 the int8 V staging ring at SBASE; tiles row-major, K and V swizzled.
+  constexpr int VBASE = RING * TBK;
+  constexpr int SBASE = VBASE + RING * TBYTES;
+  __shared__ __attribute__((aligned(16))) char smem[SBASE + (Q8 ? RING * TBK : 0)];
   lds_char* const lds = (lds_char*)smem;
 
   const int tid = threadIdx.x;
@@ -265,21 +303,23 @@ fa2_fwd_kernel(const Problem P) {
   const int64_t q_head = (int64_t)bh * P.rows * D;  // the group's first query row
   const int64_t kv_head = (int64_t)bh * N * D;
   const __amdgpu_buffer_rsrc_t q_rs = make_rsrc(P.q + q_head, (uint32_t)P.rows * D * 2);
-  const i32x4 k_rs = make_rsrc_words(P.k + kv_head, (uint32_t)N * D * 2);
-  const i32x4 v_rs = make_rsrc_words(P.v + kv_head, (uint32_t)N * D * 2);
+  constexpr int KE = Q8 ? 1 : 2;  // bytes per K / V element in HBM
+  const i32x4 k_rs = make_rsrc_words(P.k + kv_head * KE, (uint32_t)N * D * KE);
+  const i32x4 v_rs = make_rsrc_words(P.v + kv_head * KE, (uint32_t)N * D * KE);
   const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
 
-  // Global -> LDS without registers: each wave load moves 64 x 16 B into 1 KiB
-  // of LDS (lane l to byte 16*l).  The swizzle is applied on the global side:
-  // lane l fetches the logical chunk that belongs at its LDS position.  Rows
-  // past N read as zeros (buffer range check); their keys are masked later.
+  // Global -> LDS without registers: each wave load moves 64 lanes x LW bytes
+  // (lane l to byte LW*l of its piece).  The swizzles (on 16-byte chunks) are
+  // applied on the global side: a lane fetches the bytes that belong at its
+  // LDS position.  With Q8 the int8 V tile is staged unswizzled.  Rows past N
+  // read as zeros (buffer range check); their keys are masked later.
   uint32_t k_src[LOADS], v_src[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
-    const int lin = (i * NW + wave) * 64 + lane;  // physical chunk in the tile
-    const int row = lin / CPR, pc = lin % CPR;
-    k_src[i] = (uint32_t)(row * RB + k_swizzle<CPR>(row, pc) * 16);
-    v_src[i] = (uint32_t)(row * RB + v_swizzle<CPR>(row, pc) * 16);
+    const int pos = ((i * NW + wave) * 64 + lane) * LW;  // byte in the LDS tile
+    const int row = pos / RBK, pc = (pos % RBK) / 16, byte = pos % 16;
+    k_src[i] = (uint32_t)(row * RBK + k_swizzle<CPRK>(row, pc) * 16 + byte);
+    v_src[i] = Q8 ? (uint32_t)pos : (uint32_t)(row * RB + v_swizzle<CPR>(row, pc) * 16);
   }
   // `s` (an integral constant) is t modulo 4, known at compile time in the
   // loop (unrolled by 4), so the ring slot t % RING and its LDS offsets fold
@@ -289,17 +329,25 @@ fa2_fwd_kernel(const Problem P) {
   auto slot = [](int t, auto s) { return kImmBuf ? decltype(s)::value % RING : (t & (RING - 1)); };
   // Tiles past the last one read as zeros (buffer range check) and are never
   // used; loading them keeps the per-iteration load count fixed.
-  auto issue_k = [&](int t, auto s) {
-    const uint32_t dst = lds_base + slot(t, s) * TBYTES + wave * 1024;
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i)
-      load_lds16(k_rs, (uint32_t)t * TBYTES + k_src[i], dst + i * NW * 1024);
+  auto load_lds = [&](const i32x4& rs, uint32_t voff, uint32_t dst) {
+    if constexpr (LW == 4)
+      load_lds4(rs, voff, dst);
+    else
+      load_lds16(rs, voff, dst);
   };
-  auto issue_v = [&](int t, auto s) {
-    const uint32_t dst = lds_base + (RING + slot(t, s)) * TBYTES + wave * 1024;
+  auto issue_k = [&](int t, auto s) {
+    const uint32_t dst = lds_base + slot(t, s) * TBK + wave * 64 * LW;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i)
-      load_lds16(v_rs, (uint32_t)t * TBYTES + v_src[i], dst + i * NW * 1024);
+      load_lds(k_rs, (uint32_t)t * TBK + k_src[i], dst + i * NW * 64 * LW);
+  };
+  // V_t into the V ring, or with Q8 into the int8 staging ring.
+  auto issue_v = [&](int t, auto s) {
+    const uint32_t dst = lds_base + (Q8 ? SBASE + slot(t, s) * TBK : VBASE + slot(t, s) * TBYTES) +
+                         wave * 64 * LW;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i)
+      load_lds(v_rs, (uint32_t)t * TBK + v_src[i], dst + i * NW * 64 * LW);
   };
 
   // Per-lane LDS byte offsets of the MFMA operands within a tile.  The
@@ -318,7 +366,7 @@ fa2_fwd_kernel(const Problem P) {
   uint32_t k_off[KOFF];
 #pragma unroll
   for (int ks = 0; ks < KOFF; ++ks)
-    k_off[ks] = (uint32_t)(l32 * RB + k_swizzle<CPR>(l32, ks * 2 + half) * 16);
+    k_off[ks] = (uint32_t)(l32 * RBK + k_swizzle<CPRK>(l32, ks * 2 + half) * 16);
   const int tr_row = half * 4 + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   uint32_t v_off[VOFF];
@@ -354,14 +402,73 @@ fa2_fwd_kernel(const Problem P) {
     const int last_key = row_max + P.causal_off;  // may be < 0
     n_tiles = last_key < 0 ? 0 : min(n_tiles, last_key / BC + 1);
   }
-  X8 qf[QB][KS];
+  // c_q: the lane's logit multiplier (scale * log2 e, times the query row
+  // scale with Q8).
+  using QOp = std::conditional_t<Q8, i32x4, X8>;
+  QOp qf[QB][KS];
+  float c_q[QB];
 #pragma unroll
-  for (int b = 0; b < QB; ++b)
+  for (int b = 0; b < QB; ++b) {
+    c_q[b] = c;
+    const uint32_t qrow_off = (uint32_t)((q0 + 32 * b + l32) * RB);
+    if constexpr (!Q8) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qf[b][ks] = __builtin_bit_cast(
-          X8, __builtin_amdgcn_raw_buffer_load_b128(
-                  q_rs, (uint32_t)((q0 + 32 * b + l32) * RB + ks * 32 + half * 16), 0, 0));
+      for (int ks = 0; ks < KS; ++ks)
+        qf[b][ks] = __builtin_bit_cast(
+            X8, __builtin_amdgcn_raw_buffer_load_b128(q_rs, qrow_off + ks * 32 + half * 16, 0, 0));
+    } else if constexpr (MODE != kZero) {
+      // In-kernel quantization of the query row (lanes l and l+32 hold its
+      // two halves): for k-step ks this lane holds channels 32 ks + 16 half
+      // + 0..15.  u = q * ks in binary32; amax over the row; codes
+      // clamp(rint(u * (127 / amax)), +-127) and sq = amax / 127, both
+      // divisions correctly rounded (a zero row: codes 0, sq 0).
+      using Q16 = typename Vec<FP16>::x8;
+      const float* ksp = P.ks + (int64_t)bh * D;
+      float u[KS][16];
+      float amax = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int ch = 32 * ks + 16 * half;
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const Q16 qv = __builtin_bit_cast(
+              Q16, __builtin_amdgcn_raw_buffer_load_b128(q_rs, qrow_off + (ch + 8 * h2) * 2, 0, 0));
+          const float4 s0 = *(const float4*)(ksp + ch + 8 * h2);
+          const float4 s1 = *(const float4*)(ksp + ch + 8 * h2 + 4);
+          const float sk[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float v = (float)qv[e] * sk[e];
+            u[ks][8 * h2 + e] = v;
+            amax = fmaxf(amax, fabsf(v));
+          }
+        }
+      }
+      amax = fmaxf(amax, __shfl_xor(amax, 32));
+      const bool nonzero = amax > 0.0f;
+      const float inv = nonzero ? __fdiv_rn(127.0f, amax) : 0.0f;
+      const float sq = nonzero ? __fdiv_rn(amax, 127.0f) : 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        i32x4 w;
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) {
+          uint32_t packed = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float code = fminf(fmaxf(__builtin_rintf(u[ks][4 * k4 + e] * inv), -127.0f), 127.0f);
+            packed |= ((uint32_t)(int)code & 0xFFu) << (8 * e);
+          }
+          w[k4] = (int)packed;
+        }
+        qf[b][ks] = w;
+      }
+      // A zero (or underflowing) multiplier would turn the -inf of masked keys
+      // into NaN; the smallest normal keeps every unmasked logit at 0 instead.
+      const float cq = c * sq;
+      c_q[b] = cq != 0.0f ? cq : (MODE == kNegative ? -FLT_MIN : FLT_MIN);
+    }
+  }
 
   f32x16 acc[QB][DB];
   float m_ref[QB], l_part[QB];  // reference max (log2 units), lane's row sum
@@ -376,23 +483,24 @@ fa2_fwd_kernel(const Problem P) {
   }
 
   // First operands of the next products, read one iteration early.
-  X8 kpre[PK > 0 ? PK : 1], vpre[PV > 0 ? PV : 1];
+  KOp kpre[PK > 0 ? PK : 1];
+  X8 vpre[PV > 0 ? PV : 1];
 
   // Operand o of the first product, o = ks*KB + kk: rows kk*32 .. +31 of
   // K_t (k-step ks), as the A operand of S^T = K_t Q_i^T.
-  auto k_operand = [&](int t, auto s, int o) -> X8 {
+  auto k_operand = [&](int t, auto s, int o) -> KOp {
     const int ks = o / KB, kk = o % KB;
-    const lds_char* kb = lds + slot(t, s) * TBYTES;
+    const lds_char* kb = lds + slot(t, s) * TBK;
     return __builtin_bit_cast(
-        X8, *(const __attribute__((address_space(3))) u32x4*)(
-                kb + kk * 32 * RB + k_off[ks % KOFF] + (ks / KOFF) * 256));
+        KOp, *(const __attribute__((address_space(3))) u32x4*)(
+                 kb + kk * 32 * RBK + k_off[ks % KOFF] + (ks / KOFF) * 256));
   };
   // Operand o of the second product, o = st*DB + db: V_t^T for output rows
   // db*32 .. +31 and keys st*16 .. +15 in the S^T accumulator's key order,
   // from the row-major V tile through two transposing LDS reads of 4 keys.
   auto v_operand = [&](int t, auto s, int o) -> X8 {
     const int st = o / DB, db = o % DB;
-    const lds_char* vb = lds + (RING + slot(t, s)) * TBYTES;
+    const lds_char* vb = lds + VBASE + slot(t, s) * TBYTES;
     const uint32_t vo = v_off[db % VOFF] + (db / VOFF) * 256;
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (lds_s16x4*)(vb + vo + (st * 16) * RB));
@@ -405,20 +513,24 @@ fa2_fwd_kernel(const Problem P) {
   // operands come from `pre` (read during the previous iteration), the rest
   // from LDS.  With a zero scale every logit is 0 whatever Q and K hold, so S
   // stays 0 and c is taken as 1 (x = s - m_ref keeps masked keys at -inf).
-  auto gemm1 = [&](int t, auto s, const X8 (&pre)[PK > 0 ? PK : 1], f32x16 (&sd)[QB][KB]) {
+  auto gemm1 = [&](int t, auto s, const KOp (&pre)[PK > 0 ? PK : 1], SAcc (&sd)[QB][KB]) {
 #pragma unroll
     for (int b = 0; b < QB; ++b)
 #pragma unroll
       for (int kk = 0; kk < KB; ++kk)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sd[b][kk][i] = 0.0f;
+        for (int i = 0; i < 16; ++i) sd[b][kk][i] = 0;
     if constexpr (MODE == kZero) return;
 #pragma unroll
     for (int o = 0; o < KO; ++o) {
-      const X8 a = o < PK ? pre[o < PK ? o : 0] : k_operand(t, s, o);
+      const KOp a = o < PK ? pre[o < PK ? o : 0] : k_operand(t, s, o);
 #pragma unroll
-      for (int b = 0; b < QB; ++b)
-        sd[b][o % KB] = mfma32x32x16<FP16>(a, qf[b][o / KB], sd[b][o % KB]);
+      for (int b = 0; b < QB; ++b) {
+        if constexpr (Q8)  // exact int32 dot products of the codes
+          sd[b][o % KB] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qf[b][o / KB], sd[b][o % KB], 0, 0, 0);
+        else
+          sd[b][o % KB] = mfma32x32x16<FP16>(a, qf[b][o / KB], sd[b][o % KB]);
+      }
     }
   };
 
@@ -429,12 +541,12 @@ fa2_fwd_kernel(const Problem P) {
     for (int o = 0; o < VO; ++o) {
       const X8 a = o < PV ? pre[o < PV ? o : 0] : v_operand(t, s, o);
 #pragma unroll
-      for (int b = 0; b < QB; ++b) acc[b][o % DB] = mfma32x32x16<FP16>(a, pf[b][o / DB], acc[b][o % DB]);
+      for (int b = 0; b < QB; ++b) acc[b][o % DB] = mfma32x32x16<F16B>(a, pf[b][o / DB], acc[b][o % DB]);
     }
   };
 
   // The first PK / PV operands of the next iteration's products.
-  auto prefetch_k = [&](int t, auto s, X8 (&pre)[PK > 0 ? PK : 1]) {
+  auto prefetch_k = [&](int t, auto s, KOp (&pre)[PK > 0 ? PK : 1]) {
     if constexpr (MODE == kZero) return;
 #pragma unroll
     for (int o = 0; o < PK; ++o) pre[o] = k_operand(t, s, o);
@@ -444,7 +556,38 @@ fa2_fwd_kernel(const Problem P) {
     for (int o = 0; o < PV; ++o) pre[o] = v_operand(t, s, o);
   };
 
-  auto probs = [&](const f32x16 (&sc)[KB], X8 (&pf)[ST], float m) -> float {
+  // Q8: widen V_t from its int8 staging slot into the 16-bit V ring as exact
+  // fp16.  Each thread writes whole 16-byte chunks of the swizzled tile from
+  // the 8 codes of the logical chunk that belongs there: with u = code + 128
+  // (the byte xor 0x80), the fp16 pattern 0x6400 | u is 1024 + u, and
+  // subtracting 1152 leaves the code.
+  auto convert_v = [&](int t, auto s) {
+    if constexpr (Q8) {
+      using h16x8 = _Float16 __attribute__((ext_vector_type(8)));
+      constexpr int CH = TBYTES / 16;  // 16-byte fp16 chunks per tile
+      static_assert(CH % (NW * 64) == 0, "whole chunks per thread");
+#pragma unroll
+      for (int i = 0; i < CH / (NW * 64); ++i) {
+        const int lin = i * NW * 64 + tid;
+        const int row = lin / CPR, pc = lin % CPR;
+        const int lc = v_swizzle<CPR>(row, pc);
+        const u32x2 codes = *(const __attribute__((address_space(3))) u32x2*)(
+            lds + SBASE + slot(t, s) * TBK + row * D + lc * 8);
+        u32x4 w;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t biased = codes[h] ^ 0x80808080u;
+          w[2 * h] = __builtin_amdgcn_perm(0x64646464u, biased, 0x04010400u);
+          w[2 * h + 1] = __builtin_amdgcn_perm(0x64646464u, biased, 0x04030402u);
+        }
+        const h16x8 v = __builtin_bit_cast(h16x8, w) - (_Float16)1152.0f;
+        *(__attribute__((address_space(3))) u32x4*)(lds + VBASE + slot(t, s) * TBYTES + lin * 16) =
+            __builtin_bit_cast(u32x4, v);
+      }
+    }
+  };
+
+  auto probs = [&](const f32x16 (&sc)[KB], X8 (&pf)[ST], float m, float cl) -> float {
     // A causal row that has seen no key yet has m = -inf and only masked
     // logits; reference 0 gives them p = 0 rather than NaN.
     if constexpr (CAUSAL) m = m == -INFINITY ? 0.0f : m;
@@ -455,13 +598,13 @@ fa2_fwd_kernel(const Problem P) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i0 = (st & 1) * 8 + 2 * e;
-        const float x0 = __builtin_fmaf(sc[st >> 1][i0], c, -m);
-        const float x1 = __builtin_fmaf(sc[st >> 1][i0 + 1], c, -m);
+        const float x0 = __builtin_fmaf(sc[st >> 1][i0], cl, -m);
+        const float x1 = __builtin_fmaf(sc[st >> 1][i0 + 1], cl, -m);
         const float p0 = __builtin_amdgcn_exp2f(x0);
         const float p1 = __builtin_amdgcn_exp2f(x1);
         rs += p0;
         rs += p1;
-        const X2 pair = {(E)p0, (E)p1};
+        const X2 pair = {(EP)p0, (EP)p1};
         w[e] = __builtin_bit_cast(uint32_t, pair);
       }
       pf[st] = __builtin_bit_cast(X8, w);
@@ -472,14 +615,17 @@ fa2_fwd_kernel(const Problem P) {
   // One iteration j, as a single straight-line block for the scheduler:
   // S_{j+1} = K_{j+1} Q^T and O += P_{j-1} V_{j-1} on the matrix cores while
   // the VALU turns S_j into P_j.  The loads issued here are K_{j+RING} and
-  // V_{j+RING-2}; each goes to the ring slot whose previous tile (K_j,
-  // V_{j-2}) was last read before the barrier that ended iteration j-1.
+  // V_{j+VAHEAD}; each goes to the ring slot whose previous tile (K_j;
+  // V_{j-2}, or the int8 V_{j-1} widened during iteration j-2) was last read
+  // before the barrier that ended iteration j-1.  With Q8 the iteration also
+  // widens V_{j+1} (staged during iteration j-2) into its slot of the V ring,
+  // whose previous tile V_{j-3} was last read in iteration j-2.
   // With RING = 4 the iteration then reads the first operands of iteration
   // j+1 (K_{j+2}, V_j: loaded during iteration j-2 and published by the last
   // barrier) and waits only for the loads issued during iteration j-1.  The
   // last iteration's S_{j+1} product reads a tile past the end and is
   // dropped.  `ph` is j % 4.
-  auto step = [&](auto first, auto ph, int j, f32x16 (&s_cur)[QB][KB], f32x16 (&s_nxt)[QB][KB],
+  auto step = [&](auto first, auto ph, int j, SAcc (&s_cur)[QB][KB], SAcc (&s_nxt)[QB][KB],
                   const X8 (&p_prev)[QB][ST], X8 (&p_cur)[QB][ST]) {
     constexpr int p = decltype(ph)::value;
     using S0 = Ic<p>;
@@ -488,7 +634,26 @@ fa2_fwd_kernel(const Problem P) {
     using S3 = Ic<(p + 3) % 4>;
     // (RING = 2 skips loads past the end: at d = 256 that keeps it from spilling)
     if (RING == 4 || j + RING < n_tiles) issue_k(j + RING, S0{});
-    issue_v(j + RING - 2, Ic<(p + RING - 2) % 4>{});
+    issue_v(j + VAHEAD, Ic<(p + VAHEAD) % 4>{});
+    convert_v(j + 1, S1{});
+
+    // The logits of this tile in fp32 (converted from the int32 products
+    // with Q8).
+    f32x16 s_conv[Q8 ? QB : 1][Q8 ? KB : 1];
+    if constexpr (Q8) {
+#pragma unroll
+      for (int b = 0; b < QB; ++b)
+#pragma unroll
+        for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) s_conv[b][kk][i] = (float)s_cur[b][kk][i];
+    }
+    auto& sf = [&]() -> auto& {
+      if constexpr (Q8)
+        return s_conv;
+      else
+        return s_cur;
+    }();
 
     // Mask keys past N and, with the causal option, keys past a row's
     // diagonal (key > row + causal_off).  Decided per wave, from its
@@ -505,7 +670,7 @@ fa2_fwd_kernel(const Problem P) {
 #pragma unroll
           for (int i = 0; i < 16; ++i)
             if (key0 + kk * 32 + (i >> 2) * 8 + half * 4 + (i & 3) > lim)
-              s_cur[b][kk][i] = MODE == kNegative ? INFINITY : -INFINITY;
+              sf[b][kk][i] = MODE == kNegative ? INFINITY : -INFINITY;
       }
     }
 
@@ -515,7 +680,7 @@ fa2_fwd_kernel(const Problem P) {
     bool over = false;
 #pragma unroll
     for (int b = 0; b < QB; ++b) {
-      rs[b] = probs(s_cur[b], p_cur[b], m_ref[b]);
+      rs[b] = probs(sf[b], p_cur[b], m_ref[b], c_q[b]);
       over |= !(rs[b] <= kSumLimit);  // also true for inf / NaN
       // Causal rows that see no key keep m_ref = -inf; they take the rare
       // path, which leaves their p at 0.
@@ -523,7 +688,7 @@ fa2_fwd_kernel(const Problem P) {
     }
     constexpr int MF = QB * ((MODE == kZero ? 0 : KO) + (decltype(first)::value ? 0 : VO));
 #pragma unroll
-    for (int t = 0; t < (Cfg<D>::SGB ? MF : 0); ++t) {
+    for (int t = 0; t < (C::SGB ? MF : 0); ++t) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
       __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
@@ -544,13 +709,13 @@ fa2_fwd_kernel(const Problem P) {
     if (__builtin_amdgcn_ballot_w64(over) != 0) {
 #pragma unroll
       for (int b = 0; b < QB; ++b) {
-        float ext = s_cur[b][0][0];
+        float ext = sf[b][0][0];
 #pragma unroll
         for (int kk = 0; kk < KB; ++kk)
 #pragma unroll
           for (int i = 0; i < 16; ++i)
-            ext = MODE == kNegative ? fminf(ext, s_cur[b][kk][i]) : fmaxf(ext, s_cur[b][kk][i]);
-        const float t_max = __builtin_isfinite(ext) ? ext * c : -INFINITY;
+            ext = MODE == kNegative ? fminf(ext, sf[b][kk][i]) : fmaxf(ext, sf[b][kk][i]);
+        const float t_max = __builtin_isfinite(ext) ? ext * c_q[b] : -INFINITY;
         const float t_row = fmaxf(t_max, __shfl_xor(t_max, 32));
         const float mine = !(rs[b] <= kSumLimit) ? 1.0f : 0.0f;
         // a row still at -inf takes its first reference from any visible key
@@ -564,7 +729,7 @@ fa2_fwd_kernel(const Problem P) {
           for (int i = 0; i < 16; ++i) acc[b][db][i] *= alpha;
         l_part[b] *= alpha;
         m_ref[b] = m_new;
-        rs[b] = probs(s_cur[b], p_cur[b], m_ref[b]);
+        rs[b] = probs(sf[b], p_cur[b], m_ref[b], c_q[b]);
       }
     }
 #pragma unroll
@@ -586,9 +751,10 @@ fa2_fwd_kernel(const Problem P) {
     if constexpr (RING == 4) {
       issue_k(2, Ic<2>{});
       issue_k(3, Ic<3>{});
-      issue_v(0, Ic<0>{});
-      issue_v(1, Ic<1>{});
     }
+    if constexpr (VAHEAD > 0) issue_v(0, Ic<0>{});
+    if constexpr (VAHEAD > 1) issue_v(1, Ic<1>{});
+    if constexpr (VAHEAD > 2) issue_v(2, Ic<2>{});
 #pragma unroll
     for (int b = 0; b < QB; ++b)
 #pragma unroll
@@ -596,8 +762,9 @@ fa2_fwd_kernel(const Problem P) {
     wait_vmem();
     __syncthreads();
 
-    f32x16 sA[QB][KB], sB[QB][KB];
+    SAcc sA[QB][KB], sB[QB][KB];
     X8 pA[QB][ST], pB[QB][ST];
+    convert_v(0, Ic<0>{});  // Q8: V_0 widened; published by the barrier below
     prefetch_k(0, Ic<0>{}, kpre);
     gemm1(0, Ic<0>{}, kpre, sA);
     prefetch_k(1, Ic<1>{}, kpre);
@@ -658,10 +825,17 @@ fa2_fwd_kernel(const Problem P) {
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
+          const int ch = db * 32 + g4 * 8 + half * 4;  // output channels ch .. ch+3
+          float vsc[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+          if constexpr (Q8) {  // the per-channel value scales of the INT8 cache
+            const float4 f = *(const float4*)(P.vs + (int64_t)bh * D + ch);
+            vsc[0] = f.x; vsc[1] = f.y; vsc[2] = f.z; vsc[3] = f.w;
+          }
           X4 ov;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) ov[e] = (E)(acc[b][db][g4 * 4 + e] * inv);
-          *(u32x2*)(orow + db * 32 + g4 * 8 + half * 4) = __builtin_bit_cast(u32x2, ov);
+          for (int e = 0; e < 4; ++e)
+            ov[e] = (E)(Q8 ? acc[b][db][g4 * 4 + e] * vsc[e] * inv : acc[b][db][g4 * 4 + e] * inv);
+          *(u32x2*)(orow + ch) = __builtin_bit_cast(u32x2, ov);
         }
       if (half == 0)
         P.lse[(int64_t)bh * P.rows + qrow] =
@@ -672,19 +846,20 @@ fa2_fwd_kernel(const Problem P) {
 
 typedef void (*kernel_fn)(const Problem);
 
-template <int D, bool FP16, bool CAUSAL>
+template <int D, bool FP16, bool CAUSAL, bool Q8>
 kernel_fn pick_mode(int mode) {
   switch (mode) {
-    case kNegative: return fa2_fwd_kernel<D, FP16, kNegative, CAUSAL>;
-    case kZero: return fa2_fwd_kernel<D, FP16, kZero, CAUSAL>;
-    default: return fa2_fwd_kernel<D, FP16, kPositive, CAUSAL>;
+    case kNegative: return fa2_fwd_kernel<D, FP16, kNegative, CAUSAL, Q8>;
+    case kZero: return fa2_fwd_kernel<D, FP16, kZero, CAUSAL, Q8>;
+    default: return fa2_fwd_kernel<D, FP16, kPositive, CAUSAL, Q8>;
   }
 }
 
-template <int D>
+template <int D, bool Q8>
 kernel_fn pick(bool fp16, int mode, bool causal) {
-  if (fp16) return causal ? pick_mode<D, true, true>(mode) : pick_mode<D, true, false>(mode);
-  return causal ? pick_mode<D, false, true>(mode) : pick_mode<D, false, false>(mode);
+  if (fp16)
+    return causal ? pick_mode<D, true, true, Q8>(mode) : pick_mode<D, true, false, Q8>(mode);
+  return causal ? pick_mode<D, false, true, Q8>(mode) : pick_mode<D, false, false, Q8>(mode);
 }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -725,11 +900,17 @@ int fa2_tile_config(int64_t d, int dtype, int* block_q, int* block_k, int* waves
   return FA2_OK;
 }
 
-int fa2_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse,
-                int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
-                float scale, int causal, int dtype, void* stream) {
+}  // extern "C"
+
+namespace fa2 {
+
+// Validation and launch shared by the entry points.  q8 selects the INT8
+// key/value cache (k, v int8 codes; ks, vs their per-channel scales).
+int launch(const void* q, const void* k, const void* v, const float* ks, const float* vs,
+           void* o, float* lse, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
+           int64_t d, float scale, int causal, int dtype, void* stream, bool q8) {
   if (dtype != FA2_BF16 && dtype != FA2_FP16) return FA2_ERR_DTYPE;
-  if (d != 64 && d != 128 && d != 256) return FA2_ERR_HEADDIM;
+  if (q8 ? d != 128 : (d != 64 && d != 128 && d != 256)) return FA2_ERR_HEADDIM;
   if (causal != 0 && causal != 1) return FA2_ERR_OPTION;
   if (B < 0 || Hq < 0 || Hkv < 0 || Nq < 0 || Nk < 0) return FA2_ERR_SHAPE;
   if (!__builtin_isfinite(scale)) return FA2_ERR_SCALE;
@@ -745,48 +926,78 @@ int fa2_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse
   const int64_t rows = group * Nq;  // query rows per K/V head
   int bq = 0, bk = 0, nw = 0;
   fa2_tile_config(d, dtype, &bq, &bk, &nw);
+  if (q8) {
+    bq = Cfg8<128>::NW * 32 * Cfg8<128>::QB;
+    nw = Cfg8<128>::NW;
+  }
   const int64_t q_tiles = (rows + bq - 1) / bq;
   if (B > (((int64_t)1 << 31) - 1) / Hq) return FA2_ERR_SHAPE;
   const int64_t bh = B * Hq;
   if (B * Hkv > (((int64_t)1 << 31) - 1) / q_tiles) return FA2_ERR_SHAPE;
   const int64_t groups = B * Hkv * q_tiles;
   if (!q || !o || !lse || (Nk > 0 && (!k || !v))) return FA2_ERR_NULL;
+  if (q8 && (!ks || !vs)) return FA2_ERR_NULL;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return FA2_ERR_ALIGN;
+  if (((uintptr_t)ks | (uintptr_t)vs) & 15) return FA2_ERR_ALIGN;
   if ((uintptr_t)lse & 3) return FA2_ERR_ALIGN;
   const size_t qbytes = (size_t)(bh * Nq * d) * 2;
-  const size_t kbytes = (size_t)(B * Hkv * Nk * d) * 2;
+  const size_t kbytes = (size_t)(B * Hkv * Nk * d) * (q8 ? 1 : 2);
+  const size_t sbytes = q8 ? (size_t)(B * Hkv * d) * 4 : 0;
   const size_t lbytes = (size_t)(bh * Nq) * 4;
-  if (fa2::overlaps(o, qbytes, q, qbytes) || fa2::overlaps(o, qbytes, k, kbytes) ||
-      fa2::overlaps(o, qbytes, v, kbytes) || fa2::overlaps(lse, lbytes, q, qbytes) ||
-      fa2::overlaps(lse, lbytes, k, kbytes) || fa2::overlaps(lse, lbytes, v, kbytes) ||
-      fa2::overlaps(lse, lbytes, o, qbytes))
-    return FA2_ERR_ALIAS;
+  const void* in[5] = {q, k, v, ks, vs};
+  const size_t in_bytes[5] = {qbytes, kbytes, kbytes, sbytes, sbytes};
+  for (int i = 0; i < 5; ++i)
+    if (overlaps(o, qbytes, in[i], in_bytes[i]) || overlaps(lse, lbytes, in[i], in_bytes[i]))
+      return FA2_ERR_ALIAS;
+  if (overlaps(lse, lbytes, o, qbytes)) return FA2_ERR_ALIAS;
 
   // logits in log2 units: t = s * scale * log2(e)
   const float c = (float)((double)scale * 1.4426950408889634074);
   const bool fp16 = dtype == FA2_FP16;
-  const int mode = c > 0.0f ? fa2::kPositive : c < 0.0f ? fa2::kNegative : fa2::kZero;
-  fa2::Problem P;
+  const int mode = c > 0.0f ? kPositive : c < 0.0f ? kNegative : kZero;
+  Problem P;
   P.q = (const uint16_t*)q;
-  P.k = (const uint16_t*)k;
-  P.v = (const uint16_t*)v;
+  P.k = (const char*)k;
+  P.v = (const char*)v;
   P.o = (uint16_t*)o;
   P.lse = lse;
+  P.ks = ks;
+  P.vs = vs;
   P.nq = (int)Nq;
   P.nk = (int)Nk;
   P.rows = (int)rows;
   P.q_tiles = (int)q_tiles;
   P.n_groups = (int)groups;
   P.causal_off = (int)(Nk - Nq);
-  P.c = mode == fa2::kZero ? 1.0f : c;  // zero mode: logits are 0, t = s
-  fa2::kernel_fn fn = d == 64 ? fa2::pick<64>(fp16, mode, causal)
-                    : d == 128 ? fa2::pick<128>(fp16, mode, causal)
-                               : fa2::pick<256>(fp16, mode, causal);
+  P.c = mode == kZero ? 1.0f : c;  // zero mode: logits are 0, t = s
+  kernel_fn fn = q8 ? pick<128, true>(fp16, mode, causal)
+               : d == 64 ? pick<64, false>(fp16, mode, causal)
+               : d == 128 ? pick<128, false>(fp16, mode, causal)
+                          : pick<256, false>(fp16, mode, causal);
   void* args[] = {&P};
   hipError_t err = hipLaunchKernel((const void*)fn, dim3((unsigned)groups),
                                    dim3((unsigned)(nw * 64)), args, 0,
                                    (hipStream_t)stream);
   return err == hipSuccess ? FA2_OK : FA2_ERR_HIP;
+}
+
+}  // namespace fa2
+
+extern "C" {
+
+int fa2_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse,
+                int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
+                float scale, int causal, int dtype, void* stream) {
+  return fa2::launch(q, k, v, nullptr, nullptr, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal,
+                     dtype, stream, false);
+}
+
+int fa2_fwd_kv_int8(const void* q, const int8_t* kq, const float* ks, const int8_t* vq,
+                    const float* vs, void* o, float* lse, int64_t B, int64_t Hq, int64_t Hkv,
+                    int64_t Nq, int64_t Nk, int64_t d, float scale, int causal, int dtype,
+                    void* stream) {
+  return fa2::launch(q, kq, vq, ks, vs, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, dtype,
+                     stream, true);
 }
 
 int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse,

@@ -40,6 +40,7 @@ class Workload:
     Hkv: int = 0
     Nk: int = 0
     causal: bool = False
+    kv_int8: bool = False   # keys/values as an INT8 cache (int8 codes, fp32 channel scales)
 
     @property
     def kv_heads(self) -> int:
@@ -78,7 +79,10 @@ class Workload:
         """Q, K, V read once and O written once (16-bit), LSE written (fp32)."""
         q = self.B * self.H * self.N * self.d
         kv = self.B * self.kv_heads * self.keys * self.d
-        return 2 * (2 * q + 2 * kv) + self.B * self.H * self.N * 4
+        lse = self.B * self.H * self.N * 4
+        if self.kv_int8:  # 1-byte codes plus two fp32 scales per K/V channel
+            return 2 * 2 * q + 2 * kv + 2 * 4 * self.B * self.kv_heads * self.d + lse
+        return 2 * (2 * q + 2 * kv) + lse
 
     def describe(self) -> dict:
         out = {"workload": self.name, "B": self.B, "H": self.H, "N": self.N,
@@ -88,6 +92,8 @@ class Workload:
             out["Hkv"] = self.kv_heads
         if self.keys != self.N:
             out["Nk"] = self.keys
+        if self.kv_int8:
+            out["kv"] = "int8 codes, fp32 per-channel scales"
         return out
 
 
@@ -113,6 +119,10 @@ WORKLOADS = {
     # a 64-row prefill chunk against a 4096-key cache, 4 query heads per K/V
     # head: the rows of a K/V head's query heads share workgroups
     "gqa_chunk": Workload("gqa_chunk", 16, 32, 64, 128, "bf16", Hkv=8, Nk=4096, causal=True),
+    # the headline shape over an INT8 key/value cache
+    "int8_kv": Workload("int8_kv", 4, 16, 4096, 128, "bf16", kv_int8=True),
+    "int8_kv_causal": Workload("int8_kv_causal", 4, 16, 4096, 128, "bf16", causal=True,
+                               kv_int8=True),
 }
 
 
@@ -160,6 +170,9 @@ def make_inputs_kv_int8(B, Hq, Hkv, Nq, Nk, d, dtype="bf16", seed=0):
 
 
 def workload_inputs(w: Workload, seed=0):
+    """(q, k, v), or (q, kq, ks, vq, vs) for an INT8 cache workload."""
+    if w.kv_int8:
+        return make_inputs_kv_int8(w.B, w.H, w.kv_heads, w.N, w.keys, w.d, w.dtype, seed)
     return make_inputs(w.B, w.H, w.N, w.d, w.dtype, w.dist, seed, w.kv_heads, w.keys)
 
 

@@ -46,7 +46,7 @@ enum fa2_status {
                            the grid overflows, or the query rows of one K/V
                            head ((Hq/Hkv)*Nq*d) or its key rows (Nk*d) exceed
                            2^31 - 2^20 elements */
-  FA2_ERR_HEADDIM = -3, /* d is not 64, 128 or 256 */
+  FA2_ERR_HEADDIM = -3, /* d is not 64, 128 or 256 (128 for fa2_fwd_kv_int8) */
   FA2_ERR_DTYPE = -4,   /* dtype is not an fa2_dtype */
   FA2_ERR_ALIGN = -5,   /* q, k, v or o not 16-byte aligned, lse not 4-byte */
   FA2_ERR_SCALE = -6,   /* scale is NaN or infinite */
@@ -118,6 +118,43 @@ int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa2_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse,
                 int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
                 int64_t d, float scale, int causal, int dtype, void* stream);
+
+/*
+ * fa2_fwd_kv_int8 -- attention over an INT8 key/value cache.  The Colfax
+ * author page lists "FlashAttention-3 for Inference: INT8 Quantization and
+ * Query Head Packing for MQA/GQA" by title only; this is the library's
+ * reading of it.  Keys and values arrive as int8 codes with fp32 per-channel
+ * scales of their key/value head:
+ *
+ *     k[b,g,j,c] = ks[b,g,c] * kq[b,g,j,c],   v[b,g,j,c] = vs[b,g,c] * vq[b,g,j,c].
+ *
+ * Each query row is quantized to int8 inside the kernel after the key scales
+ * are folded into it, every step in IEEE binary32 with round-half-to-even:
+ *
+ *     u[c]  = q[c] * ks[c],   amax = max_c |u[c]|,
+ *     qq[c] = clamp(rint(u[c] * (127 / amax)), -127, 127),   sq = amax / 127
+ *     (a zero row: qq = 0, sq = 0),
+ *
+ * and s_j = scale * sq * sum_c qq[c] * kq[j][c] (an exact integer dot product
+ * on int8 matrix instructions).  The softmax, O and lse then follow fa2_fwd
+ * with the dequantized v; P and V meet on fp16 matrix instructions (V widened
+ * exactly), O is written in `dtype`.
+ *
+ *   q, o     : [B][Hq][Nq][d], element type `dtype` (bf16 or fp16).
+ *   kq, vq   : [B][Hkv][Nk][d] int8 codes (may be NULL when Nk == 0).
+ *   ks, vs   : [B][Hkv][d] fp32 scales (required).
+ *   lse      : [B][Hq][Nq] fp32.
+ *   d        : 128 (FA2_ERR_HEADDIM otherwise).
+ *   Alignment: q, kq, vq, o, ks, vs 16-byte aligned, lse 4-byte.  No output
+ *   may overlap an input or the other output.
+ *
+ * Heads, lengths, causal, packing of query heads, asynchrony and return codes
+ * are those of fa2_fwd_ext.
+ */
+int fa2_fwd_kv_int8(const void* q, const int8_t* kq, const float* ks, const int8_t* vq,
+                    const float* vs, void* o, float* lse, int64_t B, int64_t Hq, int64_t Hkv,
+                    int64_t Nq, int64_t Nk, int64_t d, float scale, int causal, int dtype,
+                    void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* fa2_strerror(int status);

@@ -28,8 +28,8 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["fa2_fwd", "fa2_fwd_ext", "fa2_strerror",
-                                    "fa2_tile_config"]
+    assert declared_functions() == ["fa2_fwd", "fa2_fwd_ext", "fa2_fwd_kv_int8",
+                                    "fa2_strerror", "fa2_tile_config"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -128,3 +128,37 @@ def test_ext_host_validation(lib, kw, code):
 @pytest.mark.parametrize("kw", [dict(B=0), dict(Hq=0, Hkv=0), dict(Nq=0)])
 def test_ext_empty_output_is_a_no_op(lib, kw):
     assert call_ext(q=0, k=0, v=0, o=0, lse=0, **kw) == fa2.OK
+
+
+# fa2_fwd_kv_int8: q, kq, ks, vq, vs, o, lse (fake pointers, never dereferenced)
+I8 = dict(B=2, Hq=4, Hkv=2, Nq=100, Nk=70, d=128, scale=0.1, causal=0, dtype=fa2.BF16)
+I8_PTRS = dict(q=A, kq=A + 0x1000000, ks=A + 0x2000000, vq=A + 0x3000000, vs=A + 0x4000000,
+               o=A + 0x5000000, lse=A + 0x6000000)
+
+
+def call_int8(**kw):
+    p = dict(I8)
+    p.update(I8_PTRS)
+    p.update(kw)
+    return fa2.fwd_kv_int8_raw(p["q"], p["kq"], p["ks"], p["vq"], p["vs"], p["o"], p["lse"],
+                               p["B"], p["Hq"], p["Hkv"], p["Nq"], p["Nk"], p["d"], p["scale"],
+                               p["causal"], p["dtype"], 0)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=64), fa2.ERR_HEADDIM), (dict(d=256), fa2.ERR_HEADDIM), (dict(dtype=3), fa2.ERR_DTYPE),
+    (dict(causal=2), fa2.ERR_OPTION), (dict(Hkv=3), fa2.ERR_SHAPE), (dict(Nk=-1), fa2.ERR_SHAPE),
+    (dict(q=0), fa2.ERR_NULL), (dict(kq=0), fa2.ERR_NULL), (dict(ks=0), fa2.ERR_NULL),
+    (dict(vs=0), fa2.ERR_NULL), (dict(ks=0, Nk=0), fa2.ERR_NULL),
+    (dict(ks=A + 0x2000004), fa2.ERR_ALIGN), (dict(vq=A + 0x3000008), fa2.ERR_ALIGN),
+    (dict(o=A + 0x2000000 + 256), fa2.ERR_ALIAS),   # o over ks
+    (dict(lse=A + 0x4000000), fa2.ERR_ALIAS),       # lse over vs
+    (dict(scale=float("inf")), fa2.ERR_SCALE),
+])
+def test_int8_host_validation(lib, kw, code):
+    assert call_int8(**kw) == code
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(Hq=0, Hkv=0), dict(Nq=0)])
+def test_int8_empty_output_is_a_no_op(lib, kw):
+    assert call_int8(q=0, kq=0, ks=0, vq=0, vs=0, o=0, lse=0, **kw) == fa2.OK

@@ -1,0 +1,105 @@
+"""GPU parity of fa2_fwd_kv_int8 (attention over an INT8 key/value cache)
+against the fp64 oracle's INT8 function (needs an MI355X).
+
+The query codes are an integer decision both sides take in binary32, so the
+kernel and the oracle compute the same quantized attention and differ only by
+floating-point rounding: the tolerances are those of the 16-bit path."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from flashattention_forward_tile_amd import fa2
+from flashattention_forward_tile_amd.workloads import bits, make_inputs_kv_int8
+from parity import assert_parity, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def announce(*what):
+    print("CASE", *what, flush=True)
+
+
+def run_gpu(q, kq, ks, vq, vs, scale, causal):
+    o, lse = fa2.fwd_kv_int8(q.to(DEV), kq.to(DEV), ks.to(DEV), vq.to(DEV), vs.to(DEV),
+                             scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+def check(inputs, dtype, scale, causal, tag, rows=None):
+    q, kq, ks, vq, vs = inputs
+    o, lse = run_gpu(q, kq, ks, vq, vs, scale, causal)
+    o_ref, lse_ref = oracle.attention_kv_int8(bits(q), kq.numpy(), ks.numpy(), vq.numpy(),
+                                              vs.numpy(), dtype, scale, rows=rows, causal=causal)
+    d = q.shape[-1]
+    og = o.double().numpy() if rows is None else o.double().numpy().reshape(-1, d)[rows]
+    lg = lse.double().numpy() if rows is None else lse.double().numpy().reshape(-1)[rows]
+    seen = np.isfinite(lse_ref)
+    assert np.all(og[~seen] == 0.0) and np.all(lg[~seen] == -np.inf), tag
+    assert_parity(og[seen], lg[seen], o_ref[seen], lse_ref[seen], tag, lse_abs=1e-3)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk", [
+    (1, 2, 2, 64, 64), (1, 2, 1, 100, 300), (2, 4, 2, 257, 513), (1, 8, 1, 5, 1000),
+    (1, 2, 2, 1, 1), (1, 3, 3, 300, 90), (1, 4, 4, 32, 33)])
+def test_int8_cache(B, Hq, Hkv, Nq, Nk, dtype, causal):
+    announce("int8", B, Hq, Hkv, Nq, Nk, dtype, causal)
+    inputs = make_inputs_kv_int8(B, Hq, Hkv, Nq, Nk, 128, dtype, seed=Nq + 7 * Nk + Hq)
+    check(inputs, dtype, 1.0 / math.sqrt(128), causal,
+          "int8 B=%d Hq=%d Hkv=%d Nq=%d Nk=%d %s causal=%d" % (B, Hq, Hkv, Nq, Nk, dtype, causal))
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.2, 1.5])
+@pytest.mark.parametrize("causal", [False, True])
+def test_int8_scales(scale, causal):
+    announce("int8 scale", scale, causal)
+    inputs = make_inputs_kv_int8(1, 4, 2, 200, 333, 128, "bf16", seed=3)
+    check(inputs, "bf16", scale, causal, "int8 scale=%g causal=%d" % (scale, causal))
+
+
+def test_int8_zero_query_rows():
+    """Rows of zeros quantize to zero codes and sq = 0: uniform attention over
+    the dequantized values (also under the causal mask and with tail keys)."""
+    announce("int8 zero rows")
+    q, kq, ks, vq, vs = make_inputs_kv_int8(1, 2, 1, 70, 130, 128, "bf16", seed=8)
+    q[:, :, ::3] = 0
+    for causal in (False, True):
+        check((q, kq, ks, vq, vs), "bf16", 0.1, causal, "int8 zero rows causal=%d" % causal)
+
+
+def test_int8_no_keys():
+    announce("int8 Nk=0")
+    q, _, ks, _, vs = make_inputs_kv_int8(1, 2, 2, 40, 1, 128, "fp16", seed=1)
+    empty = torch.empty((1, 2, 0, 128), dtype=torch.int8, device=DEV)
+    for causal in (False, True):
+        o, lse = fa2.fwd_kv_int8(q.to(DEV), empty, ks.to(DEV), empty.clone(), vs.to(DEV),
+                                 causal=causal)
+        torch.cuda.synchronize()
+        assert torch.all(o == 0) and torch.all(lse == -float("inf"))
+
+
+def test_int8_deterministic():
+    announce("int8 determinism")
+    inputs = [t.to(DEV) for t in make_inputs_kv_int8(2, 8, 2, 600, 700, 128, "bf16", seed=4)]
+    o1, l1 = fa2.fwd_kv_int8(*inputs, causal=True)
+    o2, l2 = fa2.fwd_kv_int8(*inputs, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_int8_headline_sampled(causal):
+    """B=4, H=16, N=4096, d=128, bf16 query over an INT8 cache, sampled rows
+    (first, last, both sides of a query tile boundary, random)."""
+    announce("int8 headline", causal)
+    inputs = make_inputs_kv_int8(4, 16, 16, 4096, 4096, 128, "bf16", seed=0)
+    bq, _, _ = fa2.tile_config(128)
+    check(inputs, "bf16", 1.0 / math.sqrt(128), causal, "int8 headline causal=%d" % causal,
+          rows=sample_rows(4, 16, 4096, bq, per_head=4, seed=2))
