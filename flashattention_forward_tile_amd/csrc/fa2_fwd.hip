@@ -173,7 +173,14 @@ template <> struct Cfg<256> { static constexpr int BC = 32, NW = 4, QB = 1, OCC 
 // Tile shape of the INT8 key/value cache kernels (d = 128 only).
 template <int D> struct Cfg8;
 template <> struct Cfg8<128> { static constexpr int BC = 32, NW = 8, QB = 1, OCC = 2, SGB = 0, RING = 4, PK = 2, PV = 2; };
-template <int D, bool Q8> using KCfg = std::conditional_t<Q8, Cfg8<D>, Cfg<D>>;
+// Short key sequences at d = 128 (at most kShortKeys keys): half the query
+// rows per workgroup, so two workgroups share a CU and one's prologue and
+// epilogue overlap the other's loop.
+template <int D> struct CfgS;
+template <> struct CfgS<128> { static constexpr int BC = 32, NW = 4, QB = 1, OCC = 2, SGB = 0, RING = 4, PK = 4, PV = 2; };
+constexpr int kShortKeys = 1024;
+template <int D, bool Q8, bool SHORT>
+using KCfg = std::conditional_t<Q8, Cfg8<D>, std::conditional_t<SHORT, CfgS<D>, Cfg<D>>>;
 // Ring slots and loop phases as compile-time constants.
 template <int X> using Ic = std::integral_constant<int, X>;
 
@@ -213,12 +220,13 @@ struct Problem {
 // per-channel scales; the first product runs on int8 matrix instructions
 // against the in-kernel quantized query, and V is widened to fp16 in LDS for
 // the second product (see the header of fa2.h for the scheme).
-template <int D, bool FP16, int MODE, bool CAUSAL, bool Q8>
-__global__ void __attribute__((amdgpu_flat_work_group_size(KCfg<D, Q8>::NW * 64,
-                                                           KCfg<D, Q8>::NW * 64),
-                               amdgpu_waves_per_eu(KCfg<D, Q8>::OCC, KCfg<D, Q8>::OCC)))
+template <int D, bool FP16, int MODE, bool CAUSAL, bool Q8, bool SHORT>
+__global__ void __attribute__((amdgpu_flat_work_group_size(KCfg<D, Q8, SHORT>::NW * 64,
+                                                           KCfg<D, Q8, SHORT>::NW * 64),
+                               amdgpu_waves_per_eu(KCfg<D, Q8, SHORT>::OCC,
+                                                   KCfg<D, Q8, SHORT>::OCC)))
 fa2_fwd_kernel(const Problem P) {
-  using C = KCfg<D, Q8>;
+  using C = KCfg<D, Q8, SHORT>;
   const int N = P.nk;  // keys per head
   const float c = P.c;
   constexpr int BC = C::BC;
@@ -846,20 +854,22 @@ fa2_fwd_kernel(const Problem P) {
 
 typedef void (*kernel_fn)(const Problem);
 
-template <int D, bool FP16, bool CAUSAL, bool Q8>
+template <int D, bool FP16, bool CAUSAL, bool Q8, bool SHORT>
 kernel_fn pick_mode(int mode) {
   switch (mode) {
-    case kNegative: return fa2_fwd_kernel<D, FP16, kNegative, CAUSAL, Q8>;
-    case kZero: return fa2_fwd_kernel<D, FP16, kZero, CAUSAL, Q8>;
-    default: return fa2_fwd_kernel<D, FP16, kPositive, CAUSAL, Q8>;
+    case kNegative: return fa2_fwd_kernel<D, FP16, kNegative, CAUSAL, Q8, SHORT>;
+    case kZero: return fa2_fwd_kernel<D, FP16, kZero, CAUSAL, Q8, SHORT>;
+    default: return fa2_fwd_kernel<D, FP16, kPositive, CAUSAL, Q8, SHORT>;
   }
 }
 
-template <int D, bool Q8>
+template <int D, bool Q8, bool SHORT = false>
 kernel_fn pick(bool fp16, int mode, bool causal) {
   if (fp16)
-    return causal ? pick_mode<D, true, true, Q8>(mode) : pick_mode<D, true, false, Q8>(mode);
-  return causal ? pick_mode<D, false, true, Q8>(mode) : pick_mode<D, false, false, Q8>(mode);
+    return causal ? pick_mode<D, true, true, Q8, SHORT>(mode)
+                  : pick_mode<D, true, false, Q8, SHORT>(mode);
+  return causal ? pick_mode<D, false, true, Q8, SHORT>(mode)
+                : pick_mode<D, false, false, Q8, SHORT>(mode);
 }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -926,9 +936,13 @@ int launch(const void* q, const void* k, const void* v, const float* ks, const f
   const int64_t rows = group * Nq;  // query rows per K/V head
   int bq = 0, bk = 0, nw = 0;
   fa2_tile_config(d, dtype, &bq, &bk, &nw);
+  const bool short_keys = !q8 && d == 128 && Nk <= kShortKeys;
   if (q8) {
     bq = Cfg8<128>::NW * 32 * Cfg8<128>::QB;
     nw = Cfg8<128>::NW;
+  } else if (short_keys) {
+    bq = CfgS<128>::NW * 32 * CfgS<128>::QB;
+    nw = CfgS<128>::NW;
   }
   const int64_t q_tiles = (rows + bq - 1) / bq;
   if (B > (((int64_t)1 << 31) - 1) / Hq) return FA2_ERR_SHAPE;
@@ -972,7 +986,8 @@ int launch(const void* q, const void* k, const void* v, const float* ks, const f
   P.c = mode == kZero ? 1.0f : c;  // zero mode: logits are 0, t = s
   kernel_fn fn = q8 ? pick<128, true>(fp16, mode, causal)
                : d == 64 ? pick<64, false>(fp16, mode, causal)
-               : d == 128 ? pick<128, false>(fp16, mode, causal)
+               : d == 128 ? (short_keys ? pick<128, false, true>(fp16, mode, causal)
+                                        : pick<128, false>(fp16, mode, causal))
                           : pick<256, false>(fp16, mode, causal);
   void* args[] = {&P};
   hipError_t err = hipLaunchKernel((const void*)fn, dim3((unsigned)groups),

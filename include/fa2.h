@@ -162,8 +162,11 @@ const char* fa2_strerror(int status);
 /*
  * fa2_tile_config -- the tile shape fa2_fwd uses for head dimension d and
  * dtype: *block_q query rows per workgroup, *block_k key rows per K/V tile,
- * *waves wavefronts (of 64 lanes) per workgroup.  Host-only, no HIP call.
- * Returns FA2_OK, FA2_ERR_HEADDIM, FA2_ERR_DTYPE or FA2_ERR_NULL.
+ * *waves wavefronts (of 64 lanes) per workgroup.  At d = 128 a call with at
+ * most 1024 keys uses half the waves and query rows instead (two workgroups
+ * then share a compute unit); block_q here is always a multiple of that.
+ * Host-only, no HIP call.  Returns FA2_OK, FA2_ERR_HEADDIM, FA2_ERR_DTYPE or
+ * FA2_ERR_NULL.
  */
 int fa2_tile_config(int64_t d, int dtype, int* block_q, int* block_k,
                     int* waves);
