@@ -3,11 +3,16 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload headline]
 
 A step is one fa2_fwd (or fa2_fwd_ext, for the causal / grouped-head / unequal
-length workloads) launch over the whole workload (every (b, h) and query row
-of one batch), inputs resident in HBM.  FLOPs count the two products over the
+length workloads; fa2_fwd_kv_int8 for the INT8 cache workloads) launch over the
+whole workload (every (b, h) and query row of one batch), inputs resident in
+HBM.  FLOPs count the two products over the
 (query, key) pairs that enter the softmax: 4*B*H*N^2*d without a mask.  W untimed steps, then exactly K
 steps timed with HIP events on the launch stream, bracketed by device
-synchronisation.  Prints ONE JSON line: forward attention TFLOP/s counting
+synchronisation.  The default warm-up is long (200 launches, about 0.1 s of
+the headline) because per-launch times settle only after roughly the first
+hundred launches of a process (the earliest run up to a third slower while
+the clock settles); the timed steps then measure the steady rate a long job
+sees.  Prints ONE JSON line: forward attention TFLOP/s counting
 4*B*H*N^2*d FLOPs, the roofline of the kernel against the dense bf16/fp16 MFMA
 peak, and the fp64 CPU oracle's rate on a bounded sample of the same workload
 on this host's cores.
@@ -148,8 +153,8 @@ def calibrate_copy(nbytes=1 << 30, reps=5):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
