@@ -45,9 +45,19 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa2_fwd_headline_traffic.json")
 CPU_SAMPLE_SECONDS = 12.0
 
 
+def code_digest(text: str) -> str:
+    """sha256 of C++ source with comments, blank lines and trailing space
+    removed, so a comment-only edit keeps the digest of the same code."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    lines = [ln.rstrip() for ln in text.splitlines() if ln.strip()]
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()
+
+
 def kernel_digest() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    with open(KERNEL_SRC) as f:
+        return code_digest(f.read())
 
 
 def measured_traffic(workload):

@@ -1,33 +1,38 @@
 // fa2_fwd.hip -- FlashAttention-2 forward pass for gfx950 (MI355X, CDNA4).
 //
-// One workgroup owns one (batch, head, query tile) and streams every key/value
-// tile of that head through LDS, keeping the running softmax state and the
-// output accumulator in registers, so the N x N score matrix never reaches
-// HBM (the fusion described in the abstract of "A Case Study in CUDA Kernel
-// Fusion: Implementing FlashAttention-2 on NVIDIA Hopper Architecture using the
+// One workgroup owns one query tile and streams every key/value tile of its
+// K/V head through LDS, keeping the running softmax state and the output
+// accumulator in registers, so the N x N score matrix never reaches HBM (the
+// fusion described in the abstract of "A Case Study in CUDA Kernel Fusion:
+// Implementing FlashAttention-2 on NVIDIA Hopper Architecture using the
 // CUTLASS Library" and in "Flash Attention 2 from scratch on Ampere", Part 1,
 // "Why Flash Attention?").  The per-workgroup flow (query tile held on chip,
 // loop over the j-th key/value tile) follows that page's Notation section.
 //
 // CDNA4 mapping (prior art re-designed, not translated):
-//  * Both products run on v_mfma_f32_32x32x16_{bf16,f16}.  The first product is
-//    computed transposed, S^T = K_j Q_i^T, so each lane of a wave owns one query
-//    column: lanes l and l+32 hold the two halves of that query's keys.  The
-//    row max and row sum of the softmax are then in-lane reductions plus one
-//    exchange between the two lane halves.
+//  * Both products run on 32x32 MFMA.  The first is computed transposed,
+//    S^T = K_j Q_i^T, so each lane of a wave owns one query column: lanes l and
+//    l+32 hold the two halves of that query's keys, and the softmax needs no
+//    cross-lane reduction except one exchange between the two halves.
 //  * The S^T accumulator layout is exactly the B-operand layout of the second
-//    product O^T += V_j^T P^T, once V_j^T is stored in LDS in the matching key
-//    order, so P never leaves registers.
-//  * K_j is staged row-major and V_j transposed into XOR-swizzled LDS (bank
-//    conflicts were the largest single gain in the Ampere series' table,
-//    kernel 2), double-buffered, with tile j+1's global loads in flight while
-//    tile j is computed (kernels 3 and 5 of that table).
+//    product O^T += V_j^T P^T once V_j^T is read in the matching key order,
+//    which ds_read_b64_tr_b16 does from the row-major V tile, so P never
+//    leaves registers.
+//  * K_j and V_j go HBM -> LDS by buffer loads that write LDS directly, into
+//    XOR-swizzled tiles (bank conflicts were the largest single gain in the
+//    Ampere series' table, kernel 2).  At d = 64 and 128 each cycles through a
+//    ring of four slots with loads two iterations ahead of their use and the
+//    next iteration's first operands read before the closing barrier; d = 256
+//    double-buffers (kernels 3 and 5 of that table pipeline one tile ahead).
 //  * Softmax in fp32 registers with exp2 and the scale folded into one FMA
-//    (kernel 6); the running-max rescale of O is skipped unless some row's max
-//    grew by more than kRescaleSlack (log2 units), which keeps the result exact
-//    because every p and l then share the same stale reference max.
-//  * Workgroup ids are remapped so all query tiles of a head land on one XCD
-//    and share that XCD's L2 copy of the head's K and V.
+//    (kernel 6), against a lazy reference max: it moves only when a row's
+//    tile sum of p would exceed kSumLimit, which keeps the result exact
+//    because every p and l then share the same stale reference.
+//  * The query heads that share a K/V head are tiled together (their rows are
+//    adjacent in memory), and workgroup ids are remapped so all query tiles of
+//    a K/V head land on one XCD and share that XCD's L2 copy of its K and V.
+//  * The INT8 key/value cache kernels (Q8) quantize each query row in the
+//    kernel, run the first product on int8 MFMA and widen V to fp16 in LDS.
 
 #include <hip/hip_runtime.h>
 #include <float.h>
