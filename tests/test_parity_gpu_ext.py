@@ -166,3 +166,50 @@ def test_widened_workloads_sampled(name):
     bq, _, _ = fa2.tile_config(w.d)
     check(q, k, v, w.dtype, w.scale, w.causal, w.name,
           rows=sample_rows(w.B, w.H, w.N, bq, per_head=4, seed=4))
+
+
+def test_maximum_key_length():
+    """The largest key length fa2_fwd_ext accepts at d = 128 (Nk*d = 2^31 -
+    2^20 elements, less a ragged 7), so K and V offsets reach the top of their
+    32-bit range.  K and V are a block of 2^20 keys repeated 15 times plus a
+    distinct tail whose last 100 keys line up with the (identical) query rows,
+    so the output hinges on the farthest keys.  Keys that repeat with their
+    values contribute 15 times one block's weights: the expected row merges the
+    oracle's (O, lse) of the block and of the tail with those weights."""
+    Nk = ((1 << 31) - (1 << 20)) // 128 - 7
+    L, R = 1 << 20, 15
+    T = Nk - R * L
+    announce("max key length", Nk)
+    g = torch.Generator().manual_seed(21)
+    qrow = torch.randn(128, generator=g)
+    q = qrow.repeat(1, 1, 64, 1).to(torch.bfloat16)                   # [1, 1, 64, 128]
+    kb = torch.randn((L, 128), generator=g).to(torch.bfloat16)
+    vb = torch.randn((L, 128), generator=g).to(torch.bfloat16)
+    kt = torch.randn((T, 128), generator=g)
+    kt[-100:] = 8.0 * qrow + 0.1 * torch.randn((100, 128), generator=g)
+    kt = kt.to(torch.bfloat16)
+    vt = torch.randn((T, 128), generator=g).to(torch.bfloat16)
+    k = torch.empty((1, 1, Nk, 128), dtype=torch.bfloat16, device=DEV)
+    v = torch.empty_like(k)
+    for r in range(R):
+        k[0, 0, r * L:(r + 1) * L] = kb.to(DEV)
+        v[0, 0, r * L:(r + 1) * L] = vb.to(DEV)
+    k[0, 0, R * L:] = kt.to(DEV)
+    v[0, 0, R * L:] = vt.to(DEV)
+    scale = 1.0 / math.sqrt(128)
+    o, lse = fa2.fwd(q.to(DEV), k, v, scale=scale)
+    torch.cuda.synchronize()
+    o, lse = o.cpu().double().numpy()[0, 0], lse.cpu().double().numpy()[0, 0]
+    del k, v
+    rows = [0, 63]
+    ob, lb = oracle.attention(bits(q), bits(kb[None, None]), bits(vb[None, None]), "bf16", scale,
+                              rows=rows, nthreads=2)
+    ot, lt = oracle.attention(bits(q), bits(kt[None, None]), bits(vt[None, None]), "bf16", scale,
+                              rows=rows, nthreads=2)
+    for n, i in enumerate(rows):
+        m = max(lb[n], lt[n])
+        wb, wt = R * math.exp(lb[n] - m), math.exp(lt[n] - m)
+        o_ref = (wb * ob[n] + wt * ot[n]) / (wb + wt)
+        lse_ref = m + math.log(wb + wt)
+        assert_parity(o[i][None], np.array([lse[i]]), o_ref[None], np.array([lse_ref]),
+                      "max key length row %d" % i, lse_abs=1e-3)
