@@ -279,7 +279,12 @@ fa2_fwd_kernel(const Problem P) {
   // Q8 the int8 V staging ring at SBASE; tiles row-major, K and V swizzled.
   constexpr int VBASE = RING * TBK;
   constexpr int SBASE = VBASE + RING * TBYTES;
-  __shared__ __attribute__((aligned(16))) char smem[SBASE + (Q8 ? RING * TBK : 0)];
+  constexpr int RING_BYTES = SBASE + (Q8 ? RING * TBK : 0);
+  // After the loop the same LDS stages the output: each wave's 32*QB rows of
+  // O, row-major, rows padded by 16 bytes (OROW) against bank conflicts.
+  constexpr int OROW = D * 2 + 16;
+  constexpr int OBYTES = NW * 32 * QB * OROW;
+  __shared__ __attribute__((aligned(16))) char smem[RING_BYTES > OBYTES ? RING_BYTES : OBYTES];
   lds_char* const lds = (lds_char*)smem;
 
   const int tid = threadIdx.x;
@@ -826,34 +831,54 @@ fa2_fwd_kernel(const Problem P) {
   }
 
   // ---- epilogue: O = acc / l, lse = (m_ref + log2 l) * ln 2; a row that saw
-  // no key (l = 0) gets O = 0 and lse = -inf
+  // no key (l = 0) gets O = 0 and lse = -inf.  O goes through LDS so that the
+  // global stores are whole rows: a lane holds 4-element pieces of one row,
+  // which written straight out would be 8-byte pieces of 32 rows per store.
+  // The LDS is reused only once every wave is done with the K and V tiles
+  // and every load into it has landed: the last iterations still load tiles
+  // past the end (waited one iteration late), whose writes must not fall
+  // into the staged output.
+  wait_vmem();
+  __syncthreads();
+  lds_char* const ow = lds + wave * (32 * QB) * OROW;  // this wave's rows
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
     const int qrow = q0 + 32 * b + l32;
     const float l_tot = l_part[b] + __shfl_xor(l_part[b], 32);
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    if (qrow < P.rows) {
-      uint16_t* orow = P.o + q_head + (int64_t)qrow * D;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int ch = db * 32 + g4 * 8 + half * 4;  // output channels ch .. ch+3
-          float vsc[4] = {1.0f, 1.0f, 1.0f, 1.0f};
-          if constexpr (Q8) {  // the per-channel value scales of the INT8 cache
-            const float4 f = *(const float4*)(P.vs + (int64_t)bh * D + ch);
-            vsc[0] = f.x; vsc[1] = f.y; vsc[2] = f.z; vsc[3] = f.w;
-          }
-          X4 ov;
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            ov[e] = (E)(Q8 ? acc[b][db][g4 * 4 + e] * vsc[e] * inv : acc[b][db][g4 * 4 + e] * inv);
-          *(u32x2*)(orow + ch) = __builtin_bit_cast(u32x2, ov);
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int ch = db * 32 + g4 * 8 + half * 4;  // output channels ch .. ch+3
+        float vsc[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+        if constexpr (Q8) {  // the per-channel value scales of the INT8 cache
+          const float4 f = *(const float4*)(P.vs + (int64_t)bh * D + ch);
+          vsc[0] = f.x; vsc[1] = f.y; vsc[2] = f.z; vsc[3] = f.w;
         }
-      if (half == 0)
-        P.lse[(int64_t)bh * P.rows + qrow] =
-            l_tot > 0.0f ? (m_ref[b] + __log2f(l_tot)) * kLn2 : -INFINITY;
-    }
+        X4 ov;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          ov[e] = (E)(Q8 ? acc[b][db][g4 * 4 + e] * vsc[e] * inv : acc[b][db][g4 * 4 + e] * inv);
+        *(__attribute__((address_space(3))) u32x2*)(ow + (32 * b + l32) * OROW + ch * 2) =
+            __builtin_bit_cast(u32x2, ov);
+      }
+    if (half == 0 && qrow < P.rows)
+      P.lse[(int64_t)bh * P.rows + qrow] =
+          l_tot > 0.0f ? (m_ref[b] + __log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+  // The wave reads back only its own rows (LDS operations of one wave are
+  // ordered): 16 lanes per row, 16 bytes each, so a store covers 64 / (D/8)
+  // whole rows.
+  constexpr int CPO = D / 8;                         // 16-byte pieces per O row
+  constexpr int OPIECES = 32 * QB * CPO;             // pieces per wave
+  static_assert(OPIECES % 64 == 0, "whole stores per wave");
+#pragma unroll
+  for (int s = 0; s < OPIECES / 64; ++s) {
+    const int lin = s * 64 + lane;
+    const int r = lin / CPO, pc = lin % CPO;
+    const u32x4 piece = *(const __attribute__((address_space(3))) u32x4*)(ow + r * OROW + pc * 16);
+    if (q0 + r < P.rows) *(u32x4*)(P.o + q_head + (int64_t)(q0 + r) * D + pc * 8) = piece;
   }
 }
 
