@@ -225,7 +225,9 @@ struct Problem {
 // per-channel scales; the first product runs on int8 matrix instructions
 // against the in-kernel quantized query, and V is widened to fp16 in LDS for
 // the second product (see the header of fa2.h for the scheme).
-template <int D, bool FP16, int MODE, bool CAUSAL, bool Q8, bool SHORT>
+// PERSIST: one workgroup per CU walks several (K/V head, query tile) items,
+// and the key/value ring runs on from one item into the next (see below).
+template <int D, bool FP16, int MODE, bool CAUSAL, bool Q8, bool SHORT, bool PERSIST>
 __global__ void __attribute__((amdgpu_flat_work_group_size(KCfg<D, Q8, SHORT>::NW * 64,
                                                            KCfg<D, Q8, SHORT>::NW * 64),
                                amdgpu_waves_per_eu(KCfg<D, Q8, SHORT>::OCC,
@@ -284,7 +286,16 @@ fa2_fwd_kernel(const Problem P) {
   // O, row-major, rows padded by 16 bytes (OROW) against bank conflicts.
   constexpr int OROW = D * 2 + 16;
   constexpr int OBYTES = NW * 32 * QB * OROW;
-  __shared__ __attribute__((aligned(16))) char smem[RING_BYTES > OBYTES ? RING_BYTES : OBYTES];
+  // PERSIST keeps the ring apart from a query / output area at QOBASE: the
+  // next item's query tile is staged there while the current one runs, and
+  // the output is staged there while the next item's first K/V tiles sit in
+  // the ring.
+  constexpr int QTB = BR * RB;  // one query tile
+  static_assert(!PERSIST || (RING == 4 && !Q8 && !CAUSAL && QB == 1), "persistent kernels");
+  constexpr int QOBASE = PERSIST ? RING_BYTES : 0;
+  constexpr int QOBYTES = QTB > OBYTES ? QTB : OBYTES;
+  __shared__ __attribute__((aligned(16)))
+  char smem[PERSIST ? RING_BYTES + QOBYTES : (RING_BYTES > OBYTES ? RING_BYTES : OBYTES)];
   lds_char* const lds = (lds_char*)smem;
 
   const int tid = threadIdx.x;
@@ -293,37 +304,83 @@ fa2_fwd_kernel(const Problem P) {
   const int half = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // All query tiles of one K/V head go to one XCD (dispatch is round-robin
-  // over the 8 XCDs): the k-th workgroup on XCD x takes logical tile
-  // x*G/8 + k.  With the causal mask the later (longer) query tiles start
-  // first.
-  int bh, qt;  // bh = b * hkv + (K/V head)
+  // Work items are (K/V head bh = b * hkv + g, query tile qt) pairs, G =
+  // n_groups of them.  All query tiles of one K/V head go to one XCD
+  // (dispatch is round-robin over the 8 XCDs): the k-th workgroup on XCD x
+  // takes logical item x*G/8 + k.  With the causal mask the later (longer)
+  // query tiles start first.  A persistent workgroup (gridDim.x of them, a
+  // multiple of 8, one per CU) takes items k, k + gridDim.x/8, ... of its XCD.
   const int id = blockIdx.x;
-  const int per_xcd = P.n_groups >> 3;
-  if ((P.n_groups & 7) == 0) {
-    const int x = id & 7, kx = id >> 3;  // k-th workgroup dispatched on XCD x
-    if (CAUSAL && per_xcd % P.q_tiles == 0) {
-      // this XCD's heads, longest query tiles of all of them first
-      const int heads = per_xcd / P.q_tiles;
-      bh = x * heads + kx % heads;
-      qt = P.q_tiles - 1 - kx / heads;
-    } else {
-      const int logical = x * per_xcd + kx;
-      bh = logical / P.q_tiles;
-      qt = logical - bh * P.q_tiles;
-      if constexpr (CAUSAL) qt = P.q_tiles - 1 - qt;
+  auto locate = [&](int r, int& bh_r, int& qt_r) -> bool {  // this workgroup's r-th item
+    const int per_xcd = P.n_groups >> 3;
+    if constexpr (PERSIST) {
+      const int x = id & 7, k = (id >> 3) + r * (int)(gridDim.x >> 3);
+      if (k >= per_xcd) return false;
+      const int logical = x * per_xcd + k;
+      bh_r = logical / P.q_tiles;
+      qt_r = logical - bh_r * P.q_tiles;
+      return true;
     }
-  } else {
-    bh = id / P.q_tiles;
-    qt = id - bh * P.q_tiles;
-    if constexpr (CAUSAL) qt = P.q_tiles - 1 - qt;
-  }
-  const int64_t q_head = (int64_t)bh * P.rows * D;  // the group's first query row
-  const int64_t kv_head = (int64_t)bh * N * D;
-  const __amdgpu_buffer_rsrc_t q_rs = make_rsrc(P.q + q_head, (uint32_t)P.rows * D * 2);
+    if ((P.n_groups & 7) == 0) {
+      const int x = id & 7, kx = id >> 3;  // k-th workgroup dispatched on XCD x
+      if (CAUSAL && per_xcd % P.q_tiles == 0) {
+        // this XCD's heads, longest query tiles of all of them first
+        const int heads = per_xcd / P.q_tiles;
+        bh_r = x * heads + kx % heads;
+        qt_r = P.q_tiles - 1 - kx / heads;
+      } else {
+        const int logical = x * per_xcd + kx;
+        bh_r = logical / P.q_tiles;
+        qt_r = logical - bh_r * P.q_tiles;
+        if constexpr (CAUSAL) qt_r = P.q_tiles - 1 - qt_r;
+      }
+    } else {
+      bh_r = id / P.q_tiles;
+      qt_r = id - bh_r * P.q_tiles;
+      if constexpr (CAUSAL) qt_r = P.q_tiles - 1 - qt_r;
+    }
+    return r == 0;
+  };
+  int bh = 0, qt = 0;
+  if (!locate(0, bh, qt)) return;  // a persistent workgroup left without items
   constexpr int KE = Q8 ? 1 : 2;  // bytes per K / V element in HBM
-  const i32x4 k_rs = make_rsrc_words(P.k + kv_head * KE, (uint32_t)N * D * KE);
-  const i32x4 v_rs = make_rsrc_words(P.v + kv_head * KE, (uint32_t)N * D * KE);
+  // Buffer descriptors of an item: its group's query rows, its K and V.
+  auto q_words = [&](int bh_r) {
+    return make_rsrc_words(P.q + (int64_t)bh_r * P.rows * D, (uint32_t)P.rows * D * 2);
+  };
+  auto k_words = [&](int bh_r) {
+    return make_rsrc_words(P.k + (int64_t)bh_r * N * D * KE, (uint32_t)N * D * KE);
+  };
+  auto v_words = [&](int bh_r) {
+    return make_rsrc_words(P.v + (int64_t)bh_r * N * D * KE, (uint32_t)N * D * KE);
+  };
+  int64_t q_head = (int64_t)bh * P.rows * D;  // the group's first query row
+  __amdgpu_buffer_rsrc_t q_rs = make_rsrc(P.q + q_head, (uint32_t)P.rows * D * 2);
+  i32x4 k_rs = k_words(bh);
+  i32x4 v_rs = v_words(bh);
+  // PERSIST: the next item (if any), whose query tile and first K/V tiles
+  // are loaded during this item's iterations; nx_delta is the byte distance
+  // from this item's K (and V) head to the next one's.  Without a next item
+  // those loads fetch this item's own tiles again, unused.
+  int bh_nx = 0, qt_nx = 0;
+  bool has_next = false;
+  int64_t nx_delta = 0;
+  auto look_ahead = [&](int r) {
+    has_next = locate(r + 1, bh_nx, qt_nx);
+    if (!has_next) {
+      bh_nx = bh;
+      qt_nx = qt;
+    }
+    nx_delta = (int64_t)(bh_nx - bh) * N * D * KE;
+  };
+  // The descriptor rs with its base moved by `delta` bytes.
+  auto rebase = [](i32x4 rs, int64_t delta) {
+    const uint64_t b = ((uint64_t)((uint32_t)rs[1] & 0xffffu) << 32 | (uint32_t)rs[0]) + (uint64_t)delta;
+    rs[0] = (int)(uint32_t)b;
+    rs[1] = (int)((uint32_t)(b >> 32) & 0xffffu);
+    return rs;
+  };
+  if constexpr (PERSIST) look_ahead(0);
   const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
 
   // Global -> LDS without registers: each wave load moves 64 lanes x LW bytes
@@ -353,19 +410,51 @@ fa2_fwd_kernel(const Problem P) {
     else
       load_lds16(rs, voff, dst);
   };
-  auto issue_k = [&](int t, auto s) {
+  // PERSIST: with `nx` (a compile-time flag) tile t is tile t - n_all of
+  // the next item (which has the same tile count).
+  const int n_all = (N + BC - 1) / BC;
+  auto issue_k = [&](int t, auto s, auto nx) {
     const uint32_t dst = lds_base + slot(t, s) * TBK + wave * 64 * LW;
+    i32x4 rs = k_rs;
+    if constexpr (decltype(nx)::value) {
+      rs = rebase(k_rs, nx_delta);
+      t -= n_all;
+    }
 #pragma unroll
     for (int i = 0; i < LOADS; ++i)
-      load_lds(k_rs, (uint32_t)t * TBK + k_src[i], dst + i * NW * 64 * LW);
+      load_lds(rs, (uint32_t)t * TBK + k_src[i], dst + i * NW * 64 * LW);
   };
   // V_t into the V ring, or with Q8 into the int8 staging ring.
-  auto issue_v = [&](int t, auto s) {
+  auto issue_v = [&](int t, auto s, auto nx) {
     const uint32_t dst = lds_base + (Q8 ? SBASE + slot(t, s) * TBK : VBASE + slot(t, s) * TBYTES) +
                          wave * 64 * LW;
+    i32x4 rs = v_rs;
+    if constexpr (decltype(nx)::value) {
+      rs = rebase(v_rs, nx_delta);
+      t -= n_all;
+    }
 #pragma unroll
     for (int i = 0; i < LOADS; ++i)
-      load_lds(v_rs, (uint32_t)t * TBK + v_src[i], dst + i * NW * 64 * LW);
+      load_lds(rs, (uint32_t)t * TBK + v_src[i], dst + i * NW * 64 * LW);
+  };
+  // PERSIST: query tile qt_r of the group that descriptor rs covers into the
+  // query / output area, swizzled like K (QLOADS 16-byte loads per thread).
+  // Load i moves the pieces (i*NW + wave)*64 + lane, rows 16 apart or more
+  // from load i-1, so the swizzle (row & 15) is that of load 0.
+  constexpr int QLOADS = QTB / (NW * 64 * 16);
+  constexpr int QSTEP = NW * 64 * 16;  // bytes of the tile per load
+  static_assert(!PERSIST || (QTB % QSTEP == 0 && QSTEP % (16 * RB) == 0), "query tile loads");
+  auto issue_q = [&](const i32x4& rs, int qt_r) {
+    if constexpr (PERSIST) {
+      // recomputed per item rather than held in registers through the loop
+      int ln = lane;
+      uint32_t dst = lds_base + QOBASE + wave * 1024;
+      asm volatile("" : "+v"(ln), "+s"(dst));
+      const int lin = wave * 64 + ln, row = lin / CPR;
+      const uint32_t src = (uint32_t)(qt_r * QTB + row * RB + k_swizzle<CPR>(row, lin % CPR) * 16);
+#pragma unroll
+      for (int i = 0; i < QLOADS; ++i) load_lds16(rs, src + i * QSTEP, dst + i * QSTEP);
+    }
   };
 
   // Per-lane LDS byte offsets of the MFMA operands within a tile.  The
@@ -396,7 +485,7 @@ fa2_fwd_kernel(const Problem P) {
 
   // Q_i fragments: the B operands of S^T = K_j Q_i^T, held for the whole
   // loop.  Query block b of this wave is packed rows q0 + 32*b + l32.
-  const int q0 = qt * BR + wave * 32 * QB;
+  int q0 = qt * BR + wave * 32 * QB;
 
   // Causal limits: a lane's last visible key (its row within its head plus
   // causal_off), and the smallest such row among the wave's rows (packed rows
@@ -429,7 +518,9 @@ fa2_fwd_kernel(const Problem P) {
   for (int b = 0; b < QB; ++b) {
     c_q[b] = c;
     const uint32_t qrow_off = (uint32_t)((q0 + 32 * b + l32) * RB);
-    if constexpr (!Q8) {
+    if constexpr (PERSIST) {
+      // fragments come through LDS (load_qf below)
+    } else if constexpr (!Q8) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
         qf[b][ks] = __builtin_bit_cast(
@@ -499,6 +590,24 @@ fa2_fwd_kernel(const Problem P) {
     m_ref[b] = -INFINITY;
     l_part[b] = 0.0f;
   }
+
+  // PERSIST: this wave's query fragments from the query tile in LDS, at the
+  // K operand offsets (the tile is swizzled like K and the wave's rows start
+  // at a multiple of 32).  The wave's base is made opaque here so that the
+  // compiler does not keep every offset plus base in a register between uses.
+  auto load_qf = [&]() {
+    if constexpr (PERSIST) {
+      uint32_t qbase = QOBASE + wave * 32 * QB * RB;
+      asm volatile("" : "+s"(qbase));
+#pragma unroll
+      for (int b = 0; b < QB; ++b)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          qf[b][ks] = __builtin_bit_cast(
+              X8, *(const __attribute__((address_space(3))) u32x4*)(
+                      lds + qbase + 32 * b * RB + k_off[ks % KOFF] + (ks / KOFF) * 256));
+    }
+  };
 
   // First operands of the next products, read one iteration early.
   KOp kpre[PK > 0 ? PK : 1];
@@ -642,18 +751,26 @@ fa2_fwd_kernel(const Problem P) {
   // j+1 (K_{j+2}, V_j: loaded during iteration j-2 and published by the last
   // barrier) and waits only for the loads issued during iteration j-1.  The
   // last iteration's S_{j+1} product reads a tile past the end and is
-  // dropped.  `ph` is j % 4.
+  // dropped.  `ph` is j % 4.  PERSIST: `tail` (compile-time) marks the last
+  // iterations of an item: bit 0, the K tile loaded is the next item's; bit 1,
+  // the V tile; bit 2, S_{j+1} is the next item's S_0 (its query fragments
+  // are read first).
   auto step = [&](auto first, auto ph, int j, SAcc (&s_cur)[QB][KB], SAcc (&s_nxt)[QB][KB],
-                  const X8 (&p_prev)[QB][ST], X8 (&p_cur)[QB][ST]) {
+                  const X8 (&p_prev)[QB][ST], X8 (&p_cur)[QB][ST], auto tail) {
     constexpr int p = decltype(ph)::value;
+    constexpr int TL = decltype(tail)::value;
     using S0 = Ic<p>;
     using S1 = Ic<(p + 1) % 4>;
     using S2 = Ic<(p + 2) % 4>;
     using S3 = Ic<(p + 3) % 4>;
     // (RING = 2 skips loads past the end: at d = 256 that keeps it from spilling)
-    if (RING == 4 || j + RING < n_tiles) issue_k(j + RING, S0{});
-    issue_v(j + VAHEAD, Ic<(p + VAHEAD) % 4>{});
+    if (RING == 4 || j + RING < n_tiles) issue_k(j + RING, S0{}, std::bool_constant<(TL & 1) != 0>{});
+    issue_v(j + VAHEAD, Ic<(p + VAHEAD) % 4>{}, std::bool_constant<(TL & 2) != 0>{});
     convert_v(j + 1, S1{});
+    // PERSIST: the next item's query tile, needed by this item's last product
+    // (issued after this iteration's K/V loads, also when there is no next
+    // item, so that the wait below counts it; waited by the next iteration)
+    if constexpr (PERSIST && decltype(first)::value) issue_q(q_words(bh_nx), qt_nx);
 
     // The logits of this tile in fp32 (converted from the int32 products
     // with Q8).
@@ -692,6 +809,9 @@ fa2_fwd_kernel(const Problem P) {
       }
     }
 
+    // PERSIST: the last iteration's S_{j+1} is the next item's S_0, against
+    // its query tile (landed by the end of iteration 1).
+    if constexpr ((TL & 4) != 0) load_qf();
     gemm1(j + 1, S1{}, kpre, s_nxt);
     if constexpr (!decltype(first)::value) gemm2(j - 1, S3{}, vpre, p_prev);
     float rs[QB];
@@ -754,25 +874,32 @@ fa2_fwd_kernel(const Problem P) {
     for (int b = 0; b < QB; ++b) l_part[b] += rs[b];
 
     // RING = 4: the loads issued during iteration j-1 have landed; RING = 2:
-    // this iteration's own.
-    wait_vmem_but<RING == 4 ? 2 * LOADS : 0>();
+    // this iteration's own.  (PERSIST: the first iteration's query loads may
+    // stay in flight too.)
+    wait_vmem_but<RING == 4 ? 2 * LOADS + (PERSIST && decltype(first)::value ? QLOADS : 0) : 0>();
     __syncthreads();
   };
 
+  // Both products' S and P register sets; with PERSIST they carry the next
+  // item's S_0 from one item into the next.
+  SAcc sA[QB][KB], sB[QB][KB];
+  X8 pA[QB][ST], pB[QB][ST];
   if (n_tiles > 0) {
     // Prologue: Q, K_0 .. K_{RING-1} and V_0 .. V_{RING-3} resident, S_0
     // computed, the first operands of K_1 in registers.  Everything retires
     // before the loop: vmcnt is a counter, so a load still in flight at the
-    // loop head would make every iteration wait on it.
-    issue_k(0, Ic<0>{});
-    issue_k(1, Ic<1>{});
+    // loop head would make every iteration wait on it.  (Later persistent
+    // items find all of this done by the item before.)
+    issue_q(q_words(bh), qt);
+    issue_k(0, Ic<0>{}, std::false_type{});
+    issue_k(1, Ic<1>{}, std::false_type{});
     if constexpr (RING == 4) {
-      issue_k(2, Ic<2>{});
-      issue_k(3, Ic<3>{});
+      issue_k(2, Ic<2>{}, std::false_type{});
+      issue_k(3, Ic<3>{}, std::false_type{});
     }
-    if constexpr (VAHEAD > 0) issue_v(0, Ic<0>{});
-    if constexpr (VAHEAD > 1) issue_v(1, Ic<1>{});
-    if constexpr (VAHEAD > 2) issue_v(2, Ic<2>{});
+    if constexpr (VAHEAD > 0) issue_v(0, Ic<0>{}, std::false_type{});
+    if constexpr (VAHEAD > 1) issue_v(1, Ic<1>{}, std::false_type{});
+    if constexpr (VAHEAD > 2) issue_v(2, Ic<2>{}, std::false_type{});
 #pragma unroll
     for (int b = 0; b < QB; ++b)
 #pragma unroll
@@ -780,43 +907,64 @@ fa2_fwd_kernel(const Problem P) {
     wait_vmem();
     __syncthreads();
 
-    SAcc sA[QB][KB], sB[QB][KB];
-    X8 pA[QB][ST], pB[QB][ST];
+    load_qf();              // PERSIST: Q from LDS (read before the next tile lands there)
     convert_v(0, Ic<0>{});  // Q8: V_0 widened; published by the barrier below
     prefetch_k(0, Ic<0>{}, kpre);
     gemm1(0, Ic<0>{}, kpre, sA);
     prefetch_k(1, Ic<1>{}, kpre);
     __syncthreads();  // every wave is done with K_0 before K_RING may overwrite it
+  }
+
+  for (int item = 0;; ++item) {
+  if (n_tiles > 0) {
 
     // Iterations run in groups of 4 so ring slots and the S / P register
     // sets (even j: S_j in sA, S_{j+1} into sB, P_j into pA) are compile-time.
-    step(std::true_type{}, Ic<0>{}, 0, sA, sB, pB, pA);
+    step(std::true_type{}, Ic<0>{}, 0, sA, sB, pB, pA, Ic<0>{});
     int j = 1;
     if constexpr (RING == 2) {  // pairs suffice; a longer body spills at d = 256
       for (; j + 1 < n_tiles; j += 2) {
-        step(std::false_type{}, Ic<1>{}, j, sB, sA, pA, pB);
-        step(std::false_type{}, Ic<2>{}, j + 1, sA, sB, pB, pA);
+        step(std::false_type{}, Ic<1>{}, j, sB, sA, pA, pB, Ic<0>{});
+        step(std::false_type{}, Ic<2>{}, j + 1, sA, sB, pB, pA, Ic<0>{});
       }
       if (j < n_tiles) {
-        step(std::false_type{}, Ic<1>{}, j, sB, sA, pA, pB);
+        step(std::false_type{}, Ic<1>{}, j, sB, sA, pA, pB, Ic<0>{});
         gemm2(j, Ic<1>{}, vpre, pB);
       } else {
         gemm2(j - 1, Ic<0>{}, vpre, pA);
       }
+    } else if constexpr (PERSIST) {
+      // n_tiles % 4 == 0 and n_tiles >= 8: the loop leaves the last seven
+      // iterations, of which the last four load the next item's K tiles 0..3
+      // and the last two its V tiles 0..1; the last computes its S_0.
+      for (; j + 7 < n_tiles; j += 4) {
+        step(std::false_type{}, Ic<1>{}, j, sB, sA, pA, pB, Ic<0>{});
+        step(std::false_type{}, Ic<2>{}, j + 1, sA, sB, pB, pA, Ic<0>{});
+        step(std::false_type{}, Ic<3>{}, j + 2, sB, sA, pA, pB, Ic<0>{});
+        step(std::false_type{}, Ic<0>{}, j + 3, sA, sB, pB, pA, Ic<0>{});
+      }
+      step(std::false_type{}, Ic<1>{}, j, sB, sA, pA, pB, Ic<0>{});
+      step(std::false_type{}, Ic<2>{}, j + 1, sA, sB, pB, pA, Ic<0>{});
+      step(std::false_type{}, Ic<3>{}, j + 2, sB, sA, pA, pB, Ic<0>{});
+      step(std::false_type{}, Ic<0>{}, j + 3, sA, sB, pB, pA, Ic<1>{});
+      step(std::false_type{}, Ic<1>{}, j + 4, sB, sA, pA, pB, Ic<1>{});
+      step(std::false_type{}, Ic<2>{}, j + 5, sA, sB, pB, pA, Ic<3>{});
+      step(std::false_type{}, Ic<3>{}, j + 6, sB, sA, pA, pB, Ic<7>{});
+      gemm2(j + 6, Ic<3>{}, vpre, pB);
     } else {
       for (; j + 3 < n_tiles; j += 4) {
-        step(std::false_type{}, Ic<1>{}, j, sB, sA, pA, pB);
-        step(std::false_type{}, Ic<2>{}, j + 1, sA, sB, pB, pA);
-        step(std::false_type{}, Ic<3>{}, j + 2, sB, sA, pA, pB);
-        step(std::false_type{}, Ic<0>{}, j + 3, sA, sB, pB, pA);
+        step(std::false_type{}, Ic<1>{}, j, sB, sA, pA, pB, Ic<0>{});
+        step(std::false_type{}, Ic<2>{}, j + 1, sA, sB, pB, pA, Ic<0>{});
+        step(std::false_type{}, Ic<3>{}, j + 2, sB, sA, pA, pB, Ic<0>{});
+        step(std::false_type{}, Ic<0>{}, j + 3, sA, sB, pB, pA, Ic<0>{});
       }
       // Up to three iterations left (j % 4 == 1), then O += P_{n-1} V_{n-1}.
       if (j < n_tiles) {
-        step(std::false_type{}, Ic<1>{}, j, sB, sA, pA, pB);
+        step(std::false_type{}, Ic<1>{}, j, sB, sA, pA, pB, Ic<0>{});
         if (j + 1 < n_tiles) {
-          step(std::false_type{}, Ic<2>{}, j + 1, sA, sB, pB, pA);
+          step(std::false_type{}, Ic<2>{}, j + 1, sA, sB, pB, pA, Ic<0>{});
           if (j + 2 < n_tiles) {
-            step(std::false_type{}, Ic<3>{}, j + 2, sB, sA, pA, pB);
+            step(std::false_type{}, Ic<3>{}, j + 2, sB, sA, pA, pB, Ic<0>{});
             gemm2(j + 2, Ic<3>{}, vpre, pB);
           } else {
             gemm2(j + 1, Ic<2>{}, vpre, pA);
@@ -837,20 +985,27 @@ fa2_fwd_kernel(const Problem P) {
   // The LDS is reused only once every wave is done with the K and V tiles
   // and every load into it has landed: the last iterations still load tiles
   // past the end (waited one iteration late), whose writes must not fall
-  // into the staged output.
-  wait_vmem();
+  // into the staged output.  PERSIST stages the output apart from the ring,
+  // where the next item's first tiles are still landing, and only waits for
+  // every wave to be done with the query tile there.
+  if constexpr (!PERSIST) wait_vmem();
   __syncthreads();
-  lds_char* const ow = lds + wave * (32 * QB) * OROW;  // this wave's rows
+  // PERSIST: the lane's addresses here are recomputed per item rather than
+  // held in registers through the loop.
+  int el = lane;
+  if constexpr (PERSIST) asm volatile("" : "+v"(el));
+  const int el32 = el & 31, ehalf = el >> 5;
+  lds_char* const ow = lds + QOBASE + wave * (32 * QB) * OROW;  // this wave's rows
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
-    const int qrow = q0 + 32 * b + l32;
+    const int qrow = q0 + 32 * b + el32;
     const float l_tot = l_part[b] + __shfl_xor(l_part[b], 32);
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int ch = db * 32 + g4 * 8 + half * 4;  // output channels ch .. ch+3
+        const int ch = db * 32 + g4 * 8 + ehalf * 4;  // output channels ch .. ch+3
         float vsc[4] = {1.0f, 1.0f, 1.0f, 1.0f};
         if constexpr (Q8) {  // the per-channel value scales of the INT8 cache
           const float4 f = *(const float4*)(P.vs + (int64_t)bh * D + ch);
@@ -860,10 +1015,10 @@ fa2_fwd_kernel(const Problem P) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           ov[e] = (E)(Q8 ? acc[b][db][g4 * 4 + e] * vsc[e] * inv : acc[b][db][g4 * 4 + e] * inv);
-        *(__attribute__((address_space(3))) u32x2*)(ow + (32 * b + l32) * OROW + ch * 2) =
+        *(__attribute__((address_space(3))) u32x2*)(ow + (32 * b + el32) * OROW + ch * 2) =
             __builtin_bit_cast(u32x2, ov);
       }
-    if (half == 0 && qrow < P.rows)
+    if (ehalf == 0 && qrow < P.rows)
       P.lse[(int64_t)bh * P.rows + qrow] =
           l_tot > 0.0f ? (m_ref[b] + __log2f(l_tot)) * kLn2 : -INFINITY;
   }
@@ -875,21 +1030,46 @@ fa2_fwd_kernel(const Problem P) {
   static_assert(OPIECES % 64 == 0, "whole stores per wave");
 #pragma unroll
   for (int s = 0; s < OPIECES / 64; ++s) {
-    const int lin = s * 64 + lane;
+    const int lin = s * 64 + el;
     const int r = lin / CPO, pc = lin % CPO;
     const u32x4 piece = *(const __attribute__((address_space(3))) u32x4*)(ow + r * OROW + pc * 16);
     if (q0 + r < P.rows) *(u32x4*)(P.o + q_head + (int64_t)(q0 + r) * D + pc * 8) = piece;
+  }
+  if constexpr (!PERSIST) {
+    break;
+  } else {
+    if (!has_next) break;
+    // The next item: its S_0 is in sA and the first operands of its K_1 in
+    // kpre (this item's last iteration), its first K/V tiles in the ring.
+    bh = bh_nx;
+    qt = qt_nx;
+    q_head = (int64_t)bh * P.rows * D;
+    q0 = qt * BR + wave * 32 * QB;
+    k_rs = rebase(k_rs, nx_delta);
+    v_rs = rebase(v_rs, nx_delta);
+    look_ahead(item + 1);
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[b][db][i] = 0.0f;
+      m_ref[b] = -INFINITY;
+      l_part[b] = 0.0f;
+    }
+    __syncthreads();  // the staged output is read before the next query tile lands there
+  }
   }
 }
 
 typedef void (*kernel_fn)(const Problem);
 
-template <int D, bool FP16, bool CAUSAL, bool Q8, bool SHORT>
+template <int D, bool FP16, bool CAUSAL, bool Q8, bool SHORT, bool PERSIST = false>
 kernel_fn pick_mode(int mode) {
   switch (mode) {
-    case kNegative: return fa2_fwd_kernel<D, FP16, kNegative, CAUSAL, Q8, SHORT>;
-    case kZero: return fa2_fwd_kernel<D, FP16, kZero, CAUSAL, Q8, SHORT>;
-    default: return fa2_fwd_kernel<D, FP16, kPositive, CAUSAL, Q8, SHORT>;
+    case kNegative: return fa2_fwd_kernel<D, FP16, kNegative, CAUSAL, Q8, SHORT, PERSIST>;
+    case kZero: return fa2_fwd_kernel<D, FP16, kZero, CAUSAL, Q8, SHORT, PERSIST>;
+    default: return fa2_fwd_kernel<D, FP16, kPositive, CAUSAL, Q8, SHORT, PERSIST>;
   }
 }
 
@@ -900,6 +1080,19 @@ kernel_fn pick(bool fp16, int mode, bool causal) {
                   : pick_mode<D, true, false, Q8, SHORT>(mode);
   return causal ? pick_mode<D, false, true, Q8, SHORT>(mode)
                 : pick_mode<D, false, false, Q8, SHORT>(mode);
+}
+
+// Compute units of the current device (0 if unknown), cached per device.
+int cu_count() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cache[dev] = n;
+  }
+  return cache[dev];
 }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -1019,8 +1212,22 @@ int launch(const void* q, const void* k, const void* v, const float* ks, const f
                : d == 128 ? (short_keys ? pick<128, false, true>(fp16, mode, causal)
                                         : pick<128, false>(fp16, mode, causal))
                           : pick<256, false>(fp16, mode, causal);
+  // Persistent workgroups, one per CU, when every one gets at least two items
+  // of the same length whose tile count the ring's four slots divide (the
+  // ring then carries on from one item into the next at slot 0).
+  int64_t grid = groups;
+  if (!q8 && !causal && !short_keys && d == 128 && Nk > 0 &&
+      ((Nk + Cfg<128>::BC - 1) / Cfg<128>::BC) % Cfg<128>::RING == 0 &&
+      groups % 8 == 0) {
+    const int cus = cu_count();
+    if (cus > 0 && cus % 8 == 0 && groups >= 2 * (int64_t)cus) {
+      fn = fp16 ? pick_mode<128, true, false, false, false, true>(mode)
+                : pick_mode<128, false, false, false, false, true>(mode);
+      grid = cus;
+    }
+  }
   void* args[] = {&P};
-  hipError_t err = hipLaunchKernel((const void*)fn, dim3((unsigned)groups),
+  hipError_t err = hipLaunchKernel((const void*)fn, dim3((unsigned)grid),
                                    dim3((unsigned)(nw * 64)), args, 0,
                                    (hipStream_t)stream);
   return err == hipSuccess ? FA2_OK : FA2_ERR_HIP;

@@ -1,0 +1,111 @@
+"""GPU parity of the persistent-workgroup launches (needs an MI355X).
+
+Non-causal d = 128 calls with enough (K/V head, query tile) items, long keys
+and a key-tile count divisible by 4 run one workgroup per compute unit, each
+walking several items with its key/value ring carried from one item into the
+next.  Each case here checks that launch against the oracle on sampled rows,
+and bit for bit against launches of one K/V head group at a time, which are
+too small for persistent workgroups and run one item per workgroup: a row's
+arithmetic does not depend on how the items are spread over workgroups.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from flashattention_forward_tile_amd import fa2
+from flashattention_forward_tile_amd.workloads import bits
+from parity import assert_parity
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+_TD = {"bf16": torch.bfloat16, "fp16": torch.float16}
+BLOCK_Q = 256   # query rows per d = 128 workgroup
+BLOCK_K = 32    # keys per tile
+
+
+def announce(*what):
+    print("CASE", *what, flush=True)
+
+
+def rand(shape, dtype, seed):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn(shape, generator=g).to(_TD[dtype])
+
+
+def persistent(B, Hq, Hkv, Nq, Nk):
+    """Whether the call's shape takes the persistent launch on this device."""
+    groups = B * Hkv * math.ceil(Hq // Hkv * Nq / BLOCK_Q)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    return (Nk > 1024 and math.ceil(Nk / BLOCK_K) % 4 == 0 and groups % 8 == 0
+            and cus % 8 == 0 and groups >= 2 * cus)
+
+
+# (B, Hq, Hkv, Nq, Nk, dtype): 512 items (two per workgroup), 576 (two or
+# three), ragged query tiles and a ragged last key tile, grouped heads.
+CASES = [
+    (2, 64, 64, 1000, 1130, "bf16"),
+    (4, 32, 8, 1100, 2048, "fp16"),
+    (2, 128, 16, 520, 1152, "bf16"),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,dtype", CASES)
+@pytest.mark.parametrize("scale_kind", ["default", "negative", "zero"])
+def test_persistent_equals_per_group_launches(B, Hq, Hkv, Nq, Nk, dtype, scale_kind):
+    announce("persistent", B, Hq, Hkv, Nq, Nk, dtype, scale_kind)
+    if not persistent(B, Hq, Hkv, Nq, Nk):
+        pytest.skip("shape does not take the persistent launch on this device")
+    scale = {"default": 1.0 / math.sqrt(128), "negative": -0.15, "zero": 0.0}[scale_kind]
+    seed = B * 1000 + Hq + Nk
+    q = rand((B, Hq, Nq, 128), dtype, seed).to(DEV)
+    k = rand((B, Hkv, Nk, 128), dtype, seed + 1).to(DEV)
+    v = rand((B, Hkv, Nk, 128), dtype, seed + 2).to(DEV)
+    o, lse = fa2.fwd(q, k, v, scale=scale)
+    torch.cuda.synchronize()
+    G = Hq // Hkv
+    for b in range(B):
+        for g in range(Hkv):
+            qs = q[b:b + 1, g * G:(g + 1) * G].contiguous()
+            o1, l1 = fa2.fwd(qs, k[b:b + 1, g:g + 1].contiguous(), v[b:b + 1, g:g + 1].contiguous(),
+                             scale=scale)
+            torch.cuda.synchronize()
+            assert torch.equal(o[b:b + 1, g * G:(g + 1) * G], o1), (b, g)
+            assert torch.equal(lse[b:b + 1, g * G:(g + 1) * G], l1), (b, g)
+    # sampled rows against the oracle: every item position of a workgroup is
+    # represented (first and last rows of query tiles across all groups)
+    rng = np.random.default_rng(seed)
+    flat = B * Hq * Nq
+    rows = np.unique(np.concatenate([
+        rng.integers(0, flat, size=48),
+        np.arange(0, flat, Nq * 7 + 255)[:48],
+        [0, flat - 1]]).astype(np.int64))
+    o_ref, lse_ref = oracle.attention(bits(q.cpu()), bits(k.cpu()), bits(v.cpu()), dtype, scale,
+                                      rows=rows, nthreads=8)
+    og = o.cpu().double().numpy().reshape(-1, 128)[rows]
+    lg = lse.cpu().double().numpy().reshape(-1)[rows]
+    assert_parity(og, lg, o_ref, lse_ref, "persistent %s" % ((B, Hq, Hkv, Nq, Nk, dtype, scale),),
+                  lse_abs=1e-3)
+
+
+def test_persistent_headline_deterministic():
+    """The B=4, H=16, N=4096 bf16 call (persistent on a 256-CU device) twice
+    on fresh outputs: the same bits, every output written."""
+    announce("persistent headline deterministic")
+    if not persistent(4, 16, 16, 4096, 4096):
+        pytest.skip("shape does not take the persistent launch on this device")
+    q = rand((4, 16, 4096, 128), "bf16", 3).to(DEV)
+    k = rand((4, 16, 4096, 128), "bf16", 4).to(DEV)
+    v = rand((4, 16, 4096, 128), "bf16", 5).to(DEV)
+    outs = []
+    for fill in (float("nan"), 7.0):
+        o = torch.full_like(q, fill)
+        lse = torch.full((4, 16, 4096), fill, device=DEV)
+        fa2.fwd(q, k, v, out=o, lse=lse)
+        torch.cuda.synchronize()
+        outs.append((o.cpu(), lse.cpu()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    assert torch.isfinite(outs[0][0]).all() and torch.isfinite(outs[0][1]).all()
