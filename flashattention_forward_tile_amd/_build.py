@@ -8,6 +8,9 @@ ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "fa2_fwd.hip")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfa2.so")
+# The race-check build of the same source (tests only): every load waited
+# where it is issued, so its results must equal libfa2.so's bit for bit.
+LIB_SYNC = os.path.join(PKG, "libfa2_sync.so")
 ARCH = "gfx950"
 
 # Packed fp32 VALU forms are kept out of the generated code; the softmax and
@@ -25,15 +28,20 @@ def compile_cmd(out, extra=()):
             "-shared", "-I", INCLUDE, *DEVICE_FLAGS, *extra, "-o", out, SRC]
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    """Compile csrc/fa2_fwd.hip into libfa2.so and return its path."""
-    tmp = LIB + ".tmp%d" % os.getpid()
+def build(verbose: bool = False, extra=(), out: str = LIB) -> str:
+    """Compile csrc/fa2_fwd.hip into `out` (libfa2.so) and return its path."""
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = compile_cmd(tmp, extra)
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
+
+
+def build_sync(verbose: bool = False) -> str:
+    """Compile the race-check build into libfa2_sync.so."""
+    return build(verbose, extra=("-DFA2_SYNC_CHECK=1",), out=LIB_SYNC)
 
 
 if __name__ == "__main__":

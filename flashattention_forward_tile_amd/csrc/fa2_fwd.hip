@@ -194,6 +194,17 @@ template <int X> using Ic = std::integral_constant<int, X>;
 // left alone.  Otherwise the row's reference moves to its true running max.
 constexpr float kSumLimit = 256.0f;
 
+// Race-check build (-DFA2_SYNC_CHECK=1, a second library used by the tests):
+// every iteration waits for all of its loads and synchronises the workgroup
+// right after issuing them, and the persistent epilogue waits as well, so no
+// tile is read before it has landed whatever the ring's deferred waits
+// assume.  The arithmetic and its order are unchanged: both builds must give
+// the same bits.
+#ifndef FA2_SYNC_CHECK
+#define FA2_SYNC_CHECK 0
+#endif
+constexpr bool kSyncCheck = FA2_SYNC_CHECK != 0;
+
 // Sign of the folded scale c = scale * log2(e): the running extreme of the raw
 // logits is a max for c > 0 and a min for c < 0; c == 0 is uniform attention.
 enum ScaleMode { kPositive = 0, kNegative = 1, kZero = 2 };
@@ -771,6 +782,10 @@ fa2_fwd_kernel(const Problem P) {
     // (issued after this iteration's K/V loads, also when there is no next
     // item, so that the wait below counts it; waited by the next iteration)
     if constexpr (PERSIST && decltype(first)::value) issue_q(q_words(bh_nx), qt_nx);
+    if constexpr (kSyncCheck) {
+      wait_vmem();
+      __syncthreads();
+    }
 
     // The logits of this tile in fp32 (converted from the int32 products
     // with Q8).
@@ -876,7 +891,10 @@ fa2_fwd_kernel(const Problem P) {
     // RING = 4: the loads issued during iteration j-1 have landed; RING = 2:
     // this iteration's own.  (PERSIST: the first iteration's query loads may
     // stay in flight too.)
-    wait_vmem_but<RING == 4 ? 2 * LOADS + (PERSIST && decltype(first)::value ? QLOADS : 0) : 0>();
+    if constexpr (kSyncCheck)
+      wait_vmem();
+    else
+      wait_vmem_but<RING == 4 ? 2 * LOADS + (PERSIST && decltype(first)::value ? QLOADS : 0) : 0>();
     __syncthreads();
   };
 
@@ -988,7 +1006,7 @@ fa2_fwd_kernel(const Problem P) {
   // into the staged output.  PERSIST stages the output apart from the ring,
   // where the next item's first tiles are still landing, and only waits for
   // every wave to be done with the query tile there.
-  if constexpr (!PERSIST) wait_vmem();
+  if constexpr (!PERSIST || kSyncCheck) wait_vmem();
   __syncthreads();
   // PERSIST: the lane's addresses here are recomputed per item rather than
   // held in registers through the loop.

@@ -65,19 +65,23 @@ def library_path() -> str:
     return _build.LIB
 
 
+def load(path: str) -> ctypes.CDLL:
+    """Load a build of the library at `path` with the declared signatures."""
+    if not os.path.exists(path):
+        raise RuntimeError("%s is not built; run __graft_entry__.build()" % path)
+    handle = ctypes.CDLL(path)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(handle, name)
+        fn.restype = res
+        fn.argtypes = args
+    return handle
+
+
 def lib() -> ctypes.CDLL:
     """The loaded libfa2.so; raises if it has not been built."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_build.LIB):
-            raise RuntimeError(
-                "libfa2.so is not built (%s); run __graft_entry__.build()" % _build.LIB)
-        handle = ctypes.CDLL(_build.LIB)
-        for name, (res, args) in _SIGNATURES.items():
-            fn = getattr(handle, name)
-            fn.restype = res
-            fn.argtypes = args
-        _lib = handle
+        _lib = load(_build.LIB)
     return _lib
 
 

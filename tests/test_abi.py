@@ -37,6 +37,16 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, name), name
 
 
+def test_race_check_build_exports_the_same_symbols():
+    """The race-check build the GPU tests compare against loads on the host
+    and exports every declared entry point."""
+    if not os.path.exists(_build.LIB_SYNC):
+        _build.build_sync()
+    handle = fa2.load(_build.LIB_SYNC)
+    for name in declared_functions():
+        assert hasattr(handle, name), name
+
+
 def test_strerror_covers_every_status(lib):
     texts = set()
     for code in range(0, -10, -1):
