@@ -520,6 +520,16 @@ fa2_fwd_kernel(const Problem P) {
     const int last_key = row_max + P.causal_off;  // may be < 0
     n_tiles = last_key < 0 ? 0 : min(n_tiles, last_key / BC + 1);
   }
+  // Leading tiles that no wave of the workgroup masks: whole tiles of keys,
+  // and with the causal mask those whose last key every row of the workgroup
+  // sees (its smallest row within a head; 0 if it spans a head boundary).
+  int n_clear = N / BC;
+  if constexpr (CAUSAL) {
+    const int first = qt * BR, last = min(P.rows, first + BR) - 1;
+    const int row_min = first / P.nq != last / P.nq ? 0 : first % P.nq;
+    const int seen = row_min + P.causal_off + 1;  // keys every row sees
+    n_clear = seen <= 0 ? 0 : min(n_clear, seen / BC);
+  }
   // c_q: the lane's logit multiplier (scale * log2 e, times the query row
   // scale with Q8).
   using QOp = std::conditional_t<Q8, i32x4, X8>;
@@ -762,10 +772,11 @@ fa2_fwd_kernel(const Problem P) {
   // j+1 (K_{j+2}, V_j: loaded during iteration j-2 and published by the last
   // barrier) and waits only for the loads issued during iteration j-1.  The
   // last iteration's S_{j+1} product reads a tile past the end and is
-  // dropped.  `ph` is j % 4.  PERSIST: `tail` (compile-time) marks the last
-  // iterations of an item: bit 0, the K tile loaded is the next item's; bit 1,
-  // the V tile; bit 2, S_{j+1} is the next item's S_0 (its query fragments
-  // are read first).
+  // dropped.  `ph` is j % 4.  `tail` (compile-time): bit 3, no wave masks
+  // this tile (the check, a branch that splits the block, is left out).
+  // PERSIST marks the last iterations of an item with bit 0, the K tile
+  // loaded is the next item's; bit 1, the V tile; bit 2, S_{j+1} is the next
+  // item's S_0 (its query fragments are read first).
   auto step = [&](auto first, auto ph, int j, SAcc (&s_cur)[QB][KB], SAcc (&s_nxt)[QB][KB],
                   const X8 (&p_prev)[QB][ST], X8 (&p_cur)[QB][ST], auto tail) {
     constexpr int p = decltype(ph)::value;
@@ -809,8 +820,11 @@ fa2_fwd_kernel(const Problem P) {
     // diagonal (key > row + causal_off).  Decided per wave, from its
     // smallest row within a head.
     const int key0 = j * BC;
-    bool masked = key0 + BC > N;
-    if constexpr (CAUSAL) masked |= key0 + BC - 1 > wave_row_min + P.causal_off;
+    bool masked = false;
+    if constexpr ((TL & 8) == 0) {
+      masked = key0 + BC > N;
+      if constexpr (CAUSAL) masked |= key0 + BC - 1 > wave_row_min + P.causal_off;
+    }
     if (masked) {
 #pragma unroll
       for (int b = 0; b < QB; ++b) {
@@ -938,7 +952,7 @@ fa2_fwd_kernel(const Problem P) {
 
     // Iterations run in groups of 4 so ring slots and the S / P register
     // sets (even j: S_j in sA, S_{j+1} into sB, P_j into pA) are compile-time.
-    step(std::true_type{}, Ic<0>{}, 0, sA, sB, pB, pA, Ic<0>{});
+    step(std::true_type{}, Ic<0>{}, 0, sA, sB, pB, pA, Ic<PERSIST ? 8 : 0>{});
     int j = 1;
     if constexpr (RING == 2) {  // pairs suffice; a longer body spills at d = 256
       for (; j + 1 < n_tiles; j += 2) {
@@ -955,21 +969,29 @@ fa2_fwd_kernel(const Problem P) {
       // n_tiles % 4 == 0 and n_tiles >= 8: the loop leaves the last seven
       // iterations, of which the last four load the next item's K tiles 0..3
       // and the last two its V tiles 0..1; the last computes its S_0.
+      // Without the causal mask only the last tile can be masked.
       for (; j + 7 < n_tiles; j += 4) {
-        step(std::false_type{}, Ic<1>{}, j, sB, sA, pA, pB, Ic<0>{});
-        step(std::false_type{}, Ic<2>{}, j + 1, sA, sB, pB, pA, Ic<0>{});
-        step(std::false_type{}, Ic<3>{}, j + 2, sB, sA, pA, pB, Ic<0>{});
-        step(std::false_type{}, Ic<0>{}, j + 3, sA, sB, pB, pA, Ic<0>{});
+        step(std::false_type{}, Ic<1>{}, j, sB, sA, pA, pB, Ic<8>{});
+        step(std::false_type{}, Ic<2>{}, j + 1, sA, sB, pB, pA, Ic<8>{});
+        step(std::false_type{}, Ic<3>{}, j + 2, sB, sA, pA, pB, Ic<8>{});
+        step(std::false_type{}, Ic<0>{}, j + 3, sA, sB, pB, pA, Ic<8>{});
       }
-      step(std::false_type{}, Ic<1>{}, j, sB, sA, pA, pB, Ic<0>{});
-      step(std::false_type{}, Ic<2>{}, j + 1, sA, sB, pB, pA, Ic<0>{});
-      step(std::false_type{}, Ic<3>{}, j + 2, sB, sA, pA, pB, Ic<0>{});
-      step(std::false_type{}, Ic<0>{}, j + 3, sA, sB, pB, pA, Ic<1>{});
-      step(std::false_type{}, Ic<1>{}, j + 4, sB, sA, pA, pB, Ic<1>{});
-      step(std::false_type{}, Ic<2>{}, j + 5, sA, sB, pB, pA, Ic<3>{});
+      step(std::false_type{}, Ic<1>{}, j, sB, sA, pA, pB, Ic<8>{});
+      step(std::false_type{}, Ic<2>{}, j + 1, sA, sB, pB, pA, Ic<8>{});
+      step(std::false_type{}, Ic<3>{}, j + 2, sB, sA, pA, pB, Ic<8>{});
+      step(std::false_type{}, Ic<0>{}, j + 3, sA, sB, pB, pA, Ic<9>{});
+      step(std::false_type{}, Ic<1>{}, j + 4, sB, sA, pA, pB, Ic<9>{});
+      step(std::false_type{}, Ic<2>{}, j + 5, sA, sB, pB, pA, Ic<11>{});
       step(std::false_type{}, Ic<3>{}, j + 6, sB, sA, pA, pB, Ic<7>{});
       gemm2(j + 6, Ic<3>{}, vpre, pB);
     } else {
+      // First the tiles no wave masks, then the rest with the per-wave check.
+      for (; j + 3 < n_clear; j += 4) {
+        step(std::false_type{}, Ic<1>{}, j, sB, sA, pA, pB, Ic<8>{});
+        step(std::false_type{}, Ic<2>{}, j + 1, sA, sB, pB, pA, Ic<8>{});
+        step(std::false_type{}, Ic<3>{}, j + 2, sB, sA, pA, pB, Ic<8>{});
+        step(std::false_type{}, Ic<0>{}, j + 3, sA, sB, pB, pA, Ic<8>{});
+      }
       for (; j + 3 < n_tiles; j += 4) {
         step(std::false_type{}, Ic<1>{}, j, sB, sA, pA, pB, Ic<0>{});
         step(std::false_type{}, Ic<2>{}, j + 1, sA, sB, pB, pA, Ic<0>{});
