@@ -180,7 +180,8 @@ template <int D> struct Cfg8;
 template <> struct Cfg8<128> { static constexpr int BC = 32, NW = 8, QB = 1, OCC = 2, SGB = 0, RING = 4, PK = 2, PV = 2; };
 // Short key sequences at d = 128 (at most kShortKeys keys): half the query
 // rows per workgroup, so two workgroups share a CU and one's prologue and
-// epilogue overlap the other's loop.
+// epilogue overlap the other's loop.  The same shape serves grids too small
+// to give every CU a full-height workgroup.
 template <int D> struct CfgS;
 template <> struct CfgS<128> { static constexpr int BC = 32, NW = 4, QB = 1, OCC = 2, SGB = 0, RING = 4, PK = 4, PV = 2; };
 constexpr int kShortKeys = 1024;
@@ -1199,7 +1200,29 @@ int launch(const void* q, const void* k, const void* v, const float* ks, const f
   const int64_t rows = group * Nq;  // query rows per K/V head
   int bq = 0, bk = 0, nw = 0;
   fa2_tile_config(d, dtype, &bq, &bk, &nw);
-  const bool short_keys = !q8 && d == 128 && Nk <= kShortKeys;
+  // Persistent workgroups (the d = 128 tile shape, one workgroup per CU) when
+  // every one gets at least two items of the same length whose key-tile count
+  // the ring's four slots divide and is at least 8 (the ring then carries on
+  // from one item into the next at slot 0), also for short key sequences.
+  bool persist = false;
+  int cus = 0;
+  if (!q8 && !causal && d == 128) {
+    const int64_t k_tiles = (Nk + Cfg<128>::BC - 1) / Cfg<128>::BC;
+    const int64_t items = B * Hkv * ((rows + bq - 1) / bq);
+    if (k_tiles >= 8 && k_tiles % Cfg<128>::RING == 0 && items % 8 == 0) {
+      cus = cu_count();
+      persist = cus > 0 && cus % 8 == 0 && items >= 2 * (int64_t)cus;
+    }
+  }
+  // Half-height workgroups for short key sequences, and when the full-height
+  // grid would leave compute units without a workgroup (few heads and query
+  // rows, as in a prefill chunk against a cache): twice the workgroups.
+  bool short_keys = !persist && !q8 && d == 128 && Nk <= kShortKeys;
+  if (!persist && !q8 && d == 128 && !short_keys) {
+    const int64_t items = B * Hkv * ((rows + bq - 1) / bq);
+    const int n_cu = cu_count();
+    short_keys = n_cu > 0 && items < n_cu;
+  }
   if (q8) {
     bq = Cfg8<128>::NW * 32 * Cfg8<128>::QB;
     nw = Cfg8<128>::NW;
@@ -1252,19 +1275,11 @@ int launch(const void* q, const void* k, const void* v, const float* ks, const f
                : d == 128 ? (short_keys ? pick<128, false, true>(fp16, mode, causal)
                                         : pick<128, false>(fp16, mode, causal))
                           : pick<256, false>(fp16, mode, causal);
-  // Persistent workgroups, one per CU, when every one gets at least two items
-  // of the same length whose tile count the ring's four slots divide (the
-  // ring then carries on from one item into the next at slot 0).
   int64_t grid = groups;
-  if (!q8 && !causal && !short_keys && d == 128 && Nk > 0 &&
-      ((Nk + Cfg<128>::BC - 1) / Cfg<128>::BC) % Cfg<128>::RING == 0 &&
-      groups % 8 == 0) {
-    const int cus = cu_count();
-    if (cus > 0 && cus % 8 == 0 && groups >= 2 * (int64_t)cus) {
-      fn = fp16 ? pick_mode<128, true, false, false, false, true>(mode)
-                : pick_mode<128, false, false, false, false, true>(mode);
-      grid = cus;
-    }
+  if (persist) {
+    fn = fp16 ? pick_mode<128, true, false, false, false, true>(mode)
+              : pick_mode<128, false, false, false, false, true>(mode);
+    grid = cus;
   }
   void* args[] = {&P};
   hipError_t err = hipLaunchKernel((const void*)fn, dim3((unsigned)grid),

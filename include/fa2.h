@@ -164,7 +164,10 @@ const char* fa2_strerror(int status);
  * dtype: *block_q query rows per workgroup, *block_k key rows per K/V tile,
  * *waves wavefronts (of 64 lanes) per workgroup.  At d = 128 a call with at
  * most 1024 keys uses half the waves and query rows instead (two workgroups
- * then share a compute unit); block_q here is always a multiple of that.
+ * then share a compute unit), unless it is non-causal and large enough for
+ * one persistent workgroup per compute unit; so does a call whose
+ * full-height workgroups would be fewer than the compute units.  block_q
+ * here is always a multiple of the smaller shape.
  * Host-only, no HIP call.  Returns FA2_OK, FA2_ERR_HEADDIM, FA2_ERR_DTYPE or
  * FA2_ERR_NULL.
  */

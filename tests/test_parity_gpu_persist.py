@@ -1,12 +1,15 @@
 """GPU parity of the persistent-workgroup launches (needs an MI355X).
 
-Non-causal d = 128 calls with enough (K/V head, query tile) items, long keys
-and a key-tile count divisible by 4 run one workgroup per compute unit, each
-walking several items with its key/value ring carried from one item into the
-next.  Each case here checks that launch against the oracle on sampled rows,
+Non-causal d = 128 calls with enough (K/V head, query tile) items and a
+key-tile count of at least 8 that 4 divides run one workgroup per compute
+unit, each walking several items with its key/value ring carried from one
+item into the next.  Each case here checks that launch against the oracle on sampled rows,
 and bit for bit against launches of one K/V head group at a time, which are
 too small for persistent workgroups and run one item per workgroup: a row's
-arithmetic does not depend on how the items are spread over workgroups.
+arithmetic does not depend on how the items are spread over workgroups.  The
+same check covers the non-persistent full-height launch (256-row workgroups),
+whose per-group launches, with fewer items than compute units, use 128-row
+workgroups.
 """
 import math
 
@@ -40,17 +43,29 @@ def persistent(B, Hq, Hkv, Nq, Nk):
     """Whether the call's shape takes the persistent launch on this device."""
     groups = B * Hkv * math.ceil(Hq // Hkv * Nq / BLOCK_Q)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    return (Nk > 1024 and math.ceil(Nk / BLOCK_K) % 4 == 0 and groups % 8 == 0
+    tiles = math.ceil(Nk / BLOCK_K)
+    return (tiles >= 8 and tiles % 4 == 0 and groups % 8 == 0
             and cus % 8 == 0 and groups >= 2 * cus)
 
 
 # (B, Hq, Hkv, Nq, Nk, dtype): 512 items (two per workgroup), 576 (two or
-# three), ragged query tiles and a ragged last key tile, grouped heads.
+# three), ragged query tiles and a ragged last key tile, grouped heads; short
+# key sequences down to the fewest key tiles the persistent loop takes (8).
 CASES = [
     (2, 64, 64, 1000, 1130, "bf16"),
     (4, 32, 8, 1100, 2048, "fp16"),
     (2, 128, 16, 520, 1152, "bf16"),
+    (16, 16, 16, 512, 500, "fp16"),
+    (4, 64, 16, 600, 256, "bf16"),
 ]
+
+
+def full_height(B, Hq, Hkv, Nq, Nk):
+    """Whether a non-causal call takes one full-height (256-row) workgroup per
+    item: not persistent, and at least as many items as compute units."""
+    groups = B * Hkv * math.ceil(Hq // Hkv * Nq / BLOCK_Q)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    return Nk > 1024 and not persistent(B, Hq, Hkv, Nq, Nk) and groups >= cus
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,dtype", CASES)
@@ -59,6 +74,21 @@ def test_persistent_equals_per_group_launches(B, Hq, Hkv, Nq, Nk, dtype, scale_k
     announce("persistent", B, Hq, Hkv, Nq, Nk, dtype, scale_kind)
     if not persistent(B, Hq, Hkv, Nq, Nk):
         pytest.skip("shape does not take the persistent launch on this device")
+    check_against_groups(B, Hq, Hkv, Nq, Nk, dtype, scale_kind)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,dtype", [(2, 128, 128, 1100, 1100, "bf16"),
+                                                  (1, 64, 16, 2000, 2050, "fp16")])
+def test_full_height_equals_per_group_launches(B, Hq, Hkv, Nq, Nk, dtype):
+    """Key-tile counts that 4 does not divide keep one full-height workgroup
+    per item; the per-group launches of the same rows use half-height ones."""
+    announce("full height", B, Hq, Hkv, Nq, Nk, dtype)
+    if not full_height(B, Hq, Hkv, Nq, Nk):
+        pytest.skip("shape does not take full-height workgroups on this device")
+    check_against_groups(B, Hq, Hkv, Nq, Nk, dtype, "default")
+
+
+def check_against_groups(B, Hq, Hkv, Nq, Nk, dtype, scale_kind):
     scale = {"default": 1.0 / math.sqrt(128), "negative": -0.15, "zero": 0.0}[scale_kind]
     seed = B * 1000 + Hq + Nk
     q = rand((B, Hq, Nq, 128), dtype, seed).to(DEV)
@@ -87,7 +117,7 @@ def test_persistent_equals_per_group_launches(B, Hq, Hkv, Nq, Nk, dtype, scale_k
                                       rows=rows, nthreads=8)
     og = o.cpu().double().numpy().reshape(-1, 128)[rows]
     lg = lse.cpu().double().numpy().reshape(-1)[rows]
-    assert_parity(og, lg, o_ref, lse_ref, "persistent %s" % ((B, Hq, Hkv, Nq, Nk, dtype, scale),),
+    assert_parity(og, lg, o_ref, lse_ref, "launch %s" % ((B, Hq, Hkv, Nq, Nk, dtype, scale),),
                   lse_abs=1e-3)
 
 

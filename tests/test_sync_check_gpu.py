@@ -80,6 +80,7 @@ def test_head_dims_match_race_check_build(d, H, causal):
     (2, 64, 64, 1000, 1130, "bf16", None),     # persistent, ragged tiles
     (4, 32, 8, 1100, 2048, "fp16", -0.15),     # persistent, grouped heads, negative scale
     (2, 128, 16, 520, 1152, "bf16", 0.0),      # persistent, zero scale
+    (16, 16, 16, 512, 500, "fp16", None),      # persistent, short keys (causal: four waves)
     (2, 4, 2, 300, 777, "bf16", None),         # one item per workgroup, Nq != Nk
 ])
 def test_shapes_match_race_check_build(B, Hq, Hkv, Nq, Nk, dtype, scale):
