@@ -193,7 +193,12 @@ template <int X> using Ic = std::integral_constant<int, X>;
 // p = exp2(t - m_ref) is summed over each lane's keys of a tile; while that
 // sum stays at or below kSumLimit no p exceeds it, and the reference max is
 // left alone.  Otherwise the row's reference moves to its true running max.
-constexpr float kSumLimit = 256.0f;
+// The limit only has to keep every p, rounded to the 16-bit type of the
+// second product, finite with room to spare (fp16 tops out at 65504); a
+// higher limit lets the reference move less often when the running max keeps
+// climbing (peaky rows: 2^14 instead of 2^8 takes about a third of the
+// tiles of N(0, 16) logits off the rescale path).
+constexpr float kSumLimit = 16384.0f;
 
 // Race-check build (-DFA2_SYNC_CHECK=1, a second library used by the tests):
 // every iteration waits for all of its loads and synchronises the workgroup

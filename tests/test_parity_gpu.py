@@ -120,6 +120,33 @@ def test_stress_distribution_all_head_dims(d):
     check_full(q, k, v, "bf16", 1.0 / math.sqrt(d), "stress d=%d" % d)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_running_max_jumps_late(d, dtype):
+    """Keys far into the sequence whose logits jump far above everything
+    before them (to about 30 and then 60 in log2 units, so the tile's sum of
+    p passes any limit the lazy reference max allows): the rows' reference
+    must move, the output already accumulated must be rescaled, and the
+    result stays within tolerance.  Full comparison with the oracle."""
+    announce("late max jump", d, dtype)
+    B, H, N = 1, 2, 1500
+    g = torch.Generator().manual_seed(40 + d)
+    q = torch.randn((B, H, N, d), generator=g)
+    k = torch.randn((B, H, N, d), generator=g)
+    v = torch.randn((B, H, N, d), generator=g)
+    scale = 1.0 / math.sqrt(d)
+    c = scale / math.log(2.0)  # logit in log2 units per unit of q.k
+    # key 700 along query row 0 with log2-unit logit 30 for that row; key 1300
+    # along row 1 with 60 (other rows see them at about +-30/sqrt(d) and
+    # +-60/sqrt(d))
+    for h in range(H):
+        for key, row, target in ((700, 0, 30.0), (1300, 1, 60.0)):
+            qr = q[0, h, row]
+            k[0, h, key] = qr * (target / (c * float(qr @ qr)))
+    q, k, v = q.to(_TD[dtype]), k.to(_TD[dtype]), v.to(_TD[dtype])
+    check_full(q, k, v, dtype, scale, "late max jump d=%d %s" % (d, dtype))
+
+
 def test_empty_inputs():
     announce("empty")
     for shape in ((0, 2, 64, 128), (1, 0, 64, 128), (1, 2, 0, 128)):
