@@ -228,9 +228,16 @@ def main():
 
     tflops = w.flops / (ms * 1e-3) / 1e12
     traffic = measured_traffic(w.name)
-    roofline = {"bound": "mfma", "achieved": round(tflops, 3), "peak": MFMA_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(tflops / MFMA_PEAK_TFLOPS, 4),
-                "traffic": traffic}
+    # The bound is the roof the workload's arithmetic intensity (FLOPs per
+    # algorithmic HBM byte) sits under: left of the ridge the HBM roof.
+    if w.flops / w.algo_bytes < MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
+        gbs = w.algo_bytes / (ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
+    else:
+        roofline = {"bound": "mfma", "achieved": round(tflops, 3), "peak": MFMA_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(tflops / MFMA_PEAK_TFLOPS, 4),
+                    "traffic": traffic}
     out = {
         "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
