@@ -1203,43 +1203,15 @@ int launch(const void* q, const void* k, const void* v, const float* ks, const f
   const int64_t group = Hq / Hkv;
   if (group > lim / (Nq * d)) return FA2_ERR_SHAPE;
   const int64_t rows = group * Nq;  // query rows per K/V head
-  int bq = 0, bk = 0, nw = 0;
-  fa2_tile_config(d, dtype, &bq, &bk, &nw);
-  // Persistent workgroups (the d = 128 tile shape, one workgroup per CU) when
-  // every one gets at least two items of the same length whose key-tile count
-  // the ring's four slots divide and is at least 8 (the ring then carries on
-  // from one item into the next at slot 0), also for short key sequences.
-  bool persist = false;
-  int cus = 0;
-  if (!q8 && !causal && d == 128) {
-    const int64_t k_tiles = (Nk + Cfg<128>::BC - 1) / Cfg<128>::BC;
-    const int64_t items = B * Hkv * ((rows + bq - 1) / bq);
-    if (k_tiles >= 8 && k_tiles % Cfg<128>::RING == 0 && items % 8 == 0) {
-      cus = cu_count();
-      persist = cus > 0 && cus % 8 == 0 && items >= 2 * (int64_t)cus;
-    }
-  }
-  // Half-height workgroups for short key sequences, and when the full-height
-  // grid would leave compute units without a workgroup (few heads and query
-  // rows, as in a prefill chunk against a cache): twice the workgroups.
-  bool short_keys = !persist && !q8 && d == 128 && Nk <= kShortKeys;
-  if (!persist && !q8 && d == 128 && !short_keys) {
-    const int64_t items = B * Hkv * ((rows + bq - 1) / bq);
-    const int n_cu = cu_count();
-    short_keys = n_cu > 0 && items < n_cu;
-  }
-  if (q8) {
-    bq = Cfg8<128>::NW * 32 * Cfg8<128>::QB;
-    nw = Cfg8<128>::NW;
-  } else if (short_keys) {
-    bq = CfgS<128>::NW * 32 * CfgS<128>::QB;
-    nw = CfgS<128>::NW;
-  }
-  const int64_t q_tiles = (rows + bq - 1) / bq;
   if (B > (((int64_t)1 << 31) - 1) / Hq) return FA2_ERR_SHAPE;
   const int64_t bh = B * Hq;
-  if (B * Hkv > (((int64_t)1 << 31) - 1) / q_tiles) return FA2_ERR_SHAPE;
-  const int64_t groups = B * Hkv * q_tiles;
+  // The workgroup count fits a 1-D grid for every tile height the call may
+  // take (the smallest, 128 query rows, gives the most workgroups).
+  int bq = 0, bk = 0, nw = 0;
+  fa2_tile_config(d, dtype, &bq, &bk, &nw);
+  const int64_t bq_min = q8 ? Cfg8<128>::NW * 32 * Cfg8<128>::QB
+                       : d == 128 ? CfgS<128>::NW * 32 * CfgS<128>::QB : bq;
+  if (B * Hkv > (((int64_t)1 << 31) - 1) / ((rows + bq_min - 1) / bq_min)) return FA2_ERR_SHAPE;
   if (!q || !o || !lse || (Nk > 0 && (!k || !v))) return FA2_ERR_NULL;
   if (q8 && (!ks || !vs)) return FA2_ERR_NULL;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return FA2_ERR_ALIGN;
@@ -1255,6 +1227,39 @@ int launch(const void* q, const void* k, const void* v, const float* ks, const f
     if (overlaps(o, qbytes, in[i], in_bytes[i]) || overlaps(lse, lbytes, in[i], in_bytes[i]))
       return FA2_ERR_ALIAS;
   if (overlaps(lse, lbytes, o, qbytes)) return FA2_ERR_ALIAS;
+
+  // Launch shape (the arguments are valid; from here on HIP may be queried).
+  // Persistent workgroups (the d = 128 tile shape, one workgroup per CU) when
+  // every one gets at least two items of the same length whose key-tile count
+  // the ring's four slots divide and is at least 8 (the ring then carries on
+  // from one item into the next at slot 0), also for short key sequences.
+  const int64_t items_full = B * Hkv * ((rows + bq - 1) / bq);  // full-height workgroups
+  bool persist = false;
+  int cus = 0;
+  if (!q8 && !causal && d == 128) {
+    const int64_t k_tiles = (Nk + Cfg<128>::BC - 1) / Cfg<128>::BC;
+    if (k_tiles >= 8 && k_tiles % Cfg<128>::RING == 0 && items_full % 8 == 0) {
+      cus = cu_count();
+      persist = cus > 0 && cus % 8 == 0 && items_full >= 2 * (int64_t)cus;
+    }
+  }
+  // Half-height workgroups for short key sequences, and when the full-height
+  // grid would leave compute units without a workgroup (few heads and query
+  // rows, as in a prefill chunk against a cache): twice the workgroups.
+  bool short_keys = !persist && !q8 && d == 128 && Nk <= kShortKeys;
+  if (!persist && !q8 && d == 128 && !short_keys) {
+    const int n_cu = cu_count();
+    short_keys = n_cu > 0 && items_full < n_cu;
+  }
+  if (q8) {
+    bq = Cfg8<128>::NW * 32 * Cfg8<128>::QB;
+    nw = Cfg8<128>::NW;
+  } else if (short_keys) {
+    bq = CfgS<128>::NW * 32 * CfgS<128>::QB;
+    nw = CfgS<128>::NW;
+  }
+  const int64_t q_tiles = (rows + bq - 1) / bq;
+  const int64_t groups = B * Hkv * q_tiles;
 
   // logits in log2 units: t = s * scale * log2(e)
   const float c = (float)((double)scale * 1.4426950408889634074);

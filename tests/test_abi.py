@@ -86,6 +86,10 @@ def call(q=A, k=A + 0x1000000, v=A + 0x2000000, o=A + 0x3000000,
     (dict(o=0), fa2.ERR_NULL), (dict(lse=0), fa2.ERR_NULL),
     (dict(B=-1), fa2.ERR_SHAPE), (dict(H=-2), fa2.ERR_SHAPE), (dict(N=-5), fa2.ERR_SHAPE),
     (dict(N=1 << 31), fa2.ERR_SHAPE), (dict(B=1 << 40, H=1 << 30), fa2.ERR_SHAPE),
+    # 2^26 heads of 32 half-height (128-row) query tiles: one past the 1-D grid
+    (dict(B=1 << 22, H=16, N=4096), fa2.ERR_SHAPE),
+    # a shape that takes the persistent launch still reports the null pointer
+    (dict(B=4, H=16, N=4096, q=0), fa2.ERR_NULL),
     (dict(d=96), fa2.ERR_HEADDIM), (dict(d=0), fa2.ERR_HEADDIM), (dict(d=512), fa2.ERR_HEADDIM),
     (dict(dtype=2), fa2.ERR_DTYPE), (dict(dtype=-1), fa2.ERR_DTYPE),
     (dict(scale=float("nan")), fa2.ERR_SCALE), (dict(scale=float("inf")), fa2.ERR_SCALE),
