@@ -515,6 +515,15 @@ fa2_fwd_kernel(const Problem P) {
     const int r0 = q0 % P.nq;
     wave_row_min = r0 + 32 * QB - 1 < P.nq ? r0 : 0;
   }
+  // Causal: the last key tile any row of this wave sees (-1: none), from its
+  // largest row within a head (nq - 1 if its rows wrap to the next head).
+  int wave_last = 0;
+  if constexpr (CAUSAL) {
+    const int r0 = q0 % P.nq;
+    const int row_max = r0 + 32 * QB - 1 < P.nq ? r0 + 32 * QB - 1 : P.nq - 1;
+    const int last_key = min(row_max + P.causal_off, N - 1);
+    wave_last = last_key < 0 ? -1 : last_key / BC;
+  }
 
   // Key tiles this workgroup needs: all of them, or with the causal mask those
   // up to the last key its rows see.  A workgroup whose rows see no key writes
@@ -847,7 +856,11 @@ fa2_fwd_kernel(const Problem P) {
     // PERSIST: the last iteration's S_{j+1} is the next item's S_0, against
     // its query tile (landed by the end of iteration 1).
     if constexpr ((TL & 4) != 0) load_qf();
-    gemm1(j + 1, S1{}, kpre, s_nxt);
+    // Causal, past the diagonal: a wave whose rows see no key of tile j+1
+    // skips S_{j+1}.  The stale registers it leaves are never used: the next
+    // iteration masks every key of that tile for this wave (to -inf, so P is
+    // 0 and adds nothing to O), as it would the computed logits.
+    if (!(CAUSAL && (TL & 8) == 0) || j + 1 <= wave_last) gemm1(j + 1, S1{}, kpre, s_nxt);
     if constexpr (!decltype(first)::value) gemm2(j - 1, S3{}, vpre, p_prev);
     float rs[QB];
     bool over = false;
