@@ -866,11 +866,18 @@ fa2_fwd_kernel(const Problem P) {
     bool over = false;
 #pragma unroll
     for (int b = 0; b < QB; ++b) {
-      rs[b] = probs(sf[b], p_cur[b], m_ref[b], c_q[b]);
-      over |= !(rs[b] <= kSumLimit);  // also true for inf / NaN
-      // Causal rows that see no key keep m_ref = -inf; they take the rare
-      // path, which leaves their p at 0.
-      if constexpr (CAUSAL) over |= m_ref[b] == -INFINITY;
+      if constexpr (decltype(first)::value) {
+        // The first tile: every reference is still -inf, so every row takes
+        // the path below, which forms the probabilities.
+        rs[b] = INFINITY;
+        over = true;
+      } else {
+        rs[b] = probs(sf[b], p_cur[b], m_ref[b], c_q[b]);
+        over |= !(rs[b] <= kSumLimit);  // also true for inf / NaN
+        // Causal rows that see no key keep m_ref = -inf; they take the rare
+        // path, which leaves their p at 0.
+        if constexpr (CAUSAL) over |= m_ref[b] == -INFINITY;
+      }
     }
     constexpr int MF = QB * ((MODE == kZero ? 0 : KO) + (decltype(first)::value ? 0 : VO));
 #pragma unroll
@@ -888,7 +895,7 @@ fa2_fwd_kernel(const Problem P) {
 
     // While the unrounded sum of a lane's p stays at or below kSumLimit no p
     // exceeds it and the reference max stands.  Otherwise (always on the
-    // first tile, where the sum is inf or NaN) rows whose sum outgrew the
+    // first tile, where no reference exists yet) rows whose sum outgrew the
     // limit move their reference to their running max, rescale O and l, and
     // get their p recomputed; other rows keep their reference, so a row's
     // arithmetic never depends on its wave-mates.
