@@ -916,13 +916,11 @@ fa2_fwd_kernel(const Problem P) {
         const float m_new = move ? fmaxf(m_ref[b], t_row) : m_ref[b];
         const float alpha =
             m_new == m_ref[b] ? 1.0f : __builtin_amdgcn_exp2f(m_ref[b] - m_new);
-        if constexpr (!decltype(first)::value) {  // on the first tile O and l are still 0
 #pragma unroll
-          for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) acc[b][db][i] *= alpha;
-          l_part[b] *= alpha;
-        }
+          for (int i = 0; i < 16; ++i) acc[b][db][i] *= alpha;
+        l_part[b] *= alpha;
         m_ref[b] = m_new;
         rs[b] = probs(sf[b], p_cur[b], m_ref[b], c_q[b]);
       }
