@@ -108,6 +108,21 @@ def write_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, workload
     print(json.dumps(out))
 
 
+def roofline_of(w, ms, traffic):
+    """The roofline object for workload w at ms per launch.  The bound is the
+    roof the workload's arithmetic intensity (FLOPs per algorithmic HBM byte)
+    sits under: left of the ridge (peak FLOP/s over peak bytes/s) the HBM
+    roof, in GB/s; otherwise the matrix-core roof, in TFLOP/s."""
+    if w.flops / w.algo_bytes < MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
+        gbs = w.algo_bytes / (ms * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
+    tflops = w.flops / (ms * 1e-3) / 1e12
+    return {"bound": "mfma", "achieved": round(tflops, 3), "peak": MFMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(tflops / MFMA_PEAK_TFLOPS, 4),
+            "traffic": traffic}
+
+
 def cpu_baseline(w, q, k, v):
     """The fp64 oracle as it stands, on whole heads of the same inputs, until
     about CPU_SAMPLE_SECONDS of wall time have passed (at least one head)."""
@@ -227,17 +242,7 @@ def main():
         raise RuntimeError("non-finite output")
 
     tflops = w.flops / (ms * 1e-3) / 1e12
-    traffic = measured_traffic(w.name)
-    # The bound is the roof the workload's arithmetic intensity (FLOPs per
-    # algorithmic HBM byte) sits under: left of the ridge the HBM roof.
-    if w.flops / w.algo_bytes < MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
-        gbs = w.algo_bytes / (ms * 1e-3) / 1e9
-        roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
-    else:
-        roofline = {"bound": "mfma", "achieved": round(tflops, 3), "peak": MFMA_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(tflops / MFMA_PEAK_TFLOPS, 4),
-                    "traffic": traffic}
+    roofline = roofline_of(w, ms, measured_traffic(w.name))
     out = {
         "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
