@@ -44,3 +44,30 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, cwd=ROOT, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_bench_parity_against_the_oracle_on_the_cpu():
+    """The parity object of the bench line, fed outputs made on the CPU: the
+    oracle's own result rounded to bf16 passes; the same with one element
+    moved by 0.05 fails (and the error is the one planted)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from flashattention_forward_tile_amd.workloads import bits, workload_inputs
+
+    w = WORKLOADS["tiny"]
+    q, k, v = workload_inputs(w, seed=0)
+    o_ref, lse_ref = oracle.attention(bits(q), bits(k), bits(v), w.dtype, w.scale)
+    o = torch.from_numpy(o_ref).to(torch.bfloat16)
+    lse = torch.from_numpy(lse_ref).to(torch.float32)
+    base, par = bench.cpu_baseline(w, q, k, v, o, lse)
+    assert base["kind"] == "oracle" and base["cores"] >= 1
+    assert par["heads"] == w.B * w.H and par["within_tolerance"], par
+    assert par["o_max_abs"] < 1e-2 and par["lse_max_rel"] < 1e-6
+    bad = o.clone()
+    bad[0, 1, 17, 3] += 0.05
+    _, par = bench.cpu_baseline(w, q, k, v, bad, lse)
+    assert not par["within_tolerance"]
+    assert par["o_max_abs"] == pytest.approx(
+        abs(float(bad[0, 1, 17, 3]) - o_ref[0, 1, 17, 3]), rel=1e-6)
