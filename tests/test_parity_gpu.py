@@ -105,8 +105,11 @@ def test_ragged_lengths(N, dtype, d):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
-@pytest.mark.parametrize("scale", [0.0, -0.09, 0.5, 1e-3, -1.0])
+@pytest.mark.parametrize("scale", [0.0, -0.09, 0.5, 1e-3, -1.0, 40.0, -40.0])
 def test_scales(scale, dtype):
+    """Scales from uniform attention (0) to near one-hot rows (+-40: logits
+    with a spread of about 450, lse up to about 2300, so the running max jumps
+    by hundreds of log2 units)."""
     announce("scale", scale, dtype)
     q, k, v = make_inputs(2, 2, 300, 128, dtype, "normal", seed=5)
     # lse can sit near 0 for a negative scale; bound it absolutely there too
