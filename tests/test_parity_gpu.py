@@ -281,6 +281,34 @@ def test_non_default_stream():
     assert torch.equal(o, ref_o) and torch.equal(lse, ref_l)
 
 
+def test_concurrent_streams():
+    """Different calls in flight at once on two streams (a persistent launch,
+    a causal grouped-head launch, a d = 64 launch) give bit for bit what each
+    gives alone: the library keeps no state between or across calls."""
+    announce("concurrent streams")
+    cases = [
+        (make_inputs(4, 16, 2048, 128, "bf16", "normal", seed=31), False),
+        (make_inputs(2, 8, 700, 128, "fp16", "normal", seed=32, Hkv=2, Nk=1500), True),
+        (make_inputs(2, 4, 900, 64, "bf16", "normal", seed=33), False),
+    ]
+    dev = [((q.to(DEV), k.to(DEV), v.to(DEV)), c) for (q, k, v), c in cases]
+    alone = []
+    for (q, k, v), c in dev:
+        alone.append(fa2.fwd(q, k, v, causal=c))
+        torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    together = []
+    for rep in range(3):
+        for i, ((q, k, v), c) in enumerate(dev):
+            with torch.cuda.stream(streams[(i + rep) % 2]):
+                together.append((i, fa2.fwd(q, k, v, causal=c)))
+    torch.cuda.synchronize()
+    for i, (o, lse) in together:
+        assert torch.equal(o, alone[i][0]) and torch.equal(lse, alone[i][1]), i
+
+
 def test_device_argument_errors():
     announce("errors")
     q = torch.randn(1, 2, 64, 128, device=DEV).to(torch.bfloat16)
