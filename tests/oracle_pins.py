@@ -578,6 +578,34 @@ def pin_int8_brute_force(orc):
                         assert lse[b, h, i] == -math.inf
 
 
+def pin_rows_subset_with_every_option(orc):
+    """rows= picks exactly the full result's rows with every option at once
+    (causal mask, grouped heads, Nq != Nk, both dtypes, and the INT8 cache):
+    the sampled comparisons of the GPU tests rest on it.  A row's position
+    within its head, which the mask needs, comes from its flat id, not from
+    its place in the sample."""
+    rng = np.random.default_rng(7)
+    B, Hq, Hkv, Nq, Nk, d = 2, 4, 2, 37, 53, 8
+    flat = B * Hq * Nq
+    rows = rng.choice(flat, size=41, replace=False)
+    for causal in (False, True):
+        for dtype in DTYPES:
+            q = _rand16((B, Hq, Nq, d), dtype, 150)
+            k = _rand16((B, Hkv, Nk, d), dtype, 151)
+            v = _rand16((B, Hkv, Nk, d), dtype, 152)
+            o, lse = _run(orc, q, k, v, dtype, 0.4, causal=causal)
+            orow, lrow = _run(orc, q, k, v, dtype, 0.4, causal=causal, rows=rows)
+            assert np.array_equal(orow, o.reshape(-1, d)[rows]), (causal, dtype)
+            assert np.array_equal(lrow, lse.reshape(-1)[rows]), (causal, dtype)
+        q = _rand16((B, Hq, Nq, 128), "bf16", 153)
+        kq, ks, vq, vs = _int8_cache(B, Hkv, Nk, 128, 154)
+        o, lse = orc.attention_kv_int8(bits(q), kq, ks, vq, vs, "bf16", 0.1, causal=causal)
+        orow, lrow = orc.attention_kv_int8(bits(q), kq, ks, vq, vs, "bf16", 0.1,
+                                           causal=causal, rows=rows)
+        assert np.array_equal(orow, o.reshape(-1, 128)[rows]), causal
+        assert np.array_equal(lrow, lse.reshape(-1)[rows]), causal
+
+
 ALL_PINS = [
     pin_decode_every_pattern,
     pin_worked_examples,
@@ -603,4 +631,5 @@ ALL_PINS = [
     pin_int8_reduces_to_dequantized_attention,
     pin_int8_zero_query_is_uniform,
     pin_int8_brute_force,
+    pin_rows_subset_with_every_option,
 ]

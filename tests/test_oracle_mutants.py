@@ -31,6 +31,8 @@ MUTANTS = [
     ("causal_top_left", "if (J->causal && i + 1 + Nk - Nq < visible) visible = i + 1 + Nk - Nq;",
      "if (J->causal && i + 1 < visible) visible = i + 1;"),
     ("empty_row_lse_zero", "*lse_out = -INFINITY;", "*lse_out = 0.0;"),
+    ("sampled_row_position_from_sample", "int64_t head = flat / Nq, i = flat % Nq;",
+     "int64_t head = flat / Nq, i = r % Nq;"),
     # INT8 key/value cache
     ("int8_truncates", "float code = rintf(u * inv);", "float code = truncf(u * inv);"),
     ("int8_ties_away", "float code = rintf(u * inv);", "float code = roundf(u * inv);"),
