@@ -103,3 +103,58 @@ def test_int8_headline_sampled(causal):
     bq, _, _ = fa2.tile_config(128)
     check(inputs, "bf16", 1.0 / math.sqrt(128), causal, "int8 headline causal=%d" % causal,
           rows=sample_rows(4, 16, 4096, bq, per_head=4, seed=2))
+
+
+def test_int8_query_codes_golden_on_gpu():
+    """The kernel's query codes are the hand-derived ones of
+    tests/golden/int8_query_codes.json (ties to even, key scales folded in,
+    a zero row, a row where binary32 and exact rationals disagree).  Each
+    fixture row, padded with zeros to d = 128, meets one-hot keys (key j holds
+    code 1 in channel j) and identity values, so the output is the softmax
+    over channels of scale * sq * code: a closed form computed here in fp64
+    from the fixture, with the scale chosen so that one code unit moves a
+    channel's probability by about 5%, far above the 16-bit rounding."""
+    import json
+    import os
+
+    announce("int8 golden codes on the GPU")
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                        "int8_query_codes.json")
+    cases = json.load(open(path))["cases"]
+    d = 128
+    eye = torch.eye(d, dtype=torch.int8)
+    for dtype in ("bf16", "fp16"):
+        sel = [c for c in cases if c["dtype"] == dtype]
+        if not sel:
+            continue
+        B = len(sel)
+        td = torch.bfloat16 if dtype == "bf16" else torch.float16
+        q = torch.zeros((B, 1, 1, d), dtype=torch.float32)
+        ks = torch.ones((B, 1, d), dtype=torch.float32)
+        for b, c in enumerate(sel):
+            n = len(c["q"])
+            q[b, 0, 0, :n] = torch.tensor(c["q"], dtype=torch.float32)
+            ks[b, 0, :n] = torch.tensor(c["ks"], dtype=torch.float32)
+        q = q.to(td)
+        for c in sel:  # the fixture's query values are exact in its dtype
+            exact = torch.tensor(c["q"], dtype=torch.float32)
+            assert torch.equal(exact.to(td).float(), exact), c["name"]
+        kq = eye.expand(B, 1, d, d).contiguous()
+        vq = eye.expand(B, 1, d, d).contiguous()
+        vs = torch.ones((B, 1, d), dtype=torch.float32)
+        for b, c in enumerate(sel):
+            sq = np.frombuffer(np.uint32(int(c["sq_bits"], 16)).tobytes(), np.float32)[0]
+            codes = np.zeros(d)
+            codes[:len(c["codes"])] = c["codes"]
+            scale = 0.05 / float(sq) if sq > 0 else 0.3
+            o, lse = fa2.fwd_kv_int8(q[b:b + 1].to(DEV), kq[b:b + 1].to(DEV), ks[b:b + 1].to(DEV),
+                                     vq[b:b + 1].to(DEV), vs[b:b + 1].to(DEV), scale=scale)
+            torch.cuda.synchronize()
+            s = scale * float(sq) * codes
+            p = np.exp(s - s.max())
+            o_ref = p / p.sum()
+            lse_ref = s.max() + math.log(p.sum())
+            og = o.cpu().double().numpy().reshape(-1)
+            rel = np.abs(og - o_ref) / o_ref
+            assert rel.max() <= 1e-2, (c["name"], float(rel.max()), int(rel.argmax()))
+            assert abs(float(lse.cpu()) - lse_ref) <= 1e-4 * max(1.0, abs(lse_ref)), c["name"]
