@@ -189,6 +189,38 @@ def test_uniform_attention(N):
     assert np.allclose(f64(lse), math.log(N), rtol=1e-6, atol=0)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_worked_examples_on_gpu(dtype):
+    """The hand-derived examples of tests/golden/worked_examples.json (exact
+    fractions for O, ln of a fraction for lse), zero-padded to d = 64 (padding
+    adds nothing to q.k and gives zero output channels), straight against the
+    printed values: no oracle in between.  The bars are the output's own
+    rounding (half an ulp of 16-bit O) plus that of P."""
+    import json
+    import os
+    from fractions import Fraction
+
+    announce("worked examples", dtype)
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                        "worked_examples.json")
+    td = _TD[dtype]
+    for case in json.load(open(path))["cases"]:
+        sign = -1.0 if case["scale"].startswith("-") else 1.0
+        scale = sign * math.log(2.0 if case["scale"].lstrip("-") == "ln2" else 3.0)
+        qa, ka, va = (torch.tensor(case[x], dtype=torch.float32) for x in ("q", "k", "v"))
+        N, dd = qa.shape
+        pad = lambda t: torch.nn.functional.pad(t, (0, 64 - t.shape[1]))[None, None].to(td)
+        o, lse = run_gpu(pad(qa), pad(ka), pad(va), scale)
+        o = f64(o)[0, 0]
+        o_ref = np.array([[float(Fraction(x)) for x in row] for row in case["O"]])
+        lse_ref = np.array([math.log(Fraction(x)) for x in case["lse_ln"]])
+        ulp = 2.0 ** (-8 if dtype == "bf16" else -11)
+        bar = ulp * np.maximum(np.abs(o_ref), 1.0) + ulp * va.abs().max().item()
+        assert np.all(np.abs(o[:, :dd] - o_ref) <= bar), (case["name"], o[:, :dd], o_ref)
+        assert np.all(o[:, dd:] == 0.0), case["name"]
+        assert np.allclose(f64(lse)[0, 0], lse_ref, rtol=0, atol=1e-5), case["name"]
+
+
 def test_rank_one_logits_closed_form():
     """Q and K nonzero only in coordinate 0: s_ij = scale * a_i * b_j, so the
     softmax is computable directly in fp64 without the oracle."""
