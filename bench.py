@@ -17,6 +17,15 @@ sees.  Prints ONE JSON line: forward attention TFLOP/s counting
 peak, and the fp64 CPU oracle's rate on a bounded sample of the same workload
 on this host's cores.
 
+With the headline workload (the default) the same run then times the
+sequence sweep (N = 512 ... 16384 at B*N = 16384, fp16) and the head-dimension
+variants (d = 64, 256) with the same --warmup / --steps, and adds them to the
+line as "sweep" (per N, plus the harmonic mean) and "head_dim", each with its
+roofline fraction (--no-extras leaves them out).  Every output is checked
+after the timing (NaN-prefilled buffers fully written with finite values, and
+the oracle's parity on the heads the CPU baseline computed): the line is
+printed either way, and the exit status is 1 if a check failed.
+
 Other modes: --workload NAME for any of the parity workloads (one line each),
 --no-cpu-baseline to skip the oracle timing, --calibrate-copy to run only a
 plain device copy of known size (for scaling HBM byte counters), and
@@ -37,9 +46,18 @@ if ROOT not in sys.path:
 
 METRIC = "fwd attention TFLOP/s, bf16 d=128 N=4096 non-causal; % of MFMA peak"
 # MI355X dense (no sparsity) MFMA peak for bf16/fp16: 256 CUs x 2.4 GHz x
-# 4096 FLOP/CU/clk = 2516.6 TFLOP/s, the published 2.5 PFLOP/s figure.
+# 4096 FLOP/CU/clk = 2516.6 TFLOP/s, the published 2.5 PFLOP/s figure; int8
+# runs at twice that (the published 5.0 POP/s).
 MFMA_PEAK_TFLOPS = 2516.6
+INT8_PEAK_TOPS = 2 * MFMA_PEAK_TFLOPS
 HBM_PEAK_GBS = 8000.0
+# Workloads timed after the headline in the default run, each with the same
+# --steps / --warmup: the sequence sweep of "Flash Attention 2 from scratch
+# on Ampere", Part 1, Performance section (reported per N and as a harmonic
+# mean), and the head-dimension variants.
+SWEEP = ["sweep_n512", "sweep_n1024", "sweep_n2048", "sweep_n4096", "sweep_n8192",
+         "sweep_n16384"]
+HEAD_DIMS = ["d64", "d256"]
 KERNEL_SRC = os.path.join(ROOT, "flashattention_forward_tile_amd", "csrc", "fa2_fwd.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa2_fwd_headline_traffic.json")
 CPU_SAMPLE_SECONDS = 12.0
@@ -108,18 +126,30 @@ def write_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, workload
     print(json.dumps(out))
 
 
+def matrix_peak(w):
+    """Matrix-core roof for workload w in TFLOP/s.  16-bit workloads: the
+    bf16/fp16 peak.  The INT8 cache runs its first product (half the FLOPs)
+    on int8 matrix instructions and its second on fp16 ones, so its roof is
+    the rate at which both halves finish at their own peaks:
+    1 / (0.5 / int8 peak + 0.5 / fp16 peak)."""
+    if w.kv_int8:
+        return round(1.0 / (0.5 / INT8_PEAK_TOPS + 0.5 / MFMA_PEAK_TFLOPS), 1)
+    return MFMA_PEAK_TFLOPS
+
+
 def roofline_of(w, ms, traffic):
     """The roofline object for workload w at ms per launch.  The bound is the
     roof the workload's arithmetic intensity (FLOPs per algorithmic HBM byte)
     sits under: left of the ridge (peak FLOP/s over peak bytes/s) the HBM
     roof, in GB/s; otherwise the matrix-core roof, in TFLOP/s."""
-    if w.flops / w.algo_bytes < MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
+    peak = matrix_peak(w)
+    if w.flops / w.algo_bytes < peak * 1e12 / (HBM_PEAK_GBS * 1e9):
         gbs = w.algo_bytes / (ms * 1e-3) / 1e9
         return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
     tflops = w.flops / (ms * 1e-3) / 1e12
-    return {"bound": "mfma", "achieved": round(tflops, 3), "peak": MFMA_PEAK_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(tflops / MFMA_PEAK_TFLOPS, 4),
+    return {"bound": "mfma", "achieved": round(tflops, 3), "peak": peak,
+            "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
             "traffic": traffic}
 
 
@@ -215,6 +245,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time the headline only (not the sweep and head-dim workloads)")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV",
                                                          "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
@@ -237,43 +269,15 @@ def main():
         calibrate_copy()
         return
 
-    from flashattention_forward_tile_amd import fa2
-    from flashattention_forward_tile_amd.workloads import WORKLOADS, workload_inputs
+    from flashattention_forward_tile_amd.workloads import WORKLOADS
 
     w = WORKLOADS[args.workload]
-    dev = torch.device("cuda:0")
-    inputs = workload_inputs(w, seed=0)
-    dev_in = [t.to(dev) for t in inputs]
-    o = torch.empty_like(dev_in[0])
-    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
-    if w.kv_int8:
-        def launch():
-            fa2.fwd_kv_int8(*dev_in, scale=w.scale, causal=w.causal, out=o, lse=lse)
-        q, k, v = inputs[0], (inputs[1], inputs[2]), (inputs[3], inputs[4])
-    else:
-        def launch():
-            fa2.fwd(*dev_in, scale=w.scale, causal=w.causal, out=o, lse=lse)
-        q, k, v = inputs
-
-    for _ in range(args.warmup):
-        launch()
-
-    # No other GPU work between the warm-up and the timed launches: an idle
-    # gap restarts the slow first launches (the outputs are checked after).
-    stream = torch.cuda.current_stream(dev)  # fa2.fwd launches on this stream
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize(dev)
-    wall0 = time.perf_counter()
-    start.record(stream)
-    for _ in range(args.steps):
-        launch()
-    stop.record(stream)
-    torch.cuda.synchronize(dev)
-    wall = time.perf_counter() - wall0
-    ms = start.elapsed_time(stop) / args.steps
-    if not (torch.isfinite(o[0, 0].float()).all() and torch.isfinite(lse[:, :, -1]).all()):
-        raise RuntimeError("non-finite output")
-
+    extras = [] if args.no_extras or w.name != "headline" else SWEEP + HEAD_DIMS
+    # Every workload's inputs are drawn and made resident first, so that no
+    # input generation sits between the timed runs.
+    runs = [Resident(WORKLOADS[n]) for n in [w.name] + extras]
+    main_run = runs[0]
+    ms, wall = main_run.time(args.warmup, args.steps)
     tflops = w.flops / (ms * 1e-3) / 1e12
     roofline = roofline_of(w, ms, measured_traffic(w.name))
     out = {
@@ -287,9 +291,94 @@ def main():
                        wall_ms_per_step=round(wall * 1e3 / args.steps, 5)),
         "roofline": roofline,
     }
+    # The other workloads right after, with the same warm-up and step count.
+    others = {}
+    for r in runs[1:]:
+        r_ms, _ = r.time(args.warmup, args.steps)
+        rl = roofline_of(r.w, r_ms, None)
+        others[r.w.name] = {"ms_per_step": round(r_ms, 5),
+                            "tflops": round(r.w.flops / (r_ms * 1e-3) / 1e12, 3),
+                            "roofline": {k: rl[k] for k in ("bound", "achieved", "unit", "frac")}}
+    ok = all(r.fully_written() for r in runs)
+    if extras:
+        sweep = {n: others[n] for n in SWEEP}
+        hm = len(sweep) / sum(1.0 / x["tflops"] for x in sweep.values())
+        out["sweep"] = dict(sweep, harmonic_mean_tflops=round(hm, 3),
+                            config="B*N = 16384, H 16, d 128, fp16, N(0,1), non-causal")
+        out["head_dim"] = {n: others[n] for n in HEAD_DIMS}
     if not args.no_cpu_baseline:
-        out["cpu_baseline"], out["parity"] = cpu_baseline(w, q, k, v, o.cpu(), lse.cpu())
+        q, k, v = main_run.host_qkv()
+        o, lse = main_run.outputs()
+        out["cpu_baseline"], out["parity"] = cpu_baseline(w, q, k, v, o, lse)
+        ok &= out["parity"] is None or out["parity"]["within_tolerance"]
+    out["outputs_ok"] = bool(ok)
     print(json.dumps(out), flush=True)
+    if not ok:
+        # a wrong result must not leave a clean benchmark record
+        print("bench.py: output check failed (unwritten / non-finite values, or parity "
+              "outside tolerance)", file=sys.stderr)
+        sys.exit(1)
+
+
+class Resident:
+    """One workload's inputs and outputs resident on the GPU, and its launch."""
+
+    def __init__(self, w):
+        import torch
+
+        from flashattention_forward_tile_amd import fa2
+        from flashattention_forward_tile_amd.workloads import workload_inputs
+
+        self.w = w
+        dev = torch.device("cuda:0")
+        self.inputs = workload_inputs(w, seed=0)
+        self.dev_in = [t.to(dev) for t in self.inputs]
+        self.o = torch.full_like(self.dev_in[0], float("nan"))
+        self.lse = torch.full((w.B, w.H, w.N), float("nan"), dtype=torch.float32, device=dev)
+        if w.kv_int8:
+            self.launch = lambda: fa2.fwd_kv_int8(*self.dev_in, scale=w.scale, causal=w.causal,
+                                                  out=self.o, lse=self.lse)
+        else:
+            self.launch = lambda: fa2.fwd(*self.dev_in, scale=w.scale, causal=w.causal,
+                                          out=self.o, lse=self.lse)
+
+    def time(self, warmup, steps):
+        """W untimed launches, then K timed with HIP events on the launch
+        stream, bracketed by device synchronisation.  Returns (ms per launch,
+        wall seconds of the timed region)."""
+        import torch
+
+        dev = self.o.device
+        for _ in range(warmup):
+            self.launch()
+        # No other GPU work between the warm-up and the timed launches: an
+        # idle gap restarts the slow first launches (outputs are checked after).
+        stream = torch.cuda.current_stream(dev)  # fa2.fwd launches on this stream
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize(dev)
+        wall0 = time.perf_counter()
+        start.record(stream)
+        for _ in range(steps):
+            self.launch()
+        stop.record(stream)
+        torch.cuda.synchronize(dev)
+        wall = time.perf_counter() - wall0
+        return start.elapsed_time(stop) / max(steps, 1), wall
+
+    def fully_written(self):
+        """Every element of O and LSE finite (they start as NaN)."""
+        import torch
+        return bool(torch.isfinite(self.o.float()).all() and torch.isfinite(self.lse).all())
+
+    def host_qkv(self):
+        if self.w.kv_int8:
+            i = self.inputs
+            return i[0], (i[1], i[2]), (i[3], i[4])
+        return self.inputs
+
+    def outputs(self):
+        return self.o.cpu(), self.lse.cpu()
 
 
 if __name__ == "__main__":

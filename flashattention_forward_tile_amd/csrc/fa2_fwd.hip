@@ -39,6 +39,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "fa2.h"
@@ -468,7 +469,8 @@ fa2_fwd_kernel(const Problem P) {
       uint32_t dst = lds_base + QOBASE + wave * 1024;
       asm volatile("" : "+v"(ln), "+s"(dst));
       const int lin = wave * 64 + ln, row = lin / CPR;
-      const uint32_t src = (uint32_t)(qt_r * QTB + row * RB + k_swizzle<CPR>(row, lin % CPR) * 16);
+      // unsigned: a group's query rows may span up to 2^32 - 2^21 bytes
+      const uint32_t src = (uint32_t)qt_r * QTB + (uint32_t)(row * RB + k_swizzle<CPR>(row, lin % CPR) * 16);
 #pragma unroll
       for (int i = 0; i < QLOADS; ++i) load_lds16(rs, src + i * QSTEP, dst + i * QSTEP);
     }
@@ -553,7 +555,7 @@ fa2_fwd_kernel(const Problem P) {
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
     c_q[b] = c;
-    const uint32_t qrow_off = (uint32_t)((q0 + 32 * b + l32) * RB);
+    const uint32_t qrow_off = (uint32_t)(q0 + 32 * b + l32) * RB;  // unsigned, as above
     if constexpr (PERSIST) {
       // fragments come through LDS (load_qf below)
     } else if constexpr (!Q8) {
@@ -1149,16 +1151,18 @@ kernel_fn pick(bool fp16, int mode, bool causal) {
 }
 
 // Compute units of the current device (0 if unknown), cached per device.
+// The cache entries are atomics: threads that race on a first call each
+// query the attribute and store the same value.
 int cu_count() {
-  static int cache[64];
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cache[dev] == 0) {
-    int n = 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cache[dev] = n;
+    cache[dev].store(n, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return n;
 }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -1212,7 +1216,9 @@ int launch(const void* q, const void* k, const void* v, const float* ks, const f
   if (q8 ? d != 128 : (d != 64 && d != 128 && d != 256)) return FA2_ERR_HEADDIM;
   if (causal != 0 && causal != 1) return FA2_ERR_OPTION;
   if (B < 0 || Hq < 0 || Hkv < 0 || Nq < 0 || Nk < 0) return FA2_ERR_SHAPE;
-  if (!__builtin_isfinite(scale)) return FA2_ERR_SCALE;
+  // logits in log2 units: t = s * scale * log2(e), which must stay finite
+  const float c = (float)((double)scale * 1.4426950408889634074);
+  if (!__builtin_isfinite(scale) || !__builtin_isfinite(c)) return FA2_ERR_SCALE;
   if (B == 0 || Hq == 0 || Nq == 0) return FA2_OK;  // no output rows
   if (Hkv == 0 || Hq % Hkv != 0) return FA2_ERR_SHAPE;
   // The query rows of one K/V head's group (group * Nq) and the key rows of
@@ -1281,8 +1287,6 @@ int launch(const void* q, const void* k, const void* v, const float* ks, const f
   const int64_t q_tiles = (rows + bq - 1) / bq;
   const int64_t groups = B * Hkv * q_tiles;
 
-  // logits in log2 units: t = s * scale * log2(e)
-  const float c = (float)((double)scale * 1.4426950408889634074);
   const bool fp16 = dtype == FA2_FP16;
   const int mode = c > 0.0f ? kPositive : c < 0.0f ? kNegative : kZero;
   Problem P;

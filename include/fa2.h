@@ -49,7 +49,8 @@ enum fa2_status {
   FA2_ERR_HEADDIM = -3, /* d is not 64, 128 or 256 (128 for fa2_fwd_kv_int8) */
   FA2_ERR_DTYPE = -4,   /* dtype is not an fa2_dtype */
   FA2_ERR_ALIGN = -5,   /* q, k, v or o not 16-byte aligned, lse not 4-byte */
-  FA2_ERR_SCALE = -6,   /* scale is NaN or infinite */
+  FA2_ERR_SCALE = -6,   /* scale is NaN or infinite, or scale * log2(e)
+                           overflows fp32 (|scale| above about 2.36e38) */
   FA2_ERR_ALIAS = -7,   /* o or lse overlaps q, k, v, or each other */
   FA2_ERR_HIP = -8,     /* the kernel launch failed (HIP error) */
   FA2_ERR_OPTION = -9   /* causal is not 0 or 1 */
@@ -67,14 +68,17 @@ enum fa2_status {
  *              If B*H*N == 0 the call returns FA2_OK and touches nothing
  *              (pointers may then be NULL).
  *   d        : head dimension, 64, 128 or 256.
- *   scale    : multiplies the logits; any finite value (1/sqrt(d) is usual;
- *              0 gives uniform attention, negative values are allowed).
+ *   scale    : multiplies the logits; any finite value whose product with
+ *              log2(e) is a finite float, |scale| <= about 2.36e38
+ *              (1/sqrt(d) is usual; 0 gives uniform attention, negative
+ *              values are allowed).
  *   dtype    : an fa2_dtype.
  *   stream   : a hipStream_t, or NULL for the default stream.
  *
  * Ownership: the caller owns every buffer; the library allocates nothing and
- * keeps no state between calls, so concurrent calls on any streams are safe as
- * long as their outputs do not overlap.  o and lse must not overlap q, k, v or
+ * keeps no state between calls (it only caches each device's compute-unit
+ * count, race-free), so concurrent calls on any streams and host threads are
+ * safe as long as their outputs do not overlap.  o and lse must not overlap q, k, v or
  * each other.
  *
  * Asynchrony: the work is enqueued on `stream` and the call returns at once;

@@ -46,18 +46,3 @@ def assert_parity(o_gpu, lse_gpu, o_ref, lse_ref, tag="", lse_abs=None):
         with open(log, "a") as f:
             f.write(json.dumps(dict(err, case=tag)) + "\n")
     return err
-
-
-def sample_rows(B, H, N, block_q, per_head=6, seed=0):
-    """Flat row ids: per (b, h) the first and last row, the rows on both sides
-    of a query-tile boundary, and random rows."""
-    rng = np.random.default_rng(seed)
-    rows = []
-    for bh in range(B * H):
-        picks = {0, N - 1}
-        if N > block_q:
-            t = int(rng.integers(1, (N - 1) // block_q + 1)) * block_q
-            picks.update({t - 1, t})
-        picks.update(int(x) for x in rng.integers(0, N, size=per_head))
-        rows.extend(bh * N + r for r in sorted(picks))
-    return np.array(rows, dtype=np.int64)

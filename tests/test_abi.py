@@ -93,6 +93,8 @@ def call(q=A, k=A + 0x1000000, v=A + 0x2000000, o=A + 0x3000000,
     (dict(d=96), fa2.ERR_HEADDIM), (dict(d=0), fa2.ERR_HEADDIM), (dict(d=512), fa2.ERR_HEADDIM),
     (dict(dtype=2), fa2.ERR_DTYPE), (dict(dtype=-1), fa2.ERR_DTYPE),
     (dict(scale=float("nan")), fa2.ERR_SCALE), (dict(scale=float("inf")), fa2.ERR_SCALE),
+    # finite in fp32, but scale * log2(e) is not
+    (dict(scale=3e38), fa2.ERR_SCALE), (dict(scale=-2.5e38), fa2.ERR_SCALE),
     (dict(q=A + 2), fa2.ERR_ALIGN), (dict(o=A + 0x3000008), fa2.ERR_ALIGN),
     (dict(lse=A + 0x4000002), fa2.ERR_ALIGN),
     (dict(o=A), fa2.ERR_ALIAS), (dict(o=A + 0x1000000 + 4096), fa2.ERR_ALIAS),

@@ -71,3 +71,16 @@ def test_bench_parity_against_the_oracle_on_the_cpu():
     assert not par["within_tolerance"]
     assert par["o_max_abs"] == pytest.approx(
         abs(float(bad[0, 1, 17, 3]) - o_ref[0, 1, 17, 3]), rel=1e-6)
+
+
+def test_int8_cache_roofline_mixes_the_two_matrix_peaks():
+    """Half the INT8-cache FLOPs run on int8 matrix instructions (twice the
+    16-bit rate), half on fp16 ones: the roof is 1 / (0.5/5033.2 + 0.5/2516.6)
+    = 3355.5 TFLOP/s, and a launch at that roof's time reads frac 1."""
+    w = WORKLOADS["int8_kv"]
+    peak = 1.0 / (0.5 / 5033.2 + 0.5 / 2516.6)
+    assert bench.matrix_peak(w) == pytest.approx(peak, abs=0.1)
+    ms = w.flops / (peak * 1e12) * 1e3
+    r = bench.roofline_of(w, ms, None)
+    assert r["bound"] == "mfma" and r["frac"] == pytest.approx(1.0, abs=1e-3)
+    assert bench.matrix_peak(WORKLOADS["headline"]) == 2516.6

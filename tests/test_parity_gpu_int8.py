@@ -13,7 +13,7 @@ import torch
 import oracle
 from flashattention_forward_tile_amd import fa2
 from flashattention_forward_tile_amd.workloads import bits, make_inputs_kv_int8
-from parity import assert_parity, sample_rows
+from parity import assert_parity
 
 pytestmark = pytest.mark.gpu
 
@@ -92,17 +92,6 @@ def test_int8_deterministic():
     o2, l2 = fa2.fwd_kv_int8(*inputs, causal=True)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
-
-
-@pytest.mark.parametrize("causal", [False, True])
-def test_int8_headline_sampled(causal):
-    """B=4, H=16, N=4096, d=128, bf16 query over an INT8 cache, sampled rows
-    (first, last, both sides of a query tile boundary, random)."""
-    announce("int8 headline", causal)
-    inputs = make_inputs_kv_int8(4, 16, 16, 4096, 4096, 128, "bf16", seed=0)
-    bq, _, _ = fa2.tile_config(128)
-    check(inputs, "bf16", 1.0 / math.sqrt(128), causal, "int8 headline causal=%d" % causal,
-          rows=sample_rows(4, 16, 4096, bq, per_head=4, seed=2))
 
 
 def test_int8_query_codes_golden_on_gpu():
