@@ -20,10 +20,13 @@
 //    leaves registers.
 //  * K_j and V_j go HBM -> LDS by buffer loads that write LDS directly, into
 //    XOR-swizzled tiles (bank conflicts were the largest single gain in the
-//    Ampere series' table, kernel 2).  At d = 64 and 128 each cycles through a
-//    ring of four slots with loads two iterations ahead of their use and the
-//    next iteration's first operands read before the closing barrier; d = 256
-//    double-buffers (kernels 3 and 5 of that table pipeline one tile ahead).
+//    Ampere series' table, kernel 2).  Each cycles through a ring of four
+//    slots with loads two iterations ahead of their use and the next
+//    iteration's first operands read before the closing barrier (kernels 3
+//    and 5 of that table pipeline one tile ahead).
+//  * d = 256 splits the head dimension between two waves of the same query
+//    rows, which sum their halves of S through LDS, so each wave's registers
+//    stay those of a d = 128 wave (kernel 15 of that table tiles along d).
 //  * Softmax in fp32 registers with exp2 and the scale folded into one FMA
 //    (kernel 6), against a lazy reference max: it moves only when a row's
 //    tile sum of p would exceed kSumLimit, which keeps the result exact
@@ -49,6 +52,7 @@ namespace fa2 {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -160,31 +164,41 @@ __device__ __forceinline__ void load_lds4(i32x4 rsrc, uint32_t voff, uint32_t ld
 // (NW), 32-query blocks per wave (QB), the waves per SIMD the register
 // budget is sized for (OCC), whether the iteration block carries explicit
 // MFMA / LDS / VALU interleave hints (SGB), the LDS slots per K and V ring
-// (RING), and how many K and V operands of each product are read from LDS one
-// iteration early (PK, PV).  Each K or V operand read from LDS feeds QB
-// matrix instructions, so LDS bytes per FLOP fall as 1/QB.
+// (RING), how many K and V operands of each product are read from LDS one
+// iteration early (PK, PV), and how many waves share one query block, each
+// holding 1/DS of the head dimension (DS; the tiling along the head
+// dimension of kernel 15 in the Ampere series' list).  Each K or V operand
+// read from LDS feeds QB matrix instructions, so LDS bytes per FLOP fall as
+// 1/QB.
 //
-// K and V tiles cycle through rings of RING LDS slots: tile t sits in slot
-// t % RING and K_t is loaded during iteration t - RING.  With RING = 4, V_t
-// is loaded during iteration t - 2 and each iteration waits only for the
-// loads of the one before it, so every load has two iterations to land and
-// the operands an iteration reads were published one barrier early (which
-// is what lets PK, PV > 0).  With RING = 2 (double buffering), V_t is loaded
-// during iteration t and each iteration waits for its own loads.
+// d = 256 splits the head dimension between two waves (DS = 2): wave w and
+// wave w + NW/2 hold the same 32 query rows, each with its half of Q, of
+// every K and V row, and of O.  Each computes a partial S over its half of
+// the contraction; the pair sums the two halves through LDS and then runs the
+// identical softmax, so each wave's registers are those of a d = 128 wave and
+// two waves fit on a SIMD.
+//
+// K and V tiles cycle through rings of RING = 4 LDS slots: tile t sits in
+// slot t % 4, K_t is loaded during iteration t - 4 and V_t during iteration
+// t - 2, and each iteration waits only for the loads of the one before it,
+// so every load has two iterations to land and the operands an iteration
+// reads were published one barrier early (which is what lets PK, PV > 0).
+// At d = 256 the rings take 128 KiB and the pairs' exchange slots the other
+// 32 KiB of a workgroup's LDS.
 template <int D> struct Cfg;
-template <> struct Cfg<64> { static constexpr int BC = 64, NW = 4, QB = 1, OCC = 2, SGB = 1, RING = 4, PK = 4, PV = 2; };
-template <> struct Cfg<128> { static constexpr int BC = 32, NW = 8, QB = 1, OCC = 2, SGB = 0, RING = 4, PK = 4, PV = 2; };
-template <> struct Cfg<256> { static constexpr int BC = 32, NW = 4, QB = 1, OCC = 1, SGB = 0, RING = 2, PK = 0, PV = 0; };
+template <> struct Cfg<64> { static constexpr int BC = 64, NW = 4, QB = 1, OCC = 2, SGB = 1, RING = 4, PK = 4, PV = 2, DS = 1; };
+template <> struct Cfg<128> { static constexpr int BC = 32, NW = 8, QB = 1, OCC = 2, SGB = 0, RING = 4, PK = 4, PV = 2, DS = 1; };
+template <> struct Cfg<256> { static constexpr int BC = 32, NW = 8, QB = 1, OCC = 2, SGB = 0, RING = 4, PK = 4, PV = 0, DS = 2; };
 
 // Tile shape of the INT8 key/value cache kernels (d = 128 only).
 template <int D> struct Cfg8;
-template <> struct Cfg8<128> { static constexpr int BC = 32, NW = 8, QB = 1, OCC = 2, SGB = 0, RING = 4, PK = 2, PV = 2; };
+template <> struct Cfg8<128> { static constexpr int BC = 32, NW = 8, QB = 1, OCC = 2, SGB = 0, RING = 4, PK = 2, PV = 2, DS = 1; };
 // Short key sequences at d = 128 (at most kShortKeys keys): half the query
 // rows per workgroup, so two workgroups share a CU and one's prologue and
 // epilogue overlap the other's loop.  The same shape serves grids too small
 // to give every CU a full-height workgroup.
 template <int D> struct CfgS;
-template <> struct CfgS<128> { static constexpr int BC = 32, NW = 4, QB = 1, OCC = 2, SGB = 0, RING = 4, PK = 4, PV = 2; };
+template <> struct CfgS<128> { static constexpr int BC = 32, NW = 4, QB = 1, OCC = 2, SGB = 0, RING = 4, PK = 4, PV = 2, DS = 1; };
 constexpr int kShortKeys = 1024;
 template <int D, bool Q8, bool SHORT>
 using KCfg = std::conditional_t<Q8, Cfg8<D>, std::conditional_t<SHORT, CfgS<D>, Cfg<D>>>;
@@ -257,7 +271,8 @@ fa2_fwd_kernel(const Problem P) {
   constexpr int BC = C::BC;
   constexpr int NW = C::NW;
   constexpr int QB = C::QB;
-  constexpr int BR = NW * 32 * QB;    // query rows per workgroup
+  constexpr int DS = C::DS;           // waves per query block (head-dimension split)
+  constexpr int BR = NW * 32 * QB / DS;  // query rows per workgroup
   constexpr int CPR = D / 8;          // 16-byte chunks per (16-bit) V row
   constexpr int RB = D * 2;           // bytes per (16-bit) V row in LDS
   constexpr int TBYTES = BC * RB;     // one V tile in LDS
@@ -270,8 +285,13 @@ fa2_fwd_kernel(const Problem P) {
   constexpr int ST = BC / 16;         // k-steps of the second product
   constexpr int KB = BC / 32;         // 32-key blocks per tile
   constexpr int DB = D / 32;          // 32-dim blocks of the output
+  constexpr int KSW = KS / DS;        // k-steps of the first product per wave
+  constexpr int DBW = DB / DS;        // 32-dim output blocks per wave
+  constexpr int DW = D / DS;          // output columns per wave
   static_assert(TBK % (NW * 64 * LW) == 0, "tile must split into wave loads");
   static_assert(BC % 32 == 0 && D % 32 == 0, "MFMA 32x32 blocking");
+  static_assert(DS == 1 || (DS == 2 && !Q8 && !PERSIST && NW % 2 == 0 && KS % 2 == 0 &&
+                            DB % 2 == 0), "head-dimension split");
   // Q and O are bf16 or fp16; P and V meet on fp16 matrix instructions in the
   // INT8 kernels (V is widened exactly), on the input type otherwise.
   constexpr bool F16B = FP16 || Q8;
@@ -285,35 +305,40 @@ fa2_fwd_kernel(const Problem P) {
 
   constexpr int PK = C::PK;           // K operands read one iteration early
   constexpr int PV = C::PV;           // V operands read one iteration early
-  constexpr int KO = KS * KB;         // K operands (A of the first product) per tile
-  constexpr int VO = ST * DB;         // V operands (A of the second product) per tile
+  constexpr int KO = KSW * KB;        // K operands (A of the first product) per tile and wave
+  constexpr int VO = ST * DBW;        // V operands (A of the second product) per tile and wave
   constexpr int RING = C::RING;
-  static_assert(RING == 2 || RING == 4, "ring of 2 or 4 slots");
-  static_assert(PK <= KO && PV <= VO && (RING == 4 || PK + PV == 0), "prefetch depth");
-  static_assert(!Q8 || RING == 4, "INT8 staging assumes four slots");
+  static_assert(RING == 4, "ring of four slots");
+  static_assert(PK <= KO && PV <= VO, "prefetch depth");
   // V_t is loaded during iteration t - VAHEAD: as int8 into a staging ring
   // three iterations ahead (Q8; widened to fp16 during iteration t - 1), else
   // straight into the V ring.
-  constexpr int VAHEAD = Q8 ? 3 : RING - 2;
+  constexpr int VAHEAD = Q8 ? 3 : 2;
   // LDS: the K ring [RING][BC][D] at 0, the (16-bit) V ring at VBASE, and with
   // Q8 the int8 V staging ring at SBASE; tiles row-major, K and V swizzled.
   constexpr int VBASE = RING * TBK;
   constexpr int SBASE = VBASE + RING * TBYTES;
   constexpr int RING_BYTES = SBASE + (Q8 ? RING * TBK : 0);
+  // DS = 2: after the ring, one slot per wave for its partial logits of a
+  // tile (QB * KB accumulators of 16 fp32 per lane, 1 KiB per 4 of them).
+  constexpr int SXG = QB * KB * 4;    // 16-byte pieces per lane
+  constexpr int SXBASE = RING_BYTES;
+  constexpr int SXBYTES = DS > 1 ? NW * SXG * 64 * 16 : 0;
   // After the loop the same LDS stages the output: each wave's 32*QB rows of
   // O, row-major, rows padded by 16 bytes (OROW) against bank conflicts.
-  constexpr int OROW = D * 2 + 16;
+  constexpr int OROW = DW * 2 + 16;
   constexpr int OBYTES = NW * 32 * QB * OROW;
   // PERSIST keeps the ring apart from a query / output area at QOBASE: the
   // next item's query tile is staged there while the current one runs, and
   // the output is staged there while the next item's first K/V tiles sit in
   // the ring.
   constexpr int QTB = BR * RB;  // one query tile
-  static_assert(!PERSIST || (RING == 4 && !Q8 && !CAUSAL && QB == 1), "persistent kernels");
+  static_assert(!PERSIST || (!Q8 && !CAUSAL && QB == 1), "persistent kernels");
   constexpr int QOBASE = PERSIST ? RING_BYTES : 0;
   constexpr int QOBYTES = QTB > OBYTES ? QTB : OBYTES;
   __shared__ __attribute__((aligned(16)))
-  char smem[PERSIST ? RING_BYTES + QOBYTES : (RING_BYTES > OBYTES ? RING_BYTES : OBYTES)];
+  char smem[PERSIST ? RING_BYTES + QOBYTES
+                    : (RING_BYTES + SXBYTES > OBYTES ? RING_BYTES + SXBYTES : OBYTES)];
   lds_char* const lds = (lds_char*)smem;
 
   const int tid = threadIdx.x;
@@ -321,6 +346,10 @@ fa2_fwd_kernel(const Problem P) {
   const int l32 = lane & 31;
   const int half = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // The wave's query block and, with DS = 2, its half of the head dimension
+  // (waves w and w + NW/2 share a query block).
+  const int wq = DS == 1 ? wave : wave % (NW / DS);
+  const int dpart = DS == 1 ? 0 : wave / (NW / DS);
 
   // Work items are (K/V head bh = b * hkv + g, query tile qt) pairs, G =
   // n_groups of them.  All query tiles of one K/V head go to one XCD
@@ -416,10 +445,8 @@ fa2_fwd_kernel(const Problem P) {
   }
   // `s` (an integral constant) is t modulo 4, known at compile time in the
   // loop (unrolled by 4), so the ring slot t % RING and its LDS offsets fold
-  // into instruction immediates.  d = 256 keeps the slot in a register: with
-  // immediates its schedule hoists more loads and spills.
-  constexpr bool kImmBuf = D != 256;
-  auto slot = [](int t, auto s) { return kImmBuf ? decltype(s)::value % RING : (t & (RING - 1)); };
+  // into instruction immediates.
+  auto slot = [](int, auto s) { return decltype(s)::value % RING; };
   // Tiles past the last one read as zeros (buffer range check) and are never
   // used; loading them keeps the per-iteration load count fixed.
   auto load_lds = [&](const i32x4& rs, uint32_t voff, uint32_t dst) {
@@ -492,19 +519,20 @@ fa2_fwd_kernel(const Problem P) {
   uint32_t k_off[KOFF];
 #pragma unroll
   for (int ks = 0; ks < KOFF; ++ks)
-    k_off[ks] = (uint32_t)(l32 * RBK + k_swizzle<CPRK>(l32, ks * 2 + half) * 16);
+    k_off[ks] = (uint32_t)(l32 * RBK + k_swizzle<CPRK>(l32, ks * 2 + half) * 16 + dpart * KSW * 32);
   const int tr_row = half * 4 + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   uint32_t v_off[VOFF];
 #pragma unroll
   for (int db = 0; db < VOFF; ++db) {
     const int col = db * 32 + tr_col;
-    v_off[db] = (uint32_t)(tr_row * RB + v_swizzle<CPR>(tr_row, col >> 3) * 16 + (col & 7) * 2);
+    v_off[db] = (uint32_t)(tr_row * RB + v_swizzle<CPR>(tr_row, col >> 3) * 16 + (col & 7) * 2 +
+                           dpart * DBW * 64);
   }
 
   // Q_i fragments: the B operands of S^T = K_j Q_i^T, held for the whole
   // loop.  Query block b of this wave is packed rows q0 + 32*b + l32.
-  int q0 = qt * BR + wave * 32 * QB;
+  int q0 = qt * BR + wq * 32 * QB;
 
   // Causal limits: a lane's last visible key (its row within its head plus
   // causal_off), and the smallest such row among the wave's rows (packed rows
@@ -550,7 +578,7 @@ fa2_fwd_kernel(const Problem P) {
   // c_q: the lane's logit multiplier (scale * log2 e, times the query row
   // scale with Q8).
   using QOp = std::conditional_t<Q8, i32x4, X8>;
-  QOp qf[QB][KS];
+  QOp qf[QB][KSW];
   float c_q[QB];
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
@@ -560,9 +588,10 @@ fa2_fwd_kernel(const Problem P) {
       // fragments come through LDS (load_qf below)
     } else if constexpr (!Q8) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
+      for (int ks = 0; ks < KSW; ++ks)
         qf[b][ks] = __builtin_bit_cast(
-            X8, __builtin_amdgcn_raw_buffer_load_b128(q_rs, qrow_off + ks * 32 + half * 16, 0, 0));
+            X8, __builtin_amdgcn_raw_buffer_load_b128(
+                    q_rs, qrow_off + (dpart * KSW + ks) * 32 + half * 16, 0, 0));
     } else if constexpr (MODE != kZero) {
       // In-kernel quantization of the query row (lanes l and l+32 hold its
       // two halves): for k-step ks this lane holds channels 32 ks + 16 half
@@ -617,12 +646,12 @@ fa2_fwd_kernel(const Problem P) {
     }
   }
 
-  f32x16 acc[QB][DB];
+  f32x16 acc[QB][DBW];
   float m_ref[QB], l_part[QB];  // reference max (log2 units), lane's row sum
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DBW; ++db)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[b][db][i] = 0.0f;
     m_ref[b] = -INFINITY;
@@ -664,7 +693,7 @@ fa2_fwd_kernel(const Problem P) {
   // db*32 .. +31 and keys st*16 .. +15 in the S^T accumulator's key order,
   // from the row-major V tile through two transposing LDS reads of 4 keys.
   auto v_operand = [&](int t, auto s, int o) -> X8 {
-    const int st = o / DB, db = o % DB;
+    const int st = o / DBW, db = o % DBW;
     const lds_char* vb = lds + VBASE + slot(t, s) * TBYTES;
     const uint32_t vo = v_off[db % VOFF] + (db / VOFF) * 256;
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -706,7 +735,7 @@ fa2_fwd_kernel(const Problem P) {
     for (int o = 0; o < VO; ++o) {
       const X8 a = o < PV ? pre[o < PV ? o : 0] : v_operand(t, s, o);
 #pragma unroll
-      for (int b = 0; b < QB; ++b) acc[b][o % DB] = mfma32x32x16<F16B>(a, pf[b][o / DB], acc[b][o % DB]);
+      for (int b = 0; b < QB; ++b) acc[b][o % DBW] = mfma32x32x16<F16B>(a, pf[b][o / DBW], acc[b][o % DBW]);
     }
   };
 
@@ -719,6 +748,42 @@ fa2_fwd_kernel(const Problem P) {
   auto prefetch_v = [&](int t, auto s, X8 (&pre)[PV > 0 ? PV : 1]) {
 #pragma unroll
     for (int o = 0; o < PV; ++o) pre[o] = v_operand(t, s, o);
+  };
+
+  // DS = 2: a wave's partial logits of one tile go to its slot of the
+  // exchange area, lane-linear (each 16-byte piece of 64 lanes is 1 KiB),
+  // and the partner wave (w xor NW/2, same query rows and layout) adds them
+  // to its own.
+  auto write_partial = [&](const SAcc (&sd)[QB][KB]) {
+    if constexpr (DS > 1) {
+      lds_char* const base = lds + SXBASE + (wave * SXG * 64 + lane) * 16;
+#pragma unroll
+      for (int b = 0; b < QB; ++b)
+#pragma unroll
+        for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 v = {sd[b][kk][4 * g], sd[b][kk][4 * g + 1], sd[b][kk][4 * g + 2],
+                             sd[b][kk][4 * g + 3]};
+            *(__attribute__((address_space(3))) f32x4*)(base + ((b * KB + kk) * 4 + g) * 1024) = v;
+          }
+    }
+  };
+  auto read_partial = [&](SAcc (&sx)[QB][KB]) {
+    if constexpr (DS > 1) {
+      const lds_char* const base = lds + SXBASE + ((wave ^ (NW / 2)) * SXG * 64 + lane) * 16;
+#pragma unroll
+      for (int b = 0; b < QB; ++b)
+#pragma unroll
+        for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 v = *(const __attribute__((address_space(3))) f32x4*)(
+                base + ((b * KB + kk) * 4 + g) * 1024);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sx[b][kk][4 * g + e] = v[e];
+          }
+    }
   };
 
   // Q8: widen V_t from its int8 staging slot into the 16-bit V ring as exact
@@ -802,8 +867,7 @@ fa2_fwd_kernel(const Problem P) {
     using S1 = Ic<(p + 1) % 4>;
     using S2 = Ic<(p + 2) % 4>;
     using S3 = Ic<(p + 3) % 4>;
-    // (RING = 2 skips loads past the end: at d = 256 that keeps it from spilling)
-    if (RING == 4 || j + RING < n_tiles) issue_k(j + RING, S0{}, std::bool_constant<(TL & 1) != 0>{});
+    issue_k(j + RING, S0{}, std::bool_constant<(TL & 1) != 0>{});
     issue_v(j + VAHEAD, Ic<(p + VAHEAD) % 4>{}, std::bool_constant<(TL & 2) != 0>{});
     convert_v(j + 1, S1{});
     // PERSIST: the next item's query tile, needed by this item's last product
@@ -813,6 +877,16 @@ fa2_fwd_kernel(const Problem P) {
     if constexpr (kSyncCheck) {
       wait_vmem();
       __syncthreads();
+    }
+    // DS = 2: the partner's half of this tile's logits (written before the
+    // barrier that ended the previous iteration), added to this wave's half.
+    if constexpr (DS > 1) {
+      SAcc sx[QB][KB];
+      read_partial(sx);
+#pragma unroll
+      for (int b = 0; b < QB; ++b)
+#pragma unroll
+        for (int kk = 0; kk < KB; ++kk) s_cur[b][kk] += sx[b][kk];
     }
 
     // The logits of this tile in fp32 (converted from the int32 products
@@ -919,7 +993,7 @@ fa2_fwd_kernel(const Problem P) {
         const float alpha =
             m_new == m_ref[b] ? 1.0f : __builtin_amdgcn_exp2f(m_ref[b] - m_new);
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DBW; ++db)
 #pragma unroll
           for (int i = 0; i < 16; ++i) acc[b][db][i] *= alpha;
         l_part[b] *= alpha;
@@ -930,13 +1004,19 @@ fa2_fwd_kernel(const Problem P) {
 #pragma unroll
     for (int b = 0; b < QB; ++b) l_part[b] += rs[b];
 
-    // RING = 4: the loads issued during iteration j-1 have landed; RING = 2:
-    // this iteration's own.  (PERSIST: the first iteration's query loads may
-    // stay in flight too.)
+    // DS = 2: once every wave has read this tile's partial logits (this
+    // barrier), the slot takes the next tile's, published by the barrier
+    // below.
+    if constexpr (DS > 1) {
+      __syncthreads();
+      write_partial(s_nxt);
+    }
+    // The loads issued during iteration j-1 have landed.  (PERSIST: the first
+    // iteration's query loads may stay in flight too.)
     if constexpr (kSyncCheck)
       wait_vmem();
     else
-      wait_vmem_but<RING == 4 ? 2 * LOADS + (PERSIST && decltype(first)::value ? QLOADS : 0) : 0>();
+      wait_vmem_but<2 * LOADS + (PERSIST && decltype(first)::value ? QLOADS : 0)>();
     __syncthreads();
   };
 
@@ -953,17 +1033,15 @@ fa2_fwd_kernel(const Problem P) {
     issue_q(q_words(bh), qt);
     issue_k(0, Ic<0>{}, std::false_type{});
     issue_k(1, Ic<1>{}, std::false_type{});
-    if constexpr (RING == 4) {
-      issue_k(2, Ic<2>{}, std::false_type{});
-      issue_k(3, Ic<3>{}, std::false_type{});
-    }
-    if constexpr (VAHEAD > 0) issue_v(0, Ic<0>{}, std::false_type{});
-    if constexpr (VAHEAD > 1) issue_v(1, Ic<1>{}, std::false_type{});
+    issue_k(2, Ic<2>{}, std::false_type{});
+    issue_k(3, Ic<3>{}, std::false_type{});
+    issue_v(0, Ic<0>{}, std::false_type{});
+    issue_v(1, Ic<1>{}, std::false_type{});
     if constexpr (VAHEAD > 2) issue_v(2, Ic<2>{}, std::false_type{});
 #pragma unroll
     for (int b = 0; b < QB; ++b)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[b][ks]));
+      for (int ks = 0; ks < KSW; ++ks) asm volatile("" ::"v"(qf[b][ks]));
     wait_vmem();
     __syncthreads();
 
@@ -972,6 +1050,7 @@ fa2_fwd_kernel(const Problem P) {
     prefetch_k(0, Ic<0>{}, kpre);
     gemm1(0, Ic<0>{}, kpre, sA);
     prefetch_k(1, Ic<1>{}, kpre);
+    write_partial(sA);  // DS = 2: this wave's half of S_0 for its partner
     __syncthreads();  // every wave is done with K_0 before K_RING may overwrite it
   }
 
@@ -982,18 +1061,7 @@ fa2_fwd_kernel(const Problem P) {
     // sets (even j: S_j in sA, S_{j+1} into sB, P_j into pA) are compile-time.
     step(std::true_type{}, Ic<0>{}, 0, sA, sB, pB, pA, Ic<PERSIST ? 8 : 0>{});
     int j = 1;
-    if constexpr (RING == 2) {  // pairs suffice; a longer body spills at d = 256
-      for (; j + 1 < n_tiles; j += 2) {
-        step(std::false_type{}, Ic<1>{}, j, sB, sA, pA, pB, Ic<0>{});
-        step(std::false_type{}, Ic<2>{}, j + 1, sA, sB, pB, pA, Ic<0>{});
-      }
-      if (j < n_tiles) {
-        step(std::false_type{}, Ic<1>{}, j, sB, sA, pA, pB, Ic<0>{});
-        gemm2(j, Ic<1>{}, vpre, pB);
-      } else {
-        gemm2(j - 1, Ic<0>{}, vpre, pA);
-      }
-    } else if constexpr (PERSIST) {
+    if constexpr (PERSIST) {
       // n_tiles % 4 == 0 and n_tiles >= 8: the loop leaves the last seven
       // iterations, of which the last four load the next item's K tiles 0..3
       // and the last two its V tiles 0..1; the last computes its S_0.
@@ -1070,10 +1138,11 @@ fa2_fwd_kernel(const Problem P) {
     const float l_tot = l_part[b] + __shfl_xor(l_part[b], 32);
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DBW; ++db)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int ch = db * 32 + g4 * 8 + ehalf * 4;  // output channels ch .. ch+3
+        // the wave's output channels ch .. ch+3 (of its DW columns)
+        const int ch = db * 32 + g4 * 8 + ehalf * 4;
         float vsc[4] = {1.0f, 1.0f, 1.0f, 1.0f};
         if constexpr (Q8) {  // the per-channel value scales of the INT8 cache
           const float4 f = *(const float4*)(P.vs + (int64_t)bh * D + ch);
@@ -1086,14 +1155,14 @@ fa2_fwd_kernel(const Problem P) {
         *(__attribute__((address_space(3))) u32x2*)(ow + (32 * b + el32) * OROW + ch * 2) =
             __builtin_bit_cast(u32x2, ov);
       }
-    if (ehalf == 0 && qrow < P.rows)
+    if (ehalf == 0 && dpart == 0 && qrow < P.rows)
       P.lse[(int64_t)bh * P.rows + qrow] =
           l_tot > 0.0f ? (m_ref[b] + __log2f(l_tot)) * kLn2 : -INFINITY;
   }
   // The wave reads back only its own rows (LDS operations of one wave are
-  // ordered): 16 lanes per row, 16 bytes each, so a store covers 64 / (D/8)
-  // whole rows.
-  constexpr int CPO = D / 8;                         // 16-byte pieces per O row
+  // ordered): DW/8 lanes per row, 16 bytes each, so a store covers 64 / (DW/8)
+  // whole rows (of the wave's DW columns).
+  constexpr int CPO = DW / 8;                        // 16-byte pieces per O row
   constexpr int OPIECES = 32 * QB * CPO;             // pieces per wave
   static_assert(OPIECES % 64 == 0, "whole stores per wave");
 #pragma unroll
@@ -1101,7 +1170,8 @@ fa2_fwd_kernel(const Problem P) {
     const int lin = s * 64 + el;
     const int r = lin / CPO, pc = lin % CPO;
     const u32x4 piece = *(const __attribute__((address_space(3))) u32x4*)(ow + r * OROW + pc * 16);
-    if (q0 + r < P.rows) *(u32x4*)(P.o + q_head + (int64_t)(q0 + r) * D + pc * 8) = piece;
+    if (q0 + r < P.rows)
+      *(u32x4*)(P.o + q_head + (int64_t)(q0 + r) * D + dpart * DW + pc * 8) = piece;
   }
   if constexpr (!PERSIST) {
     break;
@@ -1112,14 +1182,14 @@ fa2_fwd_kernel(const Problem P) {
     bh = bh_nx;
     qt = qt_nx;
     q_head = (int64_t)bh * P.rows * D;
-    q0 = qt * BR + wave * 32 * QB;
+    q0 = qt * BR + wq * 32 * QB;
     k_rs = rebase(k_rs, nx_delta);
     v_rs = rebase(v_rs, nx_delta);
     look_ahead(item + 1);
 #pragma unroll
     for (int b = 0; b < QB; ++b) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int db = 0; db < DBW; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[b][db][i] = 0.0f;
       m_ref[b] = -INFINITY;
@@ -1195,9 +1265,9 @@ int fa2_tile_config(int64_t d, int dtype, int* block_q, int* block_k, int* waves
   if (!block_q || !block_k || !waves) return FA2_ERR_NULL;
   if (dtype != FA2_BF16 && dtype != FA2_FP16) return FA2_ERR_DTYPE;
   switch (d) {
-    case 64: *block_q = fa2::Cfg<64>::NW * 32 * fa2::Cfg<64>::QB; *block_k = fa2::Cfg<64>::BC; *waves = fa2::Cfg<64>::NW; break;
-    case 128: *block_q = fa2::Cfg<128>::NW * 32 * fa2::Cfg<128>::QB; *block_k = fa2::Cfg<128>::BC; *waves = fa2::Cfg<128>::NW; break;
-    case 256: *block_q = fa2::Cfg<256>::NW * 32 * fa2::Cfg<256>::QB; *block_k = fa2::Cfg<256>::BC; *waves = fa2::Cfg<256>::NW; break;
+    case 64: *block_q = fa2::Cfg<64>::NW * 32 * fa2::Cfg<64>::QB / fa2::Cfg<64>::DS; *block_k = fa2::Cfg<64>::BC; *waves = fa2::Cfg<64>::NW; break;
+    case 128: *block_q = fa2::Cfg<128>::NW * 32 * fa2::Cfg<128>::QB / fa2::Cfg<128>::DS; *block_k = fa2::Cfg<128>::BC; *waves = fa2::Cfg<128>::NW; break;
+    case 256: *block_q = fa2::Cfg<256>::NW * 32 * fa2::Cfg<256>::QB / fa2::Cfg<256>::DS; *block_k = fa2::Cfg<256>::BC; *waves = fa2::Cfg<256>::NW; break;
     default: return FA2_ERR_HEADDIM;
   }
   return FA2_OK;
