@@ -333,7 +333,7 @@ fa2_fwd_kernel(const Problem P) {
   // the output is staged there while the next item's first K/V tiles sit in
   // the ring.
   constexpr int QTB = BR * RB;  // one query tile
-  static_assert(!PERSIST || (!Q8 && !CAUSAL && QB == 1), "persistent kernels");
+  static_assert(!PERSIST || (!Q8 && QB == 1), "persistent kernels");
   constexpr int QOBASE = PERSIST ? RING_BYTES : 0;
   constexpr int QOBYTES = QTB > OBYTES ? QTB : OBYTES;
   __shared__ __attribute__((aligned(16)))
@@ -356,11 +356,22 @@ fa2_fwd_kernel(const Problem P) {
   // (dispatch is round-robin over the 8 XCDs): the k-th workgroup on XCD x
   // takes logical item x*G/8 + k.  With the causal mask the later (longer)
   // query tiles start first.  A persistent workgroup (gridDim.x of them, a
-  // multiple of 8, one per CU) takes items k, k + gridDim.x/8, ... of its XCD.
+  // multiple of 8, one per CU) takes items k, k + gridDim.x/8, ... of its XCD;
+  // with the causal mask it takes pairs of query tiles of one K/V head,
+  // q_tiles-1-i then i, whose key-tile counts always add up to the same.
   const int id = blockIdx.x;
   auto locate = [&](int r, int& bh_r, int& qt_r) -> bool {  // this workgroup's r-th item
     const int per_xcd = P.n_groups >> 3;
-    if constexpr (PERSIST) {
+    if constexpr (PERSIST && CAUSAL) {
+      const int half_tiles = P.q_tiles >> 1;
+      const int x = id & 7, k = (id >> 3) + (r >> 1) * (int)(gridDim.x >> 3);
+      if (2 * k >= per_xcd) return false;
+      const int pair = x * (per_xcd >> 1) + k;
+      bh_r = pair / half_tiles;
+      const int pi = pair - bh_r * half_tiles;
+      qt_r = (r & 1) ? pi : P.q_tiles - 1 - pi;
+      return true;
+    } else if constexpr (PERSIST) {
       const int x = id & 7, k = (id >> 3) + r * (int)(gridDim.x >> 3);
       if (k >= per_xcd) return false;
       const int logical = x * per_xcd + k;
@@ -455,15 +466,15 @@ fa2_fwd_kernel(const Problem P) {
     else
       load_lds16(rs, voff, dst);
   };
-  // PERSIST: with `nx` (a compile-time flag) tile t is tile t - n_all of
-  // the next item (which has the same tile count).
-  const int n_all = (N + BC - 1) / BC;
+  // PERSIST: with `nx` (a compile-time flag) tile t is tile t - n_cur of
+  // the next item, n_cur being the current item's key-tile count.
+  int n_cur = (N + BC - 1) / BC;
   auto issue_k = [&](int t, auto s, auto nx) {
     const uint32_t dst = lds_base + slot(t, s) * TBK + wave * 64 * LW;
     i32x4 rs = k_rs;
     if constexpr (decltype(nx)::value) {
       rs = rebase(k_rs, nx_delta);
-      t -= n_all;
+      t -= n_cur;
     }
 #pragma unroll
     for (int i = 0; i < LOADS; ++i)
@@ -476,7 +487,7 @@ fa2_fwd_kernel(const Problem P) {
     i32x4 rs = v_rs;
     if constexpr (decltype(nx)::value) {
       rs = rebase(v_rs, nx_delta);
-      t -= n_all;
+      t -= n_cur;
     }
 #pragma unroll
     for (int i = 0; i < LOADS; ++i)
@@ -534,47 +545,44 @@ fa2_fwd_kernel(const Problem P) {
   // loop.  Query block b of this wave is packed rows q0 + 32*b + l32.
   int q0 = qt * BR + wq * 32 * QB;
 
-  // Causal limits: a lane's last visible key (its row within its head plus
-  // causal_off), and the smallest such row among the wave's rows (packed rows
-  // wrap to 0 at a head boundary).
-  int row_lim[QB];
-  int wave_row_min = 0;
-  if constexpr (CAUSAL) {
-#pragma unroll
-    for (int b = 0; b < QB; ++b) row_lim[b] = (q0 + 32 * b + l32) % P.nq + P.causal_off;
-    const int r0 = q0 % P.nq;
-    wave_row_min = r0 + 32 * QB - 1 < P.nq ? r0 : 0;
-  }
-  // Causal: the last key tile any row of this wave sees (-1: none), from its
-  // largest row within a head (nq - 1 if its rows wrap to the next head).
-  int wave_last = 0;
-  if constexpr (CAUSAL) {
-    const int r0 = q0 % P.nq;
-    const int row_max = r0 + 32 * QB - 1 < P.nq ? r0 + 32 * QB - 1 : P.nq - 1;
-    const int last_key = min(row_max + P.causal_off, N - 1);
-    wave_last = last_key < 0 ? -1 : last_key / BC;
-  }
-
-  // Key tiles this workgroup needs: all of them, or with the causal mask those
-  // up to the last key its rows see.  A workgroup whose rows see no key writes
-  // O = 0 and lse = -inf.
-  int n_tiles = (N + BC - 1) / BC;
-  if constexpr (CAUSAL) {
-    const int first = qt * BR, last = min(P.rows, first + BR) - 1;
-    const int row_max = first / P.nq != last / P.nq ? P.nq - 1 : last % P.nq;
-    const int last_key = row_max + P.causal_off;  // may be < 0
-    n_tiles = last_key < 0 ? 0 : min(n_tiles, last_key / BC + 1);
-  }
-  // Leading tiles that no wave of the workgroup masks: whole tiles of keys,
+  // Limits of the current item (recomputed for each item of a persistent
+  // workgroup).  Causal: a lane's last visible key (its row within its head
+  // plus causal_off), and the smallest such row among the wave's rows (packed
+  // rows wrap to 0 at a head boundary); the last key tile any row of the wave
+  // sees (-1: none), from its largest row within a head (nq - 1 if its rows
+  // wrap to the next head).  n_tiles: the key tiles this workgroup needs, all
+  // of them or with the causal mask those up to the last key its rows see (a
+  // workgroup whose rows see no key writes O = 0 and lse = -inf).  n_clear:
+  // the leading tiles that no wave of the workgroup masks, whole tiles of keys
   // and with the causal mask those whose last key every row of the workgroup
   // sees (its smallest row within a head; 0 if it spans a head boundary).
-  int n_clear = N / BC;
-  if constexpr (CAUSAL) {
-    const int first = qt * BR, last = min(P.rows, first + BR) - 1;
-    const int row_min = first / P.nq != last / P.nq ? 0 : first % P.nq;
-    const int seen = row_min + P.causal_off + 1;  // keys every row sees
-    n_clear = seen <= 0 ? 0 : min(n_clear, seen / BC);
-  }
+  int row_lim[QB];
+  int wave_row_min = 0, wave_last = 0, n_tiles = 0, n_clear = 0;
+  auto item_limits = [&]() {
+    if constexpr (CAUSAL) {
+      const int r0 = q0 % P.nq;
+#pragma unroll
+      for (int b = 0; b < QB; ++b) row_lim[b] = (q0 + 32 * b + l32) % P.nq + P.causal_off;
+      wave_row_min = r0 + 32 * QB - 1 < P.nq ? r0 : 0;
+      const int row_max = r0 + 32 * QB - 1 < P.nq ? r0 + 32 * QB - 1 : P.nq - 1;
+      const int last_key = min(row_max + P.causal_off, N - 1);
+      wave_last = last_key < 0 ? -1 : last_key / BC;
+    }
+    n_tiles = (N + BC - 1) / BC;
+    n_clear = N / BC;
+    if constexpr (CAUSAL) {
+      const int first = qt * BR, last = min(P.rows, first + BR) - 1;
+      const bool spans = first / P.nq != last / P.nq;
+      const int row_max = spans ? P.nq - 1 : last % P.nq;
+      const int last_key = row_max + P.causal_off;  // may be < 0
+      n_tiles = last_key < 0 ? 0 : min(n_tiles, last_key / BC + 1);
+      const int row_min = spans ? 0 : first % P.nq;
+      const int seen = row_min + P.causal_off + 1;  // keys every row sees
+      n_clear = seen <= 0 ? 0 : min(n_clear, seen / BC);
+    }
+    n_cur = n_tiles;
+  };
+  item_limits();
   // c_q: the lane's logit multiplier (scale * log2 e, times the query row
   // scale with Q8).
   using QOp = std::conditional_t<Q8, i32x4, X8>;
@@ -936,7 +944,8 @@ fa2_fwd_kernel(const Problem P) {
     // skips S_{j+1}.  The stale registers it leaves are never used: the next
     // iteration masks every key of that tile for this wave (to -inf, so P is
     // 0 and adds nothing to O), as it would the computed logits.
-    if (!(CAUSAL && (TL & 8) == 0) || j + 1 <= wave_last) gemm1(j + 1, S1{}, kpre, s_nxt);
+    if (!(CAUSAL && (TL & 8) == 0) || (TL & 4) != 0 || j + 1 <= wave_last)
+      gemm1(j + 1, S1{}, kpre, s_nxt);
     if constexpr (!decltype(first)::value) gemm2(j - 1, S3{}, vpre, p_prev);
     float rs[QB];
     bool over = false;
@@ -1059,25 +1068,35 @@ fa2_fwd_kernel(const Problem P) {
 
     // Iterations run in groups of 4 so ring slots and the S / P register
     // sets (even j: S_j in sA, S_{j+1} into sB, P_j into pA) are compile-time.
-    step(std::true_type{}, Ic<0>{}, 0, sA, sB, pB, pA, Ic<PERSIST ? 8 : 0>{});
+    step(std::true_type{}, Ic<0>{}, 0, sA, sB, pB, pA, Ic<PERSIST && !CAUSAL ? 8 : 0>{});
     int j = 1;
     if constexpr (PERSIST) {
       // n_tiles % 4 == 0 and n_tiles >= 8: the loop leaves the last seven
       // iterations, of which the last four load the next item's K tiles 0..3
       // and the last two its V tiles 0..1; the last computes its S_0.
-      // Without the causal mask only the last tile can be masked.
-      for (; j + 7 < n_tiles; j += 4) {
-        step(std::false_type{}, Ic<1>{}, j, sB, sA, pA, pB, Ic<8>{});
-        step(std::false_type{}, Ic<2>{}, j + 1, sA, sB, pB, pA, Ic<8>{});
-        step(std::false_type{}, Ic<3>{}, j + 2, sB, sA, pA, pB, Ic<8>{});
-        step(std::false_type{}, Ic<0>{}, j + 3, sA, sB, pB, pA, Ic<8>{});
+      // Without the causal mask only the last tile can be masked; with it,
+      // the tiles from n_clear on (the diagonal block) take the check.
+      constexpr int NM = CAUSAL ? 0 : 8;
+      if constexpr (CAUSAL) {
+        for (; j + 7 < n_tiles && j + 3 < n_clear; j += 4) {
+          step(std::false_type{}, Ic<1>{}, j, sB, sA, pA, pB, Ic<8>{});
+          step(std::false_type{}, Ic<2>{}, j + 1, sA, sB, pB, pA, Ic<8>{});
+          step(std::false_type{}, Ic<3>{}, j + 2, sB, sA, pA, pB, Ic<8>{});
+          step(std::false_type{}, Ic<0>{}, j + 3, sA, sB, pB, pA, Ic<8>{});
+        }
       }
-      step(std::false_type{}, Ic<1>{}, j, sB, sA, pA, pB, Ic<8>{});
-      step(std::false_type{}, Ic<2>{}, j + 1, sA, sB, pB, pA, Ic<8>{});
-      step(std::false_type{}, Ic<3>{}, j + 2, sB, sA, pA, pB, Ic<8>{});
-      step(std::false_type{}, Ic<0>{}, j + 3, sA, sB, pB, pA, Ic<9>{});
-      step(std::false_type{}, Ic<1>{}, j + 4, sB, sA, pA, pB, Ic<9>{});
-      step(std::false_type{}, Ic<2>{}, j + 5, sA, sB, pB, pA, Ic<11>{});
+      for (; j + 7 < n_tiles; j += 4) {
+        step(std::false_type{}, Ic<1>{}, j, sB, sA, pA, pB, Ic<NM>{});
+        step(std::false_type{}, Ic<2>{}, j + 1, sA, sB, pB, pA, Ic<NM>{});
+        step(std::false_type{}, Ic<3>{}, j + 2, sB, sA, pA, pB, Ic<NM>{});
+        step(std::false_type{}, Ic<0>{}, j + 3, sA, sB, pB, pA, Ic<NM>{});
+      }
+      step(std::false_type{}, Ic<1>{}, j, sB, sA, pA, pB, Ic<NM>{});
+      step(std::false_type{}, Ic<2>{}, j + 1, sA, sB, pB, pA, Ic<NM>{});
+      step(std::false_type{}, Ic<3>{}, j + 2, sB, sA, pA, pB, Ic<NM>{});
+      step(std::false_type{}, Ic<0>{}, j + 3, sA, sB, pB, pA, Ic<1 | NM>{});
+      step(std::false_type{}, Ic<1>{}, j + 4, sB, sA, pA, pB, Ic<1 | NM>{});
+      step(std::false_type{}, Ic<2>{}, j + 5, sA, sB, pB, pA, Ic<3 | NM>{});
       step(std::false_type{}, Ic<3>{}, j + 6, sB, sA, pA, pB, Ic<7>{});
       gemm2(j + 6, Ic<3>{}, vpre, pB);
     } else {
@@ -1183,6 +1202,7 @@ fa2_fwd_kernel(const Problem P) {
     qt = qt_nx;
     q_head = (int64_t)bh * P.rows * D;
     q0 = qt * BR + wq * 32 * QB;
+    item_limits();
     k_rs = rebase(k_rs, nx_delta);
     v_rs = rebase(v_rs, nx_delta);
     look_ahead(item + 1);
@@ -1326,15 +1346,25 @@ int launch(const void* q, const void* k, const void* v, const float* ks, const f
 
   // Launch shape (the arguments are valid; from here on HIP may be queried).
   // Persistent workgroups (the d = 128 tile shape, one workgroup per CU) when
-  // every one gets at least two items of the same length whose key-tile count
-  // the ring's four slots divide and is at least 8 (the ring then carries on
-  // from one item into the next at slot 0), also for short key sequences.
+  // every one gets at least two items whose key-tile counts the ring's four
+  // slots divide and are at least 8 (the ring then carries on from one item
+  // into the next at slot 0), also for short key sequences.  Without the mask
+  // every item has all key tiles.  With it, query tile i of a head needs
+  // (256 (i + 1) + Nk - Nq) / 32 key tiles when Nq is a multiple of the
+  // 256-row tile (no tile straddles two query heads), Nk of 128 and Nk >= Nq;
+  // workgroups then take pairs of query tiles i and T-1-i of one K/V head
+  // (T of them, an even number), which all cost the same.
   const int64_t items_full = B * Hkv * ((rows + bq - 1) / bq);  // full-height workgroups
   bool persist = false;
   int cus = 0;
-  if (!q8 && !causal && d == 128) {
+  if (!q8 && d == 128) {
+    constexpr int64_t BR128 = Cfg<128>::NW * 32 * Cfg<128>::QB;
     const int64_t k_tiles = (Nk + Cfg<128>::BC - 1) / Cfg<128>::BC;
-    if (k_tiles >= 8 && k_tiles % Cfg<128>::RING == 0 && items_full % 8 == 0) {
+    const bool shape_ok =
+        !causal ? (k_tiles >= 8 && k_tiles % Cfg<128>::RING == 0 && items_full % 8 == 0)
+                : (Nq % BR128 == 0 && Nk % (Cfg<128>::BC * Cfg<128>::RING) == 0 && Nk >= Nq &&
+                   (rows / BR128) % 2 == 0 && items_full % 16 == 0);
+    if (shape_ok) {
       cus = cu_count();
       persist = cus > 0 && cus % 8 == 0 && items_full >= 2 * (int64_t)cus;
     }
@@ -1381,8 +1411,10 @@ int launch(const void* q, const void* k, const void* v, const float* ks, const f
                           : pick<256, false>(fp16, mode, causal);
   int64_t grid = groups;
   if (persist) {
-    fn = fp16 ? pick_mode<128, true, false, false, false, true>(mode)
-              : pick_mode<128, false, false, false, false, true>(mode);
+    fn = fp16 ? (causal ? pick_mode<128, true, true, false, false, true>(mode)
+                        : pick_mode<128, true, false, false, false, true>(mode))
+              : (causal ? pick_mode<128, false, true, false, false, true>(mode)
+                        : pick_mode<128, false, false, false, false, true>(mode));
     grid = cus;
   }
   void* args[] = {&P};

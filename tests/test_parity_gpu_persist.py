@@ -1,9 +1,10 @@
 """GPU parity of the persistent-workgroup launches (needs an MI355X).
 
-Non-causal d = 128 calls with enough (K/V head, query tile) items and a
-key-tile count of at least 8 that 4 divides run one workgroup per compute
-unit, each walking several items with its key/value ring carried from one
-item into the next.  Each case here checks that launch against the oracle on sampled rows,
+d = 128 calls with enough (K/V head, query tile) items whose key-tile counts
+4 divides (at least 8) run one workgroup per compute unit, each walking
+several items with its key/value ring carried from one item into the next;
+with the causal mask a workgroup walks pairs of query tiles i and T-1-i of
+one K/V head.  Each case here checks that launch against the oracle on sampled rows,
 and bit for bit against launches of one K/V head group at a time, which are
 too small for persistent workgroups and run one item per workgroup: a row's
 arithmetic does not depend on how the items are spread over workgroups.  The
@@ -60,6 +61,31 @@ CASES = [
 ]
 
 
+def persistent_causal(B, Hq, Hkv, Nq, Nk):
+    """Whether a causal call takes the persistent launch (pairs of query tiles
+    of one K/V head per workgroup): no query tile straddles two query heads,
+    every tile's key count fills whole ring rotations, and the tiles of each
+    K/V head pair up."""
+    rows = Hq // Hkv * Nq
+    items = B * Hkv * rows // BLOCK_Q
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    return (Nq % BLOCK_Q == 0 and Nk % (4 * BLOCK_K) == 0 and Nk >= Nq
+            and (rows // BLOCK_Q) % 2 == 0 and items % 16 == 0
+            and cus % 8 == 0 and items >= 2 * cus)
+
+
+# Causal shapes for the persistent launch: the causal headline (1024 items,
+# four per workgroup), Nk > Nq with grouped heads, the shortest items (8 and
+# 16 key tiles), and grouped heads whose packed query tiles pair across query
+# heads (24 tiles per K/V head).
+CAUSAL_CASES = [
+    (4, 16, 16, 4096, 4096, "bf16"),
+    (4, 32, 8, 1024, 1536, "fp16"),
+    (16, 16, 16, 512, 512, "bf16"),
+    (4, 64, 8, 768, 768, "fp16"),
+]
+
+
 def full_height(B, Hq, Hkv, Nq, Nk):
     """Whether a non-causal call takes one full-height (256-row) workgroup per
     item: not persistent, and at least as many items as compute units."""
@@ -77,6 +103,19 @@ def test_persistent_equals_per_group_launches(B, Hq, Hkv, Nq, Nk, dtype, scale_k
     check_against_groups(B, Hq, Hkv, Nq, Nk, dtype, scale_kind)
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,dtype", CAUSAL_CASES)
+@pytest.mark.parametrize("scale_kind", ["default", "negative"])
+def test_persistent_causal_equals_per_group_launches(B, Hq, Hkv, Nq, Nk, dtype, scale_kind):
+    """Causal calls on persistent workgroups (pairs of query tiles i and T-1-i
+    of one K/V head, the ring carried from one item into the next) give bit
+    for bit what launches of one K/V head group at a time give (one item per
+    workgroup), and match the oracle on sampled rows."""
+    announce("persistent causal", B, Hq, Hkv, Nq, Nk, dtype, scale_kind)
+    if not persistent_causal(B, Hq, Hkv, Nq, Nk):
+        pytest.skip("shape does not take the persistent launch on this device")
+    check_against_groups(B, Hq, Hkv, Nq, Nk, dtype, scale_kind, causal=True)
+
+
 @pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,dtype", [(2, 128, 128, 1100, 1100, "bf16"),
                                                   (1, 64, 16, 2000, 2050, "fp16")])
 def test_full_height_equals_per_group_launches(B, Hq, Hkv, Nq, Nk, dtype):
@@ -88,20 +127,20 @@ def test_full_height_equals_per_group_launches(B, Hq, Hkv, Nq, Nk, dtype):
     check_against_groups(B, Hq, Hkv, Nq, Nk, dtype, "default")
 
 
-def check_against_groups(B, Hq, Hkv, Nq, Nk, dtype, scale_kind):
+def check_against_groups(B, Hq, Hkv, Nq, Nk, dtype, scale_kind, causal=False):
     scale = {"default": 1.0 / math.sqrt(128), "negative": -0.15, "zero": 0.0}[scale_kind]
     seed = B * 1000 + Hq + Nk
     q = rand((B, Hq, Nq, 128), dtype, seed).to(DEV)
     k = rand((B, Hkv, Nk, 128), dtype, seed + 1).to(DEV)
     v = rand((B, Hkv, Nk, 128), dtype, seed + 2).to(DEV)
-    o, lse = fa2.fwd(q, k, v, scale=scale)
+    o, lse = fa2.fwd(q, k, v, scale=scale, causal=causal)
     torch.cuda.synchronize()
     G = Hq // Hkv
     for b in range(B):
         for g in range(Hkv):
             qs = q[b:b + 1, g * G:(g + 1) * G].contiguous()
             o1, l1 = fa2.fwd(qs, k[b:b + 1, g:g + 1].contiguous(), v[b:b + 1, g:g + 1].contiguous(),
-                             scale=scale)
+                             scale=scale, causal=causal)
             torch.cuda.synchronize()
             assert torch.equal(o[b:b + 1, g * G:(g + 1) * G], o1), (b, g)
             assert torch.equal(lse[b:b + 1, g * G:(g + 1) * G], l1), (b, g)
@@ -114,11 +153,11 @@ def check_against_groups(B, Hq, Hkv, Nq, Nk, dtype, scale_kind):
         np.arange(0, flat, Nq * 7 + 255)[:48],
         [0, flat - 1]]).astype(np.int64))
     o_ref, lse_ref = oracle.attention(bits(q.cpu()), bits(k.cpu()), bits(v.cpu()), dtype, scale,
-                                      rows=rows, nthreads=8)
+                                      rows=rows, nthreads=8, causal=causal)
     og = o.cpu().double().numpy().reshape(-1, 128)[rows]
     lg = lse.cpu().double().numpy().reshape(-1)[rows]
-    assert_parity(og, lg, o_ref, lse_ref, "launch %s" % ((B, Hq, Hkv, Nq, Nk, dtype, scale),),
-                  lse_abs=1e-3)
+    assert_parity(og, lg, o_ref, lse_ref,
+                  "launch %s" % ((B, Hq, Hkv, Nq, Nk, dtype, scale, causal),), lse_abs=1e-3)
 
 
 def test_persistent_headline_deterministic():
