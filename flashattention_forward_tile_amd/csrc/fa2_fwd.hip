@@ -200,8 +200,14 @@ template <> struct Cfg8<128> { static constexpr int BC = 32, NW = 8, QB = 1, OCC
 template <int D> struct CfgS;
 template <> struct CfgS<128> { static constexpr int BC = 32, NW = 4, QB = 1, OCC = 2, SGB = 0, RING = 4, PK = 4, PV = 2, DS = 1; };
 constexpr int kShortKeys = 1024;
-template <int D, bool Q8, bool SHORT>
-using KCfg = std::conditional_t<Q8, Cfg8<D>, std::conditional_t<SHORT, CfgS<D>, Cfg<D>>>;
+// Persistent workgroups (one per CU, walking several items): the d = 128
+// shape, and at d = 64 eight waves of 32 rows (a four-wave workgroup's ring
+// and query/output areas, twice over, would not fit two per CU in LDS).
+template <int D> struct CfgP : Cfg<D> {};
+template <> struct CfgP<64> { static constexpr int BC = 64, NW = 8, QB = 1, OCC = 2, SGB = 1, RING = 4, PK = 4, PV = 2, DS = 1; };
+template <int D, bool Q8, bool SHORT, bool PERSIST>
+using KCfg = std::conditional_t<
+    Q8, Cfg8<D>, std::conditional_t<SHORT, CfgS<D>, std::conditional_t<PERSIST, CfgP<D>, Cfg<D>>>>;
 // Ring slots and loop phases as compile-time constants.
 template <int X> using Ic = std::integral_constant<int, X>;
 
@@ -260,12 +266,12 @@ struct Problem {
 // PERSIST: one workgroup per CU walks several (K/V head, query tile) items,
 // and the key/value ring runs on from one item into the next (see below).
 template <int D, bool FP16, int MODE, bool CAUSAL, bool Q8, bool SHORT, bool PERSIST>
-__global__ void __attribute__((amdgpu_flat_work_group_size(KCfg<D, Q8, SHORT>::NW * 64,
-                                                           KCfg<D, Q8, SHORT>::NW * 64),
-                               amdgpu_waves_per_eu(KCfg<D, Q8, SHORT>::OCC,
-                                                   KCfg<D, Q8, SHORT>::OCC)))
+__global__ void __attribute__((amdgpu_flat_work_group_size(KCfg<D, Q8, SHORT, PERSIST>::NW * 64,
+                                                           KCfg<D, Q8, SHORT, PERSIST>::NW * 64),
+                               amdgpu_waves_per_eu(KCfg<D, Q8, SHORT, PERSIST>::OCC,
+                                                   KCfg<D, Q8, SHORT, PERSIST>::OCC)))
 fa2_fwd_kernel(const Problem P) {
-  using C = KCfg<D, Q8, SHORT>;
+  using C = KCfg<D, Q8, SHORT, PERSIST>;
   const int N = P.nk;  // keys per head
   const float c = P.c;
   constexpr int BC = C::BC;
@@ -1141,10 +1147,13 @@ fa2_fwd_kernel(const Problem P) {
   // and every load into it has landed: the last iterations still load tiles
   // past the end (waited one iteration late), whose writes must not fall
   // into the staged output.  PERSIST stages the output apart from the ring,
-  // where the next item's first tiles are still landing, and only waits for
-  // every wave to be done with the query tile there.
-  if constexpr (!PERSIST || kSyncCheck) wait_vmem();
-  __syncthreads();
+  // where the next item's first tiles are still landing, in the area of the
+  // next item's query tile, which every wave read before the barrier that
+  // ended the last iteration: no further wait.
+  if constexpr (!PERSIST || kSyncCheck) {
+    wait_vmem();
+    __syncthreads();
+  }
   // PERSIST: the lane's addresses here are recomputed per item rather than
   // held in registers through the loop.
   int el = lane;
@@ -1345,18 +1354,28 @@ int launch(const void* q, const void* k, const void* v, const float* ks, const f
   if (overlaps(lse, lbytes, o, qbytes)) return FA2_ERR_ALIAS;
 
   // Launch shape (the arguments are valid; from here on HIP may be queried).
-  // Persistent workgroups (the d = 128 tile shape, one workgroup per CU) when
-  // every one gets at least two items whose key-tile counts the ring's four
-  // slots divide and are at least 8 (the ring then carries on from one item
-  // into the next at slot 0), also for short key sequences.  Without the mask
-  // every item has all key tiles.  With it, query tile i of a head needs
-  // (256 (i + 1) + Nk - Nq) / 32 key tiles when Nq is a multiple of the
+  // Persistent workgroups (one per CU) when every one gets at least two items
+  // whose key-tile counts the ring's four slots divide and are at least 8 (the
+  // ring then carries on from one item into the next at slot 0), also for
+  // short key sequences: at d = 128 (256-row items) and, without the mask, at
+  // d = 64 (the CfgP shape, 256-row items of 64-key tiles).  Without the mask
+  // every item has all key tiles.  With it (d = 128), query tile i of a head
+  // needs (256 (i + 1) + Nk - Nq) / 32 key tiles when Nq is a multiple of the
   // 256-row tile (no tile straddles two query heads), Nk of 128 and Nk >= Nq;
   // workgroups then take pairs of query tiles i and T-1-i of one K/V head
   // (T of them, an even number), which all cost the same.
   const int64_t items_full = B * Hkv * ((rows + bq - 1) / bq);  // full-height workgroups
   bool persist = false;
   int cus = 0;
+  if (!q8 && d == 64 && !causal) {
+    constexpr int64_t BRP = CfgP<64>::NW * 32 * CfgP<64>::QB;
+    const int64_t items_p = B * Hkv * ((rows + BRP - 1) / BRP);
+    const int64_t k_tiles = (Nk + CfgP<64>::BC - 1) / CfgP<64>::BC;
+    if (k_tiles >= 8 && k_tiles % CfgP<64>::RING == 0 && items_p % 8 == 0) {
+      cus = cu_count();
+      persist = cus > 0 && cus % 8 == 0 && items_p >= 2 * (int64_t)cus;
+    }
+  }
   if (!q8 && d == 128) {
     constexpr int64_t BR128 = Cfg<128>::NW * 32 * Cfg<128>::QB;
     const int64_t k_tiles = (Nk + Cfg<128>::BC - 1) / Cfg<128>::BC;
@@ -1380,6 +1399,9 @@ int launch(const void* q, const void* k, const void* v, const float* ks, const f
   if (q8) {
     bq = Cfg8<128>::NW * 32 * Cfg8<128>::QB;
     nw = Cfg8<128>::NW;
+  } else if (persist && d == 64) {
+    bq = CfgP<64>::NW * 32 * CfgP<64>::QB;
+    nw = CfgP<64>::NW;
   } else if (short_keys) {
     bq = CfgS<128>::NW * 32 * CfgS<128>::QB;
     nw = CfgS<128>::NW;
@@ -1411,10 +1433,14 @@ int launch(const void* q, const void* k, const void* v, const float* ks, const f
                           : pick<256, false>(fp16, mode, causal);
   int64_t grid = groups;
   if (persist) {
-    fn = fp16 ? (causal ? pick_mode<128, true, true, false, false, true>(mode)
-                        : pick_mode<128, true, false, false, false, true>(mode))
-              : (causal ? pick_mode<128, false, true, false, false, true>(mode)
-                        : pick_mode<128, false, false, false, false, true>(mode));
+    if (d == 64)
+      fn = fp16 ? pick_mode<64, true, false, false, false, true>(mode)
+                : pick_mode<64, false, false, false, false, true>(mode);
+    else
+      fn = fp16 ? (causal ? pick_mode<128, true, true, false, false, true>(mode)
+                          : pick_mode<128, true, false, false, false, true>(mode))
+                : (causal ? pick_mode<128, false, true, false, false, true>(mode)
+                          : pick_mode<128, false, false, false, false, true>(mode));
     grid = cus;
   }
   void* args[] = {&P};

@@ -168,10 +168,14 @@ const char* fa2_strerror(int status);
  * dtype: *block_q query rows per workgroup, *block_k key rows per K/V tile,
  * *waves wavefronts (of 64 lanes) per workgroup.  At d = 128 a call with at
  * most 1024 keys uses half the waves and query rows instead (two workgroups
- * then share a compute unit), unless it is non-causal and large enough for
- * one persistent workgroup per compute unit; so does a call whose
- * full-height workgroups would be fewer than the compute units.  block_q
- * here is always a multiple of the smaller shape.
+ * then share a compute unit), unless it is large enough for one persistent
+ * workgroup per compute unit; so does a call whose full-height workgroups
+ * would be fewer than the compute units.  Persistent workgroups (one per
+ * compute unit, each walking several query tiles) hold 256 query rows with 8
+ * waves at d = 64 (non-causal) and d = 128 (also causal, tiles taken in
+ * pairs of equal total cost).  At d = 256 two waves share each 32 query
+ * rows, each with half of the head dimension.  block_q here is always a
+ * multiple of the smaller shapes and divides the larger.
  * Host-only, no HIP call.  Returns FA2_OK, FA2_ERR_HEADDIM, FA2_ERR_DTYPE or
  * FA2_ERR_NULL.
  */

@@ -86,6 +86,26 @@ CAUSAL_CASES = [
 ]
 
 
+def persistent_d64(B, Hq, Hkv, Nq, Nk):
+    """Whether a non-causal d = 64 call takes the persistent launch (256-row
+    items, 64-key tiles)."""
+    items = B * Hkv * math.ceil(Hq // Hkv * Nq / BLOCK_Q)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    tiles = math.ceil(Nk / 64)
+    return (tiles >= 8 and tiles % 4 == 0 and items % 8 == 0
+            and cus % 8 == 0 and items >= 2 * cus)
+
+
+# d = 64 shapes for the persistent launch: the d = 64 workload (B4 H16 N4096),
+# ragged query tiles and a ragged last key tile with grouped heads, the
+# shortest key sequence it takes (8 tiles of 64 keys).
+D64_CASES = [
+    (4, 16, 16, 4096, 4096, "bf16"),
+    (2, 64, 16, 1100, 2000, "fp16"),
+    (8, 64, 64, 512, 512, "bf16"),
+]
+
+
 def full_height(B, Hq, Hkv, Nq, Nk):
     """Whether a non-causal call takes one full-height (256-row) workgroup per
     item: not persistent, and at least as many items as compute units."""
@@ -116,6 +136,18 @@ def test_persistent_causal_equals_per_group_launches(B, Hq, Hkv, Nq, Nk, dtype, 
     check_against_groups(B, Hq, Hkv, Nq, Nk, dtype, scale_kind, causal=True)
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,dtype", D64_CASES)
+@pytest.mark.parametrize("scale_kind", ["default", "negative"])
+def test_persistent_d64_equals_per_group_launches(B, Hq, Hkv, Nq, Nk, dtype, scale_kind):
+    """d = 64 on persistent eight-wave workgroups gives bit for bit what
+    launches of one K/V head group at a time give (four-wave workgroups, one
+    item each), and matches the oracle on sampled rows."""
+    announce("persistent d64", B, Hq, Hkv, Nq, Nk, dtype, scale_kind)
+    if not persistent_d64(B, Hq, Hkv, Nq, Nk):
+        pytest.skip("shape does not take the persistent launch on this device")
+    check_against_groups(B, Hq, Hkv, Nq, Nk, dtype, scale_kind, d=64)
+
+
 @pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,dtype", [(2, 128, 128, 1100, 1100, "bf16"),
                                                   (1, 64, 16, 2000, 2050, "fp16")])
 def test_full_height_equals_per_group_launches(B, Hq, Hkv, Nq, Nk, dtype):
@@ -127,12 +159,12 @@ def test_full_height_equals_per_group_launches(B, Hq, Hkv, Nq, Nk, dtype):
     check_against_groups(B, Hq, Hkv, Nq, Nk, dtype, "default")
 
 
-def check_against_groups(B, Hq, Hkv, Nq, Nk, dtype, scale_kind, causal=False):
-    scale = {"default": 1.0 / math.sqrt(128), "negative": -0.15, "zero": 0.0}[scale_kind]
+def check_against_groups(B, Hq, Hkv, Nq, Nk, dtype, scale_kind, causal=False, d=128):
+    scale = {"default": 1.0 / math.sqrt(d), "negative": -0.15, "zero": 0.0}[scale_kind]
     seed = B * 1000 + Hq + Nk
-    q = rand((B, Hq, Nq, 128), dtype, seed).to(DEV)
-    k = rand((B, Hkv, Nk, 128), dtype, seed + 1).to(DEV)
-    v = rand((B, Hkv, Nk, 128), dtype, seed + 2).to(DEV)
+    q = rand((B, Hq, Nq, d), dtype, seed).to(DEV)
+    k = rand((B, Hkv, Nk, d), dtype, seed + 1).to(DEV)
+    v = rand((B, Hkv, Nk, d), dtype, seed + 2).to(DEV)
     o, lse = fa2.fwd(q, k, v, scale=scale, causal=causal)
     torch.cuda.synchronize()
     G = Hq // Hkv
@@ -154,7 +186,7 @@ def check_against_groups(B, Hq, Hkv, Nq, Nk, dtype, scale_kind, causal=False):
         [0, flat - 1]]).astype(np.int64))
     o_ref, lse_ref = oracle.attention(bits(q.cpu()), bits(k.cpu()), bits(v.cpu()), dtype, scale,
                                       rows=rows, nthreads=8, causal=causal)
-    og = o.cpu().double().numpy().reshape(-1, 128)[rows]
+    og = o.cpu().double().numpy().reshape(-1, d)[rows]
     lg = lse.cpu().double().numpy().reshape(-1)[rows]
     assert_parity(og, lg, o_ref, lse_ref,
                   "launch %s" % ((B, Hq, Hkv, Nq, Nk, dtype, scale, causal),), lse_abs=1e-3)
