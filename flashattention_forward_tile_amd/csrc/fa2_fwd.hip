@@ -10,10 +10,11 @@
 // loop over the j-th key/value tile) follows that page's Notation section.
 //
 // CDNA4 mapping (prior art re-designed, not translated):
-//  * Both products run on 32x32 MFMA.  The first is computed transposed,
-//    S^T = K_j Q_i^T, so each lane of a wave owns one query column: lanes l and
-//    l+32 hold the two halves of that query's keys, and the softmax needs no
-//    cross-lane reduction except one exchange between the two halves.
+//  * Both products run on 32x32 MFMA (16x16 at d = 256).  The first is
+//    computed transposed, S^T = K_j Q_i^T, so each lane of a wave owns one
+//    query column: lanes l and l+32 hold the two halves of that query's keys
+//    (four lanes hold quarters with 16x16), and the softmax needs no
+//    cross-lane reduction except exchanges between those lanes.
 //  * The S^T accumulator layout is exactly the B-operand layout of the second
 //    product O^T += V_j^T P^T once V_j^T is read in the matching key order,
 //    which ds_read_b64_tr_b16 does from the row-major V tile, so P never
@@ -24,9 +25,9 @@
 //    slots with loads two iterations ahead of their use and the next
 //    iteration's first operands read before the closing barrier (kernels 3
 //    and 5 of that table pipeline one tile ahead).
-//  * d = 256 splits the head dimension between two waves of the same query
-//    rows, which sum their halves of S through LDS, so each wave's registers
-//    stay those of a d = 128 wave (kernel 15 of that table tiles along d).
+//  * d = 256 gives each wave 16 query rows on 16x16x32 MFMA, so its output
+//    accumulator and query fragments fit the register budget of two waves
+//    per SIMD.
 //  * Softmax in fp32 registers with exp2 and the scale folded into one FMA
 //    (kernel 6), against a lazy reference max: it moves only when a row's
 //    tile sum of p would exceed kSumLimit, which keeps the result exact
@@ -52,7 +53,6 @@ namespace fa2 {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -81,11 +81,23 @@ __device__ __forceinline__ f32x16 mfma32x32x16(typename Vec<FP16>::x8 a,
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+template <bool FP16>
+__device__ __forceinline__ f32x4 mfma16x16x32(typename Vec<FP16>::x8 a, typename Vec<FP16>::x8 b,
+                                              f32x4 c) {
+  if constexpr (FP16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 // LDS tiles are row-major with 16-byte chunks XOR-swizzled per row.  The
 // K tile is read with ds_read_b128 by 16 lanes at 16 consecutive rows and one
-// logical chunk; the V tile is read with ds_read_b64_tr_b16 by 16 lanes at 4
-// consecutive rows and 4 consecutive chunks.  Each swizzle spreads its pattern
-// over distinct bank groups; CPR is the row length in chunks.
+// logical chunk; the V tile is read with ds_read_b64_tr_b16, for 32x32
+// products by 32 lanes at 4 consecutive rows and 4 consecutive chunks, for
+// 16x16 products (MS = 16) at 8 consecutive rows and 2 consecutive chunks.
+// Each swizzle spreads its pattern over distinct bank groups; CPR is the row
+// length in chunks.
 template <int CPR>
 __device__ __forceinline__ int k_swizzle(int row, int chunk) {
   static_assert(CPR == 8 || CPR == 16 || CPR == 32, "row of 128, 256 or 512 B");
@@ -94,10 +106,13 @@ __device__ __forceinline__ int k_swizzle(int row, int chunk) {
   else  // 128 B rows: two rows share one sweep of the banks
     return chunk ^ ((row >> 1) & 7);
 }
-template <int CPR>
+template <int CPR, int MS = 32>
 __device__ __forceinline__ int v_swizzle(int row, int chunk) {
   static_assert(CPR == 8 || CPR == 16 || CPR == 32, "row of 128, 256 or 512 B");
-  if constexpr (CPR >= 16)
+  static_assert(MS == 32 || CPR >= 16, "16x16 reads of rows of 256 B or more");
+  if constexpr (MS == 16)
+    return chunk ^ ((row & 7) << 1);
+  else if constexpr (CPR >= 16)
     return chunk ^ ((row & 3) << 2);
   else
     return chunk ^ (((row >> 1) & 1) << 2);
@@ -161,50 +176,48 @@ __device__ __forceinline__ void load_lds4(i32x4 rsrc, uint32_t voff, uint32_t ld
 }
 
 // Tile shape per head dimension: key rows per tile (BC), waves per workgroup
-// (NW), 32-query blocks per wave (QB), the waves per SIMD the register
+// (NW), MS-query blocks per wave (QB), the waves per SIMD the register
 // budget is sized for (OCC), whether the iteration block carries explicit
 // MFMA / LDS / VALU interleave hints (SGB), the LDS slots per K and V ring
 // (RING), how many K and V operands of each product are read from LDS one
-// iteration early (PK, PV), and how many waves share one query block, each
-// holding 1/DS of the head dimension (DS; the tiling along the head
-// dimension of kernel 15 in the Ampere series' list).  Each K or V operand
-// read from LDS feeds QB matrix instructions, so LDS bytes per FLOP fall as
-// 1/QB.
+// iteration early (PK, PV), and the matrix instruction shape (MS = 32:
+// 32x32x16, MS = 16: 16x16x32), which is also the query rows of one block.
+// Each K or V operand read from LDS feeds QB matrix instructions, so LDS
+// bytes per FLOP fall as 1/QB.
 //
-// d = 256 splits the head dimension between two waves (DS = 2): wave w and
-// wave w + NW/2 hold the same 32 query rows, each with its half of Q, of
-// every K and V row, and of O.  Each computes a partial S over its half of
-// the contraction; the pair sums the two halves through LDS and then runs the
-// identical softmax, so each wave's registers are those of a d = 128 wave and
-// two waves fit on a SIMD.
+// d = 256 uses the 16x16x32 shape: a wave of 32 query rows would hold 128
+// accumulator and 64 query-fragment registers, more than two waves per SIMD
+// allow, while 16 rows hold half of each.  Every wave still reads all of each
+// K and V tile, so the LDS bytes per FLOP are twice those of the 32-row
+// waves at d = 128 (the transposed-read pattern of V then spans 8 rows, which
+// its swizzle spreads over the banks).
 //
 // K and V tiles cycle through rings of RING = 4 LDS slots: tile t sits in
 // slot t % 4, K_t is loaded during iteration t - 4 and V_t during iteration
 // t - 2, and each iteration waits only for the loads of the one before it,
 // so every load has two iterations to land and the operands an iteration
 // reads were published one barrier early (which is what lets PK, PV > 0).
-// At d = 256 the rings take 128 KiB and the pairs' exchange slots the other
-// 32 KiB of a workgroup's LDS.
+// At d = 256 the rings take 128 KiB of a workgroup's LDS.
 template <int D> struct Cfg;
-template <> struct Cfg<64> { static constexpr int BC = 64, NW = 4, QB = 1, OCC = 2, SGB = 1, RING = 4, PK = 4, PV = 2, DS = 1; };
-template <> struct Cfg<128> { static constexpr int BC = 32, NW = 8, QB = 1, OCC = 2, SGB = 0, RING = 4, PK = 4, PV = 2, DS = 1; };
-template <> struct Cfg<256> { static constexpr int BC = 32, NW = 8, QB = 1, OCC = 2, SGB = 0, RING = 4, PK = 4, PV = 0, DS = 2; };
+template <> struct Cfg<64> { static constexpr int BC = 64, NW = 4, QB = 1, OCC = 2, SGB = 1, RING = 4, PK = 4, PV = 2, MS = 32; };
+template <> struct Cfg<128> { static constexpr int BC = 32, NW = 8, QB = 1, OCC = 2, SGB = 0, RING = 4, PK = 4, PV = 2, MS = 32; };
+template <> struct Cfg<256> { static constexpr int BC = 32, NW = 8, QB = 1, OCC = 2, SGB = 0, RING = 4, PK = 4, PV = 2, MS = 16; };
 
 // Tile shape of the INT8 key/value cache kernels (d = 128 only).
 template <int D> struct Cfg8;
-template <> struct Cfg8<128> { static constexpr int BC = 32, NW = 8, QB = 1, OCC = 2, SGB = 0, RING = 4, PK = 2, PV = 2, DS = 1; };
+template <> struct Cfg8<128> { static constexpr int BC = 32, NW = 8, QB = 1, OCC = 2, SGB = 0, RING = 4, PK = 2, PV = 2, MS = 32; };
 // Short key sequences at d = 128 (at most kShortKeys keys): half the query
 // rows per workgroup, so two workgroups share a CU and one's prologue and
 // epilogue overlap the other's loop.  The same shape serves grids too small
 // to give every CU a full-height workgroup.
 template <int D> struct CfgS;
-template <> struct CfgS<128> { static constexpr int BC = 32, NW = 4, QB = 1, OCC = 2, SGB = 0, RING = 4, PK = 4, PV = 2, DS = 1; };
+template <> struct CfgS<128> { static constexpr int BC = 32, NW = 4, QB = 1, OCC = 2, SGB = 0, RING = 4, PK = 4, PV = 2, MS = 32; };
 constexpr int kShortKeys = 1024;
 // Persistent workgroups (one per CU, walking several items): the d = 128
 // shape, and at d = 64 eight waves of 32 rows (a four-wave workgroup's ring
 // and query/output areas, twice over, would not fit two per CU in LDS).
 template <int D> struct CfgP : Cfg<D> {};
-template <> struct CfgP<64> { static constexpr int BC = 64, NW = 8, QB = 1, OCC = 2, SGB = 1, RING = 4, PK = 4, PV = 2, DS = 1; };
+template <> struct CfgP<64> { static constexpr int BC = 64, NW = 8, QB = 1, OCC = 2, SGB = 1, RING = 4, PK = 4, PV = 2, MS = 32; };
 template <int D, bool Q8, bool SHORT, bool PERSIST>
 using KCfg = std::conditional_t<
     Q8, Cfg8<D>, std::conditional_t<SHORT, CfgS<D>, std::conditional_t<PERSIST, CfgP<D>, Cfg<D>>>>;
@@ -277,8 +290,12 @@ fa2_fwd_kernel(const Problem P) {
   constexpr int BC = C::BC;
   constexpr int NW = C::NW;
   constexpr int QB = C::QB;
-  constexpr int DS = C::DS;           // waves per query block (head-dimension split)
-  constexpr int BR = NW * 32 * QB / DS;  // query rows per workgroup
+  // Matrix instruction shape: 32x32x16 (MS = 32: a wave block of 32 query
+  // rows, lanes l and l+32 share a row) or 16x16x32 (MS = 16: 16 query rows,
+  // lanes l, l+16, l+32, l+48 share a row).
+  constexpr int MS = C::MS;
+  static_assert(MS == 32 || (MS == 16 && !Q8 && !PERSIST), "16x16x32 blocking");
+  constexpr int BR = NW * MS * QB;    // query rows per workgroup
   constexpr int CPR = D / 8;          // 16-byte chunks per (16-bit) V row
   constexpr int RB = D * 2;           // bytes per (16-bit) V row in LDS
   constexpr int TBYTES = BC * RB;     // one V tile in LDS
@@ -287,17 +304,15 @@ fa2_fwd_kernel(const Problem P) {
   constexpr int TBK = BC * RBK;       // one K tile in LDS (and one int8 V tile)
   constexpr int LW = Q8 ? 4 : 16;     // bytes per lane of one HBM -> LDS load
   constexpr int LOADS = TBK / (NW * 64 * LW);  // K loads per thread per tile (V: the same)
-  constexpr int KS = Q8 ? D / 32 : D / 16;     // k-steps of the first product
-  constexpr int ST = BC / 16;         // k-steps of the second product
-  constexpr int KB = BC / 32;         // 32-key blocks per tile
-  constexpr int DB = D / 32;          // 32-dim blocks of the output
-  constexpr int KSW = KS / DS;        // k-steps of the first product per wave
-  constexpr int DBW = DB / DS;        // 32-dim output blocks per wave
-  constexpr int DW = D / DS;          // output columns per wave
+  constexpr int KD = Q8 || MS == 16 ? 32 : 16;  // contraction depth of one first-product MFMA
+  constexpr int KS = D / KD;          // k-steps of the first product
+  constexpr int KPM = MS == 32 ? 16 : 32;  // keys per second-product MFMA
+  constexpr int ST = BC / KPM;        // k-steps of the second product
+  constexpr int KB = BC / MS;         // MS-key blocks per tile
+  constexpr int DB = D / MS;          // MS-dim blocks of the output
+  constexpr int NACC = MS * MS / 64;  // accumulator registers per lane of one block
   static_assert(TBK % (NW * 64 * LW) == 0, "tile must split into wave loads");
-  static_assert(BC % 32 == 0 && D % 32 == 0, "MFMA 32x32 blocking");
-  static_assert(DS == 1 || (DS == 2 && !Q8 && !PERSIST && NW % 2 == 0 && KS % 2 == 0 &&
-                            DB % 2 == 0), "head-dimension split");
+  static_assert(BC % 32 == 0 && D % 32 == 0, "MFMA blocking");
   // Q and O are bf16 or fp16; P and V meet on fp16 matrix instructions in the
   // INT8 kernels (V is widened exactly), on the input type otherwise.
   constexpr bool F16B = FP16 || Q8;
@@ -307,12 +322,13 @@ fa2_fwd_kernel(const Problem P) {
   using E = typename Vec<FP16>::e;    // element type of Q and O
   using EP = typename Vec<F16B>::e;   // element type of P
   using KOp = std::conditional_t<Q8, i32x4, X8>;        // A operand of the first product
-  using SAcc = std::conditional_t<Q8, i32x16, f32x16>;  // its accumulator
+  using FAcc = std::conditional_t<MS == 32, f32x16, f32x4>;  // fp32 accumulator block
+  using SAcc = std::conditional_t<Q8, i32x16, FAcc>;    // the first product's
 
   constexpr int PK = C::PK;           // K operands read one iteration early
   constexpr int PV = C::PV;           // V operands read one iteration early
-  constexpr int KO = KSW * KB;        // K operands (A of the first product) per tile and wave
-  constexpr int VO = ST * DBW;        // V operands (A of the second product) per tile and wave
+  constexpr int KO = KS * KB;         // K operands (A of the first product) per tile and wave
+  constexpr int VO = ST * DB;         // V operands (A of the second product) per tile and wave
   constexpr int RING = C::RING;
   static_assert(RING == 4, "ring of four slots");
   static_assert(PK <= KO && PV <= VO, "prefetch depth");
@@ -325,15 +341,10 @@ fa2_fwd_kernel(const Problem P) {
   constexpr int VBASE = RING * TBK;
   constexpr int SBASE = VBASE + RING * TBYTES;
   constexpr int RING_BYTES = SBASE + (Q8 ? RING * TBK : 0);
-  // DS = 2: after the ring, one slot per wave for its partial logits of a
-  // tile (QB * KB accumulators of 16 fp32 per lane, 1 KiB per 4 of them).
-  constexpr int SXG = QB * KB * 4;    // 16-byte pieces per lane
-  constexpr int SXBASE = RING_BYTES;
-  constexpr int SXBYTES = DS > 1 ? NW * SXG * 64 * 16 : 0;
-  // After the loop the same LDS stages the output: each wave's 32*QB rows of
+  // After the loop the same LDS stages the output: each wave's MS*QB rows of
   // O, row-major, rows padded by 16 bytes (OROW) against bank conflicts.
-  constexpr int OROW = DW * 2 + 16;
-  constexpr int OBYTES = NW * 32 * QB * OROW;
+  constexpr int OROW = D * 2 + 16;
+  constexpr int OBYTES = NW * MS * QB * OROW;
   // PERSIST keeps the ring apart from a query / output area at QOBASE: the
   // next item's query tile is staged there while the current one runs, and
   // the output is staged there while the next item's first K/V tiles sit in
@@ -344,18 +355,18 @@ fa2_fwd_kernel(const Problem P) {
   constexpr int QOBYTES = QTB > OBYTES ? QTB : OBYTES;
   __shared__ __attribute__((aligned(16)))
   char smem[PERSIST ? RING_BYTES + QOBYTES
-                    : (RING_BYTES + SXBYTES > OBYTES ? RING_BYTES + SXBYTES : OBYTES)];
+                    : (RING_BYTES > OBYTES ? RING_BYTES : OBYTES)];
   lds_char* const lds = (lds_char*)smem;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int half = lane >> 5;
+  // The lane's query row within an MFMA block, and its k-group (the lanes of
+  // one row: MS = 32, l and l + 32; MS = 16, l + 16 g for g = 0..3).
+  const int lq = lane & (MS - 1);
+  const int lg = lane / MS;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // The wave's query block and, with DS = 2, its half of the head dimension
-  // (waves w and w + NW/2 share a query block).
-  const int wq = DS == 1 ? wave : wave % (NW / DS);
-  const int dpart = DS == 1 ? 0 : wave / (NW / DS);
 
   // Work items are (K/V head bh = b * hkv + g, query tile qt) pairs, G =
   // n_groups of them.  All query tiles of one K/V head go to one XCD
@@ -458,7 +469,7 @@ fa2_fwd_kernel(const Problem P) {
     const int pos = ((i * NW + wave) * 64 + lane) * LW;  // byte in the LDS tile
     const int row = pos / RBK, pc = (pos % RBK) / 16, byte = pos % 16;
     k_src[i] = (uint32_t)(row * RBK + k_swizzle<CPRK>(row, pc) * 16 + byte);
-    v_src[i] = Q8 ? (uint32_t)pos : (uint32_t)(row * RB + v_swizzle<CPR>(row, pc) * 16);
+    v_src[i] = Q8 ? (uint32_t)pos : (uint32_t)(row * RB + v_swizzle<CPR, MS>(row, pc) * 16);
   }
   // `s` (an integral constant) is t modulo 4, known at compile time in the
   // loop (unrolled by 4), so the ring slot t % RING and its LDS offsets fold
@@ -521,35 +532,48 @@ fa2_fwd_kernel(const Problem P) {
   };
 
   // Per-lane LDS byte offsets of the MFMA operands within a tile.  The
-  // swizzle term depends only on the lane (row bits below the 32- or 16-row
-  // block), so every other index becomes an instruction immediate.
-  //   K (A operand of S^T): row kb*32 + l32, logical chunk ks*2 + half.
-  //   V^T (A operand of O^T), via ds_read_b64_tr_b16: the 16-lane group g
-  //   reads rows st*16 + sg*8 + half*4 + (lane%16)/4 and 4 elements at column
-  //   db*32 + 16*(g&1) + 4*(lane%4); lane l then holds V[key][db*32 + l32]
-  //   for keys st*16 + sg*8 + half*4 + 0..3.
+  // swizzle term depends only on the lane (row bits below the MS-row block),
+  // so every other index becomes an instruction immediate.
+  //   K (A operand of S^T): row kb*MS + lq, logical chunk ks*KCH + lg.
+  //   V^T (A operand of O^T), via ds_read_b64_tr_b16 (in each 16-lane group
+  //   lane i receives element i%4 of the 8-byte pieces that lanes i/4,
+  //   4+i/4, 8+i/4, 12+i/4 address).  MS = 32: the 16-lane group g reads rows
+  //   st*16 + sg*8 + half*4 + (lane%16)/4 and 4 elements at column
+  //   db*32 + 16*(g&1) + 4*(lane%4); lane l then holds V[key][db*32 + l32] for
+  //   keys st*16 + sg*8 + half*4 + 0..3.  MS = 16: group g reads rows
+  //   st*32 + sg*16 + 4g + (lane%16)/4 at column db*16 + 4*(lane%4); lane l
+  //   then holds V[key][db*16 + lq] for keys st*32 + sg*16 + 4g + 0..3.
+  //   Either way these are the keys whose probabilities the lane holds in
+  //   the matching slots of its B operand (the S^T accumulator layout).
   // The swizzles touch only the low 4 bits of a chunk index, so offsets
-  // repeat every 16 chunks (256 B) along a row: keep at most 8 K offsets and
-  // 4 V offsets and reach the rest with an immediate.
-  constexpr int KOFF = KS < 8 ? KS : 8;
-  constexpr int VOFF = DB < 4 ? DB : 4;
+  // repeat every 16 chunks (256 B) along a row: keep one K offset per k-step
+  // and one V offset per output block within 256 B, and reach the rest with
+  // an immediate.  The V offsets include the V ring's base and are opaque to
+  // the compiler, so that the immediate of an LDS read (16 bits) only has to
+  // hold the slot and the rows: at d = 256 the V ring starts at 64 KiB.
+  constexpr int KCH = KD * (Q8 ? 1 : 2) / 16;  // 16-byte chunks of a K row per k-step
+  constexpr int KPB = 16 / KCH;       // first-product k-steps per 256 B of a row
+  constexpr int KOFF = KS < KPB ? KS : KPB;
+  constexpr int VPB = 128 / MS;       // output blocks per 256 B of a row
+  constexpr int VOFF = DB < VPB ? DB : VPB;
   uint32_t k_off[KOFF];
 #pragma unroll
   for (int ks = 0; ks < KOFF; ++ks)
-    k_off[ks] = (uint32_t)(l32 * RBK + k_swizzle<CPRK>(l32, ks * 2 + half) * 16 + dpart * KSW * 32);
-  const int tr_row = half * 4 + ((lane & 15) >> 2);
-  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    k_off[ks] = (uint32_t)(lq * RBK + k_swizzle<CPRK>(lq, ks * KCH + lg) * 16);
+  const int tr_row = MS == 32 ? half * 4 + ((lane & 15) >> 2) : 4 * lg + ((lane & 15) >> 2);
+  const int tr_col = MS == 32 ? 16 * ((lane >> 4) & 1) + 4 * (lane & 3) : 4 * (lane & 3);
   uint32_t v_off[VOFF];
 #pragma unroll
   for (int db = 0; db < VOFF; ++db) {
-    const int col = db * 32 + tr_col;
-    v_off[db] = (uint32_t)(tr_row * RB + v_swizzle<CPR>(tr_row, col >> 3) * 16 + (col & 7) * 2 +
-                           dpart * DBW * 64);
+    const int col = db * MS + tr_col;
+    v_off[db] = (uint32_t)(VBASE + tr_row * RB + v_swizzle<CPR, MS>(tr_row, col >> 3) * 16 +
+                           (col & 7) * 2);
+    asm volatile("" : "+v"(v_off[db]));
   }
 
   // Q_i fragments: the B operands of S^T = K_j Q_i^T, held for the whole
-  // loop.  Query block b of this wave is packed rows q0 + 32*b + l32.
-  int q0 = qt * BR + wq * 32 * QB;
+  // loop.  Query block b of this wave is packed rows q0 + MS*b + lq.
+  int q0 = qt * BR + wave * MS * QB;
 
   // Limits of the current item (recomputed for each item of a persistent
   // workgroup).  Causal: a lane's last visible key (its row within its head
@@ -568,9 +592,9 @@ fa2_fwd_kernel(const Problem P) {
     if constexpr (CAUSAL) {
       const int r0 = q0 % P.nq;
 #pragma unroll
-      for (int b = 0; b < QB; ++b) row_lim[b] = (q0 + 32 * b + l32) % P.nq + P.causal_off;
-      wave_row_min = r0 + 32 * QB - 1 < P.nq ? r0 : 0;
-      const int row_max = r0 + 32 * QB - 1 < P.nq ? r0 + 32 * QB - 1 : P.nq - 1;
+      for (int b = 0; b < QB; ++b) row_lim[b] = (q0 + MS * b + lq) % P.nq + P.causal_off;
+      wave_row_min = r0 + MS * QB - 1 < P.nq ? r0 : 0;
+      const int row_max = r0 + MS * QB - 1 < P.nq ? r0 + MS * QB - 1 : P.nq - 1;
       const int last_key = min(row_max + P.causal_off, N - 1);
       wave_last = last_key < 0 ? -1 : last_key / BC;
     }
@@ -592,20 +616,19 @@ fa2_fwd_kernel(const Problem P) {
   // c_q: the lane's logit multiplier (scale * log2 e, times the query row
   // scale with Q8).
   using QOp = std::conditional_t<Q8, i32x4, X8>;
-  QOp qf[QB][KSW];
+  QOp qf[QB][KS];
   float c_q[QB];
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
     c_q[b] = c;
-    const uint32_t qrow_off = (uint32_t)(q0 + 32 * b + l32) * RB;  // unsigned, as above
+    const uint32_t qrow_off = (uint32_t)(q0 + MS * b + lq) * RB;  // unsigned, as above
     if constexpr (PERSIST) {
       // fragments come through LDS (load_qf below)
     } else if constexpr (!Q8) {
 #pragma unroll
-      for (int ks = 0; ks < KSW; ++ks)
+      for (int ks = 0; ks < KS; ++ks)
         qf[b][ks] = __builtin_bit_cast(
-            X8, __builtin_amdgcn_raw_buffer_load_b128(
-                    q_rs, qrow_off + (dpart * KSW + ks) * 32 + half * 16, 0, 0));
+            X8, __builtin_amdgcn_raw_buffer_load_b128(q_rs, qrow_off + (ks * KD + lg * 8) * 2, 0, 0));
     } else if constexpr (MODE != kZero) {
       // In-kernel quantization of the query row (lanes l and l+32 hold its
       // two halves): for k-step ks this lane holds channels 32 ks + 16 half
@@ -660,14 +683,14 @@ fa2_fwd_kernel(const Problem P) {
     }
   }
 
-  f32x16 acc[QB][DBW];
+  FAcc acc[QB][DB];
   float m_ref[QB], l_part[QB];  // reference max (log2 units), lane's row sum
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
 #pragma unroll
-    for (int db = 0; db < DBW; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[b][db][i] = 0.0f;
+      for (int i = 0; i < NACC; ++i) acc[b][db][i] = 0.0f;
     m_ref[b] = -INFINITY;
     l_part[b] = 0.0f;
   }
@@ -694,30 +717,31 @@ fa2_fwd_kernel(const Problem P) {
   KOp kpre[PK > 0 ? PK : 1];
   X8 vpre[PV > 0 ? PV : 1];
 
-  // Operand o of the first product, o = ks*KB + kk: rows kk*32 .. +31 of
+  // Operand o of the first product, o = ks*KB + kk: rows kk*MS .. +MS-1 of
   // K_t (k-step ks), as the A operand of S^T = K_t Q_i^T.
   auto k_operand = [&](int t, auto s, int o) -> KOp {
     const int ks = o / KB, kk = o % KB;
     const lds_char* kb = lds + slot(t, s) * TBK;
     return __builtin_bit_cast(
         KOp, *(const __attribute__((address_space(3))) u32x4*)(
-                 kb + kk * 32 * RBK + k_off[ks % KOFF] + (ks / KOFF) * 256));
+                 kb + kk * MS * RBK + k_off[ks % KOFF] + (ks / KOFF) * 256));
   };
   // Operand o of the second product, o = st*DB + db: V_t^T for output rows
-  // db*32 .. +31 and keys st*16 .. +15 in the S^T accumulator's key order,
-  // from the row-major V tile through two transposing LDS reads of 4 keys.
+  // db*MS .. +MS-1 and keys st*KPM .. +KPM-1 in the S^T accumulator's key
+  // order, from the row-major V tile through two transposing LDS reads of 4
+  // keys.
   auto v_operand = [&](int t, auto s, int o) -> X8 {
-    const int st = o / DBW, db = o % DBW;
-    const lds_char* vb = lds + VBASE + slot(t, s) * TBYTES;
+    const int st = o / DB, db = o % DB;
+    const lds_char* vb = lds + slot(t, s) * TBYTES;  // v_off holds VBASE
     const uint32_t vo = v_off[db % VOFF] + (db / VOFF) * 256;
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_s16x4*)(vb + vo + (st * 16) * RB));
+        (lds_s16x4*)(vb + vo + (st * KPM) * RB));
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_s16x4*)(vb + vo + (st * 16 + 8) * RB));
+        (lds_s16x4*)(vb + vo + (st * KPM + KPM / 2) * RB));
     return __builtin_bit_cast(X8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
 
-  // S^T_t = K_t Q_i^T : [BC keys] x [32 queries] per wave.  The first PK
+  // S^T_t = K_t Q_i^T : [BC keys] x [MS queries] per wave.  The first PK
   // operands come from `pre` (read during the previous iteration), the rest
   // from LDS.  With a zero scale every logit is 0 whatever Q and K hold, so S
   // stays 0 and c is taken as 1 (x = s - m_ref keeps masked keys at -inf).
@@ -727,7 +751,7 @@ fa2_fwd_kernel(const Problem P) {
 #pragma unroll
       for (int kk = 0; kk < KB; ++kk)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sd[b][kk][i] = 0;
+        for (int i = 0; i < (Q8 ? 16 : NACC); ++i) sd[b][kk][i] = 0;
     if constexpr (MODE == kZero) return;
 #pragma unroll
     for (int o = 0; o < KO; ++o) {
@@ -736,20 +760,27 @@ fa2_fwd_kernel(const Problem P) {
       for (int b = 0; b < QB; ++b) {
         if constexpr (Q8)  // exact int32 dot products of the codes
           sd[b][o % KB] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qf[b][o / KB], sd[b][o % KB], 0, 0, 0);
-        else
+        else if constexpr (MS == 32)
           sd[b][o % KB] = mfma32x32x16<FP16>(a, qf[b][o / KB], sd[b][o % KB]);
+        else
+          sd[b][o % KB] = mfma16x16x32<FP16>(a, qf[b][o / KB], sd[b][o % KB]);
       }
     }
   };
 
-  // O^T += V_t^T P_t^T : [D] x [32 queries] per wave; the first PV operands
+  // O^T += V_t^T P_t^T : [D] x [MS queries] per wave; the first PV operands
   // come from `pre`.
   auto gemm2 = [&](int t, auto s, const X8 (&pre)[PV > 0 ? PV : 1], const X8 (&pf)[QB][ST]) {
 #pragma unroll
     for (int o = 0; o < VO; ++o) {
       const X8 a = o < PV ? pre[o < PV ? o : 0] : v_operand(t, s, o);
 #pragma unroll
-      for (int b = 0; b < QB; ++b) acc[b][o % DBW] = mfma32x32x16<F16B>(a, pf[b][o / DBW], acc[b][o % DBW]);
+      for (int b = 0; b < QB; ++b) {
+        if constexpr (MS == 32)
+          acc[b][o % DB] = mfma32x32x16<F16B>(a, pf[b][o / DB], acc[b][o % DB]);
+        else
+          acc[b][o % DB] = mfma16x16x32<F16B>(a, pf[b][o / DB], acc[b][o % DB]);
+      }
     }
   };
 
@@ -762,42 +793,6 @@ fa2_fwd_kernel(const Problem P) {
   auto prefetch_v = [&](int t, auto s, X8 (&pre)[PV > 0 ? PV : 1]) {
 #pragma unroll
     for (int o = 0; o < PV; ++o) pre[o] = v_operand(t, s, o);
-  };
-
-  // DS = 2: a wave's partial logits of one tile go to its slot of the
-  // exchange area, lane-linear (each 16-byte piece of 64 lanes is 1 KiB),
-  // and the partner wave (w xor NW/2, same query rows and layout) adds them
-  // to its own.
-  auto write_partial = [&](const SAcc (&sd)[QB][KB]) {
-    if constexpr (DS > 1) {
-      lds_char* const base = lds + SXBASE + (wave * SXG * 64 + lane) * 16;
-#pragma unroll
-      for (int b = 0; b < QB; ++b)
-#pragma unroll
-        for (int kk = 0; kk < KB; ++kk)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const f32x4 v = {sd[b][kk][4 * g], sd[b][kk][4 * g + 1], sd[b][kk][4 * g + 2],
-                             sd[b][kk][4 * g + 3]};
-            *(__attribute__((address_space(3))) f32x4*)(base + ((b * KB + kk) * 4 + g) * 1024) = v;
-          }
-    }
-  };
-  auto read_partial = [&](SAcc (&sx)[QB][KB]) {
-    if constexpr (DS > 1) {
-      const lds_char* const base = lds + SXBASE + ((wave ^ (NW / 2)) * SXG * 64 + lane) * 16;
-#pragma unroll
-      for (int b = 0; b < QB; ++b)
-#pragma unroll
-        for (int kk = 0; kk < KB; ++kk)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const f32x4 v = *(const __attribute__((address_space(3))) f32x4*)(
-                base + ((b * KB + kk) * 4 + g) * 1024);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sx[b][kk][4 * g + e] = v[e];
-          }
-    }
   };
 
   // Q8: widen V_t from its int8 staging slot into the 16-bit V ring as exact
@@ -831,7 +826,21 @@ fa2_fwd_kernel(const Problem P) {
     }
   };
 
-  auto probs = [&](const f32x16 (&sc)[KB], X8 (&pf)[ST], float m, float cl) -> float {
+  // Reductions over the lanes that hold one query row.
+  auto row_max = [&](float x) -> float {
+    if constexpr (MS == 16) x = fmaxf(x, __shfl_xor(x, 16));
+    return fmaxf(x, __shfl_xor(x, 32));
+  };
+  auto row_sum = [&](float x) -> float {
+    if constexpr (MS == 16) x += __shfl_xor(x, 16);
+    return x + __shfl_xor(x, 32);
+  };
+
+  // P_t^T as the B operands of the second product.  MS = 32: k-step st
+  // takes keys 16 st .. +15, this lane's 8 of them the accumulator elements
+  // 8 (st % 2) .. +7 of key block st / 2.  MS = 16: k-step st takes key
+  // blocks 2 st and 2 st + 1, this lane's 4 keys of each.
+  auto probs = [&](const FAcc (&sc)[KB], X8 (&pf)[ST], float m, float cl) -> float {
     // A causal row that has seen no key yet has m = -inf and only masked
     // logits; reference 0 gives them p = 0 rather than NaN.
     if constexpr (CAUSAL) m = m == -INFINITY ? 0.0f : m;
@@ -841,9 +850,10 @@ fa2_fwd_kernel(const Problem P) {
       u32x4 w;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int i0 = (st & 1) * 8 + 2 * e;
-        const float x0 = __builtin_fmaf(sc[st >> 1][i0], cl, -m);
-        const float x1 = __builtin_fmaf(sc[st >> 1][i0 + 1], cl, -m);
+        const int kb = MS == 32 ? st >> 1 : 2 * st + (e >> 1);
+        const int i0 = MS == 32 ? (st & 1) * 8 + 2 * e : 2 * (e & 1);
+        const float x0 = __builtin_fmaf(sc[kb][i0], cl, -m);
+        const float x1 = __builtin_fmaf(sc[kb][i0 + 1], cl, -m);
         const float p0 = __builtin_amdgcn_exp2f(x0);
         const float p1 = __builtin_amdgcn_exp2f(x1);
         rs += p0;
@@ -892,16 +902,6 @@ fa2_fwd_kernel(const Problem P) {
       wait_vmem();
       __syncthreads();
     }
-    // DS = 2: the partner's half of this tile's logits (written before the
-    // barrier that ended the previous iteration), added to this wave's half.
-    if constexpr (DS > 1) {
-      SAcc sx[QB][KB];
-      read_partial(sx);
-#pragma unroll
-      for (int b = 0; b < QB; ++b)
-#pragma unroll
-        for (int kk = 0; kk < KB; ++kk) s_cur[b][kk] += sx[b][kk];
-    }
 
     // The logits of this tile in fp32 (converted from the int32 products
     // with Q8).
@@ -937,9 +937,11 @@ fa2_fwd_kernel(const Problem P) {
 #pragma unroll
         for (int kk = 0; kk < KB; ++kk)
 #pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (key0 + kk * 32 + (i >> 2) * 8 + half * 4 + (i & 3) > lim)
-              sf[b][kk][i] = MODE == kNegative ? INFINITY : -INFINITY;
+          for (int i = 0; i < (Q8 ? 16 : NACC); ++i) {
+            const int key = MS == 32 ? key0 + kk * 32 + (i >> 2) * 8 + half * 4 + (i & 3)
+                                     : key0 + kk * 16 + lg * 4 + i;
+            if (key > lim) sf[b][kk][i] = MODE == kNegative ? INFINITY : -INFINITY;
+          }
       }
     }
 
@@ -997,20 +999,20 @@ fa2_fwd_kernel(const Problem P) {
 #pragma unroll
         for (int kk = 0; kk < KB; ++kk)
 #pragma unroll
-          for (int i = 0; i < 16; ++i)
+          for (int i = 0; i < (Q8 ? 16 : NACC); ++i)
             ext = MODE == kNegative ? fminf(ext, sf[b][kk][i]) : fmaxf(ext, sf[b][kk][i]);
         const float t_max = __builtin_isfinite(ext) ? ext * c_q[b] : -INFINITY;
-        const float t_row = fmaxf(t_max, __shfl_xor(t_max, 32));
+        const float t_row = row_max(t_max);
         const float mine = !(rs[b] <= kSumLimit) ? 1.0f : 0.0f;
         // a row still at -inf takes its first reference from any visible key
-        const bool move = fmaxf(mine, __shfl_xor(mine, 32)) > 0.0f || m_ref[b] == -INFINITY;
+        const bool move = row_max(mine) > 0.0f || m_ref[b] == -INFINITY;
         const float m_new = move ? fmaxf(m_ref[b], t_row) : m_ref[b];
         const float alpha =
             m_new == m_ref[b] ? 1.0f : __builtin_amdgcn_exp2f(m_ref[b] - m_new);
 #pragma unroll
-        for (int db = 0; db < DBW; ++db)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) acc[b][db][i] *= alpha;
+          for (int i = 0; i < NACC; ++i) acc[b][db][i] *= alpha;
         l_part[b] *= alpha;
         m_ref[b] = m_new;
         rs[b] = probs(sf[b], p_cur[b], m_ref[b], c_q[b]);
@@ -1019,13 +1021,6 @@ fa2_fwd_kernel(const Problem P) {
 #pragma unroll
     for (int b = 0; b < QB; ++b) l_part[b] += rs[b];
 
-    // DS = 2: once every wave has read this tile's partial logits (this
-    // barrier), the slot takes the next tile's, published by the barrier
-    // below.
-    if constexpr (DS > 1) {
-      __syncthreads();
-      write_partial(s_nxt);
-    }
     // The loads issued during iteration j-1 have landed.  (PERSIST: the first
     // iteration's query loads may stay in flight too.)
     if constexpr (kSyncCheck)
@@ -1056,7 +1051,7 @@ fa2_fwd_kernel(const Problem P) {
 #pragma unroll
     for (int b = 0; b < QB; ++b)
 #pragma unroll
-      for (int ks = 0; ks < KSW; ++ks) asm volatile("" ::"v"(qf[b][ks]));
+      for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[b][ks]));
     wait_vmem();
     __syncthreads();
 
@@ -1065,7 +1060,6 @@ fa2_fwd_kernel(const Problem P) {
     prefetch_k(0, Ic<0>{}, kpre);
     gemm1(0, Ic<0>{}, kpre, sA);
     prefetch_k(1, Ic<1>{}, kpre);
-    write_partial(sA);  // DS = 2: this wave's half of S_0 for its partner
     __syncthreads();  // every wave is done with K_0 before K_RING may overwrite it
   }
 
@@ -1158,19 +1152,19 @@ fa2_fwd_kernel(const Problem P) {
   // held in registers through the loop.
   int el = lane;
   if constexpr (PERSIST) asm volatile("" : "+v"(el));
-  const int el32 = el & 31, ehalf = el >> 5;
-  lds_char* const ow = lds + QOBASE + wave * (32 * QB) * OROW;  // this wave's rows
+  const int elq = el & (MS - 1), elg = el / MS;
+  lds_char* const ow = lds + QOBASE + wave * (MS * QB) * OROW;  // this wave's rows
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
-    const int qrow = q0 + 32 * b + el32;
-    const float l_tot = l_part[b] + __shfl_xor(l_part[b], 32);
+    const int qrow = q0 + MS * b + elq;
+    const float l_tot = row_sum(l_part[b]);
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
 #pragma unroll
-    for (int db = 0; db < DBW; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        // the wave's output channels ch .. ch+3 (of its DW columns)
-        const int ch = db * 32 + g4 * 8 + ehalf * 4;
+      for (int g4 = 0; g4 < NACC / 4; ++g4) {
+        // output channels ch .. ch+3
+        const int ch = db * MS + g4 * 8 + elg * 4;
         float vsc[4] = {1.0f, 1.0f, 1.0f, 1.0f};
         if constexpr (Q8) {  // the per-channel value scales of the INT8 cache
           const float4 f = *(const float4*)(P.vs + (int64_t)bh * D + ch);
@@ -1180,18 +1174,18 @@ fa2_fwd_kernel(const Problem P) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           ov[e] = (E)(Q8 ? acc[b][db][g4 * 4 + e] * vsc[e] * inv : acc[b][db][g4 * 4 + e] * inv);
-        *(__attribute__((address_space(3))) u32x2*)(ow + (32 * b + el32) * OROW + ch * 2) =
+        *(__attribute__((address_space(3))) u32x2*)(ow + (MS * b + elq) * OROW + ch * 2) =
             __builtin_bit_cast(u32x2, ov);
       }
-    if (ehalf == 0 && dpart == 0 && qrow < P.rows)
+    if (elg == 0 && qrow < P.rows)
       P.lse[(int64_t)bh * P.rows + qrow] =
           l_tot > 0.0f ? (m_ref[b] + __log2f(l_tot)) * kLn2 : -INFINITY;
   }
   // The wave reads back only its own rows (LDS operations of one wave are
-  // ordered): DW/8 lanes per row, 16 bytes each, so a store covers 64 / (DW/8)
-  // whole rows (of the wave's DW columns).
-  constexpr int CPO = DW / 8;                        // 16-byte pieces per O row
-  constexpr int OPIECES = 32 * QB * CPO;             // pieces per wave
+  // ordered): D/8 lanes per row, 16 bytes each, so a store covers 64 / (D/8)
+  // whole rows.
+  constexpr int CPO = D / 8;                         // 16-byte pieces per O row
+  constexpr int OPIECES = MS * QB * CPO;             // pieces per wave
   static_assert(OPIECES % 64 == 0, "whole stores per wave");
 #pragma unroll
   for (int s = 0; s < OPIECES / 64; ++s) {
@@ -1199,7 +1193,7 @@ fa2_fwd_kernel(const Problem P) {
     const int r = lin / CPO, pc = lin % CPO;
     const u32x4 piece = *(const __attribute__((address_space(3))) u32x4*)(ow + r * OROW + pc * 16);
     if (q0 + r < P.rows)
-      *(u32x4*)(P.o + q_head + (int64_t)(q0 + r) * D + dpart * DW + pc * 8) = piece;
+      *(u32x4*)(P.o + q_head + (int64_t)(q0 + r) * D + pc * 8) = piece;
   }
   if constexpr (!PERSIST) {
     break;
@@ -1210,7 +1204,7 @@ fa2_fwd_kernel(const Problem P) {
     bh = bh_nx;
     qt = qt_nx;
     q_head = (int64_t)bh * P.rows * D;
-    q0 = qt * BR + wq * 32 * QB;
+    q0 = qt * BR + wave * MS * QB;
     item_limits();
     k_rs = rebase(k_rs, nx_delta);
     v_rs = rebase(v_rs, nx_delta);
@@ -1218,9 +1212,9 @@ fa2_fwd_kernel(const Problem P) {
 #pragma unroll
     for (int b = 0; b < QB; ++b) {
 #pragma unroll
-      for (int db = 0; db < DBW; ++db)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[b][db][i] = 0.0f;
+        for (int i = 0; i < NACC; ++i) acc[b][db][i] = 0.0f;
       m_ref[b] = -INFINITY;
       l_part[b] = 0.0f;
     }
@@ -1294,9 +1288,9 @@ int fa2_tile_config(int64_t d, int dtype, int* block_q, int* block_k, int* waves
   if (!block_q || !block_k || !waves) return FA2_ERR_NULL;
   if (dtype != FA2_BF16 && dtype != FA2_FP16) return FA2_ERR_DTYPE;
   switch (d) {
-    case 64: *block_q = fa2::Cfg<64>::NW * 32 * fa2::Cfg<64>::QB / fa2::Cfg<64>::DS; *block_k = fa2::Cfg<64>::BC; *waves = fa2::Cfg<64>::NW; break;
-    case 128: *block_q = fa2::Cfg<128>::NW * 32 * fa2::Cfg<128>::QB / fa2::Cfg<128>::DS; *block_k = fa2::Cfg<128>::BC; *waves = fa2::Cfg<128>::NW; break;
-    case 256: *block_q = fa2::Cfg<256>::NW * 32 * fa2::Cfg<256>::QB / fa2::Cfg<256>::DS; *block_k = fa2::Cfg<256>::BC; *waves = fa2::Cfg<256>::NW; break;
+    case 64: *block_q = fa2::Cfg<64>::NW * fa2::Cfg<64>::MS * fa2::Cfg<64>::QB; *block_k = fa2::Cfg<64>::BC; *waves = fa2::Cfg<64>::NW; break;
+    case 128: *block_q = fa2::Cfg<128>::NW * fa2::Cfg<128>::MS * fa2::Cfg<128>::QB; *block_k = fa2::Cfg<128>::BC; *waves = fa2::Cfg<128>::NW; break;
+    case 256: *block_q = fa2::Cfg<256>::NW * fa2::Cfg<256>::MS * fa2::Cfg<256>::QB; *block_k = fa2::Cfg<256>::BC; *waves = fa2::Cfg<256>::NW; break;
     default: return FA2_ERR_HEADDIM;
   }
   return FA2_OK;

@@ -173,8 +173,8 @@ const char* fa2_strerror(int status);
  * would be fewer than the compute units.  Persistent workgroups (one per
  * compute unit, each walking several query tiles) hold 256 query rows with 8
  * waves at d = 64 (non-causal) and d = 128 (also causal, tiles taken in
- * pairs of equal total cost).  At d = 256 two waves share each 32 query
- * rows, each with half of the head dimension.  block_q here is always a
+ * pairs of equal total cost).  At d = 256 each wave holds 16 query rows
+ * (16x16x32 matrix instructions), elsewhere 32.  block_q here is always a
  * multiple of the smaller shapes and divides the larger.
  * Host-only, no HIP call.  Returns FA2_OK, FA2_ERR_HEADDIM, FA2_ERR_DTYPE or
  * FA2_ERR_NULL.

@@ -60,8 +60,8 @@ def test_strerror_covers_every_status(lib):
 def test_tile_config(lib):
     for d in (64, 128, 256):
         bq, bk, nw = fa2.tile_config(d, fa2.BF16)
-        # 32 query rows per wave; at d = 256 two waves share each 32 rows
-        assert bq == 32 * nw // (2 if d == 256 else 1) and bk % 32 == 0 and nw >= 1
+        # 32 query rows per wave (16 on 16x16x32 MFMA at d = 256)
+        assert bq == (16 if d == 256 else 32) * nw and bk % 32 == 0 and nw >= 1
     with pytest.raises(fa2.FA2Error) as e:
         fa2.tile_config(96)
     assert e.value.code == fa2.ERR_HEADDIM

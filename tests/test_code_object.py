@@ -84,16 +84,15 @@ def test_lds_fits_a_workgroup(kernels):
 
 def test_two_waves_per_simd(kernels):
     """Every kernel fits two waves per SIMD (at most 256 registers, no
-    spills); d = 256 gets there by splitting the head dimension between the
-    two waves of a query block."""
+    spills); d = 256 gets there with 16-query waves on 16x16x32 MFMA."""
     for k, r in kernels.items():
         assert r["vgpr"] + r["agpr"] <= 256 and r["vgpr_spill"] == 0 and r["scratch"] == 0, (k, r)
 
 
-def test_head_dim_256_uses_the_whole_lds(kernels):
-    """d = 256: four-slot K and V rings of 32-key tiles (128 KiB) and the
-    exchange slots of the two halves of each wave pair's logits (8 waves x
-    4 KiB) fill the 160 KiB a workgroup may use."""
+def test_head_dim_256_lds_is_the_two_rings(kernels):
+    """d = 256: four-slot K and V rings of 32-key tiles (128 KiB) and nothing
+    else (the output is staged in the rings after the loop), so one
+    workgroup of 8 waves runs per CU."""
     for k, r in kernels.items():
         if k[0] == 256:
-            assert r["lds"] == 4 * 2 * 32 * 256 * 2 + 8 * 64 * 64 == LDS_LIMIT, (k, r)
+            assert r["lds"] == 4 * 2 * 32 * 256 * 2 == 128 * 1024, (k, r)
