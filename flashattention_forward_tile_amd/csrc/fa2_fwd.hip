@@ -612,6 +612,9 @@ fa2_fwd_kernel(const Problem P) {
     }
     n_cur = n_tiles;
   };
+  // Causal: whether any row of this wave sees a key of tile t (always true
+  // without the mask).
+  auto sees = [&](int t) -> bool { return !CAUSAL || t <= wave_last; };
   item_limits();
   // c_q: the lane's logit multiplier (scale * log2 e, times the query row
   // scale with Q8).
@@ -949,12 +952,15 @@ fa2_fwd_kernel(const Problem P) {
     // its query tile (landed by the end of iteration 1).
     if constexpr ((TL & 4) != 0) load_qf();
     // Causal, past the diagonal: a wave whose rows see no key of tile j+1
-    // skips S_{j+1}.  The stale registers it leaves are never used: the next
-    // iteration masks every key of that tile for this wave (to -inf, so P is
-    // 0 and adds nothing to O), as it would the computed logits.
-    if (!(CAUSAL && (TL & 8) == 0) || (TL & 4) != 0 || j + 1 <= wave_last)
-      gemm1(j + 1, S1{}, kpre, s_nxt);
-    if constexpr (!decltype(first)::value) gemm2(j - 1, S3{}, vpre, p_prev);
+    // skips S_{j+1}, and one whose rows saw no key of tile j-1 skips its P V
+    // product (P is 0), leaving the MFMA pipe of its SIMD to the other wave.
+    // The stale S registers are never used: the next iteration masks every
+    // key of that tile for this wave (to -inf, so P is 0), as it would the
+    // computed logits.
+    if ((TL & 8) != 0 || (TL & 4) != 0 || sees(j + 1)) gemm1(j + 1, S1{}, kpre, s_nxt);
+    if constexpr (!decltype(first)::value) {
+      if ((TL & 8) != 0 || sees(j - 1)) gemm2(j - 1, S3{}, vpre, p_prev);
+    }
     float rs[QB];
     bool over = false;
 #pragma unroll
@@ -1098,7 +1104,7 @@ fa2_fwd_kernel(const Problem P) {
       step(std::false_type{}, Ic<1>{}, j + 4, sB, sA, pA, pB, Ic<1 | NM>{});
       step(std::false_type{}, Ic<2>{}, j + 5, sA, sB, pB, pA, Ic<3 | NM>{});
       step(std::false_type{}, Ic<3>{}, j + 6, sB, sA, pA, pB, Ic<7>{});
-      gemm2(j + 6, Ic<3>{}, vpre, pB);
+      if (sees(j + 6)) gemm2(j + 6, Ic<3>{}, vpre, pB);
     } else {
       // First the tiles no wave masks, then the rest with the per-wave check.
       for (; j + 3 < n_clear; j += 4) {
@@ -1120,15 +1126,15 @@ fa2_fwd_kernel(const Problem P) {
           step(std::false_type{}, Ic<2>{}, j + 1, sA, sB, pB, pA, Ic<0>{});
           if (j + 2 < n_tiles) {
             step(std::false_type{}, Ic<3>{}, j + 2, sB, sA, pA, pB, Ic<0>{});
-            gemm2(j + 2, Ic<3>{}, vpre, pB);
+            if (sees(j + 2)) gemm2(j + 2, Ic<3>{}, vpre, pB);
           } else {
-            gemm2(j + 1, Ic<2>{}, vpre, pA);
+            if (sees(j + 1)) gemm2(j + 1, Ic<2>{}, vpre, pA);
           }
         } else {
-          gemm2(j, Ic<1>{}, vpre, pB);
+          if (sees(j)) gemm2(j, Ic<1>{}, vpre, pB);
         }
       } else {
-        gemm2(j - 1, Ic<0>{}, vpre, pA);
+        if (sees(j - 1)) gemm2(j - 1, Ic<0>{}, vpre, pA);
       }
     }
   }
