@@ -118,6 +118,16 @@ __device__ __forceinline__ int v_swizzle(int row, int chunk) {
     return chunk ^ (((row >> 1) & 1) << 2);
 }
 
+// x of lane l ^ 32: v_permlane32_swap exchanges lanes 32..63 of its first
+// operand with lanes 0..31 of its second; with x in both, the second result
+// holds the upper half's values in the lower lanes and the first the lower
+// half's values in the upper lanes.
+__device__ __forceinline__ float other_half(float x, int lane) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (lane & 32) ? r[0] : r[1]);
+}
+
 // s_waitcnt with only vmcnt(0): every buffer load of this wave, including
 // the ones that write LDS directly, has landed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -660,7 +670,7 @@ fa2_fwd_kernel(const Problem P) {
           }
         }
       }
-      amax = fmaxf(amax, __shfl_xor(amax, 32));
+      amax = fmaxf(amax, other_half(amax, lane));
       const bool nonzero = amax > 0.0f;
       const float inv = nonzero ? __fdiv_rn(127.0f, amax) : 0.0f;
       const float sq = nonzero ? __fdiv_rn(amax, 127.0f) : 0.0f;
@@ -829,14 +839,15 @@ fa2_fwd_kernel(const Problem P) {
     }
   };
 
-  // Reductions over the lanes that hold one query row.
+  // Reductions over the lanes that hold one query row; the exchange of the
+  // two 32-lane halves is one v_permlane32_swap (no LDS round trip).
   auto row_max = [&](float x) -> float {
     if constexpr (MS == 16) x = fmaxf(x, __shfl_xor(x, 16));
-    return fmaxf(x, __shfl_xor(x, 32));
+    return fmaxf(x, other_half(x, lane));
   };
   auto row_sum = [&](float x) -> float {
     if constexpr (MS == 16) x += __shfl_xor(x, 16);
-    return x + __shfl_xor(x, 32);
+    return x + other_half(x, lane);
   };
 
   // P_t^T as the B operands of the second product.  MS = 32: k-step st
@@ -1334,8 +1345,8 @@ int launch(const void* q, const void* k, const void* v, const float* ks, const f
   // take (the smallest, 128 query rows, gives the most workgroups).
   int bq = 0, bk = 0, nw = 0;
   fa2_tile_config(d, dtype, &bq, &bk, &nw);
-  const int64_t bq_min = q8 ? Cfg8<128>::NW * 32 * Cfg8<128>::QB
-                       : d == 128 ? CfgS<128>::NW * 32 * CfgS<128>::QB : bq;
+  const int64_t bq_min = q8 ? Cfg8<128>::NW * Cfg8<128>::MS * Cfg8<128>::QB
+                       : d == 128 ? CfgS<128>::NW * CfgS<128>::MS * CfgS<128>::QB : bq;
   if (B * Hkv > (((int64_t)1 << 31) - 1) / ((rows + bq_min - 1) / bq_min)) return FA2_ERR_SHAPE;
   if (!q || !o || !lse || (Nk > 0 && (!k || !v))) return FA2_ERR_NULL;
   if (q8 && (!ks || !vs)) return FA2_ERR_NULL;
@@ -1368,7 +1379,7 @@ int launch(const void* q, const void* k, const void* v, const float* ks, const f
   bool persist = false;
   int cus = 0;
   if (!q8 && d == 64 && !causal) {
-    constexpr int64_t BRP = CfgP<64>::NW * 32 * CfgP<64>::QB;
+    constexpr int64_t BRP = CfgP<64>::NW * CfgP<64>::MS * CfgP<64>::QB;
     const int64_t items_p = B * Hkv * ((rows + BRP - 1) / BRP);
     const int64_t k_tiles = (Nk + CfgP<64>::BC - 1) / CfgP<64>::BC;
     if (k_tiles >= 8 && k_tiles % CfgP<64>::RING == 0 && items_p % 8 == 0) {
@@ -1377,7 +1388,7 @@ int launch(const void* q, const void* k, const void* v, const float* ks, const f
     }
   }
   if (!q8 && d == 128) {
-    constexpr int64_t BR128 = Cfg<128>::NW * 32 * Cfg<128>::QB;
+    constexpr int64_t BR128 = Cfg<128>::NW * Cfg<128>::MS * Cfg<128>::QB;
     const int64_t k_tiles = (Nk + Cfg<128>::BC - 1) / Cfg<128>::BC;
     const bool shape_ok =
         !causal ? (k_tiles >= 8 && k_tiles % Cfg<128>::RING == 0 && items_full % 8 == 0)
@@ -1397,13 +1408,13 @@ int launch(const void* q, const void* k, const void* v, const float* ks, const f
     short_keys = n_cu > 0 && items_full < n_cu;
   }
   if (q8) {
-    bq = Cfg8<128>::NW * 32 * Cfg8<128>::QB;
+    bq = Cfg8<128>::NW * Cfg8<128>::MS * Cfg8<128>::QB;
     nw = Cfg8<128>::NW;
   } else if (persist && d == 64) {
-    bq = CfgP<64>::NW * 32 * CfgP<64>::QB;
+    bq = CfgP<64>::NW * CfgP<64>::MS * CfgP<64>::QB;
     nw = CfgP<64>::NW;
   } else if (short_keys) {
-    bq = CfgS<128>::NW * 32 * CfgS<128>::QB;
+    bq = CfgS<128>::NW * CfgS<128>::MS * CfgS<128>::QB;
     nw = CfgS<128>::NW;
   }
   const int64_t q_tiles = (rows + bq - 1) / bq;
