@@ -1200,7 +1200,8 @@ fa2_fwd_kernel(const Problem P) {
   }
   // The wave reads back only its own rows (LDS operations of one wave are
   // ordered): D/8 lanes per row, 16 bytes each, so a store covers 64 / (D/8)
-  // whole rows.
+  // whole rows.  O is written once and not read again here: the stores carry
+  // the non-temporal hint.
   constexpr int CPO = D / 8;                         // 16-byte pieces per O row
   constexpr int OPIECES = MS * QB * CPO;             // pieces per wave
   static_assert(OPIECES % 64 == 0, "whole stores per wave");
@@ -1210,7 +1211,7 @@ fa2_fwd_kernel(const Problem P) {
     const int r = lin / CPO, pc = lin % CPO;
     const u32x4 piece = *(const __attribute__((address_space(3))) u32x4*)(ow + r * OROW + pc * 16);
     if (q0 + r < P.rows)
-      *(u32x4*)(P.o + q_head + (int64_t)(q0 + r) * D + pc * 8) = piece;
+      __builtin_nontemporal_store(piece, (u32x4*)(P.o + q_head + (int64_t)(q0 + r) * D + pc * 8));
   }
   if constexpr (!PERSIST) {
     break;
