@@ -22,6 +22,10 @@ oracle sees bit for bit what the GPU sees.
 codes with fp32 per-channel scales; the query rows quantized to int8 after the
 key scales are folded in, every quantization step in binary32 as spelled out in
 ``attn_ref.c``), and ``quantize_q`` exposes that query quantization alone.
+``attention_kv_fp8`` and ``quantize_q_fp8`` do the same for an FP8 cache whose
+codes are OCP E4M3 values (the query rows rounded to E4M3, ties to even, after
+scaling their largest magnitude to 448); ``e4m3_decode`` and ``e4m3_round``
+expose the code conversions.
 """
 import ctypes
 import os
@@ -74,6 +78,20 @@ class Oracle:
         lib.oracle_quantize_q.argtypes = [u16p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
                                           f32p, i8p, f32p]
         lib.oracle_quantize_q.restype = ctypes.c_int
+        u8p = ctypes.POINTER(ctypes.c_uint8)
+        lib.oracle_attn_kv_fp8.argtypes = [
+            u16p, ctypes.c_int, u8p, f32p, u8p, f32p,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_double, ctypes.c_int,
+            i64p, ctypes.c_int64, f64p, f64p, ctypes.c_int]
+        lib.oracle_attn_kv_fp8.restype = ctypes.c_int
+        lib.oracle_quantize_q_fp8.argtypes = [u16p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                              f32p, u8p, f32p]
+        lib.oracle_quantize_q_fp8.restype = ctypes.c_int
+        lib.oracle_e4m3_decode.argtypes = [u8p, ctypes.c_int64, f64p]
+        lib.oracle_e4m3_decode.restype = ctypes.c_int
+        lib.oracle_e4m3_round.argtypes = [f32p, ctypes.c_int64, u8p]
+        lib.oracle_e4m3_round.restype = ctypes.c_int
         lib.oracle_decode.argtypes = [u16p, ctypes.c_int64, ctypes.c_int, f64p]
         lib.oracle_decode.restype = ctypes.c_int
         lib.oracle_host_threads.argtypes = []
@@ -178,6 +196,71 @@ class Oracle:
             raise ValueError("oracle_quantize_q failed (%d)" % rc)
         return codes, sq
 
+    def attention_kv_fp8(self, q_bits, kf, ks, vf, vs, dtype, scale, rows=None,
+                         nthreads=0, causal=False):
+        """fp64 attention over an FP8 (OCP E4M3) key/value cache.
+
+        As `attention_kv_int8` with kf, vf uint8 [B, Hkv, Nk, d] E4M3 codes
+        (k = ks * e4m3(kf), v = vs * e4m3(vf)) and the query rows rounded to
+        E4M3 (see the module docstring).
+        """
+        q = np.ascontiguousarray(q_bits, dtype=np.uint16)
+        kf = np.ascontiguousarray(kf, dtype=np.uint8)
+        vf = np.ascontiguousarray(vf, dtype=np.uint8)
+        ks = np.ascontiguousarray(ks, dtype=np.float32)
+        vs = np.ascontiguousarray(vs, dtype=np.float32)
+        if q.ndim != 4 or kf.ndim != 4 or kf.shape != vf.shape:
+            raise ValueError("q must be [B, Hq, Nq, d], kf and vf one [B, Hkv, Nk, d] shape")
+        B, Hq, Nq, d = q.shape
+        Hkv, Nk = kf.shape[1], kf.shape[2]
+        if kf.shape[0] != B or kf.shape[3] != d or Hkv < 1 or Hq % Hkv:
+            raise ValueError("kf/vf batch and head dim must match q, Hq a multiple of Hkv")
+        if ks.shape != (B, Hkv, d) or vs.shape != (B, Hkv, d):
+            raise ValueError("ks and vs must be [B, Hkv, d]")
+
+        def run(rp, nr, o, lse):
+            return self.lib.oracle_attn_kv_fp8(
+                _ptr(q, ctypes.c_uint16), _DTYPES[dtype], _ptr(kf, ctypes.c_uint8),
+                _ptr(ks, ctypes.c_float), _ptr(vf, ctypes.c_uint8), _ptr(vs, ctypes.c_float),
+                B, Hq, Hkv, Nq, Nk, d, float(scale), 1 if causal else 0, rp, nr,
+                _ptr(o, ctypes.c_double), _ptr(lse, ctypes.c_double), int(nthreads))
+        return self._rows_call(q.shape, rows, run, "oracle_attn_kv_fp8")
+
+    def quantize_q_fp8(self, q_bits, ks, dtype):
+        """E4M3 codes and row scales of query rows (the FP8 scheme): as
+        `quantize_q`, codes uint8 [..., d]."""
+        q = np.ascontiguousarray(q_bits, dtype=np.uint16)
+        ks = np.ascontiguousarray(ks, dtype=np.float32).ravel()
+        d = q.shape[-1]
+        if ks.size != d:
+            raise ValueError("ks must hold d scales")
+        n = q.size // d
+        codes = np.empty(q.shape, dtype=np.uint8)
+        sq = np.empty(q.shape[:-1], dtype=np.float32)
+        rc = self.lib.oracle_quantize_q_fp8(_ptr(q, ctypes.c_uint16), _DTYPES[dtype], n, d,
+                                            _ptr(ks, ctypes.c_float), _ptr(codes, ctypes.c_uint8),
+                                            _ptr(sq, ctypes.c_float))
+        if rc != 0:
+            raise ValueError("oracle_quantize_q_fp8 failed (%d)" % rc)
+        return codes, sq
+
+    def e4m3_decode(self, codes) -> np.ndarray:
+        """Exact fp64 value of each OCP E4M3 code (uint8)."""
+        codes = np.ascontiguousarray(codes, dtype=np.uint8)
+        out = np.empty(codes.shape, dtype=np.float64)
+        self.lib.oracle_e4m3_decode(_ptr(codes, ctypes.c_uint8), codes.size,
+                                    _ptr(out, ctypes.c_double))
+        return out
+
+    def e4m3_round(self, x) -> np.ndarray:
+        """The E4M3 code nearest to each float32 (ties to even, saturating)."""
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        codes = np.empty(x.shape, dtype=np.uint8)
+        rc = self.lib.oracle_e4m3_round(_ptr(x, ctypes.c_float), x.size, _ptr(codes, ctypes.c_uint8))
+        if rc != 0:
+            raise ValueError("e4m3_round: NaN input")
+        return codes
+
     @staticmethod
     def _rows_call(qshape, rows, run, name):
         """Run `run(rows_ptr, nrows, o, lse)` over every row (O shaped [B, Hq,
@@ -246,3 +329,25 @@ def attention_kv_int8(q_bits, kq, ks, vq, vs, dtype, scale, rows=None, nthreads=
 def quantize_q(q_bits, ks, dtype):
     """See Oracle.quantize_q."""
     return default().quantize_q(q_bits, ks, dtype)
+
+
+def attention_kv_fp8(q_bits, kf, ks, vf, vs, dtype, scale, rows=None, nthreads=0,
+                     causal=False):
+    """See Oracle.attention_kv_fp8."""
+    return default().attention_kv_fp8(q_bits, kf, ks, vf, vs, dtype, scale, rows,
+                                      nthreads, causal)
+
+
+def quantize_q_fp8(q_bits, ks, dtype):
+    """See Oracle.quantize_q_fp8."""
+    return default().quantize_q_fp8(q_bits, ks, dtype)
+
+
+def e4m3_decode(codes):
+    """See Oracle.e4m3_decode."""
+    return default().e4m3_decode(codes)
+
+
+def e4m3_round(x):
+    """See Oracle.e4m3_round."""
+    return default().e4m3_round(x)

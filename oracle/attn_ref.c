@@ -50,6 +50,21 @@
  * The logits are s_j = scale * sq * sum_c qq[c] * kq[j][c] (an exact integer
  * dot product), and the softmax, O and lse follow the definition above with
  * the dequantized v.
+ *
+ * FP8 key/value cache.  The same scheme with 8-bit floating-point codes in
+ * place of the integers (the second reading of the same title: gfx950 also
+ * multiplies FP8 matrices): every code is an OCP FP8 E4M3 value (1 sign bit,
+ * 4 exponent bits with bias 7, 3 mantissa bits; exponent field 0 holds the
+ * subnormals m * 2^-9; 0x7F and 0xFF are NaN; the largest finite magnitude is
+ * 448), and
+ *     k[j][c] = ks[c] * e4m3(kq[j][c]),   v[j][c] = vs[c] * e4m3(vq[j][c]),
+ *     qq[c] = amax > 0 ? e4m3_rne(f32(u[c] * f32(448 / amax))) : 0,
+ *     sq    = f32(amax / 448),
+ * where e4m3_rne rounds to the nearest E4M3 value, ties to the code with an
+ * even last mantissa bit (the sign kept, magnitudes above 448 saturating to
+ * 448; the query codes never exceed 448 by more than binary32 rounding).
+ * The logits are s_j = scale * sq * sum_c qq[c] * e4m3(kq[j][c]), computed
+ * here exactly in fp64.
  */
 #define _GNU_SOURCE
 #include <math.h>
@@ -92,6 +107,83 @@ int oracle_decode(const uint16_t* bits, int64_t n, int dtype, double* out) {
   if (dtype != ORACLE_BF16 && dtype != ORACLE_FP16) return -1;
   for (int64_t i = 0; i < n; ++i) out[i] = decode(bits[i], dtype);
   return 0;
+}
+
+/* OCP FP8 E4M3 (see the header): the exact value of a code. */
+static double decode_e4m3(uint8_t code) {
+  const int sign = code >> 7, e = (code >> 3) & 15, m = code & 7;
+  double mag;
+  if (e == 15 && m == 7)
+    mag = NAN;
+  else if (e == 0)
+    mag = ldexp((double)m, -9);          /* subnormal: (m / 8) * 2^-6 */
+  else
+    mag = ldexp((double)(8 + m), e - 10); /* (1 + m / 8) * 2^(e - 7) */
+  return sign ? -mag : mag;
+}
+
+/* The E4M3 code nearest to x (x not NaN): a binary search over the 127
+ * non-negative finite values, which increase with the code; a tie goes to
+ * the even code; magnitudes beyond 448 give 448; the sign of x (also of a
+ * zero) becomes the sign bit. */
+static uint8_t round_e4m3(float x) {
+  const double a = fabs((double)x);
+  int lo = 0, hi = 126; /* decode_e4m3(lo) <= a < decode_e4m3(hi), or a at an end */
+  uint8_t code;
+  if (a >= decode_e4m3(126)) {
+    code = 126;
+  } else {
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) / 2;
+      if (decode_e4m3((uint8_t)mid) <= a)
+        lo = mid;
+      else
+        hi = mid;
+    }
+    const double dl = a - decode_e4m3((uint8_t)lo), dh = decode_e4m3((uint8_t)hi) - a;
+    code = (uint8_t)(dl < dh ? lo : dh < dl ? hi : ((lo & 1) == 0 ? lo : hi));
+  }
+  return signbit(x) ? (uint8_t)(code | 0x80) : code;
+}
+
+int oracle_e4m3_decode(const uint8_t* codes, int64_t n, double* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = decode_e4m3(codes[i]);
+  return 0;
+}
+
+int oracle_e4m3_round(const float* x, int64_t n, uint8_t* codes) {
+  for (int64_t i = 0; i < n; ++i) {
+    if (isnan(x[i])) return -1;
+    codes[i] = round_e4m3(x[i]);
+  }
+  return 0;
+}
+
+/* The FP8 scheme's query quantization for one row (see the header): every
+ * operation in binary32 up to the rounding to E4M3.  Writes the codes to
+ * code_out (when not NULL) and their values to qq; returns sq. */
+static float quantize_q_row_fp8(const double* q, const float* ks, int64_t d, double* qq,
+                                uint8_t* code_out) {
+  float top = 0.0f; /* largest |q * ks| of the row */
+  for (int64_t c = 0; c < d; ++c) {
+    const float uk = (float)q[c] * ks[c];
+    top = fmaxf(top, fabsf(uk));
+  }
+  if (!(top > 0.0f)) {
+    for (int64_t c = 0; c < d; ++c) {
+      qq[c] = 0.0;
+      if (code_out) code_out[c] = 0;
+    }
+    return 0.0f;
+  }
+  const float to448 = 448.0f / top;
+  for (int64_t c = 0; c < d; ++c) {
+    const float uk = (float)q[c] * ks[c];
+    const uint8_t code = round_e4m3(uk * to448);
+    qq[c] = decode_e4m3(code);
+    if (code_out) code_out[c] = code;
+  }
+  return top / 448.0f;
 }
 
 /* The INT8 scheme's query quantization for one row (see the header): every
@@ -142,11 +234,32 @@ int oracle_quantize_q(const uint16_t* q, int dtype, int64_t n, int64_t d, const 
   return 0;
 }
 
+/* The FP8 scheme's query codes and row scales, as oracle_quantize_q. */
+int oracle_quantize_q_fp8(const uint16_t* q, int dtype, int64_t n, int64_t d, const float* ks,
+                          uint8_t* qq, float* sq) {
+  if ((dtype != ORACLE_BF16 && dtype != ORACLE_FP16) || n < 0 || d <= 0) return -1;
+  double* row = (double*)malloc(sizeof(double) * (size_t)d);
+  double* vals = (double*)malloc(sizeof(double) * (size_t)d);
+  if (!row || !vals) {
+    free(row);
+    free(vals);
+    return -1;
+  }
+  for (int64_t i = 0; i < n; ++i) {
+    for (int64_t c = 0; c < d; ++c) row[c] = decode(q[i * d + c], dtype);
+    sq[i] = quantize_q_row_fp8(row, ks, d, vals, qq + i * d);
+  }
+  free(row);
+  free(vals);
+  return 0;
+}
+
 /* ------------------------------------------------------------------------ */
 
 typedef struct {
   const uint16_t *q, *k, *v;
   const int8_t *kq, *vq;   /* INT8 cache codes (k, v unused then) */
+  const uint8_t *kf, *vf;  /* FP8 (E4M3) cache codes (k, v unused then) */
   const float *ks, *vs;    /* their per-channel scales, [B][Hkv][d] */
   int dtype;
   int64_t B, Hq, Hkv, Nq, Nk, d;
@@ -222,7 +335,17 @@ static void* worker(void* arg) {
       int64_t head = flat / Nq, i = flat % Nq;  /* head = b*Hq + h */
       int64_t kv_head = (head / J->Hq) * J->Hkv + (head % J->Hq) / group;
       if (kv_head != loaded_head) {
-        if (J->kq) {
+        if (J->kf) {
+          /* K holds the code values (the scales are folded into the query);
+           * V the dequantized values, each an exact fp64 product */
+          const uint8_t* kh = J->kf + kv_head * Nk * d;
+          const uint8_t* vh = J->vf + kv_head * Nk * d;
+          const float* vs = J->vs + kv_head * d;
+          for (int64_t t = 0; t < Nk * d; ++t) {
+            K[t] = decode_e4m3(kh[t]);
+            V[t] = (double)vs[t % d] * decode_e4m3(vh[t]);
+          }
+        } else if (J->kq) {
           /* K holds the integer codes (the scales are folded into the
            * query); V the dequantized values, each an exact fp64 product */
           const int8_t* kh = J->kq + kv_head * Nk * d;
@@ -252,6 +375,9 @@ static void* worker(void* arg) {
       if (J->kq) {  /* quantized query: codes in q, logits times sq */
         const float sq = quantize_q_row(q, J->ks + kv_head * d, d, q);
         row_scale = J->scale * (double)sq;
+      } else if (J->kf) {  /* the same with E4M3 code values */
+        const float sqf = quantize_q_row_fp8(q, J->ks + kv_head * d, d, q, NULL);
+        row_scale = (double)sqf * J->scale;
       }
       one_row(q, K, V, visible, d, row_scale, s, J->o + r * d, J->lse + r);
     }
@@ -279,7 +405,7 @@ int oracle_host_threads(void) {
  */
 static int run_job(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                    const int8_t* kq, const float* ks, const int8_t* vq, const float* vs,
-                   int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
+                   const uint8_t* kf, const uint8_t* vf, int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
                    int64_t d, double scale, int causal, const int64_t* rows, int64_t nrows,
                    double* o, double* lse, int nthreads) {
   if (dtype != ORACLE_BF16 && dtype != ORACLE_FP16) return -1;
@@ -290,7 +416,11 @@ static int run_job(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   if (nrows < 0 || nrows > total) return -1;
   if (nrows == 0) return 0;
   if (!q || !o || !lse) return -1;
-  if (kq ? (!ks || (Nk > 0 && (!vq || !vs))) : (Nk > 0 && (!k || !v))) return -1;
+  if (kq || kf) {
+    if (!ks || (Nk > 0 && (!(kq ? (const void*)vq : (const void*)vf) || !vs))) return -1;
+  } else if (Nk > 0 && (!k || !v)) {
+    return -1;
+  }
   if (rows) {
     for (int64_t r = 0; r < nrows; ++r) {
       if (rows[r] < 0 || rows[r] >= total) return -1;
@@ -303,6 +433,7 @@ static int run_job(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   memset(&J, 0, sizeof J);
   J.q = q; J.k = k; J.v = v; J.dtype = dtype;
   J.kq = kq; J.ks = ks; J.vq = vq; J.vs = vs;
+  J.kf = kf; J.vf = vf;
   J.B = B; J.Hq = Hq; J.Hkv = Hkv; J.Nq = Nq; J.Nk = Nk; J.d = d;
   J.causal = causal; J.scale = scale;
   J.rows = rows; J.nrows = nrows; J.o = o; J.lse = lse;
@@ -335,8 +466,8 @@ int oracle_attn_general(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         int64_t Nk, int64_t d, double scale, int causal,
                         const int64_t* rows, int64_t nrows, double* o, double* lse,
                         int nthreads) {
-  return run_job(q, k, v, NULL, NULL, NULL, NULL, dtype, B, Hq, Hkv, Nq, Nk, d, scale,
-                 causal, rows, nrows, o, lse, nthreads);
+  return run_job(q, k, v, NULL, NULL, NULL, NULL, NULL, NULL, dtype, B, Hq, Hkv, Nq, Nk, d,
+                 scale, causal, rows, nrows, o, lse, nthreads);
 }
 
 /*
@@ -351,8 +482,22 @@ int oracle_attn_kv_int8(const uint16_t* q, int dtype, const int8_t* kq, const fl
                         int causal, const int64_t* rows, int64_t nrows, double* o,
                         double* lse, int nthreads) {
   if (!kq) return -1;
-  return run_job(q, NULL, NULL, kq, ks, vq, vs, dtype, B, Hq, Hkv, Nq, Nk, d, scale, causal,
-                 rows, nrows, o, lse, nthreads);
+  return run_job(q, NULL, NULL, kq, ks, vq, vs, NULL, NULL, dtype, B, Hq, Hkv, Nq, Nk, d, scale,
+                 causal, rows, nrows, o, lse, nthreads);
+}
+
+/*
+ * Attention over an FP8 (E4M3) key/value cache (the scheme in the header):
+ * kf, vf [B][Hkv][Nk][d] E4M3 codes; everything else as oracle_attn_kv_int8.
+ */
+int oracle_attn_kv_fp8(const uint16_t* q, int dtype, const uint8_t* kf, const float* ks,
+                       const uint8_t* vf, const float* vs, int64_t B, int64_t Hq,
+                       int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, double scale,
+                       int causal, const int64_t* rows, int64_t nrows, double* o,
+                       double* lse, int nthreads) {
+  if (!kf) return -1;
+  return run_job(q, NULL, NULL, NULL, ks, NULL, vs, kf, vf, dtype, B, Hq, Hkv, Nq, Nk, d, scale,
+                 causal, rows, nrows, o, lse, nthreads);
 }
 
 /* The base problem: equal heads and lengths, no mask. */

@@ -578,6 +578,189 @@ def pin_int8_brute_force(orc):
                         assert lse[b, h, i] == -math.inf
 
 
+# --------------------------------------------------------------------------
+# FP8 key/value cache: the same scheme with OCP E4M3 codes (oracle/attn_ref.c).
+
+
+def _golden_value(txt):
+    """'2^-9', '7*2^-9', '-0', 'nan', '1.125' -> float."""
+    if txt == "nan":
+        return math.nan
+    sign = -1.0 if txt.startswith("-") else 1.0
+    body = txt.lstrip("-")
+    val = 1.0
+    for part in body.split("*"):
+        val *= 2.0 ** float(part[2:]) if part.startswith("2^") else float(part)
+    return math.copysign(val, sign)
+
+
+def pin_e4m3_codes_golden(orc):
+    """Hand-derived E4M3 values and roundings (tests/golden/e4m3_codes.json):
+    subnormals, the bias, the largest finite value, NaN, signed zero, ties to
+    even in the normal and subnormal ranges, and saturation."""
+    with open(os.path.join(GOLDEN, "e4m3_codes.json")) as f:
+        g = json.load(f)
+    codes = np.array([int(e["code"], 16) for e in g["decode"]], np.uint8)
+    got = orc.e4m3_decode(codes)
+    for e, v in zip(g["decode"], got):
+        want = _golden_value(e["value"])
+        if math.isnan(want):
+            assert math.isnan(v), e
+        else:
+            assert v == want and math.copysign(1.0, v) == math.copysign(1.0, want), (e, v)
+    xs = np.array([_golden_value(e["x"]) for e in g["round"]], np.float32)
+    got = orc.e4m3_round(xs)
+    for e, c in zip(g["round"], got):
+        assert int(c) == int(e["code"], 16), (e, hex(int(c)))
+
+
+def pin_e4m3_matches_torch(orc):
+    """Every code decodes as torch.float8_e4m3fn does; rounding matches
+    torch's conversion on every value within +-448: random values, every
+    representable value, and every midpoint between neighbours (the ties)."""
+    codes = np.arange(256, dtype=np.uint8)
+    mine = orc.e4m3_decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(np.isnan(mine), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(mine[ok], ref[ok]) and np.array_equal(np.signbit(mine[ok]), np.signbit(ref[ok]))
+    vals = np.unique(ref[ok & (ref >= 0)])
+    mids = (vals[1:] + vals[:-1]) / 2
+    rng = np.random.default_rng(3)
+    rnd = np.clip(rng.standard_normal(20000) * 40, -448, 448)
+    xs = np.concatenate([vals, -vals, mids, -mids, rnd, rnd * 1e-3]).astype(np.float32)
+    assert np.all(np.abs(xs) <= 448)
+    got = orc.e4m3_round(xs)
+    want = torch.from_numpy(xs).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got, want), np.flatnonzero(got != want)[:5]
+
+
+def pin_fp8_query_codes_golden(orc):
+    """Hand-derived E4M3 query codes and row scales
+    (tests/golden/fp8_query_codes.json)."""
+    with open(os.path.join(GOLDEN, "fp8_query_codes.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        q = _t16(c["q"], c["dtype"])
+        codes, sq = orc.quantize_q_fp8(bits(q)[None, :], np.asarray(c["ks"], np.float32), c["dtype"])
+        assert codes[0].tolist() == [int(x, 16) for x in c["codes"]], (c["name"], [hex(x) for x in codes[0]])
+        assert int(sq.view(np.uint32)[0]) == int(c["sq_bits"], 16), (c["name"], hex(sq.view(np.uint32)[0]))
+
+
+def _fp8_cache(B, Hkv, Nk, d, seed, pow2_scales=False):
+    """Random finite E4M3 codes [B, Hkv, Nk, d] (no NaN) and float32 scales."""
+    rng = np.random.default_rng(seed)
+    def codes():
+        c = rng.integers(0, 256, size=(B, Hkv, Nk, d)).astype(np.uint8)
+        return np.where((c & 0x7F) == 0x7F, c ^ 0x01, c).astype(np.uint8)
+    kf, vf = codes(), codes()
+    if pow2_scales:
+        ks = np.exp2(-rng.integers(2, 7, size=(B, Hkv, d))).astype(np.float32)
+        vs = np.exp2(-rng.integers(2, 7, size=(B, Hkv, d))).astype(np.float32)
+    else:
+        ks = rng.uniform(0.005, 0.02, size=(B, Hkv, d)).astype(np.float32)
+        vs = rng.uniform(0.005, 0.02, size=(B, Hkv, d)).astype(np.float32)
+    return kf, ks, vf, vs
+
+
+def _e4m3_torch(codes):
+    return torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).double().numpy()
+
+
+def pin_fp8_reduces_to_dequantized_attention(orc):
+    """A query row whose key-scaled values u = q*ks are E4M3 values with max
+    |u| = 448 quantizes to itself (448/amax = 1, sq = 1), so its logits are
+    exactly those of plain attention on q and the dequantized k = ks*e4m3(kf);
+    with v = vs*e4m3(vf) the whole result must equal the 16-bit oracle on
+    those values.  Power-of-two scales keep every value exact in 16 bits."""
+    rng = np.random.default_rng(9)
+    for dtype in DTYPES:
+        for causal in (False, True):
+            B, Hq, Hkv, Nq, Nk, d = 2, 4, 2, 5, 7, 16
+            kf, ks, vf, vs = _fp8_cache(B, Hkv, Nk, d, seed=13, pow2_scales=True)
+            # query values: E4M3 values of at most 2^-2 .. 448 in magnitude (exact in fp16 after /ks)
+            qc = rng.integers(0x10, 0x7F, size=(B, Hq, Nq, d)).astype(np.uint8) | \
+                (rng.integers(0, 2, size=(B, Hq, Nq, d)).astype(np.uint8) << 7)
+            u = _e4m3_torch(qc)
+            u[..., 5] = np.where(rng.random((B, Hq, Nq)) < 0.5, 448.0, -448.0)
+            group = Hq // Hkv
+            ks_q = np.repeat(ks, group, axis=1)[:, :, None, :].astype(np.float64)
+            q = _t16(u / ks_q, dtype)
+            kd = _t16(ks[:, :, None, :].astype(np.float64) * _e4m3_torch(kf), dtype)
+            vd = _t16(vs[:, :, None, :].astype(np.float64) * _e4m3_torch(vf), dtype)
+            o8, l8 = orc.attention_kv_fp8(bits(q), kf, ks, vf, vs, dtype, 0.01, causal=causal)
+            o, lse = _run(orc, q, kd, vd, dtype, 0.01, causal=causal)
+            np.testing.assert_allclose(o8, o, rtol=1e-13, atol=1e-13)
+            np.testing.assert_allclose(l8, lse, rtol=1e-13, atol=0)
+
+
+def pin_fp8_zero_query_is_uniform(orc):
+    """A zero query row has codes 0 and sq = 0: O is the mean of the
+    dequantized values the row sees and lse = ln(keys seen)."""
+    B, Hq, Hkv, Nq, Nk, d = 1, 2, 1, 3, 6, 8
+    kf, ks, vf, vs = _fp8_cache(B, Hkv, Nk, d, seed=6)
+    q = _t16(np.zeros((B, Hq, Nq, d)), "bf16")
+    for causal in (False, True):
+        o, lse = orc.attention_kv_fp8(bits(q), kf, ks, vf, vs, "bf16", 0.3, causal=causal)
+        vdq = vs[:, :, None, :].astype(np.float64) * _e4m3_torch(vf)
+        for i in range(Nq):
+            n = _visible(i, Nq, Nk) if causal else Nk
+            want = vdq[0, 0, :n].mean(axis=0)
+            np.testing.assert_allclose(o[0, :, i], np.broadcast_to(want, (Hq, d)), rtol=1e-12, atol=1e-15)
+            np.testing.assert_allclose(lse[0, :, i], math.log(n), rtol=1e-14)
+
+
+def _fp8_brute_row(q16, ksh, kfh, vsh, vfh, n, scale):
+    """The scheme term by term: numpy binary32 for the query scaling, torch's
+    float8_e4m3fn conversion for its rounding, exact Fractions for the code
+    dot products, math.exp / math.fsum after."""
+    u = (q16.astype(np.float32) * ksh).astype(np.float32)
+    amax = np.float32(np.max(np.abs(u)))
+    d = u.size
+    if amax > 0:
+        to448 = np.float32(np.float32(448.0) / amax)
+        t = (u * to448).astype(np.float32)
+        qv = torch.from_numpy(t).to(torch.float8_e4m3fn).double().numpy()
+        sq = float(np.float32(amax / np.float32(448.0)))
+    else:
+        qv = np.zeros(d)
+        sq = 0.0
+    if n == 0:
+        return [0.0] * d, -math.inf
+    kv = _e4m3_torch(kfh)
+    s = [scale * sq * float(sum(Fraction(qv[c]) * Fraction(kv[j, c]) for c in range(d))) for j in range(n)]
+    m = max(s)
+    w = [math.exp(x - m) for x in s]
+    l = math.fsum(w)
+    vv = _e4m3_torch(vfh)
+    o = [math.fsum(w[j] * float(vsh[c]) * vv[j, c] for j in range(n)) / l for c in range(d)]
+    return o, m + math.log(l)
+
+
+def pin_fp8_brute_force(orc):
+    """Tiny random problems (grouped heads, both masks, Nq != Nk) against the
+    term-by-term evaluation above."""
+    for dtype, causal, (B, Hq, Hkv, Nq, Nk, d) in (
+            ("bf16", False, (1, 4, 2, 3, 5, 8)), ("fp16", True, (2, 2, 1, 4, 3, 16)),
+            ("bf16", True, (1, 3, 3, 2, 6, 4))):
+        kf, ks, vf, vs = _fp8_cache(B, Hkv, Nk, d, seed=Nk + 2 * d)
+        q = _rand16((B, Hq, Nq, d), dtype, seed=d + 1)
+        o, lse = orc.attention_kv_fp8(bits(q), kf, ks, vf, vs, dtype, 0.7, causal=causal)
+        qn = _f64(q)
+        group = Hq // Hkv
+        for b in range(B):
+            for h in range(Hq):
+                g = h // group
+                for i in range(Nq):
+                    n = _visible(i, Nq, Nk) if causal else Nk
+                    ob, lb = _fp8_brute_row(qn[b, h, i], ks[b, g], kf[b, g], vs[b, g], vf[b, g], n, 0.7)
+                    np.testing.assert_allclose(o[b, h, i], ob, rtol=1e-12, atol=1e-14)
+                    if n:
+                        assert abs(lse[b, h, i] - lb) <= 1e-12 * max(1.0, abs(lb))
+                    else:
+                        assert lse[b, h, i] == -math.inf
+
+
 def pin_rows_subset_with_every_option(orc):
     """rows= picks exactly the full result's rows with every option at once
     (causal mask, grouped heads, Nq != Nk, both dtypes, and the INT8 cache):
@@ -631,5 +814,11 @@ ALL_PINS = [
     pin_int8_reduces_to_dequantized_attention,
     pin_int8_zero_query_is_uniform,
     pin_int8_brute_force,
+    pin_e4m3_codes_golden,
+    pin_e4m3_matches_torch,
+    pin_fp8_query_codes_golden,
+    pin_fp8_reduces_to_dequantized_attention,
+    pin_fp8_zero_query_is_uniform,
+    pin_fp8_brute_force,
     pin_rows_subset_with_every_option,
 ]

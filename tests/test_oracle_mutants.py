@@ -49,6 +49,21 @@ MUTANTS = [
     ("int8_row_scale_dropped", "row_scale = J->scale * (double)sq;", "row_scale = J->scale;"),
     ("int8_wrong_head_scales", "quantize_q_row(q, J->ks + kv_head * d, d, q);",
      "quantize_q_row(q, J->ks, d, q);"),
+    # FP8 key/value cache
+    ("fp8_bias_8", "mag = ldexp((double)(8 + m), e - 10);", "mag = ldexp((double)(8 + m), e - 11);"),
+    ("fp8_subnormal_scale", "mag = ldexp((double)m, -9);", "mag = ldexp((double)m, -10);"),
+    ("fp8_nan_code_finite", "if (e == 15 && m == 7)", "if (0)"),
+    ("fp8_ties_up", "((lo & 1) == 0 ? lo : hi)", "hi"),
+    ("fp8_ties_down", "((lo & 1) == 0 ? lo : hi)", "lo"),
+    ("fp8_sign_dropped", "return signbit(x) ? (uint8_t)(code | 0x80) : code;", "return code;"),
+    ("fp8_127_not_448", "const float to448 = 448.0f / top;", "const float to448 = 127.0f / top;"),
+    ("fp8_sq_over_127", "return top / 448.0f;", "return top / 127.0f;"),
+    ("fp8_key_scale_not_folded", "const float uk = (float)q[c] * ks[c];\n    const uint8_t",
+     "const float uk = (float)q[c];\n    const uint8_t"),
+    ("fp8_value_scale_dropped", "V[t] = (double)vs[t % d] * decode_e4m3(vh[t]);",
+     "V[t] = decode_e4m3(vh[t]);"),
+    ("fp8_row_scale_dropped", "row_scale = (double)sqf * J->scale;", "row_scale = J->scale;"),
+    ("fp8_codes_as_int8", "K[t] = decode_e4m3(kh[t]);", "K[t] = (double)(int8_t)kh[t];"),
 ]
 
 
