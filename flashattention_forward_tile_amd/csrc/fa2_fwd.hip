@@ -35,8 +35,9 @@
 //  * The query heads that share a K/V head are tiled together (their rows are
 //    adjacent in memory), and workgroup ids are remapped so all query tiles of
 //    a K/V head land on one XCD and share that XCD's L2 copy of its K and V.
-//  * The INT8 key/value cache kernels (Q8) quantize each query row in the
-//    kernel, run the first product on int8 MFMA and widen V to fp16 in LDS.
+//  * The INT8 and FP8 key/value cache kernels (Q8) quantize each query row in
+//    the kernel, run the first product on int8 or FP8 (E4M3) MFMA and widen V
+//    to fp16 in LDS.
 
 #include <hip/hip_runtime.h>
 #include <float.h>
@@ -54,6 +55,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -126,6 +128,27 @@ __device__ __forceinline__ float other_half(float x, int lane) {
   const uint32_t u = __builtin_bit_cast(uint32_t, x);
   const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
   return __builtin_bit_cast(float, (lane & 32) ? r[0] : r[1]);
+}
+
+// The OCP E4M3 code nearest to t (1 sign, 4 exponent bits with bias 7, 3
+// mantissa bits; below 2^-6 the subnormals m * 2^-9), ties to the even code,
+// magnitudes above 448 saturating to 448; t is not NaN.  Normal range: the
+// binary32 mantissa is rounded to 3 bits in place (a carry moves into the
+// exponent) and the exponent rebiased from 127 to 7.
+__device__ __forceinline__ uint32_t e4m3_rne(float t) {
+  const uint32_t bits = __builtin_bit_cast(uint32_t, t);
+  const uint32_t sign = (bits >> 24) & 0x80u;
+  const float a = __builtin_fabsf(t);
+  uint32_t code;
+  if (a < 0.015625f) {
+    code = (uint32_t)__builtin_rintf(a * 512.0f);  // m = 0..8; 8 is 2^-6, the code 0x08
+  } else {
+    uint32_t u = bits & 0x7fffffffu;
+    u += 0x7ffffu + ((u >> 20) & 1u);
+    code = (u >> 20) - (120u << 3);
+    code = code > 0x7eu ? 0x7eu : code;
+  }
+  return sign | code;
 }
 
 // s_waitcnt with only vmcnt(0): every buffer load of this wave, including
@@ -282,18 +305,21 @@ struct Problem {
   float c;           // scale * log2(e) (1 when the scale is 0)
 };
 
-// Q8 selects the INT8 key/value cache: K and V arrive as int8 codes with
-// per-channel scales; the first product runs on int8 matrix instructions
-// against the in-kernel quantized query, and V is widened to fp16 in LDS for
-// the second product (see the header of fa2.h for the scheme).
+// QK selects a quantized key/value cache (Q8 below): 1, int8 codes; 2, FP8
+// (OCP E4M3) codes (F8).  K and V arrive as codes with per-channel scales;
+// the first product runs on int8 or FP8 matrix instructions against the
+// in-kernel quantized query, and V is widened to fp16 in LDS for the second
+// product (see the header of fa2.h for the schemes).
 // PERSIST: one workgroup per CU walks several (K/V head, query tile) items,
 // and the key/value ring runs on from one item into the next (see below).
-template <int D, bool FP16, int MODE, bool CAUSAL, bool Q8, bool SHORT, bool PERSIST>
-__global__ void __attribute__((amdgpu_flat_work_group_size(KCfg<D, Q8, SHORT, PERSIST>::NW * 64,
-                                                           KCfg<D, Q8, SHORT, PERSIST>::NW * 64),
-                               amdgpu_waves_per_eu(KCfg<D, Q8, SHORT, PERSIST>::OCC,
-                                                   KCfg<D, Q8, SHORT, PERSIST>::OCC)))
+template <int D, bool FP16, int MODE, bool CAUSAL, int QK, bool SHORT, bool PERSIST>
+__global__ void __attribute__((amdgpu_flat_work_group_size(KCfg<D, QK != 0, SHORT, PERSIST>::NW * 64,
+                                                           KCfg<D, QK != 0, SHORT, PERSIST>::NW * 64),
+                               amdgpu_waves_per_eu(KCfg<D, QK != 0, SHORT, PERSIST>::OCC,
+                                                   KCfg<D, QK != 0, SHORT, PERSIST>::OCC)))
 fa2_fwd_kernel(const Problem P) {
+  constexpr bool Q8 = QK != 0;  // a quantized key/value cache (8-bit codes)
+  constexpr bool F8 = QK == 2;  // its codes are FP8 (E4M3) values
   using C = KCfg<D, Q8, SHORT, PERSIST>;
   const int N = P.nk;  // keys per head
   const float c = P.c;
@@ -314,7 +340,7 @@ fa2_fwd_kernel(const Problem P) {
   constexpr int TBK = BC * RBK;       // one K tile in LDS (and one int8 V tile)
   constexpr int LW = Q8 ? 4 : 16;     // bytes per lane of one HBM -> LDS load
   constexpr int LOADS = TBK / (NW * 64 * LW);  // K loads per thread per tile (V: the same)
-  constexpr int KD = Q8 || MS == 16 ? 32 : 16;  // contraction depth of one first-product MFMA
+  constexpr int KD = F8 ? 64 : Q8 || MS == 16 ? 32 : 16;  // contraction depth of one first-product MFMA
   constexpr int KS = D / KD;          // k-steps of the first product
   constexpr int KPM = MS == 32 ? 16 : 32;  // keys per second-product MFMA
   constexpr int ST = BC / KPM;        // k-steps of the second product
@@ -331,9 +357,10 @@ fa2_fwd_kernel(const Problem P) {
   using X2 = typename Vec<F16B>::x2;
   using E = typename Vec<FP16>::e;    // element type of Q and O
   using EP = typename Vec<F16B>::e;   // element type of P
-  using KOp = std::conditional_t<Q8, i32x4, X8>;        // A operand of the first product
+  // A operand of the first product: 8 16-bit, 16 int8 or 32 FP8 values
+  using KOp = std::conditional_t<F8, i32x8, std::conditional_t<Q8, i32x4, X8>>;
   using FAcc = std::conditional_t<MS == 32, f32x16, f32x4>;  // fp32 accumulator block
-  using SAcc = std::conditional_t<Q8, i32x16, FAcc>;    // the first product's
+  using SAcc = std::conditional_t<Q8 && !F8, i32x16, FAcc>;  // the first product's
 
   constexpr int PK = C::PK;           // K operands read one iteration early
   constexpr int PV = C::PV;           // V operands read one iteration early
@@ -544,7 +571,8 @@ fa2_fwd_kernel(const Problem P) {
   // Per-lane LDS byte offsets of the MFMA operands within a tile.  The
   // swizzle term depends only on the lane (row bits below the MS-row block),
   // so every other index becomes an instruction immediate.
-  //   K (A operand of S^T): row kb*MS + lq, logical chunk ks*KCH + lg.
+  //   K (A operand of S^T): row kb*MS + lq, logical chunk ks*KCH + lg (FP8:
+  //   the two chunks ks*KCH + 2 lg and ks*KCH + 2 lg + 1).
   //   V^T (A operand of O^T), via ds_read_b64_tr_b16 (in each 16-lane group
   //   lane i receives element i%4 of the 8-byte pieces that lanes i/4,
   //   4+i/4, 8+i/4, 12+i/4 address).  MS = 32: the 16-lane group g reads rows
@@ -566,10 +594,13 @@ fa2_fwd_kernel(const Problem P) {
   constexpr int KOFF = KS < KPB ? KS : KPB;
   constexpr int VPB = 128 / MS;       // output blocks per 256 B of a row
   constexpr int VOFF = DB < VPB ? DB : VPB;
-  uint32_t k_off[KOFF];
+  uint32_t k_off[KOFF], k_off2[F8 ? KOFF : 1];
 #pragma unroll
-  for (int ks = 0; ks < KOFF; ++ks)
-    k_off[ks] = (uint32_t)(lq * RBK + k_swizzle<CPRK>(lq, ks * KCH + lg) * 16);
+  for (int ks = 0; ks < KOFF; ++ks) {
+    const int ch = F8 ? ks * KCH + 2 * lg : ks * KCH + lg;
+    k_off[ks] = (uint32_t)(lq * RBK + k_swizzle<CPRK>(lq, ch) * 16);
+    if constexpr (F8) k_off2[ks] = (uint32_t)(lq * RBK + k_swizzle<CPRK>(lq, ch + 1) * 16);
+  }
   const int tr_row = MS == 32 ? half * 4 + ((lane & 15) >> 2) : 4 * lg + ((lane & 15) >> 2);
   const int tr_col = MS == 32 ? 16 * ((lane >> 4) & 1) + 4 * (lane & 3) : 4 * (lane & 3);
   uint32_t v_off[VOFF];
@@ -628,7 +659,7 @@ fa2_fwd_kernel(const Problem P) {
   item_limits();
   // c_q: the lane's logit multiplier (scale * log2 e, times the query row
   // scale with Q8).
-  using QOp = std::conditional_t<Q8, i32x4, X8>;
+  using QOp = KOp;
   QOp qf[QB][KS];
   float c_q[QB];
 #pragma unroll
@@ -642,6 +673,52 @@ fa2_fwd_kernel(const Problem P) {
       for (int ks = 0; ks < KS; ++ks)
         qf[b][ks] = __builtin_bit_cast(
             X8, __builtin_amdgcn_raw_buffer_load_b128(q_rs, qrow_off + (ks * KD + lg * 8) * 2, 0, 0));
+    } else if constexpr (F8 && MODE != kZero) {
+      // In-kernel quantization of the query row to E4M3 (lanes l and l+32
+      // hold its two halves): for k-step ks this lane holds channels
+      // 64 ks + 32 half + 0..31.  u = q * ks in binary32; amax over the
+      // row; codes e4m3_rne(u * (448 / amax)) and sq = amax / 448, both
+      // divisions correctly rounded (a zero row: codes 0, sq 0).
+      using Q16 = typename Vec<FP16>::x8;
+      const float* ksp = P.ks + (int64_t)bh * D;
+      float u[KS][32];
+      float amax = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+        for (int h4 = 0; h4 < 4; ++h4) {
+          const int ch = 64 * ks + 32 * half + 8 * h4;
+          const Q16 qv = __builtin_bit_cast(
+              Q16, __builtin_amdgcn_raw_buffer_load_b128(q_rs, qrow_off + ch * 2, 0, 0));
+          const float4 s0 = *(const float4*)(ksp + ch);
+          const float4 s1 = *(const float4*)(ksp + ch + 4);
+          const float sk[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float v = (float)qv[e] * sk[e];
+            u[ks][8 * h4 + e] = v;
+            amax = fmaxf(amax, fabsf(v));
+          }
+        }
+      }
+      amax = fmaxf(amax, other_half(amax, lane));
+      const bool nonzero = amax > 0.0f;
+      const float to448 = nonzero ? __fdiv_rn(448.0f, amax) : 0.0f;
+      const float sq = nonzero ? __fdiv_rn(amax, 448.0f) : 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        i32x8 w;
+#pragma unroll
+        for (int k4 = 0; k4 < 8; ++k4) {
+          uint32_t packed = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) packed |= e4m3_rne(u[ks][4 * k4 + e] * to448) << (8 * e);
+          w[k4] = (int)packed;
+        }
+        qf[b][ks] = w;
+      }
+      const float cq = c * sq;
+      c_q[b] = cq != 0.0f ? cq : (MODE == kNegative ? -FLT_MIN : FLT_MIN);
     } else if constexpr (MODE != kZero) {
       // In-kernel quantization of the query row (lanes l and l+32 hold its
       // two halves): for k-step ks this lane holds channels 32 ks + 16 half
@@ -735,9 +812,15 @@ fa2_fwd_kernel(const Problem P) {
   auto k_operand = [&](int t, auto s, int o) -> KOp {
     const int ks = o / KB, kk = o % KB;
     const lds_char* kb = lds + slot(t, s) * TBK;
-    return __builtin_bit_cast(
-        KOp, *(const __attribute__((address_space(3))) u32x4*)(
-                 kb + kk * MS * RBK + k_off[ks % KOFF] + (ks / KOFF) * 256));
+    const u32x4 a = *(const __attribute__((address_space(3))) u32x4*)(
+        kb + kk * MS * RBK + k_off[ks % KOFF] + (ks / KOFF) * 256);
+    if constexpr (F8) {
+      const u32x4 b = *(const __attribute__((address_space(3))) u32x4*)(
+          kb + kk * MS * RBK + k_off2[ks % KOFF] + (ks / KOFF) * 256);
+      return __builtin_bit_cast(KOp, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+    } else {
+      return __builtin_bit_cast(KOp, a);
+    }
   };
   // Operand o of the second product, o = st*DB + db: V_t^T for output rows
   // db*MS .. +MS-1 and keys st*KPM .. +KPM-1 in the S^T accumulator's key
@@ -771,7 +854,10 @@ fa2_fwd_kernel(const Problem P) {
       const KOp a = o < PK ? pre[o < PK ? o : 0] : k_operand(t, s, o);
 #pragma unroll
       for (int b = 0; b < QB; ++b) {
-        if constexpr (Q8)  // exact int32 dot products of the codes
+        if constexpr (F8)  // E4M3 x E4M3 (format 0 for both operands), fp32 sums, no block scales
+          sd[b][o % KB] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[b][o / KB], sd[b][o % KB],
+                                                                          0, 0, 0, 0, 0, 0);
+        else if constexpr (Q8)  // exact int32 dot products of the codes
           sd[b][o % KB] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qf[b][o / KB], sd[b][o % KB], 0, 0, 0);
         else if constexpr (MS == 32)
           sd[b][o % KB] = mfma32x32x16<FP16>(a, qf[b][o / KB], sd[b][o % KB]);
@@ -808,11 +894,12 @@ fa2_fwd_kernel(const Problem P) {
     for (int o = 0; o < PV; ++o) pre[o] = v_operand(t, s, o);
   };
 
-  // Q8: widen V_t from its int8 staging slot into the 16-bit V ring as exact
+  // Q8: widen V_t from its 8-bit staging slot into the 16-bit V ring as exact
   // fp16.  Each thread writes whole 16-byte chunks of the swizzled tile from
-  // the 8 codes of the logical chunk that belongs there: with u = code + 128
-  // (the byte xor 0x80), the fp16 pattern 0x6400 | u is 1024 + u, and
-  // subtracting 1152 leaves the code.
+  // the 8 codes of the logical chunk that belongs there.  int8: with u =
+  // code + 128 (the byte xor 0x80), the fp16 pattern 0x6400 | u is 1024 + u,
+  // and subtracting 1152 leaves the code.  FP8: every E4M3 value is an fp16
+  // value; the conversion instruction takes two codes at a time (scale 1).
   auto convert_v = [&](int t, auto s) {
     if constexpr (Q8) {
       using h16x8 = _Float16 __attribute__((ext_vector_type(8)));
@@ -822,17 +909,27 @@ fa2_fwd_kernel(const Problem P) {
       for (int i = 0; i < CH / (NW * 64); ++i) {
         const int lin = i * NW * 64 + tid;
         const int row = lin / CPR, pc = lin % CPR;
-        const int lc = v_swizzle<CPR>(row, pc);
+        const int lc = v_swizzle<CPR, MS>(row, pc);
         const u32x2 codes = *(const __attribute__((address_space(3))) u32x2*)(
             lds + SBASE + slot(t, s) * TBK + row * D + lc * 8);
         u32x4 w;
+        h16x8 v;
+        if constexpr (F8) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const uint32_t biased = codes[h] ^ 0x80808080u;
-          w[2 * h] = __builtin_amdgcn_perm(0x64646464u, biased, 0x04010400u);
-          w[2 * h + 1] = __builtin_amdgcn_perm(0x64646464u, biased, 0x04030402u);
+          for (int h = 0; h < 2; ++h) {
+            w[2 * h] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(codes[h], 1.0f, false));
+            w[2 * h + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(codes[h], 1.0f, true));
+          }
+          v = __builtin_bit_cast(h16x8, w);
+        } else {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const uint32_t biased = codes[h] ^ 0x80808080u;
+            w[2 * h] = __builtin_amdgcn_perm(0x64646464u, biased, 0x04010400u);
+            w[2 * h + 1] = __builtin_amdgcn_perm(0x64646464u, biased, 0x04030402u);
+          }
+          v = __builtin_bit_cast(h16x8, w) - (_Float16)1152.0f;
         }
-        const h16x8 v = __builtin_bit_cast(h16x8, w) - (_Float16)1152.0f;
         *(__attribute__((address_space(3))) u32x4*)(lds + VBASE + slot(t, s) * TBYTES + lin * 16) =
             __builtin_bit_cast(u32x4, v);
       }
@@ -918,9 +1015,10 @@ fa2_fwd_kernel(const Problem P) {
     }
 
     // The logits of this tile in fp32 (converted from the int32 products
-    // with Q8).
-    f32x16 s_conv[Q8 ? QB : 1][Q8 ? KB : 1];
-    if constexpr (Q8) {
+    // of the INT8 cache).
+    constexpr bool CONV = Q8 && !F8;
+    f32x16 s_conv[CONV ? QB : 1][CONV ? KB : 1];
+    if constexpr (CONV) {
 #pragma unroll
       for (int b = 0; b < QB; ++b)
 #pragma unroll
@@ -929,7 +1027,7 @@ fa2_fwd_kernel(const Problem P) {
           for (int i = 0; i < 16; ++i) s_conv[b][kk][i] = (float)s_cur[b][kk][i];
     }
     auto& sf = [&]() -> auto& {
-      if constexpr (Q8)
+      if constexpr (CONV)
         return s_conv;
       else
         return s_cur;
@@ -1068,7 +1166,14 @@ fa2_fwd_kernel(const Problem P) {
 #pragma unroll
     for (int b = 0; b < QB; ++b)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[b][ks]));
+      for (int ks = 0; ks < KS; ++ks) {
+        if constexpr (F8) {  // 8 registers: one operand each (the constraint takes at most 128 bits)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) asm volatile("" ::"v"(qf[b][ks][e]));
+        } else {
+          asm volatile("" ::"v"(qf[b][ks]));
+        }
+      }
     wait_vmem();
     __syncthreads();
 
@@ -1243,22 +1348,22 @@ fa2_fwd_kernel(const Problem P) {
 
 typedef void (*kernel_fn)(const Problem);
 
-template <int D, bool FP16, bool CAUSAL, bool Q8, bool SHORT, bool PERSIST = false>
+template <int D, bool FP16, bool CAUSAL, int QK, bool SHORT, bool PERSIST = false>
 kernel_fn pick_mode(int mode) {
   switch (mode) {
-    case kNegative: return fa2_fwd_kernel<D, FP16, kNegative, CAUSAL, Q8, SHORT, PERSIST>;
-    case kZero: return fa2_fwd_kernel<D, FP16, kZero, CAUSAL, Q8, SHORT, PERSIST>;
-    default: return fa2_fwd_kernel<D, FP16, kPositive, CAUSAL, Q8, SHORT, PERSIST>;
+    case kNegative: return fa2_fwd_kernel<D, FP16, kNegative, CAUSAL, QK, SHORT, PERSIST>;
+    case kZero: return fa2_fwd_kernel<D, FP16, kZero, CAUSAL, QK, SHORT, PERSIST>;
+    default: return fa2_fwd_kernel<D, FP16, kPositive, CAUSAL, QK, SHORT, PERSIST>;
   }
 }
 
-template <int D, bool Q8, bool SHORT = false>
+template <int D, int QK, bool SHORT = false>
 kernel_fn pick(bool fp16, int mode, bool causal) {
   if (fp16)
-    return causal ? pick_mode<D, true, true, Q8, SHORT>(mode)
-                  : pick_mode<D, true, false, Q8, SHORT>(mode);
-  return causal ? pick_mode<D, false, true, Q8, SHORT>(mode)
-                : pick_mode<D, false, false, Q8, SHORT>(mode);
+    return causal ? pick_mode<D, true, true, QK, SHORT>(mode)
+                  : pick_mode<D, true, false, QK, SHORT>(mode);
+  return causal ? pick_mode<D, false, true, QK, SHORT>(mode)
+                : pick_mode<D, false, false, QK, SHORT>(mode);
 }
 
 // Compute units of the current device (0 if unknown), cached per device.
@@ -1291,7 +1396,7 @@ const char* fa2_strerror(int status) {
     case FA2_OK: return "success";
     case FA2_ERR_NULL: return "a required pointer is NULL";
     case FA2_ERR_SHAPE: return "a size is negative, heads do not group, or sizes are too large";
-    case FA2_ERR_HEADDIM: return "head dimension must be 64, 128 or 256";
+    case FA2_ERR_HEADDIM: return "head dimension must be 64, 128 or 256 (128 for the quantized caches)";
     case FA2_ERR_DTYPE: return "dtype must be FA2_BF16 or FA2_FP16";
     case FA2_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
     case FA2_ERR_SCALE: return "scale must be finite";
@@ -1318,11 +1423,13 @@ int fa2_tile_config(int64_t d, int dtype, int* block_q, int* block_k, int* waves
 
 namespace fa2 {
 
-// Validation and launch shared by the entry points.  q8 selects the INT8
-// key/value cache (k, v int8 codes; ks, vs their per-channel scales).
+// Validation and launch shared by the entry points.  qk selects a quantized
+// key/value cache: 1, INT8 (k, v int8 codes); 2, FP8 (k, v E4M3 codes); ks,
+// vs are then their per-channel scales.
 int launch(const void* q, const void* k, const void* v, const float* ks, const float* vs,
            void* o, float* lse, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
-           int64_t d, float scale, int causal, int dtype, void* stream, bool q8) {
+           int64_t d, float scale, int causal, int dtype, void* stream, int qk) {
+  const bool q8 = qk != 0;
   if (dtype != FA2_BF16 && dtype != FA2_FP16) return FA2_ERR_DTYPE;
   if (q8 ? d != 128 : (d != 64 && d != 128 && d != 256)) return FA2_ERR_HEADDIM;
   if (causal != 0 && causal != 1) return FA2_ERR_OPTION;
@@ -1438,21 +1545,22 @@ int launch(const void* q, const void* k, const void* v, const float* ks, const f
   P.n_groups = (int)groups;
   P.causal_off = (int)(Nk - Nq);
   P.c = mode == kZero ? 1.0f : c;  // zero mode: logits are 0, t = s
-  kernel_fn fn = q8 ? pick<128, true>(fp16, mode, causal)
-               : d == 64 ? pick<64, false>(fp16, mode, causal)
-               : d == 128 ? (short_keys ? pick<128, false, true>(fp16, mode, causal)
-                                        : pick<128, false>(fp16, mode, causal))
-                          : pick<256, false>(fp16, mode, causal);
+  kernel_fn fn = qk == 2 ? pick<128, 2>(fp16, mode, causal)
+               : q8 ? pick<128, 1>(fp16, mode, causal)
+               : d == 64 ? pick<64, 0>(fp16, mode, causal)
+               : d == 128 ? (short_keys ? pick<128, 0, true>(fp16, mode, causal)
+                                        : pick<128, 0>(fp16, mode, causal))
+                          : pick<256, 0>(fp16, mode, causal);
   int64_t grid = groups;
   if (persist) {
     if (d == 64)
-      fn = fp16 ? pick_mode<64, true, false, false, false, true>(mode)
-                : pick_mode<64, false, false, false, false, true>(mode);
+      fn = fp16 ? pick_mode<64, true, false, 0, false, true>(mode)
+                : pick_mode<64, false, false, 0, false, true>(mode);
     else
-      fn = fp16 ? (causal ? pick_mode<128, true, true, false, false, true>(mode)
-                          : pick_mode<128, true, false, false, false, true>(mode))
-                : (causal ? pick_mode<128, false, true, false, false, true>(mode)
-                          : pick_mode<128, false, false, false, false, true>(mode));
+      fn = fp16 ? (causal ? pick_mode<128, true, true, 0, false, true>(mode)
+                          : pick_mode<128, true, false, 0, false, true>(mode))
+                : (causal ? pick_mode<128, false, true, 0, false, true>(mode)
+                          : pick_mode<128, false, false, 0, false, true>(mode));
     grid = cus;
   }
   void* args[] = {&P};
@@ -1470,7 +1578,7 @@ int fa2_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse
                 int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
                 float scale, int causal, int dtype, void* stream) {
   return fa2::launch(q, k, v, nullptr, nullptr, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal,
-                     dtype, stream, false);
+                     dtype, stream, 0);
 }
 
 int fa2_fwd_kv_int8(const void* q, const int8_t* kq, const float* ks, const int8_t* vq,
@@ -1478,7 +1586,15 @@ int fa2_fwd_kv_int8(const void* q, const int8_t* kq, const float* ks, const int8
                     int64_t Nq, int64_t Nk, int64_t d, float scale, int causal, int dtype,
                     void* stream) {
   return fa2::launch(q, kq, vq, ks, vs, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, dtype,
-                     stream, true);
+                     stream, 1);
+}
+
+int fa2_fwd_kv_fp8(const void* q, const uint8_t* kq, const float* ks, const uint8_t* vq,
+                   const float* vs, void* o, float* lse, int64_t B, int64_t Hq, int64_t Hkv,
+                   int64_t Nq, int64_t Nk, int64_t d, float scale, int causal, int dtype,
+                   void* stream) {
+  return fa2::launch(q, kq, vq, ks, vs, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, dtype,
+                     stream, 2);
 }
 
 int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse,

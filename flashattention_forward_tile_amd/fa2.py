@@ -45,6 +45,12 @@ _SIGNATURES = {
                                        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                        ctypes.c_int64, ctypes.c_float, ctypes.c_int,
                                        ctypes.c_int, ctypes.c_void_p]),
+    "fa2_fwd_kv_fp8": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                      ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                      ctypes.c_int64, ctypes.c_float, ctypes.c_int,
+                                      ctypes.c_int, ctypes.c_void_p]),
     "fa2_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "fa2_tile_config": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int,
                                        ctypes.POINTER(ctypes.c_int),
@@ -121,6 +127,13 @@ def fwd_kv_int8_raw(q_ptr, kq_ptr, ks_ptr, vq_ptr, vs_ptr, o_ptr, lse_ptr, B, Hq
                                  Hkv, Nq, Nk, d, float(scale), int(causal), int(dtype), stream)
 
 
+def fwd_kv_fp8_raw(q_ptr, kq_ptr, ks_ptr, vq_ptr, vs_ptr, o_ptr, lse_ptr, B, Hq, Hkv, Nq,
+                   Nk, d, scale, causal, dtype, stream=0) -> int:
+    """Direct call of fa2_fwd_kv_fp8 with integer pointers; returns the status."""
+    return lib().fa2_fwd_kv_fp8(q_ptr, kq_ptr, ks_ptr, vq_ptr, vs_ptr, o_ptr, lse_ptr, B, Hq,
+                                Hkv, Nq, Nk, d, float(scale), int(causal), int(dtype), stream)
+
+
 def _outputs(q, out, lse):
     B, Hq, Nq, _ = q.shape
     if out is None:
@@ -136,22 +149,16 @@ def _outputs(q, out, lse):
     return out, lse
 
 
-def fwd_kv_int8(q, kq, ks, vq, vs, scale=None, causal=False, out=None, lse=None):
-    """Attention over an INT8 key/value cache: returns (o, lse).
-
-    q: [B, Hq, Nq, 128] bf16 or fp16; kq, vq: [B, Hkv, Nk, 128] int8 codes;
-    ks, vs: [B, Hkv, 128] float32 per-channel scales (k = ks * kq, v = vs *
-    vq).  The query rows are quantized to int8 in the kernel (see fa2.h);
-    other arguments as in `fwd`.  All tensors contiguous on one GPU.
-    """
+def _kv_quantized(raw, code_dtype, what, q, kq, ks, vq, vs, scale, causal, out, lse):
+    """Shared marshalling of the quantized-cache entry points."""
     if q.dim() != 4 or kq.dim() != 4 or kq.shape != vq.shape:
         raise ValueError("q must be [B, Hq, Nq, d] and kq, vq one [B, Hkv, Nk, d] shape")
     B, Hq, Nq, d = q.shape
     _, Hkv, Nk, dk = kq.shape
     if kq.shape[0] != B or dk != d:
         raise ValueError("kq, vq must share q's batch and head dimension")
-    if q.dtype not in _DTYPE or kq.dtype != torch.int8 or vq.dtype != torch.int8:
-        raise ValueError("q must be bfloat16 or float16 and kq, vq int8")
+    if q.dtype not in _DTYPE or kq.dtype != code_dtype or vq.dtype != code_dtype:
+        raise ValueError("q must be bfloat16 or float16 and kq, vq %s" % what)
     if ks.shape != (B, Hkv, d) or vs.shape != (B, Hkv, d) or ks.dtype != torch.float32 \
             or vs.dtype != torch.float32:
         raise ValueError("ks and vs must be float32 [B, Hkv, d]")
@@ -165,12 +172,35 @@ def fwd_kv_int8(q, kq, ks, vq, vs, scale=None, causal=False, out=None, lse=None)
     out, lse = _outputs(q, out, lse)
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        code = fwd_kv_int8_raw(q.data_ptr(), kq.data_ptr(), ks.data_ptr(), vq.data_ptr(),
-                               vs.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, Nq,
-                               Nk, d, scale, 1 if causal else 0, _DTYPE[q.dtype], stream)
+        code = raw(q.data_ptr(), kq.data_ptr(), ks.data_ptr(), vq.data_ptr(), vs.data_ptr(),
+                   out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, Nq, Nk, d, scale,
+                   1 if causal else 0, _DTYPE[q.dtype], stream)
     if code != OK:
         raise FA2Error(code)
     return out, lse
+
+
+def fwd_kv_int8(q, kq, ks, vq, vs, scale=None, causal=False, out=None, lse=None):
+    """Attention over an INT8 key/value cache: returns (o, lse).
+
+    q: [B, Hq, Nq, 128] bf16 or fp16; kq, vq: [B, Hkv, Nk, 128] int8 codes;
+    ks, vs: [B, Hkv, 128] float32 per-channel scales (k = ks * kq, v = vs *
+    vq).  The query rows are quantized to int8 in the kernel (see fa2.h);
+    other arguments as in `fwd`.  All tensors contiguous on one GPU.
+    """
+    return _kv_quantized(fwd_kv_int8_raw, torch.int8, "int8", q, kq, ks, vq, vs, scale,
+                         causal, out, lse)
+
+
+def fwd_kv_fp8(q, kq, ks, vq, vs, scale=None, causal=False, out=None, lse=None):
+    """Attention over an FP8 (OCP E4M3) key/value cache: returns (o, lse).
+
+    As `fwd_kv_int8` with kq, vq uint8 tensors of E4M3 codes (k = ks *
+    e4m3(kq), v = vs * e4m3(vq)); the query rows are rounded to E4M3 in the
+    kernel (see fa2.h).
+    """
+    return _kv_quantized(fwd_kv_fp8_raw, torch.uint8, "uint8 E4M3 codes", q, kq, ks, vq, vs,
+                         scale, causal, out, lse)
 
 
 def fwd(q, k, v, scale=None, causal=False, out=None, lse=None):

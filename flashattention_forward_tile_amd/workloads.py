@@ -41,6 +41,12 @@ class Workload:
     Nk: int = 0
     causal: bool = False
     kv_int8: bool = False   # keys/values as an INT8 cache (int8 codes, fp32 channel scales)
+    kv_fp8: bool = False    # keys/values as an FP8 cache (E4M3 codes, fp32 channel scales)
+
+    @property
+    def quantized(self) -> bool:
+        """Keys and values arrive as 8-bit codes with channel scales."""
+        return self.kv_int8 or self.kv_fp8
 
     @property
     def kv_heads(self) -> int:
@@ -80,7 +86,7 @@ class Workload:
         q = self.B * self.H * self.N * self.d
         kv = self.B * self.kv_heads * self.keys * self.d
         lse = self.B * self.H * self.N * 4
-        if self.kv_int8:  # 1-byte codes plus two fp32 scales per K/V channel
+        if self.quantized:  # 1-byte codes plus two fp32 scales per K/V channel
             return 2 * 2 * q + 2 * kv + 2 * 4 * self.B * self.kv_heads * self.d + lse
         return 2 * (2 * q + 2 * kv) + lse
 
@@ -94,6 +100,8 @@ class Workload:
             out["Nk"] = self.keys
         if self.kv_int8:
             out["kv"] = "int8 codes, fp32 per-channel scales"
+        if self.kv_fp8:
+            out["kv"] = "FP8 E4M3 codes, fp32 per-channel scales"
         return out
 
 
@@ -123,6 +131,10 @@ WORKLOADS = {
     "int8_kv": Workload("int8_kv", 4, 16, 4096, 128, "bf16", kv_int8=True),
     "int8_kv_causal": Workload("int8_kv_causal", 4, 16, 4096, 128, "bf16", causal=True,
                                kv_int8=True),
+    # the same over an FP8 (E4M3) key/value cache
+    "fp8_kv": Workload("fp8_kv", 4, 16, 4096, 128, "bf16", kv_fp8=True),
+    "fp8_kv_causal": Workload("fp8_kv_causal", 4, 16, 4096, 128, "bf16", causal=True,
+                              kv_fp8=True),
 }
 
 
@@ -169,10 +181,33 @@ def make_inputs_kv_int8(B, Hq, Hkv, Nq, Nk, d, dtype="bf16", seed=0):
     return q.to(_TORCH_DTYPES[dtype]), codes[0], scales[0], codes[1], scales[1]
 
 
+def make_inputs_kv_fp8(B, Hq, Hkv, Nq, Nk, d, dtype="bf16", seed=0):
+    """Seeded CPU inputs for attention over an FP8 key/value cache: q
+    [B, Hq, Nq, d] in the 16-bit dtype (standard normal), kq and vq
+    [B, Hkv, Nk, d] uint8 OCP E4M3 codes of a standard normal times 448/4.5,
+    clipped to [-448, 448] (torch's float8_e4m3fn conversion; the shape of a
+    per-channel symmetric FP8 cache of normal data, never a NaN code), and
+    ks, vs [B, Hkv, d] float32 per-channel scales (4.5/448 times a factor
+    drawn uniformly from [0.5, 1.5))."""
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn((B, Hq, Nq, d), generator=g, dtype=torch.float32)
+    codes = []
+    for _ in range(2):
+        c = torch.randn((B, Hkv, Nk, d), generator=g, dtype=torch.float32) * (448.0 / 4.5)
+        codes.append(c.clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8))
+    scales = []
+    for _ in range(2):
+        u = torch.rand((B, Hkv, d), generator=g, dtype=torch.float32)
+        scales.append(((u + 0.5) * (4.5 / 448.0)).to(torch.float32))
+    return q.to(_TORCH_DTYPES[dtype]), codes[0], scales[0], codes[1], scales[1]
+
+
 def workload_inputs(w: Workload, seed=0):
-    """(q, k, v), or (q, kq, ks, vq, vs) for an INT8 cache workload."""
+    """(q, k, v), or (q, kq, ks, vq, vs) for a quantized cache workload."""
     if w.kv_int8:
         return make_inputs_kv_int8(w.B, w.H, w.kv_heads, w.N, w.keys, w.d, w.dtype, seed)
+    if w.kv_fp8:
+        return make_inputs_kv_fp8(w.B, w.H, w.kv_heads, w.N, w.keys, w.d, w.dtype, seed)
     return make_inputs(w.B, w.H, w.N, w.d, w.dtype, w.dist, seed, w.kv_heads, w.keys)
 
 

@@ -46,7 +46,8 @@ enum fa2_status {
                            the grid overflows, or the query rows of one K/V
                            head ((Hq/Hkv)*Nq*d) or its key rows (Nk*d) exceed
                            2^31 - 2^20 elements */
-  FA2_ERR_HEADDIM = -3, /* d is not 64, 128 or 256 (128 for fa2_fwd_kv_int8) */
+  FA2_ERR_HEADDIM = -3, /* d is not 64, 128 or 256 (128 for fa2_fwd_kv_int8 and
+                           fa2_fwd_kv_fp8) */
   FA2_ERR_DTYPE = -4,   /* dtype is not an fa2_dtype */
   FA2_ERR_ALIGN = -5,   /* q, k, v or o not 16-byte aligned, lse not 4-byte */
   FA2_ERR_SCALE = -6,   /* scale is NaN or infinite, or scale * log2(e)
@@ -159,6 +160,43 @@ int fa2_fwd_kv_int8(const void* q, const int8_t* kq, const float* ks, const int8
                     const float* vs, void* o, float* lse, int64_t B, int64_t Hq, int64_t Hkv,
                     int64_t Nq, int64_t Nk, int64_t d, float scale, int causal, int dtype,
                     void* stream);
+
+/*
+ * fa2_fwd_kv_fp8 -- attention over an FP8 key/value cache: the scheme of
+ * fa2_fwd_kv_int8 with 8-bit floating-point codes (this library's second
+ * reading of the same post title; gfx950 multiplies FP8 matrices at twice the
+ * 16-bit rate).  Every code is an OCP FP8 E4M3 value: 1 sign bit, 4 exponent
+ * bits with bias 7, 3 mantissa bits, exponent field 0 holding the subnormals
+ * m * 2^-9, 0x7F and 0xFF NaN (not diagnosed), largest magnitude 448.
+ *
+ *     k[b,g,j,c] = ks[b,g,c] * e4m3(kq[b,g,j,c]),   v[b,g,j,c] = vs[b,g,c] * e4m3(vq[b,g,j,c]).
+ *
+ * Each query row is quantized inside the kernel after the key scales are
+ * folded into it, every step in IEEE binary32 up to the last rounding:
+ *
+ *     u[c]  = q[c] * ks[c],   amax = max_c |u[c]|,
+ *     qq[c] = e4m3_rne(u[c] * (448 / amax)),   sq = amax / 448
+ *     (a zero row: qq = 0, sq = 0),
+ *
+ * where e4m3_rne rounds to the nearest E4M3 value, ties to the code with an
+ * even last mantissa bit (both divisions correctly rounded).  The logits are
+ * s_j = scale * sq * sum_c e4m3(qq[c]) * e4m3(kq[j][c]), on FP8 matrix
+ * instructions with fp32 sums; the softmax, O and lse follow fa2_fwd with the
+ * dequantized v, P and V meeting on fp16 matrix instructions (V widened
+ * exactly).
+ *
+ *   q, o     : [B][Hq][Nq][d], element type `dtype` (bf16 or fp16).
+ *   kq, vq   : [B][Hkv][Nk][d] E4M3 codes (may be NULL when Nk == 0).
+ *   ks, vs   : [B][Hkv][d] fp32 scales (required).
+ *   d        : 128 (FA2_ERR_HEADDIM otherwise).
+ *
+ * Alignment, heads, lengths, causal, asynchrony and return codes are those
+ * of fa2_fwd_kv_int8.
+ */
+int fa2_fwd_kv_fp8(const void* q, const uint8_t* kq, const float* ks, const uint8_t* vq,
+                   const float* vs, void* o, float* lse, int64_t B, int64_t Hq, int64_t Hkv,
+                   int64_t Nq, int64_t Nk, int64_t d, float scale, int causal, int dtype,
+                   void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* fa2_strerror(int status);

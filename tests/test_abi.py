@@ -28,8 +28,8 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["fa2_fwd", "fa2_fwd_ext", "fa2_fwd_kv_int8",
-                                    "fa2_strerror", "fa2_tile_config"]
+    assert declared_functions() == ["fa2_fwd", "fa2_fwd_ext", "fa2_fwd_kv_fp8",
+                                    "fa2_fwd_kv_int8", "fa2_strerror", "fa2_tile_config"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -153,13 +153,14 @@ I8_PTRS = dict(q=A, kq=A + 0x1000000, ks=A + 0x2000000, vq=A + 0x3000000, vs=A +
                o=A + 0x5000000, lse=A + 0x6000000)
 
 
-def call_int8(**kw):
+def call_int8(raw=None, **kw):
     p = dict(I8)
     p.update(I8_PTRS)
     p.update(kw)
-    return fa2.fwd_kv_int8_raw(p["q"], p["kq"], p["ks"], p["vq"], p["vs"], p["o"], p["lse"],
-                               p["B"], p["Hq"], p["Hkv"], p["Nq"], p["Nk"], p["d"], p["scale"],
-                               p["causal"], p["dtype"], 0)
+    raw = raw or fa2.fwd_kv_int8_raw
+    return raw(p["q"], p["kq"], p["ks"], p["vq"], p["vs"], p["o"], p["lse"],
+               p["B"], p["Hq"], p["Hkv"], p["Nq"], p["Nk"], p["d"], p["scale"],
+               p["causal"], p["dtype"], 0)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -174,8 +175,11 @@ def call_int8(**kw):
 ])
 def test_int8_host_validation(lib, kw, code):
     assert call_int8(**kw) == code
+    # the FP8 cache shares the INT8 cache's validation
+    assert call_int8(raw=fa2.fwd_kv_fp8_raw, **kw) == code
 
 
 @pytest.mark.parametrize("kw", [dict(B=0), dict(Hq=0, Hkv=0), dict(Nq=0)])
 def test_int8_empty_output_is_a_no_op(lib, kw):
     assert call_int8(q=0, kq=0, ks=0, vq=0, vs=0, o=0, lse=0, **kw) == fa2.OK
+    assert call_int8(raw=fa2.fwd_kv_fp8_raw, q=0, kq=0, ks=0, vq=0, vs=0, o=0, lse=0, **kw) == fa2.OK

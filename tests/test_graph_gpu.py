@@ -7,7 +7,8 @@ import pytest
 import torch
 
 from flashattention_forward_tile_amd import fa2
-from flashattention_forward_tile_amd.workloads import make_inputs, make_inputs_kv_int8
+from flashattention_forward_tile_amd.workloads import (make_inputs, make_inputs_kv_fp8,
+                                                       make_inputs_kv_int8)
 
 pytestmark = pytest.mark.gpu
 
@@ -56,4 +57,13 @@ def test_graph_fwd_kv_int8():
     o_ref, lse_ref = fa2.fwd_kv_int8(*inputs, causal=True)
     o, lse = torch.empty_like(o_ref), torch.empty_like(lse_ref)
     replay_and_check(lambda o, lse: fa2.fwd_kv_int8(*inputs, causal=True, out=o, lse=lse),
+                     o_ref, lse_ref, o, lse)
+
+
+def test_graph_fwd_kv_fp8():
+    announce("graph fwd_kv_fp8")
+    inputs = [t.to(DEV) for t in make_inputs_kv_fp8(1, 4, 2, 500, 900, 128, "fp16", seed=5)]
+    o_ref, lse_ref = fa2.fwd_kv_fp8(*inputs, causal=True)
+    o, lse = torch.empty_like(o_ref), torch.empty_like(lse_ref)
+    replay_and_check(lambda o, lse: fa2.fwd_kv_fp8(*inputs, causal=True, out=o, lse=lse),
                      o_ref, lse_ref, o, lse)

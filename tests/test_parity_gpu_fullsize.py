@@ -1,7 +1,8 @@
 """GPU parity at the full workload sizes, every row compared (needs an MI355X).
 
 Each workload that bench.py can time runs here in the same launch
-configuration (``fa2.fwd`` / ``fa2.fwd_kv_int8`` into preallocated outputs on
+configuration (``fa2.fwd`` / ``fa2.fwd_kv_int8`` / ``fa2.fwd_kv_fp8`` into
+preallocated outputs on
 the current stream), with O and LSE prefilled with NaN so that an unwritten
 row or a wrongly placed query tile cannot pass.  The output is then compared
 with the fp64 oracle element by element:
@@ -9,7 +10,7 @@ with the fp64 oracle element by element:
 * every (b, h) and every query row for the headline, the softmax-stress and
   tiny workloads, the head-dimension variants (d = 64, d = 256), the
   sequence sweep at N = 512, 1024, 2048 and 4096, and the widened workloads
-  (causal, grouped heads, KV cache, prefill chunk, INT8 cache);
+  (causal, grouped heads, KV cache, prefill chunk, INT8 and FP8 caches);
 * for the sweep at N = 8192 (B = 2) and N = 16384 (B = 1), where the oracle
   would take minutes for every head, all rows of the fixed (b, h) pairs in
   ``HEAD_SUBSETS``; every other head is still checked for being fully
@@ -19,7 +20,8 @@ The sequence sweep follows "Flash Attention 2 from scratch on Ampere",
 Part 1, Performance section (a harmonic mean over sequence lengths 512 to
 16384); the headline and head-dimension shapes follow its Kernel
 Specification (d = 128), widened to d = 64 and 256.  Tolerances: O max-abs
-<= 2e-2, mean-abs <= 2e-3, LSE relative <= 1e-3 (tests/parity.py).
+<= 2e-2, mean-abs <= 2e-3, LSE relative <= 1e-3 (tests/parity.py); for the
+FP8 cache, LSE relative or absolute <= 1e-3 per row.
 """
 import numpy as np
 import pytest
@@ -42,7 +44,8 @@ HEAD_SUBSETS = {
 
 FULL = ["tiny", "stress", "headline", "d64", "d256",
         "sweep_n512", "sweep_n1024", "sweep_n2048", "sweep_n4096",
-        "causal", "gqa", "kv_cache", "gqa_chunk", "int8_kv", "int8_kv_causal"]
+        "causal", "gqa", "kv_cache", "gqa_chunk", "int8_kv", "int8_kv_causal",
+        "fp8_kv", "fp8_kv_causal"]
 
 
 def announce(*what):
@@ -54,8 +57,9 @@ def run_like_bench(w, inputs):
     dev_in = [t.to(DEV) for t in inputs]
     o = torch.full_like(dev_in[0], float("nan"))
     lse = torch.full((w.B, w.H, w.N), float("nan"), dtype=torch.float32, device=DEV)
-    if w.kv_int8:
-        fa2.fwd_kv_int8(*dev_in, scale=w.scale, causal=w.causal, out=o, lse=lse)
+    if w.quantized:
+        fwd = fa2.fwd_kv_int8 if w.kv_int8 else fa2.fwd_kv_fp8
+        fwd(*dev_in, scale=w.scale, causal=w.causal, out=o, lse=lse)
     else:
         fa2.fwd(*dev_in, scale=w.scale, causal=w.causal, out=o, lse=lse)
     torch.cuda.synchronize()
@@ -66,10 +70,11 @@ def oracle_heads(w, inputs, heads=None):
     """The oracle over every (b, h), or over the listed (b, h) pairs only
     (stacked along a new leading axis)."""
     group = w.H // w.kv_heads
-    if w.kv_int8:
+    if w.quantized:
         q, kq, ks, vq, vs = inputs
         qb = bits(q)
-        call = lambda qs, kk: oracle.attention_kv_int8(
+        attn = oracle.attention_kv_int8 if w.kv_int8 else oracle.attention_kv_fp8
+        call = lambda qs, kk: attn(
             qs, kq.numpy()[kk], ks.numpy()[kk], vq.numpy()[kk], vs.numpy()[kk],
             w.dtype, w.scale, causal=w.causal)
     else:
@@ -103,5 +108,9 @@ def test_workload_every_row(name):
         o64 = np.stack([o64[b, h] for b, h in heads])
         lse64 = np.stack([lse64[b, h] for b, h in heads])
     assert np.isfinite(lse_ref).all(), "every row of these workloads sees a key"
+    # The FP8 matrix instruction truncates its products (see
+    # test_parity_gpu_fp8.py), which moves a logit by up to about 1e-4: an
+    # absolute floor for the causal rows whose logsumexp lies near zero.
     assert_parity(o64, lse64, o_ref, lse_ref, "%s every row%s" % (
-        name, "" if heads is None else " of (b, h) in %s" % (heads,)))
+        name, "" if heads is None else " of (b, h) in %s" % (heads,)),
+        lse_abs=1e-3 if w.kv_fp8 else None)

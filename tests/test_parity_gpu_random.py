@@ -15,7 +15,7 @@ import torch
 
 import oracle
 from flashattention_forward_tile_amd import fa2
-from flashattention_forward_tile_amd.workloads import bits, make_inputs_kv_int8
+from flashattention_forward_tile_amd.workloads import bits, make_inputs_kv_fp8, make_inputs_kv_int8
 from parity import assert_parity
 
 pytestmark = pytest.mark.gpu
@@ -87,4 +87,23 @@ def test_random_shape_int8_cache(i):
     o_ref, lse_ref = oracle.attention_kv_int8(bits(q), kq.numpy(), ks.numpy(), vq.numpy(),
                                               vs.numpy(), c["dtype"], c["scale"],
                                               causal=c["causal"])
+    compare(o.cpu(), lse.cpu(), o_ref, lse_ref, tag)
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_shape_fp8_cache(i):
+    c = draw(i + 100)
+    c["d"] = 128
+    c["Nk"] = max(c["Nk"], 1)
+    c["scale"] = c["scale"] * math.sqrt(draw(i + 100)["d"]) / math.sqrt(128)
+    tag = "random fp8 %d %s" % (i, c)
+    announce(tag)
+    q, kq, ks, vq, vs = make_inputs_kv_fp8(c["B"], c["Hq"], c["Hkv"], c["Nq"], c["Nk"], 128,
+                                           c["dtype"], seed=4000 + i)
+    o, lse = fa2.fwd_kv_fp8(q.to(DEV), kq.to(DEV), ks.to(DEV), vq.to(DEV), vs.to(DEV),
+                            scale=c["scale"], causal=c["causal"])
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_kv_fp8(bits(q), kq.numpy(), ks.numpy(), vq.numpy(),
+                                             vs.numpy(), c["dtype"], c["scale"],
+                                             causal=c["causal"])
     compare(o.cpu(), lse.cpu(), o_ref, lse_ref, tag)

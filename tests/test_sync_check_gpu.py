@@ -8,7 +8,7 @@ the next iteration as the key/value ring does.  The arithmetic and its order
 are the same, so any difference in O or LSE would mean the production
 pipeline read a tile before it landed or overwrote one still in use.  Each
 case covers one kernel family: persistent, one item per workgroup, causal,
-short keys, each head dimension, grouped heads, and the INT8 cache.
+short keys, each head dimension, grouped heads, and the INT8 and FP8 caches.
 """
 import math
 
@@ -17,7 +17,8 @@ import torch
 
 from flashattention_forward_tile_amd import _build, fa2
 from flashattention_forward_tile_amd.workloads import (WORKLOADS, make_inputs,
-                                                       make_inputs_kv_int8, workload_inputs)
+                                                       make_inputs_kv_fp8, make_inputs_kv_int8,
+                                                       workload_inputs)
 
 pytestmark = pytest.mark.gpu
 
@@ -92,19 +93,20 @@ def test_shapes_match_race_check_build(B, Hq, Hkv, Nq, Nk, dtype, scale):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-def test_int8_cache_matches_race_check_build(causal):
-    announce("int8", causal)
-    q, kq, ks, vq, vs = (t.to(DEV) for t in make_inputs_kv_int8(2, 16, 4, 1500, 3000, 128,
-                                                               "bf16", 7))
+@pytest.mark.parametrize("fmt", ["int8", "fp8"])
+def test_quantized_cache_matches_race_check_build(fmt, causal):
+    announce(fmt, causal)
+    make = make_inputs_kv_int8 if fmt == "int8" else make_inputs_kv_fp8
+    q, kq, ks, vq, vs = (t.to(DEV) for t in make(2, 16, 4, 1500, 3000, 128, "bf16", 7))
     outs = []
     for handle in (fa2.lib(), sync_lib()):
         o = torch.full_like(q, float("nan"))
         lse = torch.full(q.shape[:3], float("nan"), device=DEV)
-        code = handle.fa2_fwd_kv_int8(q.data_ptr(), kq.data_ptr(), ks.data_ptr(), vq.data_ptr(),
-                                      vs.data_ptr(), o.data_ptr(), lse.data_ptr(), 2, 16, 4,
-                                      1500, 3000, 128, 1.0 / math.sqrt(128), int(causal),
-                                      fa2.BF16, 0)
+        call = handle.fa2_fwd_kv_int8 if fmt == "int8" else handle.fa2_fwd_kv_fp8
+        code = call(q.data_ptr(), kq.data_ptr(), ks.data_ptr(), vq.data_ptr(), vs.data_ptr(),
+                    o.data_ptr(), lse.data_ptr(), 2, 16, 4, 1500, 3000, 128,
+                    1.0 / math.sqrt(128), int(causal), fa2.BF16, 0)
         assert code == 0, fa2.strerror(code)
         torch.cuda.synchronize()
         outs.append((o.cpu(), lse.cpu()))
-    assert_same(outs, "int8 causal=%d" % causal)
+    assert_same(outs, "%s causal=%d" % (fmt, causal))
