@@ -19,10 +19,11 @@ peak, and the fp64 CPU oracle's rate on a bounded sample of the same workload
 on this host's cores.
 
 With the headline workload (the default) the same run then times the
-sequence sweep (N = 512 ... 16384 at B*N = 16384, fp16) and the head-dimension
-variants (d = 64, 256) with the same --warmup / --steps, and adds them to the
-line as "sweep" (per N, plus the harmonic mean) and "head_dim", each with its
-roofline fraction (--no-extras leaves them out).  Every output is checked
+sequence sweep (N = 512 ... 16384 at B*N = 16384, fp16), the head-dimension
+variants (d = 64, 256) and two decoding workloads with key splits (one query
+row per head against 32K and 128K keys) with the same --warmup / --steps, and
+adds them to the line as "sweep" (per N, plus the harmonic mean), "head_dim"
+and "decode", each with its roofline fraction (--no-extras leaves them out).  Every output is checked
 after the timing (NaN-prefilled buffers fully written with finite values, and
 the oracle's parity on the heads the CPU baseline computed): the line is
 printed either way, and the exit status is 1 if a check failed.
@@ -60,6 +61,8 @@ HBM_PEAK_GBS = 8000.0
 SWEEP = ["sweep_n512", "sweep_n1024", "sweep_n2048", "sweep_n4096", "sweep_n8192",
          "sweep_n16384"]
 HEAD_DIMS = ["d64", "d256"]
+# ... and decoding against long caches with key splits (fa2_fwd_split).
+DECODE = ["decode", "decode_long"]
 KERNEL_SRC = os.path.join(ROOT, "flashattention_forward_tile_amd", "csrc", "fa2_fwd.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa2_fwd_headline_traffic.json")
 CPU_SAMPLE_SECONDS = 12.0
@@ -283,7 +286,7 @@ def main():
     from flashattention_forward_tile_amd.workloads import WORKLOADS
 
     w = WORKLOADS[args.workload]
-    extras = [] if args.no_extras or w.name != "headline" else SWEEP + HEAD_DIMS
+    extras = [] if args.no_extras or w.name != "headline" else SWEEP + HEAD_DIMS + DECODE
     # Every workload's inputs are drawn and made resident first, so that no
     # input generation sits between the timed runs.
     runs = [Resident(WORKLOADS[n]) for n in [w.name] + extras]
@@ -317,6 +320,7 @@ def main():
         out["sweep"] = dict(sweep, harmonic_mean_tflops=round(hm, 3),
                             config="B*N = 16384, H 16, d 128, fp16, N(0,1), non-causal")
         out["head_dim"] = {n: others[n] for n in HEAD_DIMS}
+        out["decode"] = {n: others[n] for n in DECODE}
     if not args.no_cpu_baseline:
         q, k, v = main_run.host_qkv()
         o, lse = main_run.outputs()
@@ -350,6 +354,14 @@ class Resident:
             fwd = fa2.fwd_kv_int8 if w.kv_int8 else fa2.fwd_kv_fp8
             self.launch = lambda: fwd(*self.dev_in, scale=w.scale, causal=w.causal,
                                       out=self.o, lse=self.lse)
+        elif w.split:
+            # the workspace is allocated once, outside the timed launches
+            nbytes = fa2.split_workspace_bytes(w.B, w.H, w.kv_heads, w.N, w.keys, w.d, w.causal,
+                                               self.dev_in[0].dtype, 0)
+            self.ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+            self.launch = lambda: fa2.fwd_split(*self.dev_in, scale=w.scale, causal=w.causal,
+                                                splits=0, workspace=self.ws, out=self.o,
+                                                lse=self.lse)
         else:
             self.launch = lambda: fa2.fwd(*self.dev_in, scale=w.scale, causal=w.causal,
                                           out=self.o, lse=self.lse)

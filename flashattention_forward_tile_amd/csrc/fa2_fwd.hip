@@ -38,6 +38,11 @@
 //  * The INT8 and FP8 key/value cache kernels (Q8) quantize each query row in
 //    the kernel, run the first product on int8 or FP8 (E4M3) MFMA and widen V
 //    to fp16 in LDS.
+//  * Key splits (SPLIT): when query tiles are too few to fill the chip (a
+//    few query rows against a long cache, as in decoding), each query tile's
+//    key tiles are divided among several workgroups, which write fp32
+//    partial outputs and logsumexps to a workspace; a second kernel merges
+//    them (the softmax of a union of key sets from the parts' logsumexps).
 
 #include <hip/hip_runtime.h>
 #include <float.h>
@@ -64,6 +69,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
 
 template <bool FP16> struct Vec;
 template <> struct Vec<false> {
@@ -305,6 +311,20 @@ struct Problem {
   float c;           // scale * log2(e) (1 when the scale is 0)
 };
 
+// Arguments of the key-split kernels (the others keep Problem alone, so
+// their argument block and register allocation do not change): each item's
+// key tiles are shared out among `splits` workgroups (consecutive ids),
+// which write fp32 partials: part_o [splits][part_rows][D] (O of the part's
+// keys, normalised by their own sum) and part_lse [splits][part_rows]
+// (natural log; -inf: no key seen).  part_rows = B * hq * nq, rows indexed
+// as in lse.
+struct SplitProblem : Problem {
+  float* part_o;
+  float* part_lse;
+  int64_t part_rows;
+  int splits;
+};
+
 // QK selects a quantized key/value cache (Q8 below): 1, int8 codes; 2, FP8
 // (OCP E4M3) codes (F8).  K and V arrive as codes with per-channel scales;
 // the first product runs on int8 or FP8 matrix instructions against the
@@ -312,12 +332,13 @@ struct Problem {
 // product (see the header of fa2.h for the schemes).
 // PERSIST: one workgroup per CU walks several (K/V head, query tile) items,
 // and the key/value ring runs on from one item into the next (see below).
-template <int D, bool FP16, int MODE, bool CAUSAL, int QK, bool SHORT, bool PERSIST>
+// SPLIT: key splits (see Problem); non-persistent 16-bit kernels only.
+template <int D, bool FP16, int MODE, bool CAUSAL, int QK, bool SHORT, bool PERSIST, bool SPLIT>
 __global__ void __attribute__((amdgpu_flat_work_group_size(KCfg<D, QK != 0, SHORT, PERSIST>::NW * 64,
                                                            KCfg<D, QK != 0, SHORT, PERSIST>::NW * 64),
                                amdgpu_waves_per_eu(KCfg<D, QK != 0, SHORT, PERSIST>::OCC,
                                                    KCfg<D, QK != 0, SHORT, PERSIST>::OCC)))
-fa2_fwd_kernel(const Problem P) {
+fa2_fwd_kernel(const std::conditional_t<SPLIT, SplitProblem, Problem> P) {
   constexpr bool Q8 = QK != 0;  // a quantized key/value cache (8-bit codes)
   constexpr bool F8 = QK == 2;  // its codes are FP8 (E4M3) values
   using C = KCfg<D, Q8, SHORT, PERSIST>;
@@ -388,6 +409,7 @@ fa2_fwd_kernel(const Problem P) {
   // the ring.
   constexpr int QTB = BR * RB;  // one query tile
   static_assert(!PERSIST || (!Q8 && QB == 1), "persistent kernels");
+  static_assert(!SPLIT || (!PERSIST && !Q8), "key splits");
   constexpr int QOBASE = PERSIST ? RING_BYTES : 0;
   constexpr int QOBYTES = QTB > OBYTES ? QTB : OBYTES;
   __shared__ __attribute__((aligned(16)))
@@ -432,6 +454,16 @@ fa2_fwd_kernel(const Problem P) {
       bh_r = logical / P.q_tiles;
       qt_r = logical - bh_r * P.q_tiles;
       return true;
+    }
+    if constexpr (SPLIT) {
+      // the splits of one item are consecutive workgroups (on different
+      // XCDs, reading different keys); with the causal mask the later
+      // (longer) query tiles start first
+      const int item = id / P.splits;
+      bh_r = item / P.q_tiles;
+      qt_r = item - bh_r * P.q_tiles;
+      if constexpr (CAUSAL) qt_r = P.q_tiles - 1 - qt_r;
+      return r == 0;
     }
     if ((P.n_groups & 7) == 0) {
       const int x = id & 7, kx = id >> 3;  // k-th workgroup dispatched on XCD x
@@ -627,8 +659,11 @@ fa2_fwd_kernel(const Problem P) {
   // the leading tiles that no wave of the workgroup masks, whole tiles of keys
   // and with the causal mask those whose last key every row of the workgroup
   // sees (its smallest row within a head; 0 if it spans a head boundary).
+  // SPLIT: the workgroup takes the key tiles [lo, hi) of its item's n_tiles
+  // (split id % splits of `splits` near-equal shares); key_base = lo * BC is
+  // its first key, and tile counts and wave_last become relative to lo.
   int row_lim[QB];
-  int wave_row_min = 0, wave_last = 0, n_tiles = 0, n_clear = 0;
+  int wave_row_min = 0, wave_last = 0, n_tiles = 0, n_clear = 0, key_base = 0;
   auto item_limits = [&]() {
     if constexpr (CAUSAL) {
       const int r0 = q0 % P.nq;
@@ -651,12 +686,29 @@ fa2_fwd_kernel(const Problem P) {
       const int seen = row_min + P.causal_off + 1;  // keys every row sees
       n_clear = seen <= 0 ? 0 : min(n_clear, seen / BC);
     }
+    if constexpr (SPLIT) {
+      const int sp = id % P.splits;
+      const int lo = (int)((int64_t)n_tiles * sp / P.splits);
+      const int hi = (int)((int64_t)n_tiles * (sp + 1) / P.splits);
+      key_base = lo * BC;
+      n_clear = max(0, min(n_clear, hi) - lo);
+      if constexpr (CAUSAL) wave_last -= lo;
+      n_tiles = hi - lo;
+    }
     n_cur = n_tiles;
   };
   // Causal: whether any row of this wave sees a key of tile t (always true
   // without the mask).
   auto sees = [&](int t) -> bool { return !CAUSAL || t <= wave_last; };
   item_limits();
+  if constexpr (SPLIT) {
+    // K and V from the split's first key on; key_base < N unless there are
+    // no tiles at all (then 0), so the range stays within the head
+    const int64_t off = ((int64_t)bh * N + key_base) * D * KE;
+    const uint32_t len = (uint32_t)(N - key_base) * D * KE;
+    k_rs = make_rsrc_words(P.k + off, len);
+    v_rs = make_rsrc_words(P.v + off, len);
+  }
   // c_q: the lane's logit multiplier (scale * log2 e, times the query row
   // scale with Q8).
   using QOp = KOp;
@@ -1036,7 +1088,7 @@ fa2_fwd_kernel(const Problem P) {
     // Mask keys past N and, with the causal option, keys past a row's
     // diagonal (key > row + causal_off).  Decided per wave, from its
     // smallest row within a head.
-    const int key0 = j * BC;
+    const int key0 = j * BC + (SPLIT ? key_base : 0);
     bool masked = false;
     if constexpr ((TL & 8) == 0) {
       masked = key0 + BC > N;
@@ -1270,6 +1322,34 @@ fa2_fwd_kernel(const Problem P) {
     wait_vmem();
     __syncthreads();
   }
+  if constexpr (SPLIT) {
+    // The part's fp32 output (normalised by the part's own sum) and
+    // logsumexp, straight from registers: a lane holds 4 consecutive
+    // channels of one row per store.
+    const int sp = id % P.splits;
+    const int64_t prow0 = (int64_t)sp * P.part_rows + (int64_t)bh * P.rows;
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+      const int qrow = q0 + MS * b + lq;
+      const float l_tot = row_sum(l_part[b]);
+      const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+      if (qrow < P.rows) {
+        float* const po = P.part_o + (prow0 + qrow) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int g4 = 0; g4 < NACC / 4; ++g4) {
+            const int ch = db * MS + g4 * 8 + lg * 4;
+            const float4 v = {acc[b][db][g4 * 4] * inv, acc[b][db][g4 * 4 + 1] * inv,
+                              acc[b][db][g4 * 4 + 2] * inv, acc[b][db][g4 * 4 + 3] * inv};
+            *(float4*)(po + ch) = v;
+          }
+        if (lg == 0)
+          P.part_lse[prow0 + qrow] = l_tot > 0.0f ? (m_ref[b] + __log2f(l_tot)) * kLn2 : -INFINITY;
+      }
+    }
+    break;
+  }
   // PERSIST: the lane's addresses here are recomputed per item rather than
   // held in registers through the loop.
   int el = lane;
@@ -1351,9 +1431,9 @@ typedef void (*kernel_fn)(const Problem);
 template <int D, bool FP16, bool CAUSAL, int QK, bool SHORT, bool PERSIST = false>
 kernel_fn pick_mode(int mode) {
   switch (mode) {
-    case kNegative: return fa2_fwd_kernel<D, FP16, kNegative, CAUSAL, QK, SHORT, PERSIST>;
-    case kZero: return fa2_fwd_kernel<D, FP16, kZero, CAUSAL, QK, SHORT, PERSIST>;
-    default: return fa2_fwd_kernel<D, FP16, kPositive, CAUSAL, QK, SHORT, PERSIST>;
+    case kNegative: return fa2_fwd_kernel<D, FP16, kNegative, CAUSAL, QK, SHORT, PERSIST, false>;
+    case kZero: return fa2_fwd_kernel<D, FP16, kZero, CAUSAL, QK, SHORT, PERSIST, false>;
+    default: return fa2_fwd_kernel<D, FP16, kPositive, CAUSAL, QK, SHORT, PERSIST, false>;
   }
 }
 
@@ -1364,6 +1444,72 @@ kernel_fn pick(bool fp16, int mode, bool causal) {
                   : pick_mode<D, true, false, QK, SHORT>(mode);
   return causal ? pick_mode<D, false, true, QK, SHORT>(mode)
                 : pick_mode<D, false, false, QK, SHORT>(mode);
+}
+
+// Key-split kernels: 128-query-row tiles at every head dimension (the d = 128
+// half-height shape), so that few query rows still make many workgroups.
+template <int D> struct SplitCfg { using C = Cfg<D>; };
+template <> struct SplitCfg<128> { using C = CfgS<128>; };
+template <int D>
+constexpr int kSplitRows = SplitCfg<D>::C::NW * SplitCfg<D>::C::MS * SplitCfg<D>::C::QB;
+template <int D>
+constexpr int kSplitKeys = SplitCfg<D>::C::BC;
+constexpr int kMaxSplits = 128;
+
+// Merge of the key splits' partials (see Problem): for each row, with m the
+// largest part logsumexp and w_s = exp(lse_s - m), O = sum_s w_s O_s /
+// sum_s w_s and lse = m + log(sum_s w_s), which is the softmax over the
+// union of the parts' keys (every part's O_s is normalised by its own sum
+// exp(lse_s)).  A row that no part saw (every lse_s = -inf) gets O = 0,
+// lse = -inf.  Each thread owns 4 channels of one row; plain loads and
+// stores, HBM-bound.
+constexpr int kMergeThreads = 256;
+template <int D, bool FP16>
+__global__ void __launch_bounds__(kMergeThreads)
+fa2_split_merge_kernel(const float* part_o, const float* part_lse, uint16_t* o, float* lse,
+                       int64_t rows, int splits) {
+  using X4 = typename Vec<FP16>::x4;
+  using E = typename Vec<FP16>::e;
+  constexpr int TPR = D / 4;  // threads per row
+  const int64_t gid = (int64_t)blockIdx.x * kMergeThreads + threadIdx.x;
+  const int64_t r = gid / TPR;
+  const int c4 = (int)(gid - r * TPR);
+  if (r >= rows) return;
+  float m = -INFINITY;
+  for (int s = 0; s < splits; ++s) m = fmaxf(m, part_lse[s * rows + r]);
+  float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f, wsum = 0.0f;
+  if (m != -INFINITY) {
+    for (int s = 0; s < splits; ++s) {
+      const float w = __builtin_amdgcn_exp2f((part_lse[s * rows + r] - m) * kLog2e);
+      const float4 po = *(const float4*)(part_o + (s * rows + r) * D + c4 * 4);
+      a0 += w * po.x;
+      a1 += w * po.y;
+      a2 += w * po.z;
+      a3 += w * po.w;
+      wsum += w;
+    }
+  }
+  const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+  const X4 out = {(E)(a0 * inv), (E)(a1 * inv), (E)(a2 * inv), (E)(a3 * inv)};
+  *(u32x2*)(o + r * D + c4 * 4) = __builtin_bit_cast(u32x2, out);
+  if (c4 == 0) lse[r] = wsum > 0.0f ? m + __log2f(wsum) * kLn2 : -INFINITY;
+}
+
+template <int D, bool FP16, bool CAUSAL>
+const void* pick_split_mode(int mode) {
+  constexpr bool S = D == 128;  // the half-height shape at d = 128
+  switch (mode) {
+    case kNegative: return (const void*)fa2_fwd_kernel<D, FP16, kNegative, CAUSAL, 0, S, false, true>;
+    case kZero: return (const void*)fa2_fwd_kernel<D, FP16, kZero, CAUSAL, 0, S, false, true>;
+    default: return (const void*)fa2_fwd_kernel<D, FP16, kPositive, CAUSAL, 0, S, false, true>;
+  }
+}
+
+template <int D>
+const void* pick_split(bool fp16, int mode, bool causal) {
+  if (fp16)
+    return causal ? pick_split_mode<D, true, true>(mode) : pick_split_mode<D, true, false>(mode);
+  return causal ? pick_split_mode<D, false, true>(mode) : pick_split_mode<D, false, false>(mode);
 }
 
 // Compute units of the current device (0 if unknown), cached per device.
@@ -1402,7 +1548,8 @@ const char* fa2_strerror(int status) {
     case FA2_ERR_SCALE: return "scale must be finite";
     case FA2_ERR_ALIAS: return "o or lse overlaps an input or each other";
     case FA2_ERR_HIP: return "kernel launch failed";
-    case FA2_ERR_OPTION: return "causal must be 0 or 1";
+    case FA2_ERR_OPTION: return "causal must be 0 or 1, and a split count 0 to 128";
+    case FA2_ERR_WORKSPACE: return "the key-split workspace is NULL or too small";
     default: return "unknown status";
   }
 }
@@ -1423,21 +1570,49 @@ int fa2_tile_config(int64_t d, int dtype, int* block_q, int* block_k, int* waves
 
 namespace fa2 {
 
-// Validation and launch shared by the entry points.  qk selects a quantized
-// key/value cache: 1, INT8 (k, v int8 codes); 2, FP8 (k, v E4M3 codes); ks,
-// vs are then their per-channel scales.
-int launch(const void* q, const void* k, const void* v, const float* ks, const float* vs,
-           void* o, float* lse, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
-           int64_t d, float scale, int causal, int dtype, void* stream, int qk) {
-  const bool q8 = qk != 0;
+// The key-split plan of a call whose shape has passed validation: the split
+// count (splits = 0: enough splits for one workgroup per CU over the call's
+// query tiles, each split keeping at least 8 key tiles, at most kMaxSplits;
+// 1 when that leaves a single split), the query tiles per K/V head and the
+// workspace bytes (0 without splits).  One workgroup per CU measured best
+// for decoding shapes (one to 128 query rows per K/V head, 8K to 128K keys,
+// d = 64 to 256: 4.8-5.6 TB/s of K/V reads); more splits only add partials
+// to write and merge.
+struct SplitPlan {
+  int splits;
+  int64_t q_tiles;
+  int64_t bytes;
+};
+SplitPlan plan_split(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
+                     int splits) {
+  const int64_t rows = Hq / Hkv * Nq;
+  const int64_t br = d == 64 ? kSplitRows<64> : d == 128 ? kSplitRows<128> : kSplitRows<256>;
+  const int64_t bc = d == 64 ? kSplitKeys<64> : d == 128 ? kSplitKeys<128> : kSplitKeys<256>;
+  SplitPlan p;
+  p.q_tiles = (rows + br - 1) / br;
+  if (splits == 0) {
+    const int64_t items = B * Hkv * p.q_tiles;
+    const int64_t cus = cu_count();
+    const int64_t k_tiles = (Nk + bc - 1) / bc;
+    int64_t want = cus > 0 ? (cus + items - 1) / items : 1;
+    want = want < k_tiles / 8 ? want : k_tiles / 8;
+    want = want < kMaxSplits ? want : kMaxSplits;
+    splits = (int)(want > 1 ? want : 1);
+  }
+  p.splits = splits;
+  p.bytes = splits > 1 ? (int64_t)splits * (B * Hq * Nq) * (d + 1) * 4 : 0;
+  return p;
+}
+
+// Shape checks shared by the entry points (no pointer is looked at).
+// Returns FA2_OK, an error, or 1 when the call has no output rows.
+int check_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
+                int causal, int dtype, bool q8) {
   if (dtype != FA2_BF16 && dtype != FA2_FP16) return FA2_ERR_DTYPE;
   if (q8 ? d != 128 : (d != 64 && d != 128 && d != 256)) return FA2_ERR_HEADDIM;
   if (causal != 0 && causal != 1) return FA2_ERR_OPTION;
   if (B < 0 || Hq < 0 || Hkv < 0 || Nq < 0 || Nk < 0) return FA2_ERR_SHAPE;
-  // logits in log2 units: t = s * scale * log2(e), which must stay finite
-  const float c = (float)((double)scale * 1.4426950408889634074);
-  if (!__builtin_isfinite(scale) || !__builtin_isfinite(c)) return FA2_ERR_SCALE;
-  if (B == 0 || Hq == 0 || Nq == 0) return FA2_OK;  // no output rows
+  if (B == 0 || Hq == 0 || Nq == 0) return 1;  // no output rows
   if (Hkv == 0 || Hq % Hkv != 0) return FA2_ERR_SHAPE;
   // The query rows of one K/V head's group (group * Nq) and the key rows of
   // one K/V head are addressed with 32-bit offsets (plus slack for the loads
@@ -1448,7 +1623,6 @@ int launch(const void* q, const void* k, const void* v, const float* ks, const f
   if (group > lim / (Nq * d)) return FA2_ERR_SHAPE;
   const int64_t rows = group * Nq;  // query rows per K/V head
   if (B > (((int64_t)1 << 31) - 1) / Hq) return FA2_ERR_SHAPE;
-  const int64_t bh = B * Hq;
   // The workgroup count fits a 1-D grid for every tile height the call may
   // take (the smallest, 128 query rows, gives the most workgroups).
   int bq = 0, bk = 0, nw = 0;
@@ -1456,10 +1630,46 @@ int launch(const void* q, const void* k, const void* v, const float* ks, const f
   const int64_t bq_min = q8 ? Cfg8<128>::NW * Cfg8<128>::MS * Cfg8<128>::QB
                        : d == 128 ? CfgS<128>::NW * CfgS<128>::MS * CfgS<128>::QB : bq;
   if (B * Hkv > (((int64_t)1 << 31) - 1) / ((rows + bq_min - 1) / bq_min)) return FA2_ERR_SHAPE;
+  return FA2_OK;
+}
+
+// The split plan of a call that passed check_shape, with its own limits:
+// the split count in range, the grids of both kernels within a 1-D grid.
+int check_split(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
+                int splits, SplitPlan* plan) {
+  if (splits < 0 || splits > kMaxSplits) return FA2_ERR_OPTION;
+  *plan = plan_split(B, Hq, Hkv, Nq, Nk, d, splits);
+  if (plan->splits == 1) return FA2_OK;
+  const int64_t grid_max = ((int64_t)1 << 31) - 1;
+  if (B * Hkv * plan->q_tiles > grid_max / plan->splits) return FA2_ERR_SHAPE;
+  if ((B * Hq * Nq * (d / 4) + kMergeThreads - 1) / kMergeThreads > grid_max) return FA2_ERR_SHAPE;
+  return FA2_OK;
+}
+
+// Validation and launch shared by the entry points.  qk selects a quantized
+// key/value cache: 1, INT8 (k, v int8 codes); 2, FP8 (k, v E4M3 codes); ks,
+// vs are then their per-channel scales.  splits != 1 (16-bit only): key
+// splits (0: planned here) with the partials in `ws`, ws_bytes long.
+int launch(const void* q, const void* k, const void* v, const float* ks, const float* vs,
+           void* o, float* lse, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
+           int64_t d, float scale, int causal, int dtype, void* stream, int qk,
+           int splits = 1, void* ws = nullptr, int64_t ws_bytes = 0) {
+  const bool q8 = qk != 0;
+  const int shape = check_shape(B, Hq, Hkv, Nq, Nk, d, causal, dtype, q8);
+  if (shape < 0) return shape;
+  // logits in log2 units: t = s * scale * log2(e), which must stay finite
+  const float c = (float)((double)scale * 1.4426950408889634074);
+  if (!__builtin_isfinite(scale) || !__builtin_isfinite(c)) return FA2_ERR_SCALE;
+  if (splits < 0 || splits > kMaxSplits || (q8 && splits != 1)) return FA2_ERR_OPTION;
+  if (shape == 1) return FA2_OK;  // no output rows
+  const int64_t rows = Hq / Hkv * Nq;  // query rows per K/V head
+  const int64_t bh = B * Hq;
+  int bq = 0, bk = 0, nw = 0;
+  fa2_tile_config(d, dtype, &bq, &bk, &nw);
   if (!q || !o || !lse || (Nk > 0 && (!k || !v))) return FA2_ERR_NULL;
   if (q8 && (!ks || !vs)) return FA2_ERR_NULL;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return FA2_ERR_ALIGN;
-  if (((uintptr_t)ks | (uintptr_t)vs) & 15) return FA2_ERR_ALIGN;
+  if (((uintptr_t)ks | (uintptr_t)vs | (uintptr_t)ws) & 15) return FA2_ERR_ALIGN;
   if ((uintptr_t)lse & 3) return FA2_ERR_ALIGN;
   const size_t qbytes = (size_t)(bh * Nq * d) * 2;
   const size_t kbytes = (size_t)(B * Hkv * Nk * d) * (q8 ? 1 : 2);
@@ -1471,6 +1681,21 @@ int launch(const void* q, const void* k, const void* v, const float* ks, const f
     if (overlaps(o, qbytes, in[i], in_bytes[i]) || overlaps(lse, lbytes, in[i], in_bytes[i]))
       return FA2_ERR_ALIAS;
   if (overlaps(lse, lbytes, o, qbytes)) return FA2_ERR_ALIAS;
+  // The split plan (for splits = 0 it queries the device's CU count), then
+  // the workspace it needs.
+  SplitPlan plan;
+  if (splits != 1) {
+    const int sc = check_split(B, Hq, Hkv, Nq, Nk, d, splits, &plan);
+    if (sc != FA2_OK) return sc;
+    splits = plan.splits;
+  }
+  if (splits > 1) {
+    if (!ws || ws_bytes < plan.bytes) return FA2_ERR_WORKSPACE;
+    const size_t wbytes = (size_t)plan.bytes;
+    for (int i = 0; i < 5; ++i)
+      if (overlaps(ws, wbytes, in[i], in_bytes[i])) return FA2_ERR_ALIAS;
+    if (overlaps(ws, wbytes, o, qbytes) || overlaps(ws, wbytes, lse, lbytes)) return FA2_ERR_ALIAS;
+  }
 
   // Launch shape (the arguments are valid; from here on HIP may be queried).
   // Persistent workgroups (one per CU) when every one gets at least two items
@@ -1545,6 +1770,44 @@ int launch(const void* q, const void* k, const void* v, const float* ks, const f
   P.n_groups = (int)groups;
   P.causal_off = (int)(Nk - Nq);
   P.c = mode == kZero ? 1.0f : c;  // zero mode: logits are 0, t = s
+  if (splits > 1) {
+    // Key splits: the split kernel over items x splits workgroups, then the
+    // merge, both on `stream`.
+    SplitProblem SP;
+    static_cast<Problem&>(SP) = P;
+    SP.q_tiles = (int)plan.q_tiles;
+    SP.n_groups = (int)(B * Hkv * plan.q_tiles * splits);
+    SP.part_rows = bh * Nq;
+    SP.part_o = (float*)ws;
+    SP.part_lse = (float*)ws + (int64_t)splits * SP.part_rows * d;
+    SP.splits = splits;
+    const void* sfn = d == 64 ? pick_split<64>(fp16, mode, causal)
+                    : d == 128 ? pick_split<128>(fp16, mode, causal)
+                               : pick_split<256>(fp16, mode, causal);
+    const int snw = d == 64 ? SplitCfg<64>::C::NW : d == 128 ? SplitCfg<128>::C::NW
+                                                              : SplitCfg<256>::C::NW;
+    void* sargs[] = {&SP};
+    hipError_t err = hipLaunchKernel(sfn, dim3((unsigned)SP.n_groups),
+                                     dim3((unsigned)(snw * 64)), sargs, 0, (hipStream_t)stream);
+    if (err != hipSuccess) return FA2_ERR_HIP;
+    const float* po = SP.part_o;
+    const float* pl = SP.part_lse;
+    uint16_t* oo = SP.o;
+    float* ll = lse;
+    int64_t mrows = SP.part_rows;
+    int msplits = splits;
+    void* margs[] = {&po, &pl, &oo, &ll, &mrows, &msplits};
+    const int64_t mblocks = (mrows * (d / 4) + kMergeThreads - 1) / kMergeThreads;
+    const void* mfn = d == 64 ? (fp16 ? (const void*)fa2_split_merge_kernel<64, true>
+                                      : (const void*)fa2_split_merge_kernel<64, false>)
+                    : d == 128 ? (fp16 ? (const void*)fa2_split_merge_kernel<128, true>
+                                       : (const void*)fa2_split_merge_kernel<128, false>)
+                               : (fp16 ? (const void*)fa2_split_merge_kernel<256, true>
+                                       : (const void*)fa2_split_merge_kernel<256, false>);
+    err = hipLaunchKernel(mfn, dim3((unsigned)mblocks), dim3(kMergeThreads), margs, 0,
+                          (hipStream_t)stream);
+    return err == hipSuccess ? FA2_OK : FA2_ERR_HIP;
+  }
   kernel_fn fn = qk == 2 ? pick<128, 2>(fp16, mode, causal)
                : q8 ? pick<128, 1>(fp16, mode, causal)
                : d == 64 ? pick<64, 0>(fp16, mode, causal)
@@ -1595,6 +1858,26 @@ int fa2_fwd_kv_fp8(const void* q, const uint8_t* kq, const float* ks, const uint
                    void* stream) {
   return fa2::launch(q, kq, vq, ks, vs, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, dtype,
                      stream, 2);
+}
+
+int fa2_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
+                  float scale, int causal, int dtype, int splits, void* workspace,
+                  int64_t workspace_bytes, void* stream) {
+  return fa2::launch(q, k, v, nullptr, nullptr, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal,
+                     dtype, stream, 0, splits, workspace, workspace_bytes);
+}
+
+int64_t fa2_fwd_split_workspace(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
+                                int64_t d, int causal, int dtype, int splits) {
+  const int shape = fa2::check_shape(B, Hq, Hkv, Nq, Nk, d, causal, dtype, false);
+  if (shape < 0) return shape;
+  if (splits < 0 || splits > fa2::kMaxSplits) return FA2_ERR_OPTION;
+  if (shape == 1 || splits == 1) return 0;
+  fa2::SplitPlan plan;
+  const int sc = fa2::check_split(B, Hq, Hkv, Nq, Nk, d, splits, &plan);
+  if (sc != FA2_OK) return sc;
+  return plan.bytes;
 }
 
 int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse,

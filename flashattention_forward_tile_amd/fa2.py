@@ -23,6 +23,7 @@ ERR_SCALE = -6
 ERR_ALIAS = -7
 ERR_HIP = -8
 ERR_OPTION = -9
+ERR_WORKSPACE = -10
 
 BF16 = 0
 FP16 = 1
@@ -51,6 +52,15 @@ _SIGNATURES = {
                                       ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                       ctypes.c_int64, ctypes.c_float, ctypes.c_int,
                                       ctypes.c_int, ctypes.c_void_p]),
+    "fa2_fwd_split": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                     ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                     ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
+                                     ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                     ctypes.c_int64, ctypes.c_void_p]),
+    "fa2_fwd_split_workspace": (ctypes.c_int64, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                                 ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                                 ctypes.c_int, ctypes.c_int, ctypes.c_int]),
     "fa2_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "fa2_tile_config": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int,
                                        ctypes.POINTER(ctypes.c_int),
@@ -118,6 +128,25 @@ def fwd_ext_raw(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, Hq, Hkv, Nq, Nk, d, scal
     """Direct call of fa2_fwd_ext with integer pointers; returns the status."""
     return lib().fa2_fwd_ext(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, Hq, Hkv, Nq, Nk,
                              d, float(scale), int(causal), int(dtype), stream)
+
+
+def fwd_split_raw(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, Hq, Hkv, Nq, Nk, d, scale, causal,
+                  dtype, splits, ws_ptr, ws_bytes, stream=0) -> int:
+    """Direct call of fa2_fwd_split with integer pointers; returns the status."""
+    return lib().fa2_fwd_split(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, Hq, Hkv, Nq, Nk, d,
+                               float(scale), int(causal), int(dtype), int(splits), ws_ptr,
+                               int(ws_bytes), stream)
+
+
+def split_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, causal=False, dtype=BF16, splits=0) -> int:
+    """fa2_fwd_split_workspace: workspace bytes for these arguments (0: the call
+    runs without splits); raises FA2Error for arguments it rejects."""
+    code_dtype = _DTYPE.get(dtype, -1) if isinstance(dtype, torch.dtype) else int(dtype)
+    n = lib().fa2_fwd_split_workspace(B, Hq, Hkv, Nq, Nk, d, 1 if causal else 0, code_dtype,
+                                      int(splits))
+    if n < 0:
+        raise FA2Error(int(n))
+    return int(n)
 
 
 def fwd_kv_int8_raw(q_ptr, kq_ptr, ks_ptr, vq_ptr, vs_ptr, o_ptr, lse_ptr, B, Hq, Hkv, Nq,
@@ -238,6 +267,48 @@ def fwd(q, k, v, scale=None, causal=False, out=None, lse=None):
             code = fwd_ext_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                lse.data_ptr(), B, Hq, Hkv, Nq, Nk, d, scale,
                                1 if causal else 0, _DTYPE[q.dtype], stream)
+    if code != OK:
+        raise FA2Error(code)
+    return out, lse
+
+
+def fwd_split(q, k, v, scale=None, causal=False, splits=0, workspace=None, out=None, lse=None):
+    """Attention forward with key splits (fa2_fwd_split): returns (o, lse).
+
+    Arguments as in `fwd`; splits: 0 (chosen by the library for the current
+    device), 1 (no split) or up to 128 key parts per query tile.
+    workspace: an optional device tensor of at least split_workspace_bytes()
+    bytes (any dtype, contiguous, 16-byte aligned); without one a uint8
+    tensor of that size is allocated with torch for the call.  The kernels
+    are enqueued on torch's current stream of q's device.
+    """
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape:
+        raise ValueError("q must be [B, Hq, Nq, d] and k, v one [B, Hkv, Nk, d] shape")
+    B, Hq, Nq, d = q.shape
+    _, Hkv, Nk, dk = k.shape
+    if k.shape[0] != B or dk != d:
+        raise ValueError("k, v must share q's batch and head dimension")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DTYPE:
+        raise ValueError("q, k, v must all be bfloat16 or all float16")
+    if not (q.is_cuda and k.device == q.device and v.device == q.device):
+        raise ValueError("q, k, v must be on one GPU")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out, lse = _outputs(q, out, lse)
+    with torch.cuda.device(q.device):
+        need = split_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, causal, q.dtype, splits)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        elif not (workspace.is_cuda and workspace.device == q.device
+                  and workspace.is_contiguous()):
+            raise ValueError("workspace must be a contiguous tensor on q's device")
+        ws_bytes = workspace.numel() * workspace.element_size()
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        code = fwd_split_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                             lse.data_ptr(), B, Hq, Hkv, Nq, Nk, d, scale, 1 if causal else 0,
+                             _DTYPE[q.dtype], splits, workspace.data_ptr(), ws_bytes, stream)
     if code != OK:
         raise FA2Error(code)
     return out, lse

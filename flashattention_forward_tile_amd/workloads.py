@@ -42,6 +42,7 @@ class Workload:
     causal: bool = False
     kv_int8: bool = False   # keys/values as an INT8 cache (int8 codes, fp32 channel scales)
     kv_fp8: bool = False    # keys/values as an FP8 cache (E4M3 codes, fp32 channel scales)
+    split: bool = False     # run with key splits (fa2_fwd_split, split count chosen by the library)
 
     @property
     def quantized(self) -> bool:
@@ -102,6 +103,8 @@ class Workload:
             out["kv"] = "int8 codes, fp32 per-channel scales"
         if self.kv_fp8:
             out["kv"] = "FP8 E4M3 codes, fp32 per-channel scales"
+        if self.split:
+            out["key_splits"] = "chosen by the library (fa2_fwd_split, splits = 0)"
         return out
 
 
@@ -135,6 +138,12 @@ WORKLOADS = {
     "fp8_kv": Workload("fp8_kv", 4, 16, 4096, 128, "bf16", kv_fp8=True),
     "fp8_kv_causal": Workload("fp8_kv_causal", 4, 16, 4096, 128, "bf16", causal=True,
                               kv_fp8=True),
+    # decoding: one new query row per head against a long cache, with key
+    # splits (32 query heads on 8 K/V heads)
+    "decode": Workload("decode", 4, 32, 1, 128, "bf16", Hkv=8, Nk=32768, causal=True,
+                       split=True),
+    "decode_long": Workload("decode_long", 1, 32, 1, 128, "bf16", Hkv=8, Nk=131072,
+                            causal=True, split=True),
 }
 
 

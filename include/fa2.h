@@ -38,7 +38,9 @@ enum fa2_dtype {
 };
 
 /* Return codes.  Every negative code except FA2_ERR_HIP is detected on the
- * host before any HIP call is made, and nothing is written. */
+ * host before any kernel is launched, and nothing is written; before any HIP
+ * call at all, except that fa2_fwd_split with splits = 0 queries the
+ * device's compute-unit count before it checks the workspace. */
 enum fa2_status {
   FA2_OK = 0,
   FA2_ERR_NULL = -1,    /* a required pointer is NULL */
@@ -49,12 +51,16 @@ enum fa2_status {
   FA2_ERR_HEADDIM = -3, /* d is not 64, 128 or 256 (128 for fa2_fwd_kv_int8 and
                            fa2_fwd_kv_fp8) */
   FA2_ERR_DTYPE = -4,   /* dtype is not an fa2_dtype */
-  FA2_ERR_ALIGN = -5,   /* q, k, v or o not 16-byte aligned, lse not 4-byte */
+  FA2_ERR_ALIGN = -5,   /* q, k, v, o or a workspace not 16-byte aligned, lse
+                           not 4-byte */
   FA2_ERR_SCALE = -6,   /* scale is NaN or infinite, or scale * log2(e)
                            overflows fp32 (|scale| above about 2.36e38) */
-  FA2_ERR_ALIAS = -7,   /* o or lse overlaps q, k, v, or each other */
+  FA2_ERR_ALIAS = -7,   /* o, lse or a workspace overlaps q, k, v, or each
+                           other */
   FA2_ERR_HIP = -8,     /* the kernel launch failed (HIP error) */
-  FA2_ERR_OPTION = -9   /* causal is not 0 or 1 */
+  FA2_ERR_OPTION = -9,  /* causal is not 0 or 1, or a split count is out of
+                           range */
+  FA2_ERR_WORKSPACE = -10 /* the key-split workspace is NULL or too small */
 };
 
 /*
@@ -197,6 +203,64 @@ int fa2_fwd_kv_fp8(const void* q, const uint8_t* kq, const float* ks, const uint
                    const float* vs, void* o, float* lse, int64_t B, int64_t Hq, int64_t Hkv,
                    int64_t Nq, int64_t Nk, int64_t d, float scale, int causal, int dtype,
                    void* stream);
+
+/*
+ * fa2_fwd_split -- fa2_fwd_ext with key splits, for calls whose query rows
+ * are too few to fill the GPU (decoding, or a short chunk, against a long
+ * key/value cache: the inference setting of the Colfax "FlashAttention-3 for
+ * Inference" post, title and teaser only).  Each query tile's visible key
+ * tiles are divided into `splits` near-equal parts, each run by its own
+ * workgroup, which leaves an fp32 partial result in `workspace`: O_s, the
+ * output over the part's keys normalised by their own sum, and lse_s, their
+ * logsumexp (-inf for a part with no visible key).  A second kernel on the
+ * same stream merges them into o and lse:
+ *
+ *     m = max_s lse_s,  w_s = exp(lse_s - m),
+ *     o = sum_s w_s O_s / sum_s w_s,   lse = m + ln sum_s w_s,
+ *
+ * which is the softmax over the union of the parts' keys, exactly (up to
+ * rounding), since each part's weights sum to exp(lse_s).  Results match
+ * fa2_fwd_ext up to floating-point rounding (not bit for bit).
+ *
+ *   q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, dtype, stream:
+ *              as in fa2_fwd_ext (16-bit inputs; d = 64, 128 or 256).
+ *   splits   : 1..128 key parts per query tile (a part may get no key tile:
+ *              then it contributes nothing), 1 = fa2_fwd_ext itself, or 0 =
+ *              chosen here: enough parts for one workgroup per compute unit
+ *              of the current device over the call's 128-row query tiles,
+ *              each part keeping at least 8 key tiles (1 if that leaves one
+ *              part).  The choice queries the device's compute-unit count
+ *              (a HIP attribute query, after every argument check except the
+ *              workspace's).
+ *   workspace: device memory of at least fa2_fwd_split_workspace(...) bytes
+ *              for the same arguments, 16-byte aligned, overlapping no
+ *              input or output; unused (may be NULL) when the call runs
+ *              without splits.  The caller owns it; its contents are scratch
+ *              (overwritten, never read before written), and two calls in
+ *              flight at once need two workspaces.
+ *   workspace_bytes: its size in bytes.
+ *
+ * Returns FA2_OK or a negative fa2_status: those of fa2_fwd_ext, and
+ * FA2_ERR_OPTION (splits out of range), FA2_ERR_WORKSPACE (workspace NULL or
+ * smaller than needed), FA2_ERR_ALIGN, FA2_ERR_ALIAS (workspace overlapping
+ * an input or output).  B*Hq*Nq == 0 returns FA2_OK and touches nothing.
+ */
+int fa2_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
+                  float scale, int causal, int dtype, int splits, void* workspace,
+                  int64_t workspace_bytes, void* stream);
+
+/*
+ * fa2_fwd_split_workspace -- bytes of workspace fa2_fwd_split needs for these
+ * arguments: splits * B*Hq*Nq * (d + 1) * 4 (the partial outputs, then the
+ * partial logsumexps), or 0 when the call runs without splits.  With
+ * splits = 0 the count is chosen as fa2_fwd_split chooses it on the current
+ * device.  Returns the byte count (>= 0) or a negative fa2_status for
+ * arguments fa2_fwd_split would reject (shape, head dimension, dtype, causal,
+ * splits).
+ */
+int64_t fa2_fwd_split_workspace(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
+                                int64_t d, int causal, int dtype, int splits);
 
 /* Static description of a status code (never NULL). */
 const char* fa2_strerror(int status);

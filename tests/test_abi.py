@@ -29,7 +29,9 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["fa2_fwd", "fa2_fwd_ext", "fa2_fwd_kv_fp8",
-                                    "fa2_fwd_kv_int8", "fa2_strerror", "fa2_tile_config"]
+                                    "fa2_fwd_kv_int8", "fa2_fwd_split",
+                                    "fa2_fwd_split_workspace", "fa2_strerror",
+                                    "fa2_tile_config"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -49,11 +51,11 @@ def test_race_check_build_exports_the_same_symbols():
 
 def test_strerror_covers_every_status(lib):
     texts = set()
-    for code in range(0, -10, -1):
+    for code in range(0, -11, -1):
         s = fa2.strerror(code)
         assert s and s != "unknown status", code
         texts.add(s)
-    assert len(texts) == 10
+    assert len(texts) == 11
     assert fa2.strerror(17) == "unknown status"
 
 
@@ -183,3 +185,62 @@ def test_int8_host_validation(lib, kw, code):
 def test_int8_empty_output_is_a_no_op(lib, kw):
     assert call_int8(q=0, kq=0, ks=0, vq=0, vs=0, o=0, lse=0, **kw) == fa2.OK
     assert call_int8(raw=fa2.fwd_kv_fp8_raw, q=0, kq=0, ks=0, vq=0, vs=0, o=0, lse=0, **kw) == fa2.OK
+
+
+# fa2_fwd_split: as fa2_fwd_ext plus splits, workspace, workspace_bytes
+SPLIT = dict(EXT, splits=4)
+WS = A + 0x7000000
+
+
+def call_split(ws=WS, ws_bytes=1 << 24, **kw):
+    p = dict(SPLIT)
+    ptrs = dict(q=A, k=A + 0x1000000, v=A + 0x2000000, o=A + 0x3000000, lse=A + 0x4000000)
+    for name in list(kw):
+        if name in ptrs:
+            ptrs[name] = kw.pop(name)
+    p.update(kw)
+    return fa2.fwd_split_raw(ptrs["q"], ptrs["k"], ptrs["v"], ptrs["o"], ptrs["lse"], p["B"],
+                             p["Hq"], p["Hkv"], p["Nq"], p["Nk"], p["d"], p["scale"],
+                             p["causal"], p["dtype"], p["splits"], ws, ws_bytes, 0)
+
+
+def split_bytes():
+    p = SPLIT
+    return fa2.split_workspace_bytes(p["B"], p["Hq"], p["Hkv"], p["Nq"], p["Nk"], p["d"],
+                                     p["causal"], p["dtype"], p["splits"])
+
+
+def test_split_workspace_size(lib):
+    # splits * rows of all heads * (d + 1) fp32 values
+    assert split_bytes() == 4 * (2 * 4 * 100) * 129 * 4
+    assert fa2.split_workspace_bytes(2, 4, 2, 100, 70, 128, True, fa2.BF16, 1) == 0
+    assert fa2.split_workspace_bytes(0, 4, 2, 100, 70, 128, True, fa2.BF16, 9) == 0
+    for kw, code in [(dict(splits=129), fa2.ERR_OPTION), (dict(splits=-1), fa2.ERR_OPTION),
+                     (dict(d=96), fa2.ERR_HEADDIM), (dict(Hkv=3), fa2.ERR_SHAPE),
+                     (dict(dtype=2), fa2.ERR_DTYPE), (dict(causal=2), fa2.ERR_OPTION)]:
+        a = dict(B=2, Hq=4, Hkv=2, Nq=100, Nk=70, d=128, causal=1, dtype=fa2.BF16, splits=4)
+        a.update(kw)
+        assert lib.fa2_fwd_split_workspace(a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["d"],
+                                           a["causal"], a["dtype"], a["splits"]) == code, kw
+    with pytest.raises(fa2.FA2Error) as e:
+        fa2.split_workspace_bytes(2, 4, 2, 100, 70, 96)
+    assert e.value.code == fa2.ERR_HEADDIM
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(splits=129), fa2.ERR_OPTION), (dict(splits=-3), fa2.ERR_OPTION),
+    (dict(ws=0), fa2.ERR_WORKSPACE), (dict(ws_bytes=4 * 800 * 129 * 4 - 1), fa2.ERR_WORKSPACE),
+    (dict(ws=WS + 8), fa2.ERR_ALIGN),
+    (dict(ws=A + 0x3000000 + 256), fa2.ERR_ALIAS),    # workspace over o
+    (dict(ws=A + 0x1000000), fa2.ERR_ALIAS),          # workspace over k
+    (dict(ws=A + 0x4000000 - 64), fa2.ERR_ALIAS),     # workspace over lse
+    (dict(q=0), fa2.ERR_NULL), (dict(d=32), fa2.ERR_HEADDIM), (dict(causal=3), fa2.ERR_OPTION),
+    (dict(scale=float("nan")), fa2.ERR_SCALE), (dict(Hkv=3), fa2.ERR_SHAPE),
+])
+def test_split_host_validation(lib, kw, code):
+    assert call_split(**kw) == code
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(Hq=0, Hkv=0), dict(Nq=0)])
+def test_split_empty_output_is_a_no_op(lib, kw):
+    assert call_split(q=0, k=0, v=0, o=0, lse=0, ws=0, ws_bytes=0, **kw) == fa2.OK

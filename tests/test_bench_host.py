@@ -21,7 +21,10 @@ def test_headline_roofline_is_the_matrix_core_roof():
     assert r["frac"] == pytest.approx(r["achieved"] / 2516.6, abs=1e-4)
 
 
-@pytest.mark.parametrize("name", ["sweep_n512", "gqa_chunk", "tiny"])
+HBM_BOUND = ("sweep_n512", "gqa_chunk", "tiny", "decode", "decode_long")
+
+
+@pytest.mark.parametrize("name", HBM_BOUND)
 def test_short_workloads_sit_under_the_hbm_roof(name):
     """Arithmetic intensity below 2516.6 TFLOP/s / 8 TB/s = 315 FLOP/B."""
     w = WORKLOADS[name]
@@ -34,7 +37,7 @@ def test_short_workloads_sit_under_the_hbm_roof(name):
 
 def test_every_other_workload_is_matrix_bound():
     for name, w in WORKLOADS.items():
-        if name in ("sweep_n512", "gqa_chunk", "tiny"):
+        if name in HBM_BOUND:
             continue
         assert bench.roofline_of(w, 1.0, None)["bound"] == "mfma", name
 

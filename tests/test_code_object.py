@@ -23,7 +23,7 @@ OBJDUMP = os.path.join(LLVM, "llvm-objdump")
 READELF = os.path.join(LLVM, "llvm-readelf")
 LDS_LIMIT = 160 * 1024
 
-NAME = re.compile(r"fa2_fwd_kernelILi(\d+)ELb(\d)ELi(\d)ELb(\d)ELi(\d)ELb(\d)ELb(\d)E")
+NAME = re.compile(r"fa2_fwd_kernelILi(\d+)ELb(\d)ELi(\d)ELb(\d)ELi(\d)ELb(\d)ELb(\d)ELb(\d)E")
 
 
 def field(entry, key):
@@ -55,8 +55,8 @@ def kernels():
         m = NAME.search(name)
         if not m:
             continue
-        d, fp16, mode, causal, q8, short, persist = (int(x) for x in m.groups())
-        out[(d, fp16, mode, causal, q8, short, persist)] = {
+        d, fp16, mode, causal, q8, short, persist, split = (int(x) for x in m.groups())
+        out[(d, fp16, mode, causal, q8, short, persist, split)] = {
             "agpr": int(entry.split("\n", 1)[0].strip()),
             "vgpr": field(entry, "vgpr_count"),
             "vgpr_spill": field(entry, "vgpr_spill_count"),
@@ -67,13 +67,15 @@ def kernels():
 
 
 def test_every_kernel_is_present(kernels):
-    # per (d, cache (0 none, 1 INT8, 2 FP8), half-height, persistent): 2 dtypes
-    # x 3 scale-sign modes, with and without the mask
-    families = {(64, 0, 0, 0): 12, (64, 0, 0, 1): 6, (128, 0, 0, 0): 12, (128, 0, 1, 0): 12,
-                (128, 0, 0, 1): 12, (128, 1, 0, 0): 12, (128, 2, 0, 0): 12, (256, 0, 0, 0): 12}
+    # per (d, cache (0 none, 1 INT8, 2 FP8), half-height, persistent, key
+    # splits): 2 dtypes x 3 scale-sign modes, with and without the mask
+    families = {(64, 0, 0, 0, 0): 12, (64, 0, 0, 1, 0): 6, (128, 0, 0, 0, 0): 12,
+                (128, 0, 1, 0, 0): 12, (128, 0, 0, 1, 0): 12, (128, 1, 0, 0, 0): 12,
+                (128, 2, 0, 0, 0): 12, (256, 0, 0, 0, 0): 12,
+                (64, 0, 0, 0, 1): 12, (128, 0, 1, 0, 1): 12, (256, 0, 0, 0, 1): 12}
     count = {}
-    for (d, fp16, mode, causal, q8, short, persist) in kernels:
-        key = (d, q8, short, persist)
+    for (d, fp16, mode, causal, q8, short, persist, split) in kernels:
+        key = (d, q8, short, persist, split)
         count[key] = count.get(key, 0) + 1
     assert count == families
 

@@ -1,5 +1,6 @@
-"""The entry points allocate nothing and enqueue one kernel each, so they can
-be captured in a HIP graph.  Each test captures a call with preallocated
+"""The entry points allocate nothing and enqueue one kernel each (two with
+key splits: the split kernel and the merge), so they can be captured in a
+HIP graph.  Each test captures a call with preallocated
 outputs, replays the graph several times with eager GPU work and host
 synchronisation in between, and checks every replay bit for bit against the
 eager result (needs an MI355X)."""
@@ -66,4 +67,17 @@ def test_graph_fwd_kv_fp8():
     o_ref, lse_ref = fa2.fwd_kv_fp8(*inputs, causal=True)
     o, lse = torch.empty_like(o_ref), torch.empty_like(lse_ref)
     replay_and_check(lambda o, lse: fa2.fwd_kv_fp8(*inputs, causal=True, out=o, lse=lse),
+                     o_ref, lse_ref, o, lse)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_graph_fwd_split(d):
+    announce("graph fwd_split", d)
+    q, k, v = (t.to(DEV) for t in make_inputs(2, 8, 2, d, "bf16", seed=6, Hkv=2, Nk=4000))
+    ws = torch.empty(fa2.split_workspace_bytes(2, 8, 2, 2, 4000, d, True, fa2.BF16, 6),
+                     dtype=torch.uint8, device=DEV)
+    o_ref, lse_ref = fa2.fwd_split(q, k, v, causal=True, splits=6, workspace=ws)
+    o, lse = torch.empty_like(o_ref), torch.empty_like(lse_ref)
+    replay_and_check(lambda o, lse: fa2.fwd_split(q, k, v, causal=True, splits=6, workspace=ws,
+                                                  out=o, lse=lse),
                      o_ref, lse_ref, o, lse)

@@ -1,8 +1,8 @@
 """GPU parity at the full workload sizes, every row compared (needs an MI355X).
 
 Each workload that bench.py can time runs here in the same launch
-configuration (``fa2.fwd`` / ``fa2.fwd_kv_int8`` / ``fa2.fwd_kv_fp8`` into
-preallocated outputs on
+configuration (``fa2.fwd`` / ``fa2.fwd_kv_int8`` / ``fa2.fwd_kv_fp8`` /
+``fa2.fwd_split`` into preallocated outputs on
 the current stream), with O and LSE prefilled with NaN so that an unwritten
 row or a wrongly placed query tile cannot pass.  The output is then compared
 with the fp64 oracle element by element:
@@ -10,7 +10,8 @@ with the fp64 oracle element by element:
 * every (b, h) and every query row for the headline, the softmax-stress and
   tiny workloads, the head-dimension variants (d = 64, d = 256), the
   sequence sweep at N = 512, 1024, 2048 and 4096, and the widened workloads
-  (causal, grouped heads, KV cache, prefill chunk, INT8 and FP8 caches);
+  (causal, grouped heads, KV cache, prefill chunk, INT8 and FP8 caches,
+  decoding with key splits);
 * for the sweep at N = 8192 (B = 2) and N = 16384 (B = 1), where the oracle
   would take minutes for every head, all rows of the fixed (b, h) pairs in
   ``HEAD_SUBSETS``; every other head is still checked for being fully
@@ -45,7 +46,7 @@ HEAD_SUBSETS = {
 FULL = ["tiny", "stress", "headline", "d64", "d256",
         "sweep_n512", "sweep_n1024", "sweep_n2048", "sweep_n4096",
         "causal", "gqa", "kv_cache", "gqa_chunk", "int8_kv", "int8_kv_causal",
-        "fp8_kv", "fp8_kv_causal"]
+        "fp8_kv", "fp8_kv_causal", "decode", "decode_long"]
 
 
 def announce(*what):
@@ -60,6 +61,8 @@ def run_like_bench(w, inputs):
     if w.quantized:
         fwd = fa2.fwd_kv_int8 if w.kv_int8 else fa2.fwd_kv_fp8
         fwd(*dev_in, scale=w.scale, causal=w.causal, out=o, lse=lse)
+    elif w.split:
+        fa2.fwd_split(*dev_in, scale=w.scale, causal=w.causal, splits=0, out=o, lse=lse)
     else:
         fa2.fwd(*dev_in, scale=w.scale, causal=w.causal, out=o, lse=lse)
     torch.cuda.synchronize()
@@ -111,6 +114,7 @@ def test_workload_every_row(name):
     # The FP8 matrix instruction truncates its products (see
     # test_parity_gpu_fp8.py), which moves a logit by up to about 1e-4: an
     # absolute floor for the causal rows whose logsumexp lies near zero.
+    # Split and unsplit runs share the 16-bit tolerances otherwise.
     assert_parity(o64, lse64, o_ref, lse_ref, "%s every row%s" % (
         name, "" if heads is None else " of (b, h) in %s" % (heads,)),
         lse_abs=1e-3 if w.kv_fp8 else None)

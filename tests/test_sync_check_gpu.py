@@ -8,7 +8,8 @@ the next iteration as the key/value ring does.  The arithmetic and its order
 are the same, so any difference in O or LSE would mean the production
 pipeline read a tile before it landed or overwrote one still in use.  Each
 case covers one kernel family: persistent, one item per workgroup, causal,
-short keys, each head dimension, grouped heads, and the INT8 and FP8 caches.
+short keys, each head dimension, grouped heads, the INT8 and FP8 caches, and
+key splits.
 """
 import math
 
@@ -110,3 +111,24 @@ def test_quantized_cache_matches_race_check_build(fmt, causal):
         torch.cuda.synchronize()
         outs.append((o.cpu(), lse.cpu()))
     assert_same(outs, "%s causal=%d" % (fmt, causal))
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("causal", [False, True])
+def test_key_splits_match_race_check_build(d, causal):
+    announce("split", d, causal)
+    B, Hq, Hkv, Nq, Nk, splits = 2, 8, 2, 3, 6000, 7
+    q, k, v = (t.to(DEV) for t in make_inputs(B, Hq, Nq, d, "fp16", "normal", 8, Hkv, Nk))
+    nbytes = fa2.split_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, causal, fa2.FP16, splits)
+    outs = []
+    for handle in (fa2.lib(), sync_lib()):
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+        o = torch.full_like(q, float("nan"))
+        lse = torch.full((B, Hq, Nq), float("nan"), device=DEV)
+        code = handle.fa2_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                    lse.data_ptr(), B, Hq, Hkv, Nq, Nk, d, 1.0 / math.sqrt(d),
+                                    int(causal), fa2.FP16, splits, ws.data_ptr(), nbytes, 0)
+        assert code == 0, fa2.strerror(code)
+        torch.cuda.synchronize()
+        outs.append((o.cpu(), lse.cpu()))
+    assert_same(outs, "split d=%d causal=%d" % (d, causal))
