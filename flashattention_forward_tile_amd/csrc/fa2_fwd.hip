@@ -1527,6 +1527,28 @@ int cu_count() {
   return n;
 }
 
+// The fixed scratch of fa2_fwd_split_noalloc (key-split partials for
+// callers that cannot allocate): one array per device, held until the
+// process ends.  Host code never uses the array's name as an address (on the
+// host it only names the symbol): scratch_ptr() looks up each device's copy
+// once, with that device current, and every use goes through that pointer.
+constexpr int64_t kScratchBytes = (int64_t)16 << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+// This device's scratch address (nullptr if the lookup fails), cached per
+// device; threads that race on a first lookup store the same value.
+void* scratch_ptr() {
+  static std::atomic<void*> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  void* p = cache[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    cache[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   if (na == 0 || nb == 0) return false;
   const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
@@ -1550,6 +1572,7 @@ const char* fa2_strerror(int status) {
     case FA2_ERR_HIP: return "kernel launch failed";
     case FA2_ERR_OPTION: return "causal must be 0 or 1, and a split count 0 to 128";
     case FA2_ERR_WORKSPACE: return "the key-split workspace is NULL or too small";
+    case FA2_ERR_SCRATCH: return "the key-split partials exceed the 16 MiB fixed scratch";
     default: return "unknown status";
   }
 }
@@ -1878,6 +1901,22 @@ int64_t fa2_fwd_split_workspace(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, 
   const int sc = fa2::check_split(B, Hq, Hkv, Nq, Nk, d, splits, &plan);
   if (sc != FA2_OK) return sc;
   return plan.bytes;
+}
+
+int fa2_fwd_split_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
+                          int64_t d, float scale, int causal, int dtype, int splits,
+                          void* stream) {
+  const int64_t need = fa2_fwd_split_workspace(B, Hq, Hkv, Nq, Nk, d, causal, dtype, splits);
+  if (need < 0) return (int)need;
+  if (need > fa2::kScratchBytes) return FA2_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (need > 0) {
+    ws = fa2::scratch_ptr();
+    if (ws == nullptr) return FA2_ERR_HIP;
+  }
+  return fa2::launch(q, k, v, nullptr, nullptr, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal,
+                     dtype, stream, 0, splits, ws, fa2::kScratchBytes);
 }
 
 int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse,

@@ -24,6 +24,7 @@ ERR_ALIAS = -7
 ERR_HIP = -8
 ERR_OPTION = -9
 ERR_WORKSPACE = -10
+ERR_SCRATCH = -11
 
 BF16 = 0
 FP16 = 1
@@ -61,6 +62,12 @@ _SIGNATURES = {
     "fa2_fwd_split_workspace": (ctypes.c_int64, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                                  ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                                  ctypes.c_int, ctypes.c_int, ctypes.c_int]),
+    "fa2_fwd_split_noalloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                             ctypes.c_int64, ctypes.c_float, ctypes.c_int,
+                                             ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
     "fa2_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "fa2_tile_config": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int,
                                        ctypes.POINTER(ctypes.c_int),

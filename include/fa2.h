@@ -60,7 +60,9 @@ enum fa2_status {
   FA2_ERR_HIP = -8,     /* the kernel launch failed (HIP error) */
   FA2_ERR_OPTION = -9,  /* causal is not 0 or 1, or a split count is out of
                            range */
-  FA2_ERR_WORKSPACE = -10 /* the key-split workspace is NULL or too small */
+  FA2_ERR_WORKSPACE = -10, /* the key-split workspace is NULL or too small */
+  FA2_ERR_SCRATCH = -11   /* fa2_fwd_split_noalloc: the partials would exceed
+                             its 16 MiB fixed scratch */
 };
 
 /*
@@ -261,6 +263,32 @@ int fa2_fwd_split(const void* q, const void* k, const void* v, void* o, float* l
  */
 int64_t fa2_fwd_split_workspace(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
                                 int64_t d, int causal, int dtype, int splits);
+
+/*
+ * fa2_fwd_split_noalloc -- fa2_fwd_split for callers that cannot allocate
+ * device memory, not even a workspace to pass in (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation).  The
+ * partials go to a fixed scratch array of 16 MiB in the library's device
+ * memory, one per GPU, held until the process ends; the call allocates
+ * nothing.  Its first call on a device (with that device current) looks up
+ * that device's array.
+ *
+ *   Arguments as in fa2_fwd_split, without workspace and workspace_bytes.
+ *   A call whose partials (fa2_fwd_split_workspace bytes for the same
+ *   arguments) exceed 16 MiB returns FA2_ERR_SCRATCH and launches nothing;
+ *   e.g. with d = 128 that is splits * B*Hq*Nq above 32768 rows.
+ *
+ * Every call on one GPU shares that GPU's array, and a call only writes
+ * partials before reading them (nothing needs to start at zero), so calls
+ * in sequence on one stream are safe; calls that overlap in time on one GPU
+ * (other streams, other host threads) race on the array and may corrupt
+ * each other's results.  Returns the codes of fa2_fwd_split, FA2_ERR_SCRATCH,
+ * or FA2_ERR_HIP if the array's address cannot be looked up.
+ */
+int fa2_fwd_split_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
+                          int64_t d, float scale, int causal, int dtype, int splits,
+                          void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* fa2_strerror(int status);

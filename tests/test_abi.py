@@ -30,8 +30,8 @@ def lib():
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["fa2_fwd", "fa2_fwd_ext", "fa2_fwd_kv_fp8",
                                     "fa2_fwd_kv_int8", "fa2_fwd_split",
-                                    "fa2_fwd_split_workspace", "fa2_strerror",
-                                    "fa2_tile_config"]
+                                    "fa2_fwd_split_noalloc", "fa2_fwd_split_workspace",
+                                    "fa2_strerror", "fa2_tile_config"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -51,11 +51,11 @@ def test_race_check_build_exports_the_same_symbols():
 
 def test_strerror_covers_every_status(lib):
     texts = set()
-    for code in range(0, -11, -1):
+    for code in range(0, -12, -1):
         s = fa2.strerror(code)
         assert s and s != "unknown status", code
         texts.add(s)
-    assert len(texts) == 11
+    assert len(texts) == 12
     assert fa2.strerror(17) == "unknown status"
 
 
