@@ -20,8 +20,8 @@ on this host's cores.
 
 With the headline workload (the default) the same run then times the
 sequence sweep (N = 512 ... 16384 at B*N = 16384, fp16), the head-dimension
-variants (d = 64, 256) and two decoding workloads with key splits (one query
-row per head against 32K and 128K keys) with the same --warmup / --steps, and
+variants (d = 64, 256) and four decoding workloads with key splits (one query
+row per head against 32K and 128K keys, and 32K over INT8 and FP8 caches) with the same --warmup / --steps, and
 adds them to the line as "sweep" (per N, plus the harmonic mean), "head_dim"
 and "decode", each with its roofline fraction (--no-extras leaves them out).  Every output is checked
 after the timing (NaN-prefilled buffers fully written with finite values, and
@@ -62,7 +62,7 @@ SWEEP = ["sweep_n512", "sweep_n1024", "sweep_n2048", "sweep_n4096", "sweep_n8192
          "sweep_n16384"]
 HEAD_DIMS = ["d64", "d256"]
 # ... and decoding against long caches with key splits (fa2_fwd_split).
-DECODE = ["decode", "decode_long"]
+DECODE = ["decode", "decode_long", "decode_int8", "decode_fp8"]
 KERNEL_SRC = os.path.join(ROOT, "flashattention_forward_tile_amd", "csrc", "fa2_fwd.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa2_fwd_headline_traffic.json")
 CPU_SAMPLE_SECONDS = 12.0
@@ -350,7 +350,15 @@ class Resident:
         self.dev_in = [t.to(dev) for t in self.inputs]
         self.o = torch.full_like(self.dev_in[0], float("nan"))
         self.lse = torch.full((w.B, w.H, w.N), float("nan"), dtype=torch.float32, device=dev)
-        if w.quantized:
+        if w.quantized and w.split:
+            cache = fa2.CACHE_INT8 if w.kv_int8 else fa2.CACHE_FP8
+            nbytes = fa2.split_workspace_bytes(w.B, w.H, w.kv_heads, w.N, w.keys, w.d, w.causal,
+                                               self.dev_in[0].dtype, 0, cache)
+            self.ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+            self.launch = lambda: fa2.fwd_kv_split(*self.dev_in, cache, scale=w.scale,
+                                                   causal=w.causal, splits=0, workspace=self.ws,
+                                                   out=self.o, lse=self.lse)
+        elif w.quantized:
             fwd = fa2.fwd_kv_int8 if w.kv_int8 else fa2.fwd_kv_fp8
             self.launch = lambda: fwd(*self.dev_in, scale=w.scale, causal=w.causal,
                                       out=self.o, lse=self.lse)

@@ -245,6 +245,10 @@ template <> struct Cfg<256> { static constexpr int BC = 32, NW = 8, QB = 1, OCC 
 // Tile shape of the INT8 key/value cache kernels (d = 128 only).
 template <int D> struct Cfg8;
 template <> struct Cfg8<128> { static constexpr int BC = 32, NW = 8, QB = 1, OCC = 2, SGB = 0, RING = 4, PK = 2, PV = 2, MS = 32; };
+// The quantized caches with key splits: 128-row tiles (four waves), as the
+// 16-bit split kernels, so that decoding forms one tile per K/V head.
+template <int D> struct Cfg8S;
+template <> struct Cfg8S<128> { static constexpr int BC = 32, NW = 4, QB = 1, OCC = 2, SGB = 0, RING = 4, PK = 2, PV = 2, MS = 32; };
 // Short key sequences at d = 128 (at most kShortKeys keys): half the query
 // rows per workgroup, so two workgroups share a CU and one's prologue and
 // epilogue overlap the other's loop.  The same shape serves grids too small
@@ -259,7 +263,8 @@ template <int D> struct CfgP : Cfg<D> {};
 template <> struct CfgP<64> { static constexpr int BC = 64, NW = 8, QB = 1, OCC = 2, SGB = 1, RING = 4, PK = 4, PV = 2, MS = 32; };
 template <int D, bool Q8, bool SHORT, bool PERSIST>
 using KCfg = std::conditional_t<
-    Q8, Cfg8<D>, std::conditional_t<SHORT, CfgS<D>, std::conditional_t<PERSIST, CfgP<D>, Cfg<D>>>>;
+    Q8, std::conditional_t<SHORT, Cfg8S<D>, Cfg8<D>>,
+    std::conditional_t<SHORT, CfgS<D>, std::conditional_t<PERSIST, CfgP<D>, Cfg<D>>>>;
 // Ring slots and loop phases as compile-time constants.
 template <int X> using Ic = std::integral_constant<int, X>;
 
@@ -332,7 +337,7 @@ struct SplitProblem : Problem {
 // product (see the header of fa2.h for the schemes).
 // PERSIST: one workgroup per CU walks several (K/V head, query tile) items,
 // and the key/value ring runs on from one item into the next (see below).
-// SPLIT: key splits (see Problem); non-persistent 16-bit kernels only.
+// SPLIT: key splits (see SplitProblem); non-persistent kernels only.
 template <int D, bool FP16, int MODE, bool CAUSAL, int QK, bool SHORT, bool PERSIST, bool SPLIT>
 __global__ void __attribute__((amdgpu_flat_work_group_size(KCfg<D, QK != 0, SHORT, PERSIST>::NW * 64,
                                                            KCfg<D, QK != 0, SHORT, PERSIST>::NW * 64),
@@ -409,7 +414,7 @@ fa2_fwd_kernel(const std::conditional_t<SPLIT, SplitProblem, Problem> P) {
   // the ring.
   constexpr int QTB = BR * RB;  // one query tile
   static_assert(!PERSIST || (!Q8 && QB == 1), "persistent kernels");
-  static_assert(!SPLIT || (!PERSIST && !Q8), "key splits");
+  static_assert(!SPLIT || !PERSIST, "key splits");
   constexpr int QOBASE = PERSIST ? RING_BYTES : 0;
   constexpr int QOBYTES = QTB > OBYTES ? QTB : OBYTES;
   __shared__ __attribute__((aligned(16)))
@@ -1340,8 +1345,13 @@ fa2_fwd_kernel(const std::conditional_t<SPLIT, SplitProblem, Problem> P) {
 #pragma unroll
           for (int g4 = 0; g4 < NACC / 4; ++g4) {
             const int ch = db * MS + g4 * 8 + lg * 4;
-            const float4 v = {acc[b][db][g4 * 4] * inv, acc[b][db][g4 * 4 + 1] * inv,
-                              acc[b][db][g4 * 4 + 2] * inv, acc[b][db][g4 * 4 + 3] * inv};
+            float vsc[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+            if constexpr (Q8) {  // the per-channel value scales of the quantized cache
+              const float4 f = *(const float4*)(P.vs + (int64_t)bh * D + ch);
+              vsc[0] = f.x; vsc[1] = f.y; vsc[2] = f.z; vsc[3] = f.w;
+            }
+            const float4 v = {acc[b][db][g4 * 4] * vsc[0] * inv, acc[b][db][g4 * 4 + 1] * vsc[1] * inv,
+                              acc[b][db][g4 * 4 + 2] * vsc[2] * inv, acc[b][db][g4 * 4 + 3] * vsc[3] * inv};
             *(float4*)(po + ch) = v;
           }
         if (lg == 0)
@@ -1505,6 +1515,26 @@ const void* pick_split_mode(int mode) {
   }
 }
 
+// Quantized caches (QK 1: INT8, 2: FP8), d = 128, 128-row tiles.
+template <int QK, bool FP16, bool CAUSAL>
+const void* pick_split_q8_mode(int mode) {
+  switch (mode) {
+    case kNegative: return (const void*)fa2_fwd_kernel<128, FP16, kNegative, CAUSAL, QK, true, false, true>;
+    case kZero: return (const void*)fa2_fwd_kernel<128, FP16, kZero, CAUSAL, QK, true, false, true>;
+    default: return (const void*)fa2_fwd_kernel<128, FP16, kPositive, CAUSAL, QK, true, false, true>;
+  }
+}
+
+template <int QK>
+const void* pick_split_q8(bool fp16, int mode, bool causal) {
+  if (fp16)
+    return causal ? pick_split_q8_mode<QK, true, true>(mode) : pick_split_q8_mode<QK, true, false>(mode);
+  return causal ? pick_split_q8_mode<QK, false, true>(mode) : pick_split_q8_mode<QK, false, false>(mode);
+}
+static_assert(kSplitRows<128> == Cfg8S<128>::NW * Cfg8S<128>::MS * Cfg8S<128>::QB &&
+                  kSplitKeys<128> == Cfg8S<128>::BC,
+              "the quantized split kernels share the d = 128 split plan");
+
 template <int D>
 const void* pick_split(bool fp16, int mode, bool causal) {
   if (fp16)
@@ -1595,19 +1625,21 @@ namespace fa2 {
 
 // The key-split plan of a call whose shape has passed validation: the split
 // count (splits = 0: enough splits for one workgroup per CU over the call's
-// query tiles, each split keeping at least 8 key tiles, at most kMaxSplits;
-// 1 when that leaves a single split), the query tiles per K/V head and the
-// workspace bytes (0 without splits).  One workgroup per CU measured best
-// for decoding shapes (one to 128 query rows per K/V head, 8K to 128K keys,
-// d = 64 to 256: 4.8-5.6 TB/s of K/V reads); more splits only add partials
-// to write and merge.
+// query tiles, two with a quantized cache (qk != 0), each split keeping at
+// least 8 key tiles, at most kMaxSplits; 1 when that leaves a single
+// split), the query tiles per K/V head and the workspace bytes (0 without
+// splits).  Those targets measured best for decoding shapes (one to 128
+// query rows per K/V head, 8K to 128K keys: 4.8-5.6 TB/s of 16-bit K/V reads
+// at d = 64 to 256, 3.0-4.4 TB/s of INT8 / FP8 codes, whose kernels also
+// widen V and quantize the query); more splits only add partials to write
+// and merge.
 struct SplitPlan {
   int splits;
   int64_t q_tiles;
   int64_t bytes;
 };
 SplitPlan plan_split(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
-                     int splits) {
+                     int qk, int splits) {
   const int64_t rows = Hq / Hkv * Nq;
   const int64_t br = d == 64 ? kSplitRows<64> : d == 128 ? kSplitRows<128> : kSplitRows<256>;
   const int64_t bc = d == 64 ? kSplitKeys<64> : d == 128 ? kSplitKeys<128> : kSplitKeys<256>;
@@ -1617,7 +1649,8 @@ SplitPlan plan_split(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
     const int64_t items = B * Hkv * p.q_tiles;
     const int64_t cus = cu_count();
     const int64_t k_tiles = (Nk + bc - 1) / bc;
-    int64_t want = cus > 0 ? (cus + items - 1) / items : 1;
+    const int64_t per_cu = qk != 0 ? 2 : 1;
+    int64_t want = cus > 0 ? (per_cu * cus + items - 1) / items : 1;
     want = want < k_tiles / 8 ? want : k_tiles / 8;
     want = want < kMaxSplits ? want : kMaxSplits;
     splits = (int)(want > 1 ? want : 1);
@@ -1659,9 +1692,9 @@ int check_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int6
 // The split plan of a call that passed check_shape, with its own limits:
 // the split count in range, the grids of both kernels within a 1-D grid.
 int check_split(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
-                int splits, SplitPlan* plan) {
+                int qk, int splits, SplitPlan* plan) {
   if (splits < 0 || splits > kMaxSplits) return FA2_ERR_OPTION;
-  *plan = plan_split(B, Hq, Hkv, Nq, Nk, d, splits);
+  *plan = plan_split(B, Hq, Hkv, Nq, Nk, d, qk, splits);
   if (plan->splits == 1) return FA2_OK;
   const int64_t grid_max = ((int64_t)1 << 31) - 1;
   if (B * Hkv * plan->q_tiles > grid_max / plan->splits) return FA2_ERR_SHAPE;
@@ -1683,7 +1716,7 @@ int launch(const void* q, const void* k, const void* v, const float* ks, const f
   // logits in log2 units: t = s * scale * log2(e), which must stay finite
   const float c = (float)((double)scale * 1.4426950408889634074);
   if (!__builtin_isfinite(scale) || !__builtin_isfinite(c)) return FA2_ERR_SCALE;
-  if (splits < 0 || splits > kMaxSplits || (q8 && splits != 1)) return FA2_ERR_OPTION;
+  if (splits < 0 || splits > kMaxSplits) return FA2_ERR_OPTION;
   if (shape == 1) return FA2_OK;  // no output rows
   const int64_t rows = Hq / Hkv * Nq;  // query rows per K/V head
   const int64_t bh = B * Hq;
@@ -1708,7 +1741,7 @@ int launch(const void* q, const void* k, const void* v, const float* ks, const f
   // the workspace it needs.
   SplitPlan plan;
   if (splits != 1) {
-    const int sc = check_split(B, Hq, Hkv, Nq, Nk, d, splits, &plan);
+    const int sc = check_split(B, Hq, Hkv, Nq, Nk, d, qk, splits, &plan);
     if (sc != FA2_OK) return sc;
     splits = plan.splits;
   }
@@ -1804,11 +1837,14 @@ int launch(const void* q, const void* k, const void* v, const float* ks, const f
     SP.part_o = (float*)ws;
     SP.part_lse = (float*)ws + (int64_t)splits * SP.part_rows * d;
     SP.splits = splits;
-    const void* sfn = d == 64 ? pick_split<64>(fp16, mode, causal)
+    const void* sfn = qk == 2 ? pick_split_q8<2>(fp16, mode, causal)
+                    : qk == 1 ? pick_split_q8<1>(fp16, mode, causal)
+                    : d == 64 ? pick_split<64>(fp16, mode, causal)
                     : d == 128 ? pick_split<128>(fp16, mode, causal)
                                : pick_split<256>(fp16, mode, causal);
-    const int snw = d == 64 ? SplitCfg<64>::C::NW : d == 128 ? SplitCfg<128>::C::NW
-                                                              : SplitCfg<256>::C::NW;
+    const int snw = q8 ? Cfg8S<128>::NW
+                  : d == 64 ? SplitCfg<64>::C::NW : d == 128 ? SplitCfg<128>::C::NW
+                                                             : SplitCfg<256>::C::NW;
     void* sargs[] = {&SP};
     hipError_t err = hipLaunchKernel(sfn, dim3((unsigned)SP.n_groups),
                                      dim3((unsigned)(snw * 64)), sargs, 0, (hipStream_t)stream);
@@ -1892,22 +1928,34 @@ int fa2_fwd_split(const void* q, const void* k, const void* v, void* o, float* l
 }
 
 int64_t fa2_fwd_split_workspace(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
-                                int64_t d, int causal, int dtype, int splits) {
-  const int shape = fa2::check_shape(B, Hq, Hkv, Nq, Nk, d, causal, dtype, false);
+                                int64_t d, int causal, int dtype, int cache, int splits) {
+  if (cache != 0 && cache != FA2_CACHE_INT8 && cache != FA2_CACHE_FP8) return FA2_ERR_OPTION;
+  const int shape = fa2::check_shape(B, Hq, Hkv, Nq, Nk, d, causal, dtype, cache != 0);
   if (shape < 0) return shape;
   if (splits < 0 || splits > fa2::kMaxSplits) return FA2_ERR_OPTION;
   if (shape == 1 || splits == 1) return 0;
   fa2::SplitPlan plan;
-  const int sc = fa2::check_split(B, Hq, Hkv, Nq, Nk, d, splits, &plan);
+  const int sc = fa2::check_split(B, Hq, Hkv, Nq, Nk, d, cache, splits, &plan);
   if (sc != FA2_OK) return sc;
   return plan.bytes;
+}
+
+int fa2_fwd_kv_split(const void* q, const void* kq, const float* ks, const void* vq,
+                     const float* vs, void* o, float* lse, int64_t B, int64_t Hq, int64_t Hkv,
+                     int64_t Nq, int64_t Nk, int64_t d, float scale, int causal, int dtype,
+                     int cache, int splits, void* workspace, int64_t workspace_bytes,
+                     void* stream) {
+  if (cache != FA2_CACHE_INT8 && cache != FA2_CACHE_FP8) return FA2_ERR_OPTION;
+  return fa2::launch(q, kq, vq, ks, vs, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, dtype,
+                     stream, cache == FA2_CACHE_INT8 ? 1 : 2, splits, workspace,
+                     workspace_bytes);
 }
 
 int fa2_fwd_split_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
                           int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
                           int64_t d, float scale, int causal, int dtype, int splits,
                           void* stream) {
-  const int64_t need = fa2_fwd_split_workspace(B, Hq, Hkv, Nq, Nk, d, causal, dtype, splits);
+  const int64_t need = fa2_fwd_split_workspace(B, Hq, Hkv, Nq, Nk, d, causal, dtype, 0, splits);
   if (need < 0) return (int)need;
   if (need > fa2::kScratchBytes) return FA2_ERR_SCRATCH;
   void* ws = nullptr;

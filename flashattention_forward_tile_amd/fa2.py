@@ -28,6 +28,8 @@ ERR_SCRATCH = -11
 
 BF16 = 0
 FP16 = 1
+CACHE_INT8 = 1
+CACHE_FP8 = 2
 _DTYPE = {torch.bfloat16: BF16, torch.float16: FP16}
 
 # Entry points declared in include/fa2.h, with their ctypes signatures.
@@ -61,7 +63,15 @@ _SIGNATURES = {
                                      ctypes.c_int64, ctypes.c_void_p]),
     "fa2_fwd_split_workspace": (ctypes.c_int64, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                                  ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
-                                                 ctypes.c_int, ctypes.c_int, ctypes.c_int]),
+                                                 ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                 ctypes.c_int]),
+    "fa2_fwd_kv_split": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                        ctypes.c_int64, ctypes.c_float, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]),
     "fa2_fwd_split_noalloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p,
                                              ctypes.c_void_p, ctypes.c_void_p,
                                              ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
@@ -145,12 +155,14 @@ def fwd_split_raw(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, Hq, Hkv, Nq, Nk, d, sc
                                int(ws_bytes), stream)
 
 
-def split_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, causal=False, dtype=BF16, splits=0) -> int:
-    """fa2_fwd_split_workspace: workspace bytes for these arguments (0: the call
-    runs without splits); raises FA2Error for arguments it rejects."""
+def split_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, causal=False, dtype=BF16, splits=0,
+                          cache=0) -> int:
+    """fa2_fwd_split_workspace: workspace bytes for these arguments (cache 0:
+    fwd_split, CACHE_INT8 / CACHE_FP8: fwd_kv_split; 0 bytes: the call runs
+    without splits); raises FA2Error for arguments it rejects."""
     code_dtype = _DTYPE.get(dtype, -1) if isinstance(dtype, torch.dtype) else int(dtype)
     n = lib().fa2_fwd_split_workspace(B, Hq, Hkv, Nq, Nk, d, 1 if causal else 0, code_dtype,
-                                      int(splits))
+                                      int(cache), int(splits))
     if n < 0:
         raise FA2Error(int(n))
     return int(n)
@@ -319,3 +331,40 @@ def fwd_split(q, k, v, scale=None, causal=False, splits=0, workspace=None, out=N
     if code != OK:
         raise FA2Error(code)
     return out, lse
+
+
+def fwd_kv_split_raw(q_ptr, kq_ptr, ks_ptr, vq_ptr, vs_ptr, o_ptr, lse_ptr, B, Hq, Hkv, Nq, Nk,
+                     d, scale, causal, dtype, cache, splits, ws_ptr, ws_bytes, stream=0) -> int:
+    """Direct call of fa2_fwd_kv_split with integer pointers; returns the status."""
+    return lib().fa2_fwd_kv_split(q_ptr, kq_ptr, ks_ptr, vq_ptr, vs_ptr, o_ptr, lse_ptr, B, Hq,
+                                  Hkv, Nq, Nk, d, float(scale), int(causal), int(dtype),
+                                  int(cache), int(splits), ws_ptr, int(ws_bytes), stream)
+
+
+def fwd_kv_split(q, kq, ks, vq, vs, cache, scale=None, causal=False, splits=0, workspace=None,
+                 out=None, lse=None):
+    """Key splits over a quantized cache (fa2_fwd_kv_split): returns (o, lse).
+
+    As `fwd_kv_int8` (cache = CACHE_INT8, kq/vq int8) or `fwd_kv_fp8`
+    (cache = CACHE_FP8, kq/vq uint8 E4M3 codes), with splits and workspace
+    as in `fwd_split`.
+    """
+    code_dtype = {CACHE_INT8: torch.int8, CACHE_FP8: torch.uint8}.get(cache)
+    if code_dtype is None:
+        raise ValueError("cache must be CACHE_INT8 or CACHE_FP8")
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = kq.shape[1], kq.shape[2]
+    if workspace is None:
+        need = split_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, causal, q.dtype, splits, cache) \
+            if q.dtype in _DTYPE else 0
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    elif not (workspace.is_cuda and workspace.device == q.device and workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous tensor on q's device")
+    ws_bytes = workspace.numel() * workspace.element_size()
+
+    def raw(qp, kqp, ksp, vqp, vsp, op, lp, B_, Hq_, Hkv_, Nq_, Nk_, d_, sc, ca, dt, st):
+        return fwd_kv_split_raw(qp, kqp, ksp, vqp, vsp, op, lp, B_, Hq_, Hkv_, Nq_, Nk_, d_, sc,
+                                ca, dt, cache, splits, workspace.data_ptr(), ws_bytes, st)
+
+    return _kv_quantized(raw, code_dtype, "int8" if cache == CACHE_INT8 else "uint8 E4M3 codes",
+                         q, kq, ks, vq, vs, scale, causal, out, lse)

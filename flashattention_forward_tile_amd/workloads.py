@@ -144,6 +144,11 @@ WORKLOADS = {
                        split=True),
     "decode_long": Workload("decode_long", 1, 32, 1, 128, "bf16", Hkv=8, Nk=131072,
                             causal=True, split=True),
+    # the same decoding step over INT8 and FP8 caches
+    "decode_int8": Workload("decode_int8", 4, 32, 1, 128, "bf16", Hkv=8, Nk=32768, causal=True,
+                            kv_int8=True, split=True),
+    "decode_fp8": Workload("decode_fp8", 4, 32, 1, 128, "bf16", Hkv=8, Nk=32768, causal=True,
+                           kv_fp8=True, split=True),
 }
 
 

@@ -37,6 +37,12 @@ enum fa2_dtype {
   FA2_FP16 = 1  /* IEEE binary16 */
 };
 
+/* Code format of a quantized key/value cache (fa2_fwd_kv_split). */
+enum fa2_cache {
+  FA2_CACHE_INT8 = 1, /* int8 codes, the scheme of fa2_fwd_kv_int8 */
+  FA2_CACHE_FP8 = 2   /* OCP E4M3 codes, the scheme of fa2_fwd_kv_fp8 */
+};
+
 /* Return codes.  Every negative code except FA2_ERR_HIP is detected on the
  * host before any kernel is launched, and nothing is written; before any HIP
  * call at all, except that fa2_fwd_split with splits = 0 queries the
@@ -235,7 +241,7 @@ int fa2_fwd_kv_fp8(const void* q, const uint8_t* kq, const float* ks, const uint
  *              (a HIP attribute query, after every argument check except the
  *              workspace's).
  *   workspace: device memory of at least fa2_fwd_split_workspace(...) bytes
- *              for the same arguments, 16-byte aligned, overlapping no
+ *              for the same arguments (cache = 0), 16-byte aligned, overlapping no
  *              input or output; unused (may be NULL) when the call runs
  *              without splits.  The caller owns it; its contents are scratch
  *              (overwritten, never read before written), and two calls in
@@ -253,16 +259,42 @@ int fa2_fwd_split(const void* q, const void* k, const void* v, void* o, float* l
                   int64_t workspace_bytes, void* stream);
 
 /*
- * fa2_fwd_split_workspace -- bytes of workspace fa2_fwd_split needs for these
- * arguments: splits * B*Hq*Nq * (d + 1) * 4 (the partial outputs, then the
- * partial logsumexps), or 0 when the call runs without splits.  With
- * splits = 0 the count is chosen as fa2_fwd_split chooses it on the current
- * device.  Returns the byte count (>= 0) or a negative fa2_status for
- * arguments fa2_fwd_split would reject (shape, head dimension, dtype, causal,
- * splits).
+ * fa2_fwd_split_workspace -- bytes of workspace fa2_fwd_split (cache = 0) or
+ * fa2_fwd_kv_split (cache = FA2_CACHE_INT8 or FA2_CACHE_FP8, d = 128) needs
+ * for these arguments: splits * B*Hq*Nq * (d + 1) * 4 (the partial outputs,
+ * then the partial logsumexps), or 0 when the call runs without splits.
+ * With splits = 0 the count is chosen as those calls choose it on the
+ * current device (one workgroup per compute unit, two for a quantized
+ * cache).  Returns the byte count (>= 0) or a negative fa2_status for
+ * arguments those calls would reject (shape, head dimension, dtype, causal,
+ * cache, splits).
  */
 int64_t fa2_fwd_split_workspace(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
-                                int64_t d, int causal, int dtype, int splits);
+                                int64_t d, int causal, int dtype, int cache, int splits);
+
+/*
+ * fa2_fwd_kv_split -- key splits (as in fa2_fwd_split) over a quantized
+ * key/value cache: the operation of fa2_fwd_kv_int8 (cache = FA2_CACHE_INT8)
+ * or fa2_fwd_kv_fp8 (cache = FA2_CACHE_FP8), for decoding against a long
+ * INT8 or FP8 cache.  Each part quantizes its query rows exactly as the
+ * unsplit call does, so the parts' logits are those of fa2_fwd_kv_int8 /
+ * fa2_fwd_kv_fp8; their partials are merged as in fa2_fwd_split.
+ *
+ *   q, kq, ks, vq, vs, o, lse, B, Hq, Hkv, Nq, Nk, d (128), scale, causal,
+ *   dtype, stream: as in fa2_fwd_kv_int8 (kq, vq void: int8 or E4M3 codes).
+ *   cache    : an fa2_cache (FA2_ERR_OPTION otherwise).
+ *   splits, workspace, workspace_bytes: as in fa2_fwd_split (splits = 0
+ *              targets two workgroups per compute unit here); the workspace
+ *              size is fa2_fwd_split_workspace(B, Hq, Hkv, Nq, Nk, 128,
+ *              causal, dtype, cache, splits).
+ *
+ * Returns the codes of fa2_fwd_kv_int8 and fa2_fwd_split.
+ */
+int fa2_fwd_kv_split(const void* q, const void* kq, const float* ks, const void* vq,
+                     const float* vs, void* o, float* lse, int64_t B, int64_t Hq, int64_t Hkv,
+                     int64_t Nq, int64_t Nk, int64_t d, float scale, int causal, int dtype,
+                     int cache, int splits, void* workspace, int64_t workspace_bytes,
+                     void* stream);
 
 /*
  * fa2_fwd_split_noalloc -- fa2_fwd_split for callers that cannot allocate

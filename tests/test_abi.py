@@ -29,7 +29,7 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["fa2_fwd", "fa2_fwd_ext", "fa2_fwd_kv_fp8",
-                                    "fa2_fwd_kv_int8", "fa2_fwd_split",
+                                    "fa2_fwd_kv_int8", "fa2_fwd_kv_split", "fa2_fwd_split",
                                     "fa2_fwd_split_noalloc", "fa2_fwd_split_workspace",
                                     "fa2_strerror", "fa2_tile_config"]
 
@@ -217,11 +217,13 @@ def test_split_workspace_size(lib):
     assert fa2.split_workspace_bytes(0, 4, 2, 100, 70, 128, True, fa2.BF16, 9) == 0
     for kw, code in [(dict(splits=129), fa2.ERR_OPTION), (dict(splits=-1), fa2.ERR_OPTION),
                      (dict(d=96), fa2.ERR_HEADDIM), (dict(Hkv=3), fa2.ERR_SHAPE),
-                     (dict(dtype=2), fa2.ERR_DTYPE), (dict(causal=2), fa2.ERR_OPTION)]:
+                     (dict(dtype=2), fa2.ERR_DTYPE), (dict(causal=2), fa2.ERR_OPTION),
+                     (dict(cache=3), fa2.ERR_OPTION), (dict(cache=1, d=64), fa2.ERR_HEADDIM)]:
         a = dict(B=2, Hq=4, Hkv=2, Nq=100, Nk=70, d=128, causal=1, dtype=fa2.BF16, splits=4)
         a.update(kw)
         assert lib.fa2_fwd_split_workspace(a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["d"],
-                                           a["causal"], a["dtype"], a["splits"]) == code, kw
+                                           a["causal"], a["dtype"], a.get("cache", 0),
+                                           a["splits"]) == code, kw
     with pytest.raises(fa2.FA2Error) as e:
         fa2.split_workspace_bytes(2, 4, 2, 100, 70, 96)
     assert e.value.code == fa2.ERR_HEADDIM
@@ -244,3 +246,24 @@ def test_split_host_validation(lib, kw, code):
 @pytest.mark.parametrize("kw", [dict(B=0), dict(Hq=0, Hkv=0), dict(Nq=0)])
 def test_split_empty_output_is_a_no_op(lib, kw):
     assert call_split(q=0, k=0, v=0, o=0, lse=0, ws=0, ws_bytes=0, **kw) == fa2.OK
+
+
+def call_kv_split(cache=fa2.CACHE_FP8, splits=4, ws=WS, ws_bytes=1 << 24, **kw):
+    p = dict(I8)
+    p.update(I8_PTRS)
+    p.update(kw)
+    return fa2.fwd_kv_split_raw(p["q"], p["kq"], p["ks"], p["vq"], p["vs"], p["o"], p["lse"],
+                                p["B"], p["Hq"], p["Hkv"], p["Nq"], p["Nk"], p["d"], p["scale"],
+                                p["causal"], p["dtype"], cache, splits, ws, ws_bytes, 0)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cache=0), fa2.ERR_OPTION), (dict(cache=3), fa2.ERR_OPTION),
+    (dict(splits=200), fa2.ERR_OPTION), (dict(d=256), fa2.ERR_HEADDIM),
+    (dict(ks=0), fa2.ERR_NULL), (dict(ws=0), fa2.ERR_WORKSPACE),
+    (dict(ws_bytes=100), fa2.ERR_WORKSPACE), (dict(ws=WS + 4), fa2.ERR_ALIGN),
+    (dict(ws=A + 0x4000000), fa2.ERR_ALIAS),           # workspace over vs
+    (dict(cache=fa2.CACHE_INT8, vs=A + 0x4000008), fa2.ERR_ALIGN),
+])
+def test_kv_split_host_validation(lib, kw, code):
+    assert call_kv_split(**kw) == code

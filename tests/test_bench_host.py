@@ -21,7 +21,8 @@ def test_headline_roofline_is_the_matrix_core_roof():
     assert r["frac"] == pytest.approx(r["achieved"] / 2516.6, abs=1e-4)
 
 
-HBM_BOUND = ("sweep_n512", "gqa_chunk", "tiny", "decode", "decode_long")
+HBM_BOUND = ("sweep_n512", "gqa_chunk", "tiny", "decode", "decode_long", "decode_int8",
+             "decode_fp8")
 
 
 @pytest.mark.parametrize("name", HBM_BOUND)

@@ -46,7 +46,7 @@ HEAD_SUBSETS = {
 FULL = ["tiny", "stress", "headline", "d64", "d256",
         "sweep_n512", "sweep_n1024", "sweep_n2048", "sweep_n4096",
         "causal", "gqa", "kv_cache", "gqa_chunk", "int8_kv", "int8_kv_causal",
-        "fp8_kv", "fp8_kv_causal", "decode", "decode_long"]
+        "fp8_kv", "fp8_kv_causal", "decode", "decode_long", "decode_int8", "decode_fp8"]
 
 
 def announce(*what):
@@ -58,7 +58,11 @@ def run_like_bench(w, inputs):
     dev_in = [t.to(DEV) for t in inputs]
     o = torch.full_like(dev_in[0], float("nan"))
     lse = torch.full((w.B, w.H, w.N), float("nan"), dtype=torch.float32, device=DEV)
-    if w.quantized:
+    if w.quantized and w.split:
+        cache = fa2.CACHE_INT8 if w.kv_int8 else fa2.CACHE_FP8
+        fa2.fwd_kv_split(*dev_in, cache, scale=w.scale, causal=w.causal, splits=0, out=o,
+                         lse=lse)
+    elif w.quantized:
         fwd = fa2.fwd_kv_int8 if w.kv_int8 else fa2.fwd_kv_fp8
         fwd(*dev_in, scale=w.scale, causal=w.causal, out=o, lse=lse)
     elif w.split:

@@ -1,8 +1,9 @@
 """GPU parity of fa2_fwd_split (key splits with a merge) against the fp64
 oracle (needs an MI355X).
 
-The split path computes the same attention as fa2_fwd_ext through a
-different reduction order (partial softmaxes over key ranges, merged by
+The split path (fa2_fwd_split; fa2_fwd_kv_split over INT8 and FP8 caches)
+computes the same attention as the unsplit calls through a different
+reduction order (partial softmaxes over key ranges, merged by
 their logsumexps), so it is compared with the oracle at the 16-bit path's
 tolerances, and with fa2_fwd_ext only loosely.  Outputs start as NaN, so an
 unwritten row cannot pass; split counts cover the library's own choice, a
@@ -15,7 +16,8 @@ import torch
 
 import oracle
 from flashattention_forward_tile_amd import fa2
-from flashattention_forward_tile_amd.workloads import bits, make_inputs
+from flashattention_forward_tile_amd.workloads import (bits, make_inputs, make_inputs_kv_fp8,
+                                                       make_inputs_kv_int8)
 from parity import assert_parity
 
 pytestmark = pytest.mark.gpu
@@ -129,3 +131,40 @@ def test_chosen_split_count_uses_the_compute_units():
     assert n % per_split == 0
     items = 4 * 8 * 1  # one 128-row query tile per K/V head
     assert n // per_split == min(-(-cus // items), 32768 // 32 // 8, 128)
+    # quantized caches: two workgroups per compute unit
+    for cache in (fa2.CACHE_INT8, fa2.CACHE_FP8):
+        n = fa2.split_workspace_bytes(4, 32, 8, 1, 32768, 128, True, fa2.BF16, 0, cache)
+        assert n // per_split == min(-(-2 * cus // items), 32768 // 32 // 8, 128)
+
+
+QUANTIZED = {"int8": (fa2.CACHE_INT8, make_inputs_kv_int8, "attention_kv_int8"),
+             "fp8": (fa2.CACHE_FP8, make_inputs_kv_fp8, "attention_kv_fp8")}
+
+
+@pytest.mark.parametrize("splits", [0, 3, 16])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("fmt", ["int8", "fp8"])
+def test_quantized_cache_decode(fmt, dtype, causal, splits):
+    """Decode rows over an INT8 / FP8 cache with key splits, against the
+    oracle's quantized functions (each part quantizes the query row as the
+    unsplit call does) and against the unsplit call."""
+    announce("split", fmt, dtype, causal, splits)
+    cache, make, attn = QUANTIZED[fmt]
+    q, kq, ks, vq, vs = make(2, 8, 2, 2, 5000, 128, dtype, seed=splits + 17)
+    q[0, 0, 1] = 0  # a zero row: codes 0, sq 0
+    dev = [t.to(DEV) for t in (q, kq, ks, vq, vs)]
+    o = torch.full_like(dev[0], float("nan"))
+    lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device=DEV)
+    fa2.fwd_kv_split(*dev, cache, causal=causal, splits=splits, out=o, lse=lse)
+    unsplit = fa2.fwd_kv_int8 if fmt == "int8" else fa2.fwd_kv_fp8
+    o1, l1 = unsplit(*dev, causal=causal)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = getattr(oracle, attn)(bits(q), kq.numpy(), ks.numpy(), vq.numpy(),
+                                           vs.numpy(), dtype, 1.0 / math.sqrt(128),
+                                           causal=causal)
+    tag = "split %s %s causal=%d splits=%d" % (fmt, dtype, causal, splits)
+    assert_parity(o.cpu().double().numpy(), lse.cpu().double().numpy(), o_ref, lse_ref, tag,
+                  lse_abs=1e-3)
+    assert (o.float() - o1.float()).abs().max().item() <= 2e-2, tag
+    assert (lse - l1).abs().max().item() <= 1e-3, tag

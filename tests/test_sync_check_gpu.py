@@ -132,3 +132,25 @@ def test_key_splits_match_race_check_build(d, causal):
         torch.cuda.synchronize()
         outs.append((o.cpu(), lse.cpu()))
     assert_same(outs, "split d=%d causal=%d" % (d, causal))
+
+
+@pytest.mark.parametrize("cache", [fa2.CACHE_INT8, fa2.CACHE_FP8])
+def test_quantized_key_splits_match_race_check_build(cache):
+    announce("split cache", cache)
+    B, Hq, Hkv, Nq, Nk, splits = 2, 8, 2, 3, 6000, 7
+    make = make_inputs_kv_int8 if cache == fa2.CACHE_INT8 else make_inputs_kv_fp8
+    q, kq, ks, vq, vs = (t.to(DEV) for t in make(B, Hq, Hkv, Nq, Nk, 128, "bf16", 9))
+    nbytes = fa2.split_workspace_bytes(B, Hq, Hkv, Nq, Nk, 128, True, fa2.BF16, splits, cache)
+    outs = []
+    for handle in (fa2.lib(), sync_lib()):
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+        o = torch.full_like(q, float("nan"))
+        lse = torch.full((B, Hq, Nq), float("nan"), device=DEV)
+        code = handle.fa2_fwd_kv_split(q.data_ptr(), kq.data_ptr(), ks.data_ptr(), vq.data_ptr(),
+                                       vs.data_ptr(), o.data_ptr(), lse.data_ptr(), B, Hq, Hkv,
+                                       Nq, Nk, 128, 1.0 / math.sqrt(128), 1, fa2.BF16, cache,
+                                       splits, ws.data_ptr(), nbytes, 0)
+        assert code == 0, fa2.strerror(code)
+        torch.cuda.synchronize()
+        outs.append((o.cpu(), lse.cpu()))
+    assert_same(outs, "split cache %d" % cache)
