@@ -1466,13 +1466,16 @@ template <int D>
 constexpr int kSplitKeys = SplitCfg<D>::C::BC;
 constexpr int kMaxSplits = 128;
 
-// Merge of the key splits' partials (see Problem): for each row, with m the
-// largest part logsumexp and w_s = exp(lse_s - m), O = sum_s w_s O_s /
+// Merge of the key splits' partials (see SplitProblem): for each row, with
+// m the largest part logsumexp and w_s = exp(lse_s - m), O = sum_s w_s O_s /
 // sum_s w_s and lse = m + log(sum_s w_s), which is the softmax over the
 // union of the parts' keys (every part's O_s is normalised by its own sum
 // exp(lse_s)).  A row that no part saw (every lse_s = -inf) gets O = 0,
-// lse = -inf.  Each thread owns 4 channels of one row; plain loads and
-// stores, HBM-bound.
+// lse = -inf.  Each thread owns 4 channels of one row.  There are few rows
+// when splits pay (decoding), so the merge is bound by load latency, not
+// bytes: the parts are read 8 at a time, every load of a chunk issued
+// before any is used, and folded into running sums whose reference m moves
+// chunk by chunk as in an online softmax.
 constexpr int kMergeThreads = 256;
 template <int D, bool FP16>
 __global__ void __launch_bounds__(kMergeThreads)
@@ -1485,22 +1488,42 @@ fa2_split_merge_kernel(const float* part_o, const float* part_lse, uint16_t* o, 
   const int64_t r = gid / TPR;
   const int c4 = (int)(gid - r * TPR);
   if (r >= rows) return;
-  float m = -INFINITY;
-  for (int s = 0; s < splits; ++s) m = fmaxf(m, part_lse[s * rows + r]);
-  float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f, wsum = 0.0f;
-  if (m != -INFINITY) {
-    for (int s = 0; s < splits; ++s) {
-      const float w = __builtin_amdgcn_exp2f((part_lse[s * rows + r] - m) * kLog2e);
-      const float4 po = *(const float4*)(part_o + (s * rows + r) * D + c4 * 4);
-      a0 += w * po.x;
-      a1 += w * po.y;
-      a2 += w * po.z;
-      a3 += w * po.w;
-      wsum += w;
+  float m = -INFINITY, wsum = 0.0f;
+  float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  auto fold = [&](int s0, auto count) {
+    constexpr int U = decltype(count)::value;
+    float ls[U];
+    float4 po[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t row = (int64_t)(s0 + u) * rows + r;
+      ls[u] = part_lse[row];
+      po[u] = *(const float4*)(part_o + row * D + c4 * 4);
     }
-  }
+    float mc = m;
+#pragma unroll
+    for (int u = 0; u < U; ++u) mc = fmaxf(mc, ls[u]);
+    if (mc == -INFINITY) return;  // no part so far saw a key
+    const float alpha = __builtin_amdgcn_exp2f((m - mc) * kLog2e);  // 0 while m = -inf
+    wsum *= alpha;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] *= alpha;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float w = __builtin_amdgcn_exp2f((ls[u] - mc) * kLog2e);
+      wsum += w;
+      a[0] += w * po[u].x;
+      a[1] += w * po[u].y;
+      a[2] += w * po[u].z;
+      a[3] += w * po[u].w;
+    }
+    m = mc;
+  };
+  int s = 0;
+  for (; s + 8 <= splits; s += 8) fold(s, Ic<8>{});
+  for (; s < splits; ++s) fold(s, Ic<1>{});
   const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
-  const X4 out = {(E)(a0 * inv), (E)(a1 * inv), (E)(a2 * inv), (E)(a3 * inv)};
+  const X4 out = {(E)(a[0] * inv), (E)(a[1] * inv), (E)(a[2] * inv), (E)(a[3] * inv)};
   *(u32x2*)(o + r * D + c4 * 4) = __builtin_bit_cast(u32x2, out);
   if (c4 == 0) lse[r] = wsum > 0.0f ? m + __log2f(wsum) * kLn2 : -INFINITY;
 }
