@@ -3,8 +3,8 @@
 The targeted tests pin one feature at a time; these cases draw every option
 together (head dimension, dtype, grouped K/V heads, unequal and ragged query
 and key lengths, the causal mask, positive, negative and zero scales, an empty
-key set) so that combinations no targeted case lists are still compared with
-the oracle in full.  Each case is fixed by its index: the shapes do not change
+key set, key splits) so that combinations no targeted case lists are still
+compared with the oracle in full.  Each case is fixed by its index: the shapes do not change
 from run to run.
 """
 import math
@@ -106,4 +106,25 @@ def test_random_shape_fp8_cache(i):
     o_ref, lse_ref = oracle.attention_kv_fp8(bits(q), kq.numpy(), ks.numpy(), vq.numpy(),
                                              vs.numpy(), c["dtype"], c["scale"],
                                              causal=c["causal"])
+    compare(o.cpu(), lse.cpu(), o_ref, lse_ref, tag)
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_shape_key_splits(i):
+    """The drawn shapes through fa2_fwd_split, with a split count drawn from
+    0 (the library's choice) to 40."""
+    c = draw(i + 200)
+    splits = int(np.random.default_rng(500 + i).integers(0, 41))
+    tag = "random split %d %s splits=%d" % (i, c, splits)
+    announce(tag)
+    g = torch.Generator().manual_seed(5000 + i)
+    td = _TD[c["dtype"]]
+    q = torch.randn((c["B"], c["Hq"], c["Nq"], c["d"]), generator=g).to(td)
+    k = torch.randn((c["B"], c["Hkv"], c["Nk"], c["d"]), generator=g).to(td)
+    v = torch.randn((c["B"], c["Hkv"], c["Nk"], c["d"]), generator=g).to(td)
+    o, lse = fa2.fwd_split(q.to(DEV), k.to(DEV), v.to(DEV), scale=c["scale"],
+                           causal=c["causal"], splits=splits)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention(bits(q), bits(k), bits(v), c["dtype"], c["scale"],
+                                      causal=c["causal"])
     compare(o.cpu(), lse.cpu(), o_ref, lse_ref, tag)
