@@ -704,7 +704,14 @@ fa2_fwd_kernel(const std::conditional_t<SPLIT, SplitProblem, Problem> P) {
   };
   // Causal: whether any row of this wave sees a key of tile t (always true
   // without the mask).
-  auto sees = [&](int t) -> bool { return !CAUSAL || t <= wave_last; };
+  // SPLIT: a wave whose query rows all lie past the item's last row (the
+  // padding of a short query block: decoding fills one of four waves) runs
+  // neither product and reads no operands; it still issues its share of the
+  // loads, widens its share of V and meets every barrier.  Its logits stay
+  // 0 (set once below), so its softmax is cheap and never takes the rare
+  // path after the first tile; its rows are never written.
+  const bool live = !SPLIT || q0 < P.rows;
+  auto sees = [&](int t) -> bool { return live && (!CAUSAL || t <= wave_last); };
   item_limits();
   if constexpr (SPLIT) {
     // K and V from the split's first key on; key_base < N unless there are
@@ -1123,9 +1130,9 @@ fa2_fwd_kernel(const std::conditional_t<SPLIT, SplitProblem, Problem> P) {
     // The stale S registers are never used: the next iteration masks every
     // key of that tile for this wave (to -inf, so P is 0), as it would the
     // computed logits.
-    if ((TL & 8) != 0 || (TL & 4) != 0 || sees(j + 1)) gemm1(j + 1, S1{}, kpre, s_nxt);
+    if (((TL & 8) != 0 || (TL & 4) != 0 || sees(j + 1)) && live) gemm1(j + 1, S1{}, kpre, s_nxt);
     if constexpr (!decltype(first)::value) {
-      if ((TL & 8) != 0 || sees(j - 1)) gemm2(j - 1, S3{}, vpre, p_prev);
+      if (((TL & 8) != 0 || sees(j - 1)) && live) gemm2(j - 1, S3{}, vpre, p_prev);
     }
     float rs[QB];
     bool over = false;
@@ -1155,8 +1162,10 @@ fa2_fwd_kernel(const std::conditional_t<SPLIT, SplitProblem, Problem> P) {
 
     // First operands of the next iteration: K_{j+2} and V_j, both published
     // by the barrier that ended the previous iteration.
-    prefetch_k(j + 2, S2{}, kpre);
-    prefetch_v(j, S0{}, vpre);
+    if (live) {
+      prefetch_k(j + 2, S2{}, kpre);
+      prefetch_v(j, S0{}, vpre);
+    }
 
     // While the unrounded sum of a lane's p stays at or below kSumLimit no p
     // exceeds it and the reference max stands.  Otherwise (always on the
@@ -1206,6 +1215,14 @@ fa2_fwd_kernel(const std::conditional_t<SPLIT, SplitProblem, Problem> P) {
   // item's S_0 from one item into the next.
   SAcc sA[QB][KB], sB[QB][KB];
   X8 pA[QB][ST], pB[QB][ST];
+  if constexpr (SPLIT) {
+#pragma unroll
+    for (int b = 0; b < QB; ++b)
+#pragma unroll
+      for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+        for (int i = 0; i < (Q8 ? 16 : NACC); ++i) sA[b][kk][i] = sB[b][kk][i] = 0;
+  }
   if (n_tiles > 0) {
     // Prologue: Q, K_0 .. K_{RING-1} and V_0 .. V_{RING-3} resident, S_0
     // computed, the first operands of K_1 in registers.  Everything retires
@@ -1236,9 +1253,11 @@ fa2_fwd_kernel(const std::conditional_t<SPLIT, SplitProblem, Problem> P) {
 
     load_qf();              // PERSIST: Q from LDS (read before the next tile lands there)
     convert_v(0, Ic<0>{});  // Q8: V_0 widened; published by the barrier below
-    prefetch_k(0, Ic<0>{}, kpre);
-    gemm1(0, Ic<0>{}, kpre, sA);
-    prefetch_k(1, Ic<1>{}, kpre);
+    if (live) {
+      prefetch_k(0, Ic<0>{}, kpre);
+      gemm1(0, Ic<0>{}, kpre, sA);
+      prefetch_k(1, Ic<1>{}, kpre);
+    }
     __syncthreads();  // every wave is done with K_0 before K_RING may overwrite it
   }
 

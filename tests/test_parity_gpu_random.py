@@ -128,3 +128,29 @@ def test_random_shape_key_splits(i):
     o_ref, lse_ref = oracle.attention(bits(q), bits(k), bits(v), c["dtype"], c["scale"],
                                       causal=c["causal"])
     compare(o.cpu(), lse.cpu(), o_ref, lse_ref, tag)
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_shape_quantized_key_splits(i):
+    """Drawn shapes (d = 128) over INT8 (even i) or FP8 (odd i) caches
+    through fa2_fwd_kv_split, with a split count drawn from 0 to 40."""
+    c = draw(i + 300)
+    c["d"] = 128
+    c["scale"] = c["scale"] * math.sqrt(draw(i + 300)["d"]) / math.sqrt(128)
+    splits = int(np.random.default_rng(700 + i).integers(0, 41))
+    fmt = "int8" if i % 2 == 0 else "fp8"
+    tag = "random split %s %d %s splits=%d" % (fmt, i, c, splits)
+    announce(tag)
+    make = make_inputs_kv_int8 if fmt == "int8" else make_inputs_kv_fp8
+    q, kq, ks, vq, vs = make(c["B"], c["Hq"], c["Hkv"], c["Nq"], max(c["Nk"], 1), 128,
+                             c["dtype"], seed=6000 + i)
+    if c["Nk"] == 0:
+        kq, vq = kq[:, :, :0].contiguous(), vq[:, :, :0].contiguous()
+    cache = fa2.CACHE_INT8 if fmt == "int8" else fa2.CACHE_FP8
+    o, lse = fa2.fwd_kv_split(q.to(DEV), kq.to(DEV), ks.to(DEV), vq.to(DEV), vs.to(DEV), cache,
+                              scale=c["scale"], causal=c["causal"], splits=splits)
+    torch.cuda.synchronize()
+    attn = oracle.attention_kv_int8 if fmt == "int8" else oracle.attention_kv_fp8
+    o_ref, lse_ref = attn(bits(q), kq.numpy(), ks.numpy(), vq.numpy(), vs.numpy(), c["dtype"],
+                          c["scale"], causal=c["causal"])
+    compare(o.cpu(), lse.cpu(), o_ref, lse_ref, tag)
