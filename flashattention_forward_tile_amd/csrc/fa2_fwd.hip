@@ -108,11 +108,13 @@ __device__ __forceinline__ f32x4 mfma16x16x32(typename Vec<FP16>::x8 a, typename
 // length in chunks.
 template <int CPR>
 __device__ __forceinline__ int k_swizzle(int row, int chunk) {
-  static_assert(CPR == 8 || CPR == 16 || CPR == 32, "row of 128, 256 or 512 B");
+  static_assert(CPR == 4 || CPR == 8 || CPR == 16 || CPR == 32, "row of 64 to 512 B");
   if constexpr (CPR >= 16)
     return chunk ^ (row & 15);
-  else  // 128 B rows: two rows share one sweep of the banks
+  else if constexpr (CPR == 8)  // 128 B rows: two rows share one sweep of the banks
     return chunk ^ ((row >> 1) & 7);
+  else  // 64 B rows (8-bit codes at d = 64): four rows share one sweep
+    return chunk ^ ((row >> 2) & 3);
 }
 template <int CPR, int MS = 32>
 __device__ __forceinline__ int v_swizzle(int row, int chunk) {
@@ -245,10 +247,14 @@ template <> struct Cfg<256> { static constexpr int BC = 32, NW = 8, QB = 1, OCC 
 // Tile shape of the INT8 key/value cache kernels (d = 128 only).
 template <int D> struct Cfg8;
 template <> struct Cfg8<128> { static constexpr int BC = 32, NW = 8, QB = 1, OCC = 2, SGB = 0, RING = 4, PK = 2, PV = 2, MS = 32; };
+// d = 64: 64-key tiles, so a code tile (4 KiB) and its fp16 widening (8 KiB)
+// split into whole loads and chunks over the eight waves.
+template <> struct Cfg8<64> { static constexpr int BC = 64, NW = 8, QB = 1, OCC = 2, SGB = 0, RING = 4, PK = 2, PV = 2, MS = 32; };
 // The quantized caches with key splits: 128-row tiles (four waves), as the
 // 16-bit split kernels, so that decoding forms one tile per K/V head.
 template <int D> struct Cfg8S;
 template <> struct Cfg8S<128> { static constexpr int BC = 32, NW = 4, QB = 1, OCC = 2, SGB = 0, RING = 4, PK = 2, PV = 2, MS = 32; };
+template <> struct Cfg8S<64> { static constexpr int BC = 64, NW = 4, QB = 1, OCC = 2, SGB = 0, RING = 4, PK = 2, PV = 2, MS = 32; };
 // Short key sequences at d = 128 (at most kShortKeys keys): half the query
 // rows per workgroup, so two workgroups share a CU and one's prologue and
 // epilogue overlap the other's loop.  The same shape serves grids too small
@@ -1557,25 +1563,27 @@ const void* pick_split_mode(int mode) {
   }
 }
 
-// Quantized caches (QK 1: INT8, 2: FP8), d = 128, 128-row tiles.
-template <int QK, bool FP16, bool CAUSAL>
+// Quantized caches (QK 1: INT8, 2: FP8), d = 64 or 128, 128-row tiles.
+template <int D, int QK, bool FP16, bool CAUSAL>
 const void* pick_split_q8_mode(int mode) {
   switch (mode) {
-    case kNegative: return (const void*)fa2_fwd_kernel<128, FP16, kNegative, CAUSAL, QK, true, false, true>;
-    case kZero: return (const void*)fa2_fwd_kernel<128, FP16, kZero, CAUSAL, QK, true, false, true>;
-    default: return (const void*)fa2_fwd_kernel<128, FP16, kPositive, CAUSAL, QK, true, false, true>;
+    case kNegative: return (const void*)fa2_fwd_kernel<D, FP16, kNegative, CAUSAL, QK, true, false, true>;
+    case kZero: return (const void*)fa2_fwd_kernel<D, FP16, kZero, CAUSAL, QK, true, false, true>;
+    default: return (const void*)fa2_fwd_kernel<D, FP16, kPositive, CAUSAL, QK, true, false, true>;
   }
 }
 
-template <int QK>
+template <int D, int QK>
 const void* pick_split_q8(bool fp16, int mode, bool causal) {
   if (fp16)
-    return causal ? pick_split_q8_mode<QK, true, true>(mode) : pick_split_q8_mode<QK, true, false>(mode);
-  return causal ? pick_split_q8_mode<QK, false, true>(mode) : pick_split_q8_mode<QK, false, false>(mode);
+    return causal ? pick_split_q8_mode<D, QK, true, true>(mode) : pick_split_q8_mode<D, QK, true, false>(mode);
+  return causal ? pick_split_q8_mode<D, QK, false, true>(mode) : pick_split_q8_mode<D, QK, false, false>(mode);
 }
 static_assert(kSplitRows<128> == Cfg8S<128>::NW * Cfg8S<128>::MS * Cfg8S<128>::QB &&
-                  kSplitKeys<128> == Cfg8S<128>::BC,
-              "the quantized split kernels share the d = 128 split plan");
+                  kSplitKeys<128> == Cfg8S<128>::BC &&
+                  kSplitRows<64> == Cfg8S<64>::NW * Cfg8S<64>::MS * Cfg8S<64>::QB &&
+                  kSplitKeys<64> == Cfg8S<64>::BC,
+              "the quantized split kernels share the 16-bit split plan");
 
 template <int D>
 const void* pick_split(bool fp16, int mode, bool causal) {
@@ -1636,7 +1644,7 @@ const char* fa2_strerror(int status) {
     case FA2_OK: return "success";
     case FA2_ERR_NULL: return "a required pointer is NULL";
     case FA2_ERR_SHAPE: return "a size is negative, heads do not group, or sizes are too large";
-    case FA2_ERR_HEADDIM: return "head dimension must be 64, 128 or 256 (128 for the quantized caches)";
+    case FA2_ERR_HEADDIM: return "head dimension must be 64, 128 or 256 (64 or 128 for the quantized caches)";
     case FA2_ERR_DTYPE: return "dtype must be FA2_BF16 or FA2_FP16";
     case FA2_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
     case FA2_ERR_SCALE: return "scale must be finite";
@@ -1707,7 +1715,7 @@ SplitPlan plan_split(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
 int check_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
                 int causal, int dtype, bool q8) {
   if (dtype != FA2_BF16 && dtype != FA2_FP16) return FA2_ERR_DTYPE;
-  if (q8 ? d != 128 : (d != 64 && d != 128 && d != 256)) return FA2_ERR_HEADDIM;
+  if (q8 ? (d != 64 && d != 128) : (d != 64 && d != 128 && d != 256)) return FA2_ERR_HEADDIM;
   if (causal != 0 && causal != 1) return FA2_ERR_OPTION;
   if (B < 0 || Hq < 0 || Hkv < 0 || Nq < 0 || Nk < 0) return FA2_ERR_SHAPE;
   if (B == 0 || Hq == 0 || Nq == 0) return 1;  // no output rows
@@ -1725,7 +1733,8 @@ int check_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int6
   // take (the smallest, 128 query rows, gives the most workgroups).
   int bq = 0, bk = 0, nw = 0;
   fa2_tile_config(d, dtype, &bq, &bk, &nw);
-  const int64_t bq_min = q8 ? Cfg8<128>::NW * Cfg8<128>::MS * Cfg8<128>::QB
+  const int64_t bq_min = q8 ? (d == 64 ? Cfg8<64>::NW * Cfg8<64>::MS * Cfg8<64>::QB
+                                      : Cfg8<128>::NW * Cfg8<128>::MS * Cfg8<128>::QB)
                        : d == 128 ? CfgS<128>::NW * CfgS<128>::MS * CfgS<128>::QB : bq;
   if (B * Hkv > (((int64_t)1 << 31) - 1) / ((rows + bq_min - 1) / bq_min)) return FA2_ERR_SHAPE;
   return FA2_OK;
@@ -1839,8 +1848,9 @@ int launch(const void* q, const void* k, const void* v, const float* ks, const f
     short_keys = n_cu > 0 && items_full < n_cu;
   }
   if (q8) {
-    bq = Cfg8<128>::NW * Cfg8<128>::MS * Cfg8<128>::QB;
-    nw = Cfg8<128>::NW;
+    bq = d == 64 ? Cfg8<64>::NW * Cfg8<64>::MS * Cfg8<64>::QB
+                 : Cfg8<128>::NW * Cfg8<128>::MS * Cfg8<128>::QB;
+    nw = d == 64 ? Cfg8<64>::NW : Cfg8<128>::NW;
   } else if (persist && d == 64) {
     bq = CfgP<64>::NW * CfgP<64>::MS * CfgP<64>::QB;
     nw = CfgP<64>::NW;
@@ -1879,12 +1889,14 @@ int launch(const void* q, const void* k, const void* v, const float* ks, const f
     SP.part_o = (float*)ws;
     SP.part_lse = (float*)ws + (int64_t)splits * SP.part_rows * d;
     SP.splits = splits;
-    const void* sfn = qk == 2 ? pick_split_q8<2>(fp16, mode, causal)
-                    : qk == 1 ? pick_split_q8<1>(fp16, mode, causal)
+    const void* sfn = qk == 2 ? (d == 64 ? pick_split_q8<64, 2>(fp16, mode, causal)
+                                         : pick_split_q8<128, 2>(fp16, mode, causal))
+                    : qk == 1 ? (d == 64 ? pick_split_q8<64, 1>(fp16, mode, causal)
+                                         : pick_split_q8<128, 1>(fp16, mode, causal))
                     : d == 64 ? pick_split<64>(fp16, mode, causal)
                     : d == 128 ? pick_split<128>(fp16, mode, causal)
                                : pick_split<256>(fp16, mode, causal);
-    const int snw = q8 ? Cfg8S<128>::NW
+    const int snw = q8 ? (d == 64 ? Cfg8S<64>::NW : Cfg8S<128>::NW)
                   : d == 64 ? SplitCfg<64>::C::NW : d == 128 ? SplitCfg<128>::C::NW
                                                              : SplitCfg<256>::C::NW;
     void* sargs[] = {&SP};
@@ -1909,8 +1921,8 @@ int launch(const void* q, const void* k, const void* v, const float* ks, const f
                           (hipStream_t)stream);
     return err == hipSuccess ? FA2_OK : FA2_ERR_HIP;
   }
-  kernel_fn fn = qk == 2 ? pick<128, 2>(fp16, mode, causal)
-               : q8 ? pick<128, 1>(fp16, mode, causal)
+  kernel_fn fn = qk == 2 ? (d == 64 ? pick<64, 2>(fp16, mode, causal) : pick<128, 2>(fp16, mode, causal))
+               : q8 ? (d == 64 ? pick<64, 1>(fp16, mode, causal) : pick<128, 1>(fp16, mode, causal))
                : d == 64 ? pick<64, 0>(fp16, mode, causal)
                : d == 128 ? (short_keys ? pick<128, 0, true>(fp16, mode, causal)
                                         : pick<128, 0>(fp16, mode, causal))

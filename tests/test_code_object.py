@@ -73,7 +73,9 @@ def test_every_kernel_is_present(kernels):
                 (128, 0, 1, 0, 0): 12, (128, 0, 0, 1, 0): 12, (128, 1, 0, 0, 0): 12,
                 (128, 2, 0, 0, 0): 12, (256, 0, 0, 0, 0): 12,
                 (64, 0, 0, 0, 1): 12, (128, 0, 1, 0, 1): 12, (256, 0, 0, 0, 1): 12,
-                (128, 1, 1, 0, 1): 12, (128, 2, 1, 0, 1): 12}
+                (128, 1, 1, 0, 1): 12, (128, 2, 1, 0, 1): 12,
+                (64, 1, 0, 0, 0): 12, (64, 2, 0, 0, 0): 12, (64, 1, 1, 0, 1): 12,
+                (64, 2, 1, 0, 1): 12}
     count = {}
     for (d, fp16, mode, causal, q8, short, persist, split) in kernels:
         key = (d, q8, short, persist, split)

@@ -46,22 +46,25 @@ def check(inputs, dtype, scale, causal, tag, rows=None):
 
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk", [
     (1, 2, 2, 64, 64), (1, 2, 1, 100, 300), (2, 4, 2, 257, 513), (1, 8, 1, 5, 1000),
     (1, 2, 2, 1, 1), (1, 3, 3, 300, 90), (1, 4, 4, 32, 33)])
-def test_int8_cache(B, Hq, Hkv, Nq, Nk, dtype, causal):
-    announce("int8", B, Hq, Hkv, Nq, Nk, dtype, causal)
-    inputs = make_inputs_kv_int8(B, Hq, Hkv, Nq, Nk, 128, dtype, seed=Nq + 7 * Nk + Hq)
-    check(inputs, dtype, 1.0 / math.sqrt(128), causal,
-          "int8 B=%d Hq=%d Hkv=%d Nq=%d Nk=%d %s causal=%d" % (B, Hq, Hkv, Nq, Nk, dtype, causal))
+def test_int8_cache(B, Hq, Hkv, Nq, Nk, d, dtype, causal):
+    announce("int8", B, Hq, Hkv, Nq, Nk, d, dtype, causal)
+    inputs = make_inputs_kv_int8(B, Hq, Hkv, Nq, Nk, d, dtype, seed=Nq + 7 * Nk + Hq + d)
+    check(inputs, dtype, 1.0 / math.sqrt(d), causal,
+          "int8 B=%d Hq=%d Hkv=%d Nq=%d Nk=%d d=%d %s causal=%d" % (
+              B, Hq, Hkv, Nq, Nk, d, dtype, causal))
 
 
 @pytest.mark.parametrize("scale", [0.0, -0.2, 1.5])
 @pytest.mark.parametrize("causal", [False, True])
-def test_int8_scales(scale, causal):
-    announce("int8 scale", scale, causal)
-    inputs = make_inputs_kv_int8(1, 4, 2, 200, 333, 128, "bf16", seed=3)
-    check(inputs, "bf16", scale, causal, "int8 scale=%g causal=%d" % (scale, causal))
+@pytest.mark.parametrize("d", [64, 128])
+def test_int8_scales(d, scale, causal):
+    announce("int8 scale", d, scale, causal)
+    inputs = make_inputs_kv_int8(1, 4, 2, 200, 333, d, "bf16", seed=3)
+    check(inputs, "bf16", scale, causal, "int8 d=%d scale=%g causal=%d" % (d, scale, causal))
 
 
 def test_int8_zero_query_rows():

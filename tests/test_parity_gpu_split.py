@@ -144,14 +144,15 @@ QUANTIZED = {"int8": (fa2.CACHE_INT8, make_inputs_kv_int8, "attention_kv_int8"),
 @pytest.mark.parametrize("splits", [0, 3, 16])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("fmt", ["int8", "fp8"])
-def test_quantized_cache_decode(fmt, dtype, causal, splits):
+def test_quantized_cache_decode(fmt, d, dtype, causal, splits):
     """Decode rows over an INT8 / FP8 cache with key splits, against the
     oracle's quantized functions (each part quantizes the query row as the
     unsplit call does) and against the unsplit call."""
-    announce("split", fmt, dtype, causal, splits)
+    announce("split", fmt, d, dtype, causal, splits)
     cache, make, attn = QUANTIZED[fmt]
-    q, kq, ks, vq, vs = make(2, 8, 2, 2, 5000, 128, dtype, seed=splits + 17)
+    q, kq, ks, vq, vs = make(2, 8, 2, 2, 5000, d, dtype, seed=splits + 17 + d)
     q[0, 0, 1] = 0  # a zero row: codes 0, sq 0
     dev = [t.to(DEV) for t in (q, kq, ks, vq, vs)]
     o = torch.full_like(dev[0], float("nan"))
@@ -161,9 +162,9 @@ def test_quantized_cache_decode(fmt, dtype, causal, splits):
     o1, l1 = unsplit(*dev, causal=causal)
     torch.cuda.synchronize()
     o_ref, lse_ref = getattr(oracle, attn)(bits(q), kq.numpy(), ks.numpy(), vq.numpy(),
-                                           vs.numpy(), dtype, 1.0 / math.sqrt(128),
+                                           vs.numpy(), dtype, 1.0 / math.sqrt(d),
                                            causal=causal)
-    tag = "split %s %s causal=%d splits=%d" % (fmt, dtype, causal, splits)
+    tag = "split %s d=%d %s causal=%d splits=%d" % (fmt, d, dtype, causal, splits)
     assert_parity(o.cpu().double().numpy(), lse.cpu().double().numpy(), o_ref, lse_ref, tag,
                   lse_abs=1e-3)
     assert (o.float() - o1.float()).abs().max().item() <= 2e-2, tag
