@@ -250,11 +250,15 @@ template <> struct Cfg8<128> { static constexpr int BC = 32, NW = 8, QB = 1, OCC
 // d = 64: 64-key tiles, so a code tile (4 KiB) and its fp16 widening (8 KiB)
 // split into whole loads and chunks over the eight waves.
 template <> struct Cfg8<64> { static constexpr int BC = 64, NW = 8, QB = 1, OCC = 2, SGB = 0, RING = 4, PK = 2, PV = 2, MS = 32; };
+// d = 256: 16-row waves on the 16x16 int8 / FP8 shapes, as the 16-bit d = 256
+// kernels.
+template <> struct Cfg8<256> { static constexpr int BC = 32, NW = 8, QB = 1, OCC = 2, SGB = 0, RING = 4, PK = 1, PV = 2, MS = 16; };
 // The quantized caches with key splits: 128-row tiles (four waves), as the
 // 16-bit split kernels, so that decoding forms one tile per K/V head.
 template <int D> struct Cfg8S;
 template <> struct Cfg8S<128> { static constexpr int BC = 32, NW = 4, QB = 1, OCC = 2, SGB = 0, RING = 4, PK = 2, PV = 2, MS = 32; };
 template <> struct Cfg8S<64> { static constexpr int BC = 64, NW = 4, QB = 1, OCC = 2, SGB = 0, RING = 4, PK = 2, PV = 2, MS = 32; };
+template <> struct Cfg8S<256> { static constexpr int BC = 32, NW = 8, QB = 1, OCC = 2, SGB = 0, RING = 4, PK = 2, PV = 2, MS = 16; };
 // Short key sequences at d = 128 (at most kShortKeys keys): half the query
 // rows per workgroup, so two workgroups share a CU and one's prologue and
 // epilogue overlap the other's loop.  The same shape serves grids too small
@@ -362,7 +366,7 @@ fa2_fwd_kernel(const std::conditional_t<SPLIT, SplitProblem, Problem> P) {
   // rows, lanes l and l+32 share a row) or 16x16x32 (MS = 16: 16 query rows,
   // lanes l, l+16, l+32, l+48 share a row).
   constexpr int MS = C::MS;
-  static_assert(MS == 32 || (MS == 16 && !Q8 && !PERSIST), "16x16x32 blocking");
+  static_assert(MS == 32 || (MS == 16 && !PERSIST), "16x16 blocking");
   constexpr int BR = NW * MS * QB;    // query rows per workgroup
   constexpr int CPR = D / 8;          // 16-byte chunks per (16-bit) V row
   constexpr int RB = D * 2;           // bytes per (16-bit) V row in LDS
@@ -372,7 +376,9 @@ fa2_fwd_kernel(const std::conditional_t<SPLIT, SplitProblem, Problem> P) {
   constexpr int TBK = BC * RBK;       // one K tile in LDS (and one int8 V tile)
   constexpr int LW = Q8 ? 4 : 16;     // bytes per lane of one HBM -> LDS load
   constexpr int LOADS = TBK / (NW * 64 * LW);  // K loads per thread per tile (V: the same)
-  constexpr int KD = F8 ? 64 : Q8 || MS == 16 ? 32 : 16;  // contraction depth of one first-product MFMA
+  // contraction depth of one first-product MFMA (16 bytes of codes per lane,
+  // 32 for FP8, 8 16-bit values otherwise)
+  constexpr int KD = F8 ? (MS == 16 ? 128 : 64) : Q8 ? (MS == 16 ? 64 : 32) : MS == 16 ? 32 : 16;
   constexpr int KS = D / KD;          // k-steps of the first product
   constexpr int KPM = MS == 32 ? 16 : 32;  // keys per second-product MFMA
   constexpr int ST = BC / KPM;        // k-steps of the second product
@@ -392,7 +398,7 @@ fa2_fwd_kernel(const std::conditional_t<SPLIT, SplitProblem, Problem> P) {
   // A operand of the first product: 8 16-bit, 16 int8 or 32 FP8 values
   using KOp = std::conditional_t<F8, i32x8, std::conditional_t<Q8, i32x4, X8>>;
   using FAcc = std::conditional_t<MS == 32, f32x16, f32x4>;  // fp32 accumulator block
-  using SAcc = std::conditional_t<Q8 && !F8, i32x16, FAcc>;  // the first product's
+  using SAcc = std::conditional_t<Q8 && !F8, std::conditional_t<MS == 32, i32x16, i32x4>, FAcc>;  // the first product's
 
   constexpr int PK = C::PK;           // K operands read one iteration early
   constexpr int PV = C::PV;           // V operands read one iteration early
@@ -744,11 +750,11 @@ fa2_fwd_kernel(const std::conditional_t<SPLIT, SplitProblem, Problem> P) {
         qf[b][ks] = __builtin_bit_cast(
             X8, __builtin_amdgcn_raw_buffer_load_b128(q_rs, qrow_off + (ks * KD + lg * 8) * 2, 0, 0));
     } else if constexpr (F8 && MODE != kZero) {
-      // In-kernel quantization of the query row to E4M3 (lanes l and l+32
-      // hold its two halves): for k-step ks this lane holds channels
-      // 64 ks + 32 half + 0..31.  u = q * ks in binary32; amax over the
-      // row; codes e4m3_rne(u * (448 / amax)) and sq = amax / 448, both
-      // divisions correctly rounded (a zero row: codes 0, sq 0).
+      // In-kernel quantization of the query row to E4M3 (the lanes of a row,
+      // k-group lg = lane / MS, hold its parts): for k-step ks this lane
+      // holds channels KD ks + 32 lg + 0..31.  u = q * ks in binary32; amax
+      // over the row; codes e4m3_rne(u * (448 / amax)) and sq = amax / 448,
+      // both divisions correctly rounded (a zero row: codes 0, sq 0).
       using Q16 = typename Vec<FP16>::x8;
       const float* ksp = P.ks + (int64_t)bh * D;
       float u[KS][32];
@@ -757,7 +763,7 @@ fa2_fwd_kernel(const std::conditional_t<SPLIT, SplitProblem, Problem> P) {
       for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
         for (int h4 = 0; h4 < 4; ++h4) {
-          const int ch = 64 * ks + 32 * half + 8 * h4;
+          const int ch = KD * ks + 32 * lg + 8 * h4;
           const Q16 qv = __builtin_bit_cast(
               Q16, __builtin_amdgcn_raw_buffer_load_b128(q_rs, qrow_off + ch * 2, 0, 0));
           const float4 s0 = *(const float4*)(ksp + ch);
@@ -771,6 +777,7 @@ fa2_fwd_kernel(const std::conditional_t<SPLIT, SplitProblem, Problem> P) {
           }
         }
       }
+      if constexpr (MS == 16) amax = fmaxf(amax, __shfl_xor(amax, 16));
       amax = fmaxf(amax, other_half(amax, lane));
       const bool nonzero = amax > 0.0f;
       const float to448 = nonzero ? __fdiv_rn(448.0f, amax) : 0.0f;
@@ -790,9 +797,9 @@ fa2_fwd_kernel(const std::conditional_t<SPLIT, SplitProblem, Problem> P) {
       const float cq = c * sq;
       c_q[b] = cq != 0.0f ? cq : (MODE == kNegative ? -FLT_MIN : FLT_MIN);
     } else if constexpr (MODE != kZero) {
-      // In-kernel quantization of the query row (lanes l and l+32 hold its
-      // two halves): for k-step ks this lane holds channels 32 ks + 16 half
-      // + 0..15.  u = q * ks in binary32; amax over the row; codes
+      // In-kernel quantization of the query row (the lanes of a row, k-group
+      // lg = lane / MS, hold its parts): for k-step ks this lane holds
+      // channels KD ks + 16 lg + 0..15.  u = q * ks in binary32; amax over the row; codes
       // clamp(rint(u * (127 / amax)), +-127) and sq = amax / 127, both
       // divisions correctly rounded (a zero row: codes 0, sq 0).
       using Q16 = typename Vec<FP16>::x8;
@@ -801,7 +808,7 @@ fa2_fwd_kernel(const std::conditional_t<SPLIT, SplitProblem, Problem> P) {
       float amax = 0.0f;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const int ch = 32 * ks + 16 * half;
+        const int ch = KD * ks + 16 * lg;
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
           const Q16 qv = __builtin_bit_cast(
@@ -817,6 +824,7 @@ fa2_fwd_kernel(const std::conditional_t<SPLIT, SplitProblem, Problem> P) {
           }
         }
       }
+      if constexpr (MS == 16) amax = fmaxf(amax, __shfl_xor(amax, 16));
       amax = fmaxf(amax, other_half(amax, lane));
       const bool nonzero = amax > 0.0f;
       const float inv = nonzero ? __fdiv_rn(127.0f, amax) : 0.0f;
@@ -917,18 +925,23 @@ fa2_fwd_kernel(const std::conditional_t<SPLIT, SplitProblem, Problem> P) {
 #pragma unroll
       for (int kk = 0; kk < KB; ++kk)
 #pragma unroll
-        for (int i = 0; i < (Q8 ? 16 : NACC); ++i) sd[b][kk][i] = 0;
+        for (int i = 0; i < NACC; ++i) sd[b][kk][i] = 0;
     if constexpr (MODE == kZero) return;
 #pragma unroll
     for (int o = 0; o < KO; ++o) {
       const KOp a = o < PK ? pre[o < PK ? o : 0] : k_operand(t, s, o);
 #pragma unroll
       for (int b = 0; b < QB; ++b) {
-        if constexpr (F8)  // E4M3 x E4M3 (format 0 for both operands), fp32 sums, no block scales
+        if constexpr (F8 && MS == 32)  // E4M3 x E4M3 (format 0 for both operands), fp32 sums, no block scales
           sd[b][o % KB] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[b][o / KB], sd[b][o % KB],
                                                                           0, 0, 0, 0, 0, 0);
-        else if constexpr (Q8)  // exact int32 dot products of the codes
+        else if constexpr (F8)
+          sd[b][o % KB] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qf[b][o / KB], sd[b][o % KB],
+                                                                           0, 0, 0, 0, 0, 0);
+        else if constexpr (Q8 && MS == 32)  // exact int32 dot products of the codes
           sd[b][o % KB] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qf[b][o / KB], sd[b][o % KB], 0, 0, 0);
+        else if constexpr (Q8)
+          sd[b][o % KB] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, qf[b][o / KB], sd[b][o % KB], 0, 0, 0);
         else if constexpr (MS == 32)
           sd[b][o % KB] = mfma32x32x16<FP16>(a, qf[b][o / KB], sd[b][o % KB]);
         else
@@ -1087,14 +1100,14 @@ fa2_fwd_kernel(const std::conditional_t<SPLIT, SplitProblem, Problem> P) {
     // The logits of this tile in fp32 (converted from the int32 products
     // of the INT8 cache).
     constexpr bool CONV = Q8 && !F8;
-    f32x16 s_conv[CONV ? QB : 1][CONV ? KB : 1];
+    FAcc s_conv[CONV ? QB : 1][CONV ? KB : 1];
     if constexpr (CONV) {
 #pragma unroll
       for (int b = 0; b < QB; ++b)
 #pragma unroll
         for (int kk = 0; kk < KB; ++kk)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) s_conv[b][kk][i] = (float)s_cur[b][kk][i];
+          for (int i = 0; i < NACC; ++i) s_conv[b][kk][i] = (float)s_cur[b][kk][i];
     }
     auto& sf = [&]() -> auto& {
       if constexpr (CONV)
@@ -1119,7 +1132,7 @@ fa2_fwd_kernel(const std::conditional_t<SPLIT, SplitProblem, Problem> P) {
 #pragma unroll
         for (int kk = 0; kk < KB; ++kk)
 #pragma unroll
-          for (int i = 0; i < (Q8 ? 16 : NACC); ++i) {
+          for (int i = 0; i < NACC; ++i) {
             const int key = MS == 32 ? key0 + kk * 32 + (i >> 2) * 8 + half * 4 + (i & 3)
                                      : key0 + kk * 16 + lg * 4 + i;
             if (key > lim) sf[b][kk][i] = MODE == kNegative ? INFINITY : -INFINITY;
@@ -1186,7 +1199,7 @@ fa2_fwd_kernel(const std::conditional_t<SPLIT, SplitProblem, Problem> P) {
 #pragma unroll
         for (int kk = 0; kk < KB; ++kk)
 #pragma unroll
-          for (int i = 0; i < (Q8 ? 16 : NACC); ++i)
+          for (int i = 0; i < NACC; ++i)
             ext = MODE == kNegative ? fminf(ext, sf[b][kk][i]) : fmaxf(ext, sf[b][kk][i]);
         const float t_max = __builtin_isfinite(ext) ? ext * c_q[b] : -INFINITY;
         const float t_row = row_max(t_max);
@@ -1227,7 +1240,7 @@ fa2_fwd_kernel(const std::conditional_t<SPLIT, SplitProblem, Problem> P) {
 #pragma unroll
       for (int kk = 0; kk < KB; ++kk)
 #pragma unroll
-        for (int i = 0; i < (Q8 ? 16 : NACC); ++i) sA[b][kk][i] = sB[b][kk][i] = 0;
+        for (int i = 0; i < NACC; ++i) sA[b][kk][i] = sB[b][kk][i] = 0;
   }
   if (n_tiles > 0) {
     // Prologue: Q, K_0 .. K_{RING-1} and V_0 .. V_{RING-3} resident, S_0
@@ -1563,7 +1576,7 @@ const void* pick_split_mode(int mode) {
   }
 }
 
-// Quantized caches (QK 1: INT8, 2: FP8), d = 64 or 128, 128-row tiles.
+// Quantized caches (QK 1: INT8, 2: FP8), 128-row tiles.
 template <int D, int QK, bool FP16, bool CAUSAL>
 const void* pick_split_q8_mode(int mode) {
   switch (mode) {
@@ -1582,7 +1595,9 @@ const void* pick_split_q8(bool fp16, int mode, bool causal) {
 static_assert(kSplitRows<128> == Cfg8S<128>::NW * Cfg8S<128>::MS * Cfg8S<128>::QB &&
                   kSplitKeys<128> == Cfg8S<128>::BC &&
                   kSplitRows<64> == Cfg8S<64>::NW * Cfg8S<64>::MS * Cfg8S<64>::QB &&
-                  kSplitKeys<64> == Cfg8S<64>::BC,
+                  kSplitKeys<64> == Cfg8S<64>::BC &&
+                  kSplitRows<256> == Cfg8S<256>::NW * Cfg8S<256>::MS * Cfg8S<256>::QB &&
+                  kSplitKeys<256> == Cfg8S<256>::BC,
               "the quantized split kernels share the 16-bit split plan");
 
 template <int D>
@@ -1644,7 +1659,7 @@ const char* fa2_strerror(int status) {
     case FA2_OK: return "success";
     case FA2_ERR_NULL: return "a required pointer is NULL";
     case FA2_ERR_SHAPE: return "a size is negative, heads do not group, or sizes are too large";
-    case FA2_ERR_HEADDIM: return "head dimension must be 64, 128 or 256 (64 or 128 for the quantized caches)";
+    case FA2_ERR_HEADDIM: return "head dimension must be 64, 128 or 256";
     case FA2_ERR_DTYPE: return "dtype must be FA2_BF16 or FA2_FP16";
     case FA2_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
     case FA2_ERR_SCALE: return "scale must be finite";
@@ -1715,7 +1730,7 @@ SplitPlan plan_split(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
 int check_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
                 int causal, int dtype, bool q8) {
   if (dtype != FA2_BF16 && dtype != FA2_FP16) return FA2_ERR_DTYPE;
-  if (q8 ? (d != 64 && d != 128) : (d != 64 && d != 128 && d != 256)) return FA2_ERR_HEADDIM;
+  if (d != 64 && d != 128 && d != 256) return FA2_ERR_HEADDIM;
   if (causal != 0 && causal != 1) return FA2_ERR_OPTION;
   if (B < 0 || Hq < 0 || Hkv < 0 || Nq < 0 || Nk < 0) return FA2_ERR_SHAPE;
   if (B == 0 || Hq == 0 || Nq == 0) return 1;  // no output rows
@@ -1734,7 +1749,8 @@ int check_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int6
   int bq = 0, bk = 0, nw = 0;
   fa2_tile_config(d, dtype, &bq, &bk, &nw);
   const int64_t bq_min = q8 ? (d == 64 ? Cfg8<64>::NW * Cfg8<64>::MS * Cfg8<64>::QB
-                                      : Cfg8<128>::NW * Cfg8<128>::MS * Cfg8<128>::QB)
+                               : d == 128 ? Cfg8<128>::NW * Cfg8<128>::MS * Cfg8<128>::QB
+                                          : Cfg8<256>::NW * Cfg8<256>::MS * Cfg8<256>::QB)
                        : d == 128 ? CfgS<128>::NW * CfgS<128>::MS * CfgS<128>::QB : bq;
   if (B * Hkv > (((int64_t)1 << 31) - 1) / ((rows + bq_min - 1) / bq_min)) return FA2_ERR_SHAPE;
   return FA2_OK;
@@ -1849,8 +1865,9 @@ int launch(const void* q, const void* k, const void* v, const float* ks, const f
   }
   if (q8) {
     bq = d == 64 ? Cfg8<64>::NW * Cfg8<64>::MS * Cfg8<64>::QB
-                 : Cfg8<128>::NW * Cfg8<128>::MS * Cfg8<128>::QB;
-    nw = d == 64 ? Cfg8<64>::NW : Cfg8<128>::NW;
+       : d == 128 ? Cfg8<128>::NW * Cfg8<128>::MS * Cfg8<128>::QB
+                  : Cfg8<256>::NW * Cfg8<256>::MS * Cfg8<256>::QB;
+    nw = d == 64 ? Cfg8<64>::NW : d == 128 ? Cfg8<128>::NW : Cfg8<256>::NW;
   } else if (persist && d == 64) {
     bq = CfgP<64>::NW * CfgP<64>::MS * CfgP<64>::QB;
     nw = CfgP<64>::NW;
@@ -1890,13 +1907,15 @@ int launch(const void* q, const void* k, const void* v, const float* ks, const f
     SP.part_lse = (float*)ws + (int64_t)splits * SP.part_rows * d;
     SP.splits = splits;
     const void* sfn = qk == 2 ? (d == 64 ? pick_split_q8<64, 2>(fp16, mode, causal)
-                                         : pick_split_q8<128, 2>(fp16, mode, causal))
+                                 : d == 128 ? pick_split_q8<128, 2>(fp16, mode, causal)
+                                            : pick_split_q8<256, 2>(fp16, mode, causal))
                     : qk == 1 ? (d == 64 ? pick_split_q8<64, 1>(fp16, mode, causal)
-                                         : pick_split_q8<128, 1>(fp16, mode, causal))
+                                 : d == 128 ? pick_split_q8<128, 1>(fp16, mode, causal)
+                                            : pick_split_q8<256, 1>(fp16, mode, causal))
                     : d == 64 ? pick_split<64>(fp16, mode, causal)
                     : d == 128 ? pick_split<128>(fp16, mode, causal)
                                : pick_split<256>(fp16, mode, causal);
-    const int snw = q8 ? (d == 64 ? Cfg8S<64>::NW : Cfg8S<128>::NW)
+    const int snw = q8 ? (d == 64 ? Cfg8S<64>::NW : d == 128 ? Cfg8S<128>::NW : Cfg8S<256>::NW)
                   : d == 64 ? SplitCfg<64>::C::NW : d == 128 ? SplitCfg<128>::C::NW
                                                              : SplitCfg<256>::C::NW;
     void* sargs[] = {&SP};
@@ -1921,8 +1940,10 @@ int launch(const void* q, const void* k, const void* v, const float* ks, const f
                           (hipStream_t)stream);
     return err == hipSuccess ? FA2_OK : FA2_ERR_HIP;
   }
-  kernel_fn fn = qk == 2 ? (d == 64 ? pick<64, 2>(fp16, mode, causal) : pick<128, 2>(fp16, mode, causal))
-               : q8 ? (d == 64 ? pick<64, 1>(fp16, mode, causal) : pick<128, 1>(fp16, mode, causal))
+  kernel_fn fn = qk == 2 ? (d == 64 ? pick<64, 2>(fp16, mode, causal)
+                           : d == 128 ? pick<128, 2>(fp16, mode, causal) : pick<256, 2>(fp16, mode, causal))
+               : q8 ? (d == 64 ? pick<64, 1>(fp16, mode, causal)
+                       : d == 128 ? pick<128, 1>(fp16, mode, causal) : pick<256, 1>(fp16, mode, causal))
                : d == 64 ? pick<64, 0>(fp16, mode, causal)
                : d == 128 ? (short_keys ? pick<128, 0, true>(fp16, mode, causal)
                                         : pick<128, 0>(fp16, mode, causal))

@@ -231,7 +231,7 @@ def _kv_quantized(raw, code_dtype, what, q, kq, ks, vq, vs, scale, causal, out, 
 def fwd_kv_int8(q, kq, ks, vq, vs, scale=None, causal=False, out=None, lse=None):
     """Attention over an INT8 key/value cache: returns (o, lse).
 
-    q: [B, Hq, Nq, d] bf16 or fp16 (d = 64 or 128); kq, vq: [B, Hkv, Nk, d]
+    q: [B, Hq, Nq, d] bf16 or fp16 (d = 64, 128 or 256); kq, vq: [B, Hkv, Nk, d]
     int8 codes; ks, vs: [B, Hkv, d] float32 per-channel scales (k = ks * kq, v = vs *
     vq).  The query rows are quantized to int8 in the kernel (see fa2.h);
     other arguments as in `fwd`.  All tensors contiguous on one GPU.

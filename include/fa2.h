@@ -54,8 +54,7 @@ enum fa2_status {
                            the grid overflows, or the query rows of one K/V
                            head ((Hq/Hkv)*Nq*d) or its key rows (Nk*d) exceed
                            2^31 - 2^20 elements */
-  FA2_ERR_HEADDIM = -3, /* d is not 64, 128 or 256 (64 or 128 for the INT8 and
-                           FP8 caches) */
+  FA2_ERR_HEADDIM = -3, /* d is not 64, 128 or 256 */
   FA2_ERR_DTYPE = -4,   /* dtype is not an fa2_dtype */
   FA2_ERR_ALIGN = -5,   /* q, k, v, o or a workspace not 16-byte aligned, lse
                            not 4-byte */
@@ -163,7 +162,7 @@ int fa2_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse
  *   kq, vq   : [B][Hkv][Nk][d] int8 codes (may be NULL when Nk == 0).
  *   ks, vs   : [B][Hkv][d] fp32 scales (required).
  *   lse      : [B][Hq][Nq] fp32.
- *   d        : 64 or 128 (FA2_ERR_HEADDIM otherwise).
+ *   d        : 64, 128 or 256 (FA2_ERR_HEADDIM otherwise).
  *   Alignment: q, kq, vq, o, ks, vs 16-byte aligned, lse 4-byte.  No output
  *   may overlap an input or the other output.
  *
@@ -202,7 +201,7 @@ int fa2_fwd_kv_int8(const void* q, const int8_t* kq, const float* ks, const int8
  *   q, o     : [B][Hq][Nq][d], element type `dtype` (bf16 or fp16).
  *   kq, vq   : [B][Hkv][Nk][d] E4M3 codes (may be NULL when Nk == 0).
  *   ks, vs   : [B][Hkv][d] fp32 scales (required).
- *   d        : 64 or 128 (FA2_ERR_HEADDIM otherwise).
+ *   d        : 64, 128 or 256 (FA2_ERR_HEADDIM otherwise).
  *
  * Alignment, heads, lengths, causal, asynchrony and return codes are those
  * of fa2_fwd_kv_int8.
@@ -260,7 +259,7 @@ int fa2_fwd_split(const void* q, const void* k, const void* v, void* o, float* l
 
 /*
  * fa2_fwd_split_workspace -- bytes of workspace fa2_fwd_split (cache = 0) or
- * fa2_fwd_kv_split (cache = FA2_CACHE_INT8 or FA2_CACHE_FP8, d = 64 or 128) needs
+ * fa2_fwd_kv_split (cache = FA2_CACHE_INT8 or FA2_CACHE_FP8) needs
  * for these arguments: splits * B*Hq*Nq * (d + 1) * 4 (the partial outputs,
  * then the partial logsumexps), or 0 when the call runs without splits.
  * With splits = 0 the count is chosen as those calls choose it on the
@@ -280,7 +279,7 @@ int64_t fa2_fwd_split_workspace(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, 
  * unsplit call does, so the parts' logits are those of fa2_fwd_kv_int8 /
  * fa2_fwd_kv_fp8; their partials are merged as in fa2_fwd_split.
  *
- *   q, kq, ks, vq, vs, o, lse, B, Hq, Hkv, Nq, Nk, d (64 or 128), scale, causal,
+ *   q, kq, ks, vq, vs, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal,
  *   dtype, stream: as in fa2_fwd_kv_int8 (kq, vq void: int8 or E4M3 codes).
  *   cache    : an fa2_cache (FA2_ERR_OPTION otherwise).
  *   splits, workspace, workspace_bytes: as in fa2_fwd_split (splits = 0

@@ -166,7 +166,7 @@ def call_int8(raw=None, **kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(d=96), fa2.ERR_HEADDIM), (dict(d=256), fa2.ERR_HEADDIM), (dict(dtype=3), fa2.ERR_DTYPE),
+    (dict(d=96), fa2.ERR_HEADDIM), (dict(d=512), fa2.ERR_HEADDIM), (dict(dtype=3), fa2.ERR_DTYPE),
     (dict(causal=2), fa2.ERR_OPTION), (dict(Hkv=3), fa2.ERR_SHAPE), (dict(Nk=-1), fa2.ERR_SHAPE),
     (dict(q=0), fa2.ERR_NULL), (dict(kq=0), fa2.ERR_NULL), (dict(ks=0), fa2.ERR_NULL),
     (dict(vs=0), fa2.ERR_NULL), (dict(ks=0, Nk=0), fa2.ERR_NULL),
@@ -218,7 +218,7 @@ def test_split_workspace_size(lib):
     for kw, code in [(dict(splits=129), fa2.ERR_OPTION), (dict(splits=-1), fa2.ERR_OPTION),
                      (dict(d=96), fa2.ERR_HEADDIM), (dict(Hkv=3), fa2.ERR_SHAPE),
                      (dict(dtype=2), fa2.ERR_DTYPE), (dict(causal=2), fa2.ERR_OPTION),
-                     (dict(cache=3), fa2.ERR_OPTION), (dict(cache=1, d=256), fa2.ERR_HEADDIM)]:
+                     (dict(cache=3), fa2.ERR_OPTION), (dict(cache=1, d=96), fa2.ERR_HEADDIM)]:
         a = dict(B=2, Hq=4, Hkv=2, Nq=100, Nk=70, d=128, causal=1, dtype=fa2.BF16, splits=4)
         a.update(kw)
         assert lib.fa2_fwd_split_workspace(a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["d"],
@@ -259,7 +259,7 @@ def call_kv_split(cache=fa2.CACHE_FP8, splits=4, ws=WS, ws_bytes=1 << 24, **kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(cache=0), fa2.ERR_OPTION), (dict(cache=3), fa2.ERR_OPTION),
-    (dict(splits=200), fa2.ERR_OPTION), (dict(d=256), fa2.ERR_HEADDIM),
+    (dict(splits=200), fa2.ERR_OPTION), (dict(d=32), fa2.ERR_HEADDIM),
     (dict(ks=0), fa2.ERR_NULL), (dict(ws=0), fa2.ERR_WORKSPACE),
     (dict(ws_bytes=100), fa2.ERR_WORKSPACE), (dict(ws=WS + 4), fa2.ERR_ALIGN),
     (dict(ws=A + 0x4000000), fa2.ERR_ALIAS),           # workspace over vs

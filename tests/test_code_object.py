@@ -75,7 +75,8 @@ def test_every_kernel_is_present(kernels):
                 (64, 0, 0, 0, 1): 12, (128, 0, 1, 0, 1): 12, (256, 0, 0, 0, 1): 12,
                 (128, 1, 1, 0, 1): 12, (128, 2, 1, 0, 1): 12,
                 (64, 1, 0, 0, 0): 12, (64, 2, 0, 0, 0): 12, (64, 1, 1, 0, 1): 12,
-                (64, 2, 1, 0, 1): 12}
+                (64, 2, 1, 0, 1): 12, (256, 1, 0, 0, 0): 12, (256, 2, 0, 0, 0): 12,
+                (256, 1, 1, 0, 1): 12, (256, 2, 1, 0, 1): 12}
     count = {}
     for (d, fp16, mode, causal, q8, short, persist, split) in kernels:
         key = (d, q8, short, persist, split)
@@ -98,7 +99,9 @@ def test_two_waves_per_simd(kernels):
 def test_head_dim_256_lds_is_the_two_rings(kernels):
     """d = 256: four-slot K and V rings of 32-key tiles (128 KiB) and nothing
     else (the output is staged in the rings after the loop), so one
-    workgroup of 8 waves runs per CU."""
+    workgroup of 8 waves runs per CU.  The quantized caches hold 8-bit K
+    tiles and an 8-bit V staging ring beside the 16-bit V ring: the same
+    128 KiB."""
     for k, r in kernels.items():
         if k[0] == 256:
             assert r["lds"] == 4 * 2 * 32 * 256 * 2 == 128 * 1024, (k, r)

@@ -46,7 +46,7 @@ def check(inputs, dtype, scale, causal, tag, rows=None):
 
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk", [
     (1, 2, 2, 64, 64), (1, 2, 1, 100, 300), (2, 4, 2, 257, 513), (1, 8, 1, 5, 1000),
     (1, 2, 2, 1, 1), (1, 3, 3, 300, 90), (1, 4, 4, 32, 33)])
@@ -60,7 +60,7 @@ def test_int8_cache(B, Hq, Hkv, Nq, Nk, d, dtype, causal):
 
 @pytest.mark.parametrize("scale", [0.0, -0.2, 1.5])
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_int8_scales(d, scale, causal):
     announce("int8 scale", d, scale, causal)
     inputs = make_inputs_kv_int8(1, 4, 2, 200, 333, d, "bf16", seed=3)

@@ -144,7 +144,7 @@ QUANTIZED = {"int8": (fa2.CACHE_INT8, make_inputs_kv_int8, "attention_kv_int8"),
 @pytest.mark.parametrize("splits", [0, 3, 16])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("fmt", ["int8", "fp8"])
 def test_quantized_cache_decode(fmt, d, dtype, causal, splits):
     """Decode rows over an INT8 / FP8 cache with key splits, against the
