@@ -244,7 +244,7 @@ template <> struct Cfg<64> { static constexpr int BC = 64, NW = 4, QB = 1, OCC =
 template <> struct Cfg<128> { static constexpr int BC = 32, NW = 8, QB = 1, OCC = 2, SGB = 0, RING = 4, PK = 4, PV = 2, MS = 32; };
 template <> struct Cfg<256> { static constexpr int BC = 32, NW = 8, QB = 1, OCC = 2, SGB = 0, RING = 4, PK = 4, PV = 2, MS = 16; };
 
-// Tile shape of the INT8 key/value cache kernels (d = 128 only).
+// Tile shapes of the INT8 and FP8 key/value cache kernels.
 template <int D> struct Cfg8;
 template <> struct Cfg8<128> { static constexpr int BC = 32, NW = 8, QB = 1, OCC = 2, SGB = 0, RING = 4, PK = 2, PV = 2, MS = 32; };
 // d = 64: 64-key tiles, so a code tile (4 KiB) and its fp16 widening (8 KiB)
@@ -253,8 +253,9 @@ template <> struct Cfg8<64> { static constexpr int BC = 64, NW = 8, QB = 1, OCC 
 // d = 256: 16-row waves on the 16x16 int8 / FP8 shapes, as the 16-bit d = 256
 // kernels.
 template <> struct Cfg8<256> { static constexpr int BC = 32, NW = 8, QB = 1, OCC = 2, SGB = 0, RING = 4, PK = 1, PV = 2, MS = 16; };
-// The quantized caches with key splits: 128-row tiles (four waves), as the
-// 16-bit split kernels, so that decoding forms one tile per K/V head.
+// The quantized caches with key splits: 128-row tiles (four 32-row waves, or
+// eight 16-row waves at d = 256), as the 16-bit split kernels, so that
+// decoding forms one tile per K/V head.
 template <int D> struct Cfg8S;
 template <> struct Cfg8S<128> { static constexpr int BC = 32, NW = 4, QB = 1, OCC = 2, SGB = 0, RING = 4, PK = 2, PV = 2, MS = 32; };
 template <> struct Cfg8S<64> { static constexpr int BC = 64, NW = 4, QB = 1, OCC = 2, SGB = 0, RING = 4, PK = 2, PV = 2, MS = 32; };
@@ -312,11 +313,11 @@ enum ScaleMode { kPositive = 0, kNegative = 1, kZero = 2 };
 // (causal_off = nk - nq).
 struct Problem {
   const uint16_t* q;
-  const char* k;     // 16-bit elements, or int8 codes for the INT8 cache
+  const char* k;     // 16-bit elements, or 8-bit codes for the INT8 / FP8 caches
   const char* v;
   uint16_t* o;
   float* lse;
-  const float* ks;   // INT8 cache only: per-channel scales [B][hkv][D]
+  const float* ks;   // quantized caches only: per-channel scales [B][hkv][D]
   const float* vs;
   int nq, nk;        // query rows per query head, key rows per K/V head
   int rows;          // query rows per K/V head (its query heads back to back)
@@ -373,7 +374,7 @@ fa2_fwd_kernel(const std::conditional_t<SPLIT, SplitProblem, Problem> P) {
   constexpr int TBYTES = BC * RB;     // one V tile in LDS
   constexpr int RBK = Q8 ? D : RB;    // bytes per K row in LDS (int8 or 16-bit)
   constexpr int CPRK = RBK / 16;      // 16-byte chunks per K row
-  constexpr int TBK = BC * RBK;       // one K tile in LDS (and one int8 V tile)
+  constexpr int TBK = BC * RBK;       // one K tile in LDS (and one 8-bit V tile)
   constexpr int LW = Q8 ? 4 : 16;     // bytes per lane of one HBM -> LDS load
   constexpr int LOADS = TBK / (NW * 64 * LW);  // K loads per thread per tile (V: the same)
   // contraction depth of one first-product MFMA (16 bytes of codes per lane,
@@ -547,7 +548,7 @@ fa2_fwd_kernel(const std::conditional_t<SPLIT, SplitProblem, Problem> P) {
   // Global -> LDS without registers: each wave load moves 64 lanes x LW bytes
   // (lane l to byte LW*l of its piece).  The swizzles (on 16-byte chunks) are
   // applied on the global side: a lane fetches the bytes that belong at its
-  // LDS position.  With Q8 the int8 V tile is staged unswizzled.  Rows past N
+  // LDS position.  With Q8 the 8-bit V tile is staged unswizzled.  Rows past N
   // read as zeros (buffer range check); their keys are masked later.
   uint32_t k_src[LOADS], v_src[LOADS];
 #pragma unroll
@@ -1098,7 +1099,7 @@ fa2_fwd_kernel(const std::conditional_t<SPLIT, SplitProblem, Problem> P) {
     }
 
     // The logits of this tile in fp32 (converted from the int32 products
-    // of the INT8 cache).
+    // of the INT8 cache; the FP8 products are fp32 already).
     constexpr bool CONV = Q8 && !F8;
     FAcc s_conv[CONV ? QB : 1][CONV ? KB : 1];
     if constexpr (CONV) {
@@ -1416,7 +1417,7 @@ fa2_fwd_kernel(const std::conditional_t<SPLIT, SplitProblem, Problem> P) {
         // output channels ch .. ch+3
         const int ch = db * MS + g4 * 8 + elg * 4;
         float vsc[4] = {1.0f, 1.0f, 1.0f, 1.0f};
-        if constexpr (Q8) {  // the per-channel value scales of the INT8 cache
+        if constexpr (Q8) {  // the per-channel value scales of the quantized cache
           const float4 f = *(const float4*)(P.vs + (int64_t)bh * D + ch);
           vsc[0] = f.x; vsc[1] = f.y; vsc[2] = f.z; vsc[3] = f.w;
         }
