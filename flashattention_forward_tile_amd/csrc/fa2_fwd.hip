@@ -208,13 +208,6 @@ __device__ __forceinline__ void load_lds16(i32x4 rsrc, uint32_t voff, uint32_t l
                : "v"(voff), "s"(rsrc), "{m0}"(lds_addr)
                : "memory");
 }
-// The same with 4 bytes per lane: lane l writes LDS bytes [m0 + 4 l, m0 + 4 l + 4).
-__device__ __forceinline__ void load_lds4(i32x4 rsrc, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("buffer_load_dword %0, %1, 0 offen lds"
-               :
-               : "v"(voff), "s"(rsrc), "{m0}"(lds_addr)
-               : "memory");
-}
 
 // Tile shape per head dimension: key rows per tile (BC), waves per workgroup
 // (NW), MS-query blocks per wave (QB), the waves per SIMD the register
@@ -375,8 +368,12 @@ fa2_fwd_kernel(const std::conditional_t<SPLIT, SplitProblem, Problem> P) {
   constexpr int RBK = Q8 ? D : RB;    // bytes per K row in LDS (int8 or 16-bit)
   constexpr int CPRK = RBK / 16;      // 16-byte chunks per K row
   constexpr int TBK = BC * RBK;       // one K tile in LDS (and one 8-bit V tile)
-  constexpr int LW = Q8 ? 4 : 16;     // bytes per lane of one HBM -> LDS load
-  constexpr int LOADS = TBK / (NW * 64 * LW);  // K loads per thread per tile (V: the same)
+  // HBM -> LDS loads move 16 bytes per lane.  A tile smaller than one such
+  // load per lane of the workgroup (8-bit tiles of 4 KiB over eight waves)
+  // is loaded by its first LNW waves only.
+  constexpr int LW = 16;
+  constexpr int LNW = TBK / (64 * LW) < NW ? TBK / (64 * LW) : NW;  // waves that load K / V
+  constexpr int LOADS = TBK / (LNW * 64 * LW);  // K loads per loading thread per tile (V: the same)
   // contraction depth of one first-product MFMA (16 bytes of codes per lane,
   // 32 for FP8, 8 16-bit values otherwise)
   constexpr int KD = F8 ? (MS == 16 ? 128 : 64) : Q8 ? (MS == 16 ? 64 : 32) : MS == 16 ? 32 : 16;
@@ -386,7 +383,7 @@ fa2_fwd_kernel(const std::conditional_t<SPLIT, SplitProblem, Problem> P) {
   constexpr int KB = BC / MS;         // MS-key blocks per tile
   constexpr int DB = D / MS;          // MS-dim blocks of the output
   constexpr int NACC = MS * MS / 64;  // accumulator registers per lane of one block
-  static_assert(TBK % (NW * 64 * LW) == 0, "tile must split into wave loads");
+  static_assert(TBK % (LNW * 64 * LW) == 0, "tile must split into wave loads");
   static_assert(BC % 32 == 0 && D % 32 == 0, "MFMA blocking");
   // Q and O are bf16 or fp16; P and V meet on fp16 matrix instructions in the
   // INT8 kernels (V is widened exactly), on the input type otherwise.
@@ -545,17 +542,17 @@ fa2_fwd_kernel(const std::conditional_t<SPLIT, SplitProblem, Problem> P) {
   if constexpr (PERSIST) look_ahead(0);
   const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
 
-  // Global -> LDS without registers: each wave load moves 64 lanes x LW bytes
-  // (lane l to byte LW*l of its piece).  The swizzles (on 16-byte chunks) are
+  // Global -> LDS without registers: each wave load moves 64 lanes x 16 bytes
+  // (lane l to byte 16*l of its piece).  The swizzles (on 16-byte chunks) are
   // applied on the global side: a lane fetches the bytes that belong at its
   // LDS position.  With Q8 the 8-bit V tile is staged unswizzled.  Rows past N
   // read as zeros (buffer range check); their keys are masked later.
   uint32_t k_src[LOADS], v_src[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
-    const int pos = ((i * NW + wave) * 64 + lane) * LW;  // byte in the LDS tile
-    const int row = pos / RBK, pc = (pos % RBK) / 16, byte = pos % 16;
-    k_src[i] = (uint32_t)(row * RBK + k_swizzle<CPRK>(row, pc) * 16 + byte);
+    const int pos = ((i * LNW + wave) * 64 + lane) * LW;  // byte in the LDS tile (wave < LNW)
+    const int row = pos / RBK, pc = (pos % RBK) / 16;
+    k_src[i] = (uint32_t)(row * RBK + k_swizzle<CPRK>(row, pc) * 16);
     v_src[i] = Q8 ? (uint32_t)pos : (uint32_t)(row * RB + v_swizzle<CPR, MS>(row, pc) * 16);
   }
   // `s` (an integral constant) is t modulo 4, known at compile time in the
@@ -564,12 +561,6 @@ fa2_fwd_kernel(const std::conditional_t<SPLIT, SplitProblem, Problem> P) {
   auto slot = [](int, auto s) { return decltype(s)::value % RING; };
   // Tiles past the last one read as zeros (buffer range check) and are never
   // used; loading them keeps the per-iteration load count fixed.
-  auto load_lds = [&](const i32x4& rs, uint32_t voff, uint32_t dst) {
-    if constexpr (LW == 4)
-      load_lds4(rs, voff, dst);
-    else
-      load_lds16(rs, voff, dst);
-  };
   // PERSIST: with `nx` (a compile-time flag) tile t is tile t - n_cur of
   // the next item, n_cur being the current item's key-tile count.
   int n_cur = (N + BC - 1) / BC;
@@ -580,9 +571,10 @@ fa2_fwd_kernel(const std::conditional_t<SPLIT, SplitProblem, Problem> P) {
       rs = rebase(k_rs, nx_delta);
       t -= n_cur;
     }
+    if (LNW == NW || wave < LNW)
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i)
-      load_lds(rs, (uint32_t)t * TBK + k_src[i], dst + i * NW * 64 * LW);
+      for (int i = 0; i < LOADS; ++i)
+        load_lds16(rs, (uint32_t)t * TBK + k_src[i], dst + i * LNW * 64 * LW);
   };
   // V_t into the V ring, or with Q8 into the int8 staging ring.
   auto issue_v = [&](int t, auto s, auto nx) {
@@ -593,9 +585,10 @@ fa2_fwd_kernel(const std::conditional_t<SPLIT, SplitProblem, Problem> P) {
       rs = rebase(v_rs, nx_delta);
       t -= n_cur;
     }
+    if (LNW == NW || wave < LNW)
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i)
-      load_lds(rs, (uint32_t)t * TBK + v_src[i], dst + i * NW * 64 * LW);
+      for (int i = 0; i < LOADS; ++i)
+        load_lds16(rs, (uint32_t)t * TBK + v_src[i], dst + i * LNW * 64 * LW);
   };
   // PERSIST: query tile qt_r of the group that descriptor rs covers into the
   // query / output area, swizzled like K (QLOADS 16-byte loads per thread).
@@ -1222,8 +1215,9 @@ fa2_fwd_kernel(const std::conditional_t<SPLIT, SplitProblem, Problem> P) {
 #pragma unroll
     for (int b = 0; b < QB; ++b) l_part[b] += rs[b];
 
-    // The loads issued during iteration j-1 have landed.  (PERSIST: the first
-    // iteration's query loads may stay in flight too.)
+    // The loads issued during iteration j-1 have landed (waves past LNW have
+    // none in flight).  (PERSIST: the first iteration's query loads may stay
+    // in flight too.)
     if constexpr (kSyncCheck)
       wait_vmem();
     else
