@@ -1216,8 +1216,9 @@ fa2_fwd_kernel(const std::conditional_t<SPLIT, SplitProblem, Problem> P) {
     for (int b = 0; b < QB; ++b) l_part[b] += rs[b];
 
     // The loads issued during iteration j-1 have landed (waves past LNW have
-    // none in flight).  (PERSIST: the first iteration's query loads may stay
-    // in flight too.)
+    // none in flight: LNW < NW only with 8-bit tiles, never persistent, so
+    // such a wave issues no query loads either).  (PERSIST: the first
+    // iteration's query loads may stay in flight too.)
     if constexpr (kSyncCheck)
       wait_vmem();
     else
