@@ -1712,6 +1712,12 @@ SplitPlan plan_split(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
     const int64_t k_tiles = (Nk + bc - 1) / bc;
     const int64_t per_cu = qk != 0 ? 2 : 1;
     int64_t want = cus > 0 ? (per_cu * cus + items - 1) / items : 1;
+    // Items whose rows fill at most half a tile (a few query rows per K/V
+    // head, as in decoding) take at least two parts once the keys are long
+    // enough, even when the items alone fill the GPU: the split kernels'
+    // half-height tiles leave their padding waves idle, which the unsplit
+    // ones do not.
+    if (rows * 2 <= br && k_tiles >= 64 && want < 2) want = 2;
     want = want < k_tiles / 8 ? want : k_tiles / 8;
     want = want < kMaxSplits ? want : kMaxSplits;
     splits = (int)(want > 1 ? want : 1);

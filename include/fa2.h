@@ -235,8 +235,11 @@ int fa2_fwd_kv_fp8(const void* q, const uint8_t* kq, const float* ks, const uint
  *              then it contributes nothing), 1 = fa2_fwd_ext itself, or 0 =
  *              chosen here: enough parts for one workgroup per compute unit
  *              of the current device over the call's 128-row query tiles,
- *              each part keeping at least 8 key tiles (1 if that leaves one
- *              part).  The choice queries the device's compute-unit count
+ *              and at least 2 when each K/V head has at most 64 query rows
+ *              (Hq / Hkv * Nq) and at least 64 key tiles (of 32 keys; 64
+ *              at d = 64), each part keeping at least 8 key tiles (1 if
+ *              that leaves one part).  The
+ *              choice queries the device's compute-unit count
  *              (a HIP attribute query, after every argument check except the
  *              workspace's).
  *   workspace: device memory of at least fa2_fwd_split_workspace(...) bytes

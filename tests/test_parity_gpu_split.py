@@ -66,7 +66,8 @@ def test_decode_rows(d, dtype, causal, splits):
     (1, 4, 1, 37, 3000, 0), (2, 8, 2, 64, 4096, 3), (1, 2, 2, 130, 2049, 7),
     (1, 4, 4, 200, 100, 8),      # more splits than key tiles: empty parts
     (1, 2, 1, 300, 200, 4),      # causal: rows before Nq - Nk see no key
-    (3, 6, 3, 5, 33, 2), (1, 1, 1, 1, 1, 2), (1, 4, 2, 1, 70000, 128)])
+    (3, 6, 3, 5, 33, 2), (1, 1, 1, 1, 1, 2), (1, 4, 2, 1, 70000, 128),
+    (128, 4, 2, 1, 2048, 0)])    # items fill the GPU: the library's floor of two parts
 @pytest.mark.parametrize("causal", [False, True])
 def test_chunks(B, Hq, Hkv, Nq, Nk, splits, causal):
     announce("split chunk", B, Hq, Hkv, Nq, Nk, splits, causal)
@@ -135,6 +136,15 @@ def test_chosen_split_count_uses_the_compute_units():
     for cache in (fa2.CACHE_INT8, fa2.CACHE_FP8):
         n = fa2.split_workspace_bytes(4, 32, 8, 1, 32768, 128, True, fa2.BF16, 0, cache)
         assert n // per_split == min(-(-2 * cus // items), 32768 // 32 // 8, 128)
+    # Items of a few rows each that already fill the GPU: at least two parts
+    # from 64 key tiles on, none below that or for rows filling most of a tile.
+    for B, Nk in ((64, 4096), (2 * cus, 2048)):
+        for cache in (0, fa2.CACHE_INT8, fa2.CACHE_FP8):
+            n = fa2.split_workspace_bytes(B, 32, 8, 1, Nk, 128, True, fa2.BF16, 0, cache)
+            parts = n // (B * 32 * 1 * (128 + 1) * 4)
+            assert parts == max(2, -(-(2 if cache else 1) * cus // (B * 8))), (B, Nk, cache, parts)
+    assert fa2.split_workspace_bytes(2 * cus, 32, 8, 1, 1024, 128, True, fa2.BF16, 0) == 0
+    assert fa2.split_workspace_bytes(2 * cus, 32, 8, 32, 4096, 128, True, fa2.BF16, 0) == 0
 
 
 QUANTIZED = {"int8": (fa2.CACHE_INT8, make_inputs_kv_int8, "attention_kv_int8"),
