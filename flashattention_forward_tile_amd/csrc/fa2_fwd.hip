@@ -710,13 +710,16 @@ fa2_fwd_kernel(const std::conditional_t<SPLIT, SplitProblem, Problem> P) {
   };
   // Causal: whether any row of this wave sees a key of tile t (always true
   // without the mask).
-  // SPLIT: a wave whose query rows all lie past the item's last row (the
-  // padding of a short query block: decoding fills one of four waves) runs
-  // neither product and reads no operands; it still issues its share of the
-  // loads, widens its share of V and meets every barrier.  Its logits stay
-  // 0 (set once below), so its softmax is cheap and never takes the rare
-  // path after the first tile; its rows are never written.
-  const bool live = !SPLIT || q0 < P.rows;
+  // SKIP (the key-split kernels, and the 16-bit d = 256 ones): a wave whose
+  // query rows all lie past the item's last row (the padding of a short
+  // query block: decoding fills one of four waves) runs neither product and
+  // reads no operands; it still issues its share of the loads, widens its
+  // share of V and meets every barrier.  Its logits stay 0 (set once below),
+  // so its softmax is cheap and never takes the rare path after the first
+  // tile; its rows are never written.  (The other kernels compute such waves:
+  // the check cost them 5-12% in register allocation at 254-256 VGPRs.)
+  constexpr bool SKIP = SPLIT || (D == 256 && !Q8 && !PERSIST);
+  const bool live = !SKIP || q0 < P.rows;
   auto sees = [&](int t) -> bool { return live && (!CAUSAL || t <= wave_last); };
   item_limits();
   if constexpr (SPLIT) {
@@ -1230,7 +1233,7 @@ fa2_fwd_kernel(const std::conditional_t<SPLIT, SplitProblem, Problem> P) {
   // item's S_0 from one item into the next.
   SAcc sA[QB][KB], sB[QB][KB];
   X8 pA[QB][ST], pB[QB][ST];
-  if constexpr (SPLIT) {
+  if constexpr (SKIP) {
 #pragma unroll
     for (int b = 0; b < QB; ++b)
 #pragma unroll
