@@ -2035,8 +2035,15 @@ int fa2_fwd_split_noalloc(const void* q, const void* k, const void* v, void* o, 
                           int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
                           int64_t d, float scale, int causal, int dtype, int splits,
                           void* stream) {
-  const int64_t need = fa2_fwd_split_workspace(B, Hq, Hkv, Nq, Nk, d, causal, dtype, 0, splits);
+  int64_t need = fa2_fwd_split_workspace(B, Hq, Hkv, Nq, Nk, d, causal, dtype, 0, splits);
   if (need < 0) return (int)need;
+  if (need > fa2::kScratchBytes && splits == 0) {
+    // The library's own count does not fit: the most parts that do, or none.
+    const int64_t per_part = fa2_fwd_split_workspace(B, Hq, Hkv, Nq, Nk, d, causal, dtype, 0, 2) / 2;
+    const int64_t fit = per_part > 0 ? fa2::kScratchBytes / per_part : 0;
+    splits = fit >= 2 ? (int)fit : 1;
+    need = fit >= 2 ? fit * per_part : 0;
+  }
   if (need > fa2::kScratchBytes) return FA2_ERR_SCRATCH;
   void* ws = nullptr;
   if (need > 0) {

@@ -310,7 +310,9 @@ int fa2_fwd_kv_split(const void* q, const void* kq, const float* ks, const void*
  *   Arguments as in fa2_fwd_split, without workspace and workspace_bytes.
  *   A call whose partials (fa2_fwd_split_workspace bytes for the same
  *   arguments) exceed 16 MiB returns FA2_ERR_SCRATCH and launches nothing;
- *   e.g. with d = 128 that is splits * B*Hq*Nq above 32768 rows.
+ *   e.g. with d = 128 that is splits * B*Hq*Nq above 32513 rows.  With
+ *   splits = 0 the library's count is lowered instead to the most parts
+ *   that fit, or to none (fa2_fwd_ext) when two do not.
  *
  * Every call on one GPU shares that GPU's array, and a call only writes
  * partials before reading them (nothing needs to start at zero), so calls

@@ -67,3 +67,18 @@ def test_no_alloc_refuses_partials_beyond_its_scratch():
                                            o.data_ptr(), lse.data_ptr(), B, Hq, Hkv, Nq, Nk, d,
                                            0.1, 0, fa2.BF16, 128, 0)
     assert code == fa2.ERR_SCRATCH
+
+
+def test_no_alloc_lowers_its_own_split_count_to_fit():
+    """splits = 0 where the library's count (two parts: items of one query
+    row each with 64 key tiles) needs more than the 16 MiB scratch: the call
+    runs with the most parts that fit, here none, i.e. as fa2_fwd_ext."""
+    B, Hq, Hkv, Nq, Nk, d = 256, 64, 1, 1, 2048, 128
+    announce("no-alloc lowered count", B, Hq, Hkv, Nq, Nk, d)
+    assert fa2.split_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, True, fa2.BF16, 0) > 16 << 20
+    assert fa2.split_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, True, fa2.BF16, 2) > 16 << 20
+    q, k, v = (t.to(DEV) for t in make_inputs(B, Hq, Nq, d, "bf16", seed=7, Hkv=Hkv, Nk=Nk))
+    o, lse = no_alloc(q, k, v, True, 0)
+    o_ref, lse_ref = fa2.fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(lse, lse_ref)
