@@ -1364,10 +1364,11 @@ fa2_fwd_kernel(const std::conditional_t<SPLIT, SplitProblem, Problem> P) {
     wait_vmem();
     __syncthreads();
   }
-  if constexpr (SPLIT) {
-    // The part's fp32 output (normalised by the part's own sum) and
-    // logsumexp, straight from registers: a lane holds 4 consecutive
-    // channels of one row per store.
+  // SPLIT with part_o set: the part's fp32 output (normalised by the part's
+  // own sum) and logsumexp, straight from registers: a lane holds 4
+  // consecutive channels of one row per store.  Without part_o (one part,
+  // no workspace) the kernel writes O and lse itself, below.
+  if constexpr (SPLIT) if (P.part_o != nullptr) {
     const int sp = id % P.splits;
     const int64_t prow0 = (int64_t)sp * P.part_rows + (int64_t)bh * P.rows;
 #pragma unroll
@@ -1900,16 +1901,29 @@ int launch(const void* q, const void* k, const void* v, const float* ks, const f
   P.n_groups = (int)groups;
   P.causal_off = (int)(Nk - Nq);
   P.c = mode == kZero ? 1.0f : c;  // zero mode: logits are 0, t = s
-  if (splits > 1) {
+  // Items of at most half a key-split tile's rows (a few query rows per K/V
+  // head, as in decoding) run on the key-split kernels also without splits,
+  // as one part that writes O and lse itself: their 128-row tiles leave the
+  // padding waves idle, which the other kernels' tiles compute.  The 16-bit
+  // kernels take that route only once the items fill the compute units (on
+  // fewer workgroups the half-height kernels ran 0-16% faster); the 8-bit
+  // caches always (10-49% faster).
+  const int64_t sbr = d == 64 ? kSplitRows<64> : d == 128 ? kSplitRows<128> : kSplitRows<256>;
+  bool one_part = splits == 1 && rows * 2 <= sbr;
+  if (one_part && !q8) {
+    const int n_cu = cu_count();
+    one_part = n_cu > 0 && B * Hkv * ((rows + sbr - 1) / sbr) >= n_cu;
+  }
+  if (splits > 1 || one_part) {
     // Key splits: the split kernel over items x splits workgroups, then the
-    // merge, both on `stream`.
+    // merge, both on `stream` (one part: the split kernel alone).
     SplitProblem SP;
     static_cast<Problem&>(SP) = P;
-    SP.q_tiles = (int)plan.q_tiles;
-    SP.n_groups = (int)(B * Hkv * plan.q_tiles * splits);
+    SP.q_tiles = (int)((rows + sbr - 1) / sbr);
+    SP.n_groups = (int)(B * Hkv * SP.q_tiles * splits);
     SP.part_rows = bh * Nq;
-    SP.part_o = (float*)ws;
-    SP.part_lse = (float*)ws + (int64_t)splits * SP.part_rows * d;
+    SP.part_o = one_part ? nullptr : (float*)ws;
+    SP.part_lse = one_part ? nullptr : (float*)ws + (int64_t)splits * SP.part_rows * d;
     SP.splits = splits;
     const void* sfn = qk == 2 ? (d == 64 ? pick_split_q8<64, 2>(fp16, mode, causal)
                                  : d == 128 ? pick_split_q8<128, 2>(fp16, mode, causal)
@@ -1927,6 +1941,7 @@ int launch(const void* q, const void* k, const void* v, const float* ks, const f
     hipError_t err = hipLaunchKernel(sfn, dim3((unsigned)SP.n_groups),
                                      dim3((unsigned)(snw * 64)), sargs, 0, (hipStream_t)stream);
     if (err != hipSuccess) return FA2_ERR_HIP;
+    if (one_part) return FA2_OK;
     const float* po = SP.part_o;
     const float* pl = SP.part_lse;
     uint16_t* oo = SP.o;

@@ -340,8 +340,12 @@ const char* fa2_strerror(int status);
  * compute unit, each walking several query tiles) hold 256 query rows with 8
  * waves at d = 64 (non-causal) and d = 128 (also causal, tiles taken in
  * pairs of equal total cost).  At d = 256 each wave holds 16 query rows
- * (16x16x32 matrix instructions), elsewhere 32.  block_q here is always a
- * multiple of the smaller shapes and divides the larger.
+ * (16x16x32 matrix instructions), elsewhere 32.  A call whose K/V heads
+ * have at most 64 query rows each (Hq / Hkv * Nq, as in decoding) runs on
+ * the 128-row tiles of the key-split kernels, as one part: over a quantized
+ * cache always, with 16-bit K/V once B*Hkv is at least the number of
+ * compute units.  block_q here is
+ * always a multiple of the smaller shapes and divides the larger.
  * Host-only, no HIP call.  Returns FA2_OK, FA2_ERR_HEADDIM, FA2_ERR_DTYPE or
  * FA2_ERR_NULL.
  */
