@@ -1901,15 +1901,15 @@ int launch(const void* q, const void* k, const void* v, const float* ks, const f
   P.n_groups = (int)groups;
   P.causal_off = (int)(Nk - Nq);
   P.c = mode == kZero ? 1.0f : c;  // zero mode: logits are 0, t = s
-  // Items of at most half a key-split tile's rows (a few query rows per K/V
+  // Items of at most one key-split tile's rows (a few query rows per K/V
   // head, as in decoding) run on the key-split kernels also without splits,
   // as one part that writes O and lse itself: their 128-row tiles leave the
-  // padding waves idle, which the other kernels' tiles compute.  The 16-bit
+  // padding waves idle, which the other kernels' 256-row tiles compute.  The 16-bit
   // kernels take that route only once the items fill the compute units (on
   // fewer workgroups the half-height kernels ran 0-16% faster); the 8-bit
   // caches always (10-49% faster).
   const int64_t sbr = d == 64 ? kSplitRows<64> : d == 128 ? kSplitRows<128> : kSplitRows<256>;
-  bool one_part = splits == 1 && rows * 2 <= sbr;
+  bool one_part = splits == 1 && rows <= sbr;
   if (one_part && !q8) {
     const int n_cu = cu_count();
     one_part = n_cu > 0 && B * Hkv * ((rows + sbr - 1) / sbr) >= n_cu;

@@ -341,7 +341,7 @@ const char* fa2_strerror(int status);
  * waves at d = 64 (non-causal) and d = 128 (also causal, tiles taken in
  * pairs of equal total cost).  At d = 256 each wave holds 16 query rows
  * (16x16x32 matrix instructions), elsewhere 32.  A call whose K/V heads
- * have at most 64 query rows each (Hq / Hkv * Nq, as in decoding) runs on
+ * have at most 128 query rows each (Hq / Hkv * Nq, as in decoding) runs on
  * the 128-row tiles of the key-split kernels, as one part: over a quantized
  * cache always, with 16-bit K/V once B*Hkv is at least the number of
  * compute units.  block_q here is

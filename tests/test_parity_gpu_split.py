@@ -184,7 +184,7 @@ def test_quantized_cache_decode(fmt, d, dtype, causal, splits):
 @pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("fmt", ["bf16", "int8", "fp8"])
 def test_unsplit_calls_on_few_rows(fmt, d):
-    """Calls without splits whose items hold at most 64 query rows (here 4
+    """Calls without splits whose items hold at most 128 query rows (here 4
     query heads on each K/V head, one row each) run on the key-split
     kernels as one part writing O itself (16-bit inputs once the K/V heads
     number at least the compute units, as here; quantized caches always):
