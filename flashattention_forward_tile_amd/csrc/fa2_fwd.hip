@@ -326,7 +326,8 @@ struct Problem {
 // which write fp32 partials: part_o [splits][part_rows][D] (O of the part's
 // keys, normalised by their own sum) and part_lse [splits][part_rows]
 // (natural log; -inf: no key seen).  part_rows = B * hq * nq, rows indexed
-// as in lse.
+// as in lse.  With part_o null (one part, splits = 1) the kernel writes o and
+// lse itself.
 struct SplitProblem : Problem {
   float* part_o;
   float* part_lse;
