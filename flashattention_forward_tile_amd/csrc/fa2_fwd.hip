@@ -1915,6 +1915,14 @@ int launch(const void* q, const void* k, const void* v, const float* ks, const f
     const int n_cu = cu_count();
     one_part = n_cu > 0 && B * Hkv * ((rows + sbr - 1) / sbr) >= n_cu;
   }
+  // The same tiles are the 8-bit caches' half-height shape: taken also for
+  // longer query blocks when the 256-row grid would leave compute units idle
+  // (as the 16-bit half-height kernels are; 8-26% faster), except at d = 256
+  // (no gain).
+  if (splits == 1 && q8 && !one_part && d != 256) {
+    const int n_cu = cu_count();
+    one_part = n_cu > 0 && groups < n_cu;
+  }
   if (splits > 1 || one_part) {
     // Key splits: the split kernel over items x splits workgroups, then the
     // merge, both on `stream` (one part: the split kernel alone).

@@ -344,7 +344,9 @@ const char* fa2_strerror(int status);
  * have at most 128 query rows each (Hq / Hkv * Nq, as in decoding) runs on
  * the 128-row tiles of the key-split kernels, as one part: over a quantized
  * cache always, with 16-bit K/V once B*Hkv is at least the number of
- * compute units.  block_q here is
+ * compute units.  Over a quantized cache at d = 64 or 128 any call whose
+ * 256-row workgroups would be fewer than the compute units does the same.
+ * block_q here is
  * always a multiple of the smaller shapes and divides the larger.
  * Host-only, no HIP call.  Returns FA2_OK, FA2_ERR_HEADDIM, FA2_ERR_DTYPE or
  * FA2_ERR_NULL.

@@ -58,6 +58,21 @@ def test_int8_cache(B, Hq, Hkv, Nq, Nk, d, dtype, causal):
               B, Hq, Hkv, Nq, Nk, d, dtype, causal))
 
 
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_int8_cache_full_height(d, causal):
+    """Enough K/V heads that the 256-row workgroups fill the compute units
+    (smaller calls at d = 64 and 128 take the 128-row one-part kernels):
+    ragged query and key counts on the full-height path."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    H = cus + 16
+    announce("int8 full height", H, d, causal)
+    inputs = make_inputs_kv_int8(1, H, H, 300, 513, d, "bf16", seed=d + causal)
+    check(inputs, "bf16", 1.0 / math.sqrt(d), causal,
+          "int8 full height H=%d d=%d causal=%d" % (H, d, causal))
+
+
 @pytest.mark.parametrize("scale", [0.0, -0.2, 1.5])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("d", [64, 128, 256])
