@@ -181,39 +181,41 @@ def test_quantized_cache_decode(fmt, d, dtype, causal, splits):
     assert (lse - l1).abs().max().item() <= 1e-3, tag
 
 
+@pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("d", [64, 128, 256])
-@pytest.mark.parametrize("fmt", ["bf16", "int8", "fp8"])
-def test_unsplit_calls_on_few_rows(fmt, d):
+@pytest.mark.parametrize("fmt", ["bf16", "fp16", "int8", "fp8"])
+def test_unsplit_calls_on_few_rows(fmt, d, causal):
     """Calls without splits whose items hold at most 128 query rows (here 4
     query heads on each K/V head, one row each) run on the key-split
     kernels as one part writing O itself (16-bit inputs once the K/V heads
     number at least the compute units, as here; quantized caches always):
     against the oracle, and bit for bit the same through fa2_fwd_split with
     splits = 1."""
-    announce("one part", fmt, d)
+    announce("one part", fmt, d, causal)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    B, Hq, Hkv, Nq, Nk = (cus // 2 + 1, 8, 2, 1, 1500) if fmt == "bf16" else (3, 8, 2, 1, 3000)
+    wide = fmt in ("bf16", "fp16")
+    B, Hq, Hkv, Nq, Nk = (cus // 2 + 1, 8, 2, 1, 1500) if wide else (3, 8, 2, 1, 3000)
     scale = 1.0 / math.sqrt(d)
-    if fmt == "bf16":
-        q, k, v = make_inputs(B, Hq, Nq, d, "bf16", seed=d, Hkv=Hkv, Nk=Nk)
+    if wide:
+        q, k, v = make_inputs(B, Hq, Nq, d, fmt, seed=d + causal, Hkv=Hkv, Nk=Nk)
         qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
-        o, lse = fa2.fwd(qd, kd, vd, causal=True)
+        o, lse = fa2.fwd(qd, kd, vd, causal=causal)
         o1 = torch.full_like(qd, float("nan"))
         l1 = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device=DEV)
-        fa2.fwd_split(qd, kd, vd, causal=True, splits=1, out=o1, lse=l1)
-        o_ref, lse_ref = oracle.attention(bits(q), bits(k), bits(v), "bf16", scale, causal=True)
+        fa2.fwd_split(qd, kd, vd, causal=causal, splits=1, out=o1, lse=l1)
+        o_ref, lse_ref = oracle.attention(bits(q), bits(k), bits(v), fmt, scale, causal=causal)
     else:
         cache, make, attn = QUANTIZED[fmt]
-        q, kq, ks, vq, vs = make(B, Hq, Hkv, Nq, Nk, d, "bf16", seed=d)
+        q, kq, ks, vq, vs = make(B, Hq, Hkv, Nq, Nk, d, "bf16", seed=d + causal)
         dev = [t.to(DEV) for t in (q, kq, ks, vq, vs)]
         unsplit = fa2.fwd_kv_int8 if fmt == "int8" else fa2.fwd_kv_fp8
-        o, lse = unsplit(*dev, causal=True)
+        o, lse = unsplit(*dev, causal=causal)
         o1 = torch.full_like(dev[0], float("nan"))
         l1 = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device=DEV)
-        fa2.fwd_kv_split(*dev, cache, causal=True, splits=1, out=o1, lse=l1)
+        fa2.fwd_kv_split(*dev, cache, causal=causal, splits=1, out=o1, lse=l1)
         o_ref, lse_ref = getattr(oracle, attn)(bits(q), kq.numpy(), ks.numpy(), vq.numpy(),
-                                               vs.numpy(), "bf16", scale, causal=True)
+                                               vs.numpy(), "bf16", scale, causal=causal)
     torch.cuda.synchronize()
     assert torch.equal(o, o1) and torch.equal(lse, l1)
     assert_parity(o.cpu().double().numpy(), lse.cpu().double().numpy(), o_ref, lse_ref,
-                  "one part %s d=%d" % (fmt, d), lse_abs=1e-3)
+                  "one part %s d=%d causal=%d" % (fmt, d, causal), lse_abs=1e-3)
