@@ -219,3 +219,33 @@ def test_unsplit_calls_on_few_rows(fmt, d, causal):
     assert torch.equal(o, o1) and torch.equal(lse, l1)
     assert_parity(o.cpu().double().numpy(), lse.cpu().double().numpy(), o_ref, lse_ref,
                   "one part %s d=%d causal=%d" % (fmt, d, causal), lse_abs=1e-3)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("fmt", ["bf16", "int8", "fp8"])
+def test_one_part_matches_the_other_kernels_bit_for_bit(fmt, d):
+    """The one-part route computes each row exactly as the kernels it
+    replaces: the first batch entries of a call large enough to take one
+    route equal, bit for bit, a call of just those entries, which takes the
+    other (16-bit: one query row per head, routed only once B*Hkv reaches
+    the compute units; 8-bit caches at d = 64 and 128: 200 rows per K/V
+    head, routed only while the 256-row grid is smaller than the compute
+    units)."""
+    if fmt != "bf16" and d == 256:
+        pytest.skip("the 8-bit caches keep one shape at d = 256")
+    announce("one part vs other kernels", fmt, d)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    B, Hq, Hkv, Nk = cus // 2 + 1, 8, 2, 1500
+    Nq = 1 if fmt == "bf16" else 50
+    if fmt == "bf16":
+        q, k, v = (t.to(DEV) for t in make_inputs(B, Hq, Nq, d, "bf16", seed=d, Hkv=Hkv, Nk=Nk))
+        o, lse = fa2.fwd(q, k, v, causal=True)
+        o3, l3 = fa2.fwd(q[:3].contiguous(), k[:3].contiguous(), v[:3].contiguous(), causal=True)
+    else:
+        cache, make, _ = QUANTIZED[fmt]
+        dev = [t.to(DEV) for t in make(B, Hq, Hkv, Nq, Nk, d, "bf16", seed=d)]
+        unsplit = fa2.fwd_kv_int8 if fmt == "int8" else fa2.fwd_kv_fp8
+        o, lse = unsplit(*dev, causal=True)
+        o3, l3 = unsplit(*[t[:3].contiguous() for t in dev], causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o[:3], o3) and torch.equal(lse[:3], l3)
